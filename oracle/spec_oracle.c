@@ -1,0 +1,489 @@
+/*
+ * spec_oracle.c -- plain fp64 CPU oracle of the speculative-sampling verification step.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the CPU-baseline
+ * leg of the benchmark may load or call this library. The GPU library never links,
+ * includes or calls it, and it shares no header, helper, table or constant generator with
+ * the GPU library: everything below is written out here, once, from the pages.
+ *
+ * Sources (page title, then section):
+ *   [KV]   "KV Cache 优化（四）：Speculative Decoding 投机解码"
+ *          §4 acceptance and rejection (eq. a(x), eq. p'(x), the A/B table),
+ *          §5 complete example, §6 KV cache commit and rollback.
+ *   [LI]   "10.6 投机解码：为什么'先猜后验'能加速" (llm_internals)
+ *          §10.6.1 the round in five steps, the losslessness argument, the greedy special case;
+ *          §10.6.2 expected tokens per round; §10.6.3 verify-step shape and cache truncation,
+ *          tree drafts and Table 10-17.
+ *   [GL]   "投机解码" (LLM glossary), section on exact acceptance and the correction
+ *          distribution, incl. its edge cases q=0 and a vanishing residual mass.
+ *   [TR]   "投机推理：小模型搭树，大模型一次验证", sections on the validation pass and on
+ *          walking the accepted path.
+ *
+ * Readings where the pages leave a step open (each is a plain reading, stated once here):
+ *   R1  temperature is applied as softmax(l/T); T = 0 means greedy (one-hot argmax).
+ *   R2  temperature first, then top-p on the tempered law; the same T and top-p for p and q.
+ *   R3  top-p is a value threshold over the logits: t* is the largest logit value whose
+ *       cumulative mass (all tokens with logit >= t*) reaches P; every token with logit
+ *       >= t* is kept (ties included). P = 1 switches the filter off.
+ *   R4  acceptance is the strict test u < a.
+ *   R5  q(d) = 0: a = 1 if p(d) > 0 else 0 (flag Q_ZERO).
+ *   R6  residual mass R <= 0: sample from p itself (flag RESID_FALLBACK).
+ *   R7  sampling is the inverse CDF in ascending token id: the smallest v whose running sum
+ *       exceeds u*W; if rounding leaves none, the largest v with positive weight.
+ *   R8  uniforms: Philox4x32-10, key = (seed low 32, seed high 32), counter = (id, pos,
+ *       purpose, 0), u = (word0 >> 8) * 2^-24. pos is the absolute slot of the token being
+ *       decided: L+k for the test and residual at draft k, L+gamma+1 for the bonus.
+ *   R9  argmax ties go to the lowest token id.
+ *   R10 committed length after a chain round is L + lead_slots + n_acc.
+ *   R11 tree walk: greedy, lowest node index among matching siblings; the extra token is
+ *       the argmax at the stopping node and is emitted only if that node has a row.
+ *   R12 tree KV commit copies, in depth order, slot base+path[j] to slot base+j,
+ *       base = L + lead_slots - 1, for every layer, K and V, and head.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Sequence flag bits reported by the oracle (same meaning as the library's, defined here
+ * independently). */
+#define OF_BAD_TOKEN 1
+#define OF_Q_ZERO 2
+#define OF_RESID_FALLBACK 4
+#define OF_NO_ROW 8
+#define OF_SLOT_OOB 16
+#define OF_BAD_TREE 32
+#define OF_BAD_PARAM 128
+
+#define PURPOSE_ACCEPT 0u
+#define PURPOSE_RESIDUAL 1u
+#define PURPOSE_BONUS 2u
+
+/* ------------------------------------------------------------------------------------ */
+/* Philox4x32-10: J. Salmon, M. Moraes, R. Dror, D. Shaw, "Parallel random numbers: as easy */
+/* as 1, 2, 3", SC'11. Ten rounds of the 4x32 Philox S-box with the Weyl key schedule.      */
+/* ------------------------------------------------------------------------------------ */
+void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u; /* round multipliers */
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u; /* key increments    */
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    uint64_t prod0 = (uint64_t)M0 * (uint64_t)c0;
+    uint64_t prod1 = (uint64_t)M1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+    uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += W0;
+    k1 += W1;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Reading R8. */
+double oracle_uniform(uint64_t seed, uint32_t id, uint32_t pos, uint32_t purpose) {
+  uint32_t ctr[4] = {id, pos, purpose, 0u};
+  uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  return (double)(out[0] >> 8) * (1.0 / 16777216.0);
+}
+
+/* bf16 bit pattern -> double, exactly (bf16 is the top half of an IEEE binary32). */
+double oracle_bf16_to_double(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* The per-row law: temperature softmax and top-p ([KV] §4: the law actually sampled,      */
+/* after temperature and top-k/top-p, is the one the acceptance rule must use; [LI] §10.6.1 */
+/* greedy special case). Readings R1-R3, R9.                                               */
+/* ------------------------------------------------------------------------------------ */
+typedef struct {
+  int argmax;          /* lowest token id holding the maximum logit            */
+  int nucleus;         /* |S|                                                  */
+  double m;            /* maximum logit                                        */
+  double tstar;        /* nucleus threshold logit; -inf when top-p is off      */
+  double z;            /* sum over all tokens of exp((l-m)/T)                  */
+  double zs;           /* the same sum over S                                  */
+  double topp_margin;  /* min(|mass(S)-P|, |mass(S minus lowest group)-P|)     */
+} orow_t;
+
+static int cmp_desc(const void* a, const void* b) {
+  double x = *(const double*)a, y = *(const double*)b;
+  return (x < y) - (x > y);
+}
+
+/* Fills pi[0..V) with the filtered, normalised law of one bf16 logits row.
+ * scratch must hold V doubles. Returns 0, or -1 if the row has no finite maximum. */
+int oracle_dist(const uint16_t* row, int V, double T, double P, double* pi, double* scratch,
+                orow_t* info) {
+  double m = -INFINITY;
+  int am = 0;
+  for (int v = 0; v < V; ++v) {
+    double l = oracle_bf16_to_double(row[v]);
+    if (l > m) { m = l; am = v; }
+  }
+  info->argmax = am;
+  info->m = m;
+  info->tstar = -INFINITY;
+  info->topp_margin = INFINITY;
+  if (!(m > -INFINITY) || isinf(m) || isnan(m)) return -1;
+  if (T == 0.0) { /* greedy: the target law is one-hot at the argmax */
+    for (int v = 0; v < V; ++v) pi[v] = 0.0;
+    pi[am] = 1.0;
+    info->nucleus = 1;
+    info->z = info->zs = 1.0;
+    return 0;
+  }
+  double z = 0.0;
+  for (int v = 0; v < V; ++v) {
+    pi[v] = exp((oracle_bf16_to_double(row[v]) - m) / T);
+    z += pi[v];
+  }
+  info->z = z;
+  double tstar = -INFINITY;
+  if (P < 1.0) {
+    /* Walk the distinct logit values from the largest down; the first value at which the
+     * mass of all tokens at or above it reaches P is the threshold. */
+    for (int v = 0; v < V; ++v) scratch[v] = oracle_bf16_to_double(row[v]);
+    qsort(scratch, (size_t)V, sizeof(double), cmp_desc);
+    double cum = 0.0, above = 0.0;
+    for (int i = 0; i < V; ++i) {
+      cum += exp((scratch[i] - m) / T);
+      int group_end = (i + 1 == V) || (scratch[i + 1] != scratch[i]);
+      if (!group_end) continue;
+      if (cum / z >= P) {
+        tstar = scratch[i];
+        double d1 = fabs(cum / z - P), d2 = fabs(above / z - P);
+        info->topp_margin = d1 < d2 ? d1 : d2;
+        break;
+      }
+      above = cum;
+    }
+    if (tstar == -INFINITY) { /* rounding kept the total just below P: keep everything */
+      tstar = scratch[V - 1];
+      info->topp_margin = 0.0;
+    }
+  }
+  info->tstar = tstar;
+  double zs = 0.0;
+  int count = 0;
+  for (int v = 0; v < V; ++v) {
+    if (oracle_bf16_to_double(row[v]) >= tstar) { zs += pi[v]; ++count; }
+    else pi[v] = 0.0;
+  }
+  info->zs = zs;
+  info->nucleus = count;
+  for (int v = 0; v < V; ++v) pi[v] /= zs;
+  return 0;
+}
+
+/* Inverse-CDF draw from non-negative weights (reading R7). *margin receives the distance of
+ * u*W from the nearer of the two cumulative sums that bracket the chosen token, in the
+ * weights' own units. */
+int oracle_sample(const double* w, int V, double u, double* margin) {
+  double W = 0.0;
+  for (int v = 0; v < V; ++v) W += w[v];
+  double x = u * W, c = 0.0;
+  for (int v = 0; v < V; ++v) {
+    double prev = c;
+    c += w[v];
+    if (c > x) {
+      double a = x - prev, b = c - x;
+      if (margin) *margin = a < b ? a : b;
+      return v;
+    }
+  }
+  if (margin) *margin = 0.0;
+  for (int v = V - 1; v >= 0; --v)
+    if (w[v] > 0.0) return v;
+  return 0;
+}
+
+/* One verified position on probability vectors ([KV] §4 eq. a(x) and eq. p'(x); [LI]
+ * §10.6.1 steps 3-4; [GL] exact acceptance and its q=0 / vanishing-residual cases).
+ * Returns 1 if the draft token d is accepted, else 0 with *token set to the residual draw.
+ * info[0] = a, info[1] = R (NaN when accepted), info[2] = the drawn token's probability
+ * under the residual law (NaN when accepted), info[3] = smallest decision margin. */
+int oracle_position_step(const double* p, const double* q, int V, int d, double u_acc,
+                         double u_res, int* token, int* flags, double* r_scratch,
+                         double info[4]) {
+  double pd = p[d], qd = q[d], a;
+  if (qd > 0.0) a = fmin(1.0, pd / qd);
+  else { a = pd > 0.0 ? 1.0 : 0.0; *flags |= OF_Q_ZERO; }
+  info[0] = a;
+  info[3] = fabs(u_acc - a);
+  if (u_acc < a) { info[1] = NAN; info[2] = NAN; return 1; }
+  double R = 0.0;
+  for (int v = 0; v < V; ++v) {
+    double r = p[v] - q[v];
+    r_scratch[v] = r > 0.0 ? r : 0.0;
+    R += r_scratch[v];
+  }
+  double sm;
+  int y;
+  if (R > 0.0) {
+    y = oracle_sample(r_scratch, V, u_res, &sm);
+    info[2] = r_scratch[y] / R;
+  } else {
+    *flags |= OF_RESID_FALLBACK;
+    y = oracle_sample(p, V, u_res, &sm);
+    info[2] = p[y];
+  }
+  info[1] = R;
+  if (sm < info[3]) info[3] = sm;
+  *token = y;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Chain verification over a ragged batch ([LI] §10.6.1 steps 1-5; [KV] §5 and §6;        */
+/* [LI] §10.6.3 verify shape logits[B, gamma+1, n_vocab] and per-request start points).    */
+/* Row layout: target row of (b,k), k=1..gamma_b+1, is cu_gamma[b]+b+k-1; draft row of     */
+/* (b,k), k=1..gamma_b, is cu_gamma[b]+k-1.                                                */
+/* ------------------------------------------------------------------------------------ */
+int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
+                        const uint16_t* draft, const int32_t* cu_gamma,
+                        const int32_t* draft_tokens, const float* temperature,
+                        const float* top_p, const uint32_t* seq_id,
+                        const int32_t* committed_len_in, int lead_slots, uint64_t seed,
+                        const float* uniform_override, int32_t* out_tokens,
+                        int32_t* num_accepted, int32_t* committed_len_out, int32_t* seq_flags,
+                        double* probe_rows, double* probe_seq, double* margin_out,
+                        int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    double* q = (double*)malloc(sizeof(double) * (size_t)V);
+    double* r = (double*)malloc(sizeof(double) * (size_t)V);
+    double* scratch = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!p || !q || !r || !scratch) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+      if (failed) continue;
+      const int g = cu_gamma[b + 1] - cu_gamma[b];
+      const int trow0 = cu_gamma[b] + b, drow0 = cu_gamma[b];
+      const int L = committed_len_in[b];
+      const uint32_t id = seq_id ? seq_id[b] : (uint32_t)b;
+      const double T = (double)temperature[b];
+      const double P = top_p ? (double)top_p[b] : 1.0;
+      int flags = 0, n_acc = 0, y = -1;
+      double margin = INFINITY, R_out = NAN, py_out = NAN;
+      for (int k = 0; k < g; ++k) {
+        double* pr = probe_rows ? probe_rows + 3 * (size_t)(drow0 + k) : NULL;
+        if (pr) pr[0] = pr[1] = pr[2] = NAN;
+      }
+      int bad = 0;
+      for (int k = 0; k < g; ++k) {
+        int d = draft_tokens[drow0 + k];
+        if (d < 0 || d >= V) bad = 1;
+      }
+      if (bad) flags |= OF_BAD_TOKEN;
+      if (!(T >= 0.0) || !(P > 0.0 && P <= 1.0) || (T > 0.0 && g > 0 && !draft)) {
+        flags |= OF_BAD_PARAM;
+        bad = 1;
+      }
+      if (bad) {
+        num_accepted[b] = 0;
+        committed_len_out[b] = L;
+        if (seq_flags) seq_flags[b] = flags;
+        if (probe_seq) { probe_seq[2 * b] = NAN; probe_seq[2 * b + 1] = NAN; }
+        if (margin_out) margin_out[b] = INFINITY;
+        continue;
+      }
+      orow_t ip, iq;
+      int stopped = 0;
+      for (int k = 1; k <= g && !stopped; ++k) {
+        const uint16_t* trow = target + (size_t)(trow0 + k - 1) * row_stride;
+        const int d = draft_tokens[drow0 + k - 1];
+        double* pr = probe_rows ? probe_rows + 3 * (size_t)(drow0 + k - 1) : NULL;
+        const size_t ovr = (size_t)(trow0 + k - 1) * 2;
+        if (T == 0.0) {
+          /* Greedy: accept iff the draft token is the target argmax; at the first mismatch
+           * the target's argmax is emitted ([LI] §10.6.1 greedy special case; [KV] §4). */
+          oracle_dist(trow, V, 0.0, 1.0, p, scratch, &ip);
+          int acc = (d == ip.argmax);
+          if (pr) { pr[0] = acc ? 1.0 : 0.0; pr[1] = NAN; pr[2] = acc ? 1.0 : 0.0; }
+          if (acc) { n_acc = k; continue; }
+          y = ip.argmax;
+          py_out = 1.0;
+          stopped = 1;
+          break;
+        }
+        const uint16_t* drow = draft + (size_t)(drow0 + k - 1) * row_stride;
+        oracle_dist(trow, V, T, P, p, scratch, &ip);
+        oracle_dist(drow, V, T, P, q, scratch, &iq);
+        if (ip.topp_margin < margin) margin = ip.topp_margin;
+        if (iq.topp_margin < margin) margin = iq.topp_margin;
+        double u_acc = uniform_override ? (double)uniform_override[ovr]
+                                        : oracle_uniform(seed, id, (uint32_t)(L + k), PURPOSE_ACCEPT);
+        double u_res = uniform_override ? (double)uniform_override[ovr + 1]
+                                        : oracle_uniform(seed, id, (uint32_t)(L + k), PURPOSE_RESIDUAL);
+        double info[4];
+        int tok = -1;
+        int acc = oracle_position_step(p, q, V, d, u_acc, u_res, &tok, &flags, r, info);
+        if (pr) { pr[0] = p[d]; pr[1] = q[d]; pr[2] = info[0]; }
+        if (info[3] < margin) margin = info[3];
+        if (acc) { n_acc = k; continue; }
+        y = tok;
+        R_out = info[1];
+        py_out = info[2];
+        stopped = 1;
+      }
+      if (!stopped) {
+        /* Every draft accepted: one more token from p_{gamma+1} ([LI] §10.6.1 step 5;
+         * [KV] §5 bonus token). */
+        const uint16_t* trow = target + (size_t)(trow0 + g) * row_stride;
+        const size_t ovr = (size_t)(trow0 + g) * 2;
+        if (T == 0.0) {
+          oracle_dist(trow, V, 0.0, 1.0, p, scratch, &ip);
+          y = ip.argmax;
+          py_out = 1.0;
+        } else {
+          oracle_dist(trow, V, T, P, p, scratch, &ip);
+          if (ip.topp_margin < margin) margin = ip.topp_margin;
+          double u = uniform_override ? (double)uniform_override[ovr + 1]
+                                      : oracle_uniform(seed, id, (uint32_t)(L + g + 1), PURPOSE_BONUS);
+          double sm;
+          y = oracle_sample(p, V, u, &sm);
+          if (sm < margin) margin = sm;
+          py_out = p[y];
+        }
+        n_acc = g;
+      }
+      for (int k = 0; k < n_acc; ++k) out_tokens[trow0 + k] = draft_tokens[drow0 + k];
+      out_tokens[trow0 + n_acc] = y;
+      num_accepted[b] = n_acc;
+      committed_len_out[b] = L + lead_slots + n_acc; /* reading R10 ([KV] §6 pointer) */
+      if (seq_flags) seq_flags[b] = flags;
+      if (probe_seq) { probe_seq[2 * b] = R_out; probe_seq[2 * b + 1] = py_out; }
+      if (margin_out) margin_out[b] = margin;
+    }
+    free(p); free(q); free(r); free(scratch);
+  }
+  return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Greedy tree verification ([TR] validation and path walk; [LI] §10.6.3 tree drafts).     */
+/* Reading R11. parent/node_row are [num_nodes] per sequence (tree_stride elements apart,  */
+/* 0 = one topology for the batch); node_token is [B][num_nodes]; rows are                  */
+/* [B][rows_per_seq][row_stride].                                                          */
+/* ------------------------------------------------------------------------------------ */
+int oracle_verify_tree(int B, int V, int row_stride, int rows_per_seq, int num_nodes,
+                       int max_depth, int tree_stride, const uint16_t* logits,
+                       const int32_t* parent, const int32_t* node_row,
+                       const int32_t* node_token, int32_t* path_nodes, int32_t* path_len,
+                       int32_t* out_tokens, int32_t* num_emitted, int32_t* seq_flags,
+                       int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b) {
+    const int32_t* par = parent + (size_t)b * tree_stride;
+    const int32_t* nrow = node_row + (size_t)b * tree_stride;
+    const int32_t* tok = node_token + (size_t)b * num_nodes;
+    int flags = 0, ok = (par[0] == -1);
+    for (int i = 1; i < num_nodes; ++i)
+      if (par[i] < 0 || par[i] >= i) ok = 0;
+    for (int i = 0; i < num_nodes; ++i)
+      if (nrow[i] < -1 || nrow[i] >= rows_per_seq) ok = 0;
+    for (int j = 0; j < max_depth; ++j) path_nodes[(size_t)b * max_depth + j] = -1;
+    if (!ok) {
+      path_len[b] = 0;
+      num_emitted[b] = 0;
+      if (seq_flags) seq_flags[b] = OF_BAD_TREE;
+      continue;
+    }
+    int v = 0, D = 0, extra = -1;
+    for (;;) {
+      if (nrow[v] < 0) { flags |= OF_NO_ROW; break; }
+      const uint16_t* row = logits + ((size_t)b * rows_per_seq + nrow[v]) * row_stride;
+      int am = 0;
+      double best = -INFINITY;
+      for (int t = 0; t < V; ++t) {
+        double l = oracle_bf16_to_double(row[t]);
+        if (l > best) { best = l; am = t; }
+      }
+      int child = -1;
+      if (D < max_depth)
+        for (int i = v + 1; i < num_nodes; ++i)
+          if (par[i] == v && tok[i] == am) { child = i; break; }
+      if (child < 0) { extra = am; break; }
+      path_nodes[(size_t)b * max_depth + D] = child;
+      out_tokens[(size_t)b * (max_depth + 1) + D] = tok[child];
+      ++D;
+      v = child;
+    }
+    path_len[b] = D;
+    if (extra >= 0) out_tokens[(size_t)b * (max_depth + 1) + D] = extra;
+    num_emitted[b] = D + (extra >= 0 ? 1 : 0);
+    if (seq_flags) seq_flags[b] = flags;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* KV commit of an accepted path ([KV] §6: reserved slots and one committed-length pointer, */
+/* the same boundary in every layer; [LI] §10.6.3 cache truncation after a rejection).     */
+/* Reading R12. Caches are host arrays of uint16 (bf16 bits); layer l's K cache starts at  */
+/* k_cache[l]. Element (b, slot, head, e) sits at b*seq_stride + slot*slot_stride +        */
+/* head*head_stride + e.                                                                   */
+/* ------------------------------------------------------------------------------------ */
+int oracle_kv_commit(int B, int num_layers, int num_kv_heads, int head_dim,
+                     uint16_t* const* k_cache, uint16_t* const* v_cache, int64_t seq_stride,
+                     int64_t slot_stride, int64_t head_stride, int slot_capacity,
+                     int lead_slots, int max_depth, const int32_t* path_nodes,
+                     const int32_t* path_len, int32_t* committed_len, int32_t* seq_flags) {
+  for (int b = 0; b < B; ++b) {
+    const int L = committed_len[b], D = path_len[b];
+    const int base = L + lead_slots - 1;
+    int ok = (D >= 0 && D <= max_depth);
+    for (int j = 0; ok && j < D; ++j) {
+      int node = path_nodes[(size_t)b * max_depth + j];
+      if (node < 1 || base + node >= slot_capacity || base + j + 1 >= slot_capacity) ok = 0;
+    }
+    if (!ok || base + D + 1 > slot_capacity || base < -1) {
+      if (seq_flags) seq_flags[b] |= OF_SLOT_OOB;
+      continue;
+    }
+    for (int j = 1; j <= D; ++j) {
+      const int src = base + path_nodes[(size_t)b * max_depth + j - 1], dst = base + j;
+      if (src == dst) continue;
+      for (int l = 0; l < num_layers; ++l)
+        for (int kv = 0; kv < 2; ++kv) {
+          uint16_t* c = kv ? v_cache[l] : k_cache[l];
+          for (int h = 0; h < num_kv_heads; ++h)
+            memmove(c + b * seq_stride + (int64_t)dst * slot_stride + h * head_stride,
+                    c + b * seq_stride + (int64_t)src * slot_stride + h * head_stride,
+                    sizeof(uint16_t) * (size_t)head_dim);
+        }
+    }
+    committed_len[b] = L + lead_slots + D;
+  }
+  return 0;
+}
