@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the verification step on one MI355X.
+
+A step is one spec_verify_chain call (row pass + resolve: temperature/top-p laws, acceptance
+test, first rejection, residual/bonus draw, committed-length pointer) over the chain
+workload B=256, gamma=8, V=128256, T=0.7, top-p 0.9 with its inputs resident in HBM.
+Prints one JSON line with verify rows/s (rows = (sequence, position) target rows,
+sum(gamma_b+1) per call), the row-pass kernel's achieved HBM bandwidth against 8 TB/s
+(timed live with HIP events on the launch stream), and the fp64 CPU oracle timed on a
+bounded sample of the same workload as a reported baseline.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # a plain copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "verify rows/sec at B=256 γ=8 V=128k; achieved HBM GB/s vs peak"
+SEED = 2024
+SEED_DRAFT = 9090
+ROW_KERNEL = "chain_row_kernel"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "chain_row_kernel_c3.md")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_verification_03_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(x) -> dict:
+    """Bytes the verification must move at least once, per call: each logits row read once
+    (draft positions: the p row and the q row; bonus positions: the p row), the draft tokens,
+    and the outputs (tokens, accepted counts, committed lengths)."""
+    import numpy as np
+    cu = x["cu_gamma"]
+    B = len(cu) - 1
+    nd = int(cu[-1])
+    V = x["vocab"]
+    logits = (2 * nd + B) * V * 2
+    tokens_in = nd * 4
+    outputs = (nd + B) * 4 + B * 4 * 2
+    return dict(logits=logits, tokens=tokens_in, outputs=outputs,
+                row_pass=logits + tokens_in, call=logits + tokens_in + outputs,
+                rows=int(np.sum(np.diff(cu) + 1)))
+
+
+def read_traffic(src_hash):
+    """HBM traffic per row-pass launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None
+    text = open(PROFILE_SUMMARY).read()
+    m = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    t = re.search(r"traffic per launch \(bytes\):\s*([0-9.e+]+)", text)
+    if not m or not t or m.group(1) != src_hash:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(x, n_seq):
+    """The fp64 oracle as it is, on the first n_seq sequences of the same workload."""
+    import numpy as np
+    import oracle
+    cu = x["cu_gamma"][:n_seq + 1]
+    nd = int(cu[-1])
+    sub = dict(x)
+    sub.update(target=x["target"][:nd + n_seq], draft=x["draft"][:nd], cu_gamma=cu,
+               temperature=x["temperature"][:n_seq],
+               top_p=None if x["top_p"] is None else x["top_p"][:n_seq],
+               seq_id=x["seq_id"][:n_seq], committed_len=x["committed_len"][:n_seq])
+    b_of = np.repeat(np.arange(n_seq), np.diff(cu))
+    tok = oracle.draw_tokens(sub["draft"], sub["temperature"][b_of],
+                             None if sub["top_p"] is None else sub["top_p"][b_of], SEED_DRAFT,
+                             sub["seq_id"][b_of], sub["committed_len"][b_of] + np.arange(nd) - cu[b_of],
+                             vocab=x["vocab"])
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.verify_chain_v(sub["target"], sub["draft"], cu, tok, sub["temperature"], sub["top_p"],
+                          sub["seq_id"], sub["committed_len"], seed=SEED, vocab=x["vocab"],
+                          nthreads=threads)
+    dt = time.perf_counter() - t0
+    rows = nd + n_seq
+    return dict(value=rows / dt, unit="verify rows/s", cores=threads, kind="oracle",
+                sample=f"first {n_seq} of 256 sequences ({rows} verify rows), "
+                       f"{dt:.2f} s wall, draft tokens drawn beforehand")
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
+              "this build (batch sharding is independent per GPU); run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from draft_verification_03_amd import binding as B
+    from draft_verification_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("generating the c3 workload (B=256, gamma=8, V=128256, T=0.7, top-p 0.9)")
+    x = W.chain_inputs("c3")
+    cu = x["cu_gamma"]
+    Bn, nd, V = len(cu) - 1, int(cu[-1]), x["vocab"]
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
+        {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}.get(a.dtype, a.dtype))).cuda()
+    tgt, drf = dv(x["target"]), dv(x["draft"])
+    temp, topp, sid, cu_d = dv(x["temperature"]), dv(x["top_p"]), dv(x["seq_id"]), dv(cu)
+    L0 = dv(x["committed_len"])
+
+    # The drafter's tokens: one gamma = 0 round per draft row through the same library.
+    log("drawing draft tokens (gamma = 0 rounds over the draft rows)")
+    b_of = np.repeat(np.arange(Bn), np.diff(cu))
+    k_of = np.arange(nd) - cu[b_of]
+    d_out = torch.empty(nd, dtype=torch.int32, device="cuda")
+    da = B.chain_args(target_logits=drf, cu_gamma=dv(np.zeros(nd + 1, np.int32)),
+                      temperature=dv(x["temperature"][b_of]), top_p=dv(x["top_p"][b_of]),
+                      seq_id=dv(x["seq_id"][b_of]),
+                      committed_len=dv((x["committed_len"][b_of] + k_of).astype(np.int32)),
+                      out_tokens=d_out, num_accepted=torch.empty(nd, dtype=torch.int32,
+                                                                 device="cuda"),
+                      seed=SEED_DRAFT, vocab=V, max_gamma=0, total_draft_rows=0,
+                      row_stride=x["stride"])
+    B.spec_verify_chain(da)
+    torch.cuda.synchronize()
+    toks = d_out
+
+    L = L0.clone()
+    out = torch.empty(nd + Bn, dtype=torch.int32, device="cuda")
+    nacc = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    flags = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    ev = B.EventPair()
+    a = B.chain_args(target_logits=tgt, draft_logits=drf, cu_gamma=cu_d, draft_tokens=toks,
+                     temperature=temp, top_p=topp, seq_id=sid, committed_len=L,
+                     out_tokens=out, num_accepted=nacc, seq_flags=flags, seed=SEED, vocab=V,
+                     max_gamma=int(np.diff(cu).max()), total_draft_rows=nd,
+                     row_stride=x["stride"], profile_events=ev.ptr)
+    ws = torch.empty(B.spec_verify_chain_workspace_size(Bn, nd, V), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        B.spec_verify_chain(a, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    row_ms = []
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        B.spec_verify_chain(a, workspace=ws)
+        # events of this step's row pass; reading them synchronises the step's row pass only
+        row_ms.append(ev.elapsed_ms())
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # The per-step event read above waits for each row pass; time the steps again back to
+    # back for the headline number, with no host wait inside the timed region.
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        B.spec_verify_chain(a, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    ab = algorithmic_bytes(x)
+    rows = ab["rows"]
+    value = rows / (ms_step / 1e3)
+    row_avg_ms = float(np.mean(row_ms))
+    achieved = ab["row_pass"] / (row_avg_ms / 1e3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash)
+    fl = flags.cpu().numpy()
+    log(f"step {ms_step * 1e3:.1f} us, row pass {row_avg_ms * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s), accepted/seq {nacc.float().mean().item():.3f}, "
+        f"top-p multi-pass sequences {int(((fl & B.FLAG_TOPP_SLOW) != 0).sum())}")
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verify rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "chain verify B=256 gamma=8 V=128256 bf16 logits, target "
+                               "N(0,3^2) with 1% of ids +8, draft = target + N(0,1^2), T=0.7, "
+                               "top-p 0.9 on p and q",
+                   "batch": Bn, "gamma": int(np.diff(cu).max()), "vocab": V,
+                   "verify_rows_per_call": rows, "call_algorithmic_bytes": ab["call"],
+                   "call_hbm_gbs": ab["call"] / (ms_step / 1e3) / 1e9},
+        "roofline": {"bound": "hbm", "kernel": ROW_KERNEL, "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic, "bytes_per_launch": ab["row_pass"],
+                     "avg_launch_us": row_avg_ms * 1e3, "kernel_source_hash": src_hash},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on the first {args.cpu_sample_seqs} sequences")
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,294 @@
+"""Thin ctypes binding of libspecv.so (include/spec_verify.h).
+
+Argument marshalling only: every step of the verification runs in the library's gfx950
+kernels. PyTorch supplies device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``). The library must have been built
+(``draft_verification_03_amd.build``); loading fails loudly if it is missing -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+SPEC_OK = 0
+SPEC_ERR_INVALID_ARG = -1
+SPEC_ERR_UNSUPPORTED = -2
+SPEC_ERR_HIP = -3
+SPEC_ERR_WORKSPACE = -4
+
+FLAG_BAD_TOKEN, FLAG_Q_ZERO, FLAG_RESID_FALLBACK, FLAG_NO_ROW = 1, 2, 4, 8
+FLAG_SLOT_OOB, FLAG_BAD_TREE, FLAG_TOPP_SLOW, FLAG_BAD_PARAM = 16, 32, 64, 128
+
+
+class spec_chain_args(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("vocab", _I32), ("row_stride", _I32), ("max_gamma", _I32),
+        ("total_draft_rows", _I32), ("lead_slots", _I32), ("seed", ctypes.c_uint64),
+        ("target_logits", _P), ("draft_logits", _P), ("cu_gamma", _P), ("draft_tokens", _P),
+        ("temperature", _P), ("top_p", _P), ("top_k", _P), ("seq_id", _P),
+        ("committed_len", _P), ("out_tokens", _P), ("num_accepted", _P), ("seq_flags", _P),
+        ("probe_rows", _P), ("probe_seq", _P), ("uniform_override", _P),
+        ("profile_events", _P),
+    ]
+
+
+class spec_tree_args(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("vocab", _I32), ("row_stride", _I32), ("num_nodes", _I32),
+        ("rows_per_seq", _I32), ("max_depth", _I32), ("tree_stride", _I32),
+        ("target_logits", _P), ("parent", _P), ("node_row", _P), ("node_token", _P),
+        ("path_nodes", _P), ("path_len", _P), ("out_tokens", _P), ("num_emitted", _P),
+        ("seq_flags", _P),
+    ]
+
+
+class spec_kv_args(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("num_layers", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
+        ("seq_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64), ("slot_capacity", _I32), ("lead_slots", _I32),
+        ("max_depth", _I32), ("k_cache", _P), ("v_cache", _P), ("path_nodes", _P),
+        ("path_len", _P), ("committed_len", _P), ("seq_flags", _P),
+    ]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libspecv error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """The loaded library. Raises if libspecv.so has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"{_build.LIB} is missing: build it with "
+                               "`python -m draft_verification_03_amd.build` (no fallback path)")
+        L = ctypes.CDLL(_build.LIB)
+        L.spec_abi_version.restype = ctypes.c_int
+        L.spec_last_error.restype = ctypes.c_char_p
+        L.spec_verify_chain_workspace_size.argtypes = [_I32, _I32, _I32]
+        L.spec_verify_chain_workspace_size.restype = ctypes.c_size_t
+        L.spec_verify_chain.argtypes = [ctypes.POINTER(spec_chain_args), _P, ctypes.c_size_t, _P]
+        L.spec_verify_chain.restype = ctypes.c_int
+        L.spec_verify_tree_workspace_size.argtypes = [_I32, _I32]
+        L.spec_verify_tree_workspace_size.restype = ctypes.c_size_t
+        L.spec_verify_tree.argtypes = [ctypes.POINTER(spec_tree_args), _P, ctypes.c_size_t, _P]
+        L.spec_verify_tree.restype = ctypes.c_int
+        L.kv_commit_path.argtypes = [ctypes.POINTER(spec_kv_args), _P]
+        L.kv_commit_path.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def spec_abi_version() -> int:
+    return lib().spec_abi_version()
+
+
+def spec_last_error() -> str:
+    return lib().spec_last_error().decode()
+
+
+def spec_verify_chain_workspace_size(batch, total_draft_rows, vocab) -> int:
+    return lib().spec_verify_chain_workspace_size(batch, total_draft_rows, vocab)
+
+
+def spec_verify_tree_workspace_size(batch, rows_per_seq) -> int:
+    return lib().spec_verify_tree_workspace_size(batch, rows_per_seq)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(rc):
+    if rc != SPEC_OK:
+        raise SpecError(rc, spec_last_error())
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def chain_args(*, target_logits, cu_gamma, temperature, committed_len, out_tokens,
+               num_accepted, vocab, max_gamma, total_draft_rows, draft_logits=None,
+               draft_tokens=None, top_p=None, seq_id=None, seq_flags=None, probe_rows=None,
+               probe_seq=None, uniform_override=None, seed=0, lead_slots=1, row_stride=None,
+               profile_events=None, top_k=None):
+    """Fills a spec_chain_args from tensors (device) or raw pointers."""
+    B = int(cu_gamma.shape[0]) - 1 if hasattr(cu_gamma, "shape") else None
+    a = spec_chain_args()
+    a.batch = B
+    a.vocab = int(vocab)
+    a.row_stride = int(row_stride if row_stride is not None else target_logits.shape[-1])
+    a.max_gamma = int(max_gamma)
+    a.total_draft_rows = int(total_draft_rows)
+    a.lead_slots = int(lead_slots)
+    a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    a.target_logits = _ptr(target_logits)
+    a.draft_logits = _ptr(draft_logits)
+    a.cu_gamma = _ptr(cu_gamma)
+    a.draft_tokens = _ptr(draft_tokens)
+    a.temperature = _ptr(temperature)
+    a.top_p = _ptr(top_p)
+    a.top_k = _ptr(top_k)
+    a.seq_id = _ptr(seq_id)
+    a.committed_len = _ptr(committed_len)
+    a.out_tokens = _ptr(out_tokens)
+    a.num_accepted = _ptr(num_accepted)
+    a.seq_flags = _ptr(seq_flags)
+    a.probe_rows = _ptr(probe_rows)
+    a.probe_seq = _ptr(probe_seq)
+    a.uniform_override = _ptr(uniform_override)
+    a.profile_events = profile_events
+    return a
+
+
+def spec_verify_chain(args: spec_chain_args, workspace=None, stream=None, device=None):
+    """Enqueues chain verification (see spec_verify.h). ``workspace`` is a uint8 device
+    tensor (allocated here when None). Returns the workspace tensor for reuse."""
+    need = spec_verify_chain_workspace_size(max(args.batch, 0), max(args.total_draft_rows, 0),
+                                            max(args.vocab, 1))
+    if workspace is None and args.batch > 0 and need > 0:
+        workspace = _workspace(need, device or torch.device("cuda"))
+    ws = _ptr(workspace)
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(lib().spec_verify_chain(ctypes.byref(args), ws, nbytes, _stream(stream)))
+    return workspace
+
+
+def tree_args(*, target_logits, parent, node_row, node_token, path_nodes, path_len,
+              out_tokens, num_emitted, vocab, rows_per_seq, max_depth, tree_stride,
+              seq_flags=None, row_stride=None):
+    a = spec_tree_args()
+    a.batch = int(node_token.shape[0])
+    a.vocab = int(vocab)
+    a.row_stride = int(row_stride if row_stride is not None else target_logits.shape[-1])
+    a.num_nodes = int(node_token.shape[1])
+    a.rows_per_seq = int(rows_per_seq)
+    a.max_depth = int(max_depth)
+    a.tree_stride = int(tree_stride)
+    a.target_logits = _ptr(target_logits)
+    a.parent = _ptr(parent)
+    a.node_row = _ptr(node_row)
+    a.node_token = _ptr(node_token)
+    a.path_nodes = _ptr(path_nodes)
+    a.path_len = _ptr(path_len)
+    a.out_tokens = _ptr(out_tokens)
+    a.num_emitted = _ptr(num_emitted)
+    a.seq_flags = _ptr(seq_flags)
+    return a
+
+
+def spec_verify_tree(args: spec_tree_args, workspace=None, stream=None, device=None):
+    need = spec_verify_tree_workspace_size(max(args.batch, 0), max(args.rows_per_seq, 1))
+    if workspace is None and args.batch > 0 and need > 0:
+        workspace = _workspace(need, device or torch.device("cuda"))
+    ws = _ptr(workspace)
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(lib().spec_verify_tree(ctypes.byref(args), ws, nbytes, _stream(stream)))
+    return workspace
+
+
+def kv_args(*, k_cache, v_cache, path_nodes, path_len, committed_len, num_kv_heads, head_dim,
+            seq_stride, slot_stride, head_stride, slot_capacity, lead_slots, max_depth,
+            seq_flags=None):
+    """k_cache / v_cache: lists of device tensors (one per layer) or raw pointers."""
+    nl = len(k_cache)
+    a = spec_kv_args()
+    a.batch = int(path_len.shape[0])
+    a.num_layers = nl
+    a.num_kv_heads = int(num_kv_heads)
+    a.head_dim = int(head_dim)
+    a.seq_stride, a.slot_stride, a.head_stride = int(seq_stride), int(slot_stride), int(head_stride)
+    a.slot_capacity = int(slot_capacity)
+    a.lead_slots = int(lead_slots)
+    a.max_depth = int(max_depth)
+    arr_k = (ctypes.c_void_p * nl)(*[_ptr(t) for t in k_cache])
+    arr_v = (ctypes.c_void_p * nl)(*[_ptr(t) for t in v_cache])
+    a._keep = (arr_k, arr_v)  # the host arrays must live until the call returns
+    a.k_cache = ctypes.cast(arr_k, _P)
+    a.v_cache = ctypes.cast(arr_v, _P)
+    a.path_nodes = _ptr(path_nodes)
+    a.path_len = _ptr(path_len)
+    a.committed_len = _ptr(committed_len)
+    a.seq_flags = _ptr(seq_flags)
+    return a
+
+
+def kv_commit_path(args: spec_kv_args, stream=None):
+    _check(lib().kv_commit_path(ctypes.byref(args), _stream(stream)))
+
+
+# ---- HIP events for the optional row-pass timing (profile_events) -----------------------
+
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(_P)]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+        _hip.hipEventSynchronize.argtypes = [_P]
+        _hip.hipEventDestroy.argtypes = [_P]
+    return _hip
+
+
+class EventPair:
+    """Two hipEvent_t for spec_chain_args.profile_events (row-pass start / end)."""
+
+    def __init__(self):
+        h = _hiprt()
+        self.ev = (_P * 2)()
+        for i in range(2):
+            e = _P()
+            rc = h.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.ev[i] = e
+        self.ptr = ctypes.cast(self.ev, _P).value
+
+    def elapsed_ms(self) -> float:
+        h = _hiprt()
+        h.hipEventSynchronize(self.ev[1])
+        ms = ctypes.c_float(0)
+        rc = h.hipEventElapsedTime(ctypes.byref(ms), self.ev[0], self.ev[1])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        try:
+            h = _hiprt()
+            for i in range(2):
+                h.hipEventDestroy(self.ev[i])
+        except Exception:
+            pass

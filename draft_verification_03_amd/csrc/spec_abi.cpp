@@ -1,0 +1,162 @@
+// spec_abi.cpp -- the exported C entry points of libspecv: argument validation (host-visible
+// fields only, before any HIP call), workspace sizing, error reporting, and the hand-off to
+// the kernel launchers. The contract of every call is documented in include/spec_verify.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "spec_verify.h"
+#include "specv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int32_t kMaxVocab = 1 << 19;  // resolve-pass tile table bound (1024 tiles of 512)
+constexpr int32_t kMaxGamma = 64;       // first-rejection scan is one wave64 ballot
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SPEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_abi_version(void) { return SPEC_ABI_VERSION; }
+
+const char* spec_last_error(void) { return g_err; }
+
+size_t spec_verify_chain_workspace_size(int32_t batch, int32_t total_draft_rows, int32_t vocab) {
+  if (batch < 0 || total_draft_rows < 0 || vocab < 1 || vocab > kMaxVocab) return 0;
+  return specv::chain_workspace_bytes(batch, total_draft_rows, vocab);
+}
+
+int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  g_err[0] = '\0';
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "spec_verify_chain: args is NULL");
+  if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->vocab < 1 || a->vocab > kMaxVocab)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", kMaxVocab, a->vocab);
+  if (a->row_stride < a->vocab || a->row_stride % 8 != 0)
+    return fail(SPEC_ERR_INVALID_ARG,
+                "row_stride must be >= vocab and a multiple of 8 (got %d, vocab %d)",
+                a->row_stride, a->vocab);
+  if (a->max_gamma < 0 || a->max_gamma > kMaxGamma)
+    return fail(SPEC_ERR_INVALID_ARG, "max_gamma must be in [0, %d] (got %d)", kMaxGamma,
+                a->max_gamma);
+  if (a->total_draft_rows < 0 ||
+      (int64_t)a->total_draft_rows > (int64_t)a->batch * a->max_gamma)
+    return fail(SPEC_ERR_INVALID_ARG, "total_draft_rows must be in [0, batch*max_gamma] (got %d)",
+                a->total_draft_rows);
+  if (a->lead_slots != 0 && a->lead_slots != 1)
+    return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
+  if (a->top_k) return fail(SPEC_ERR_UNSUPPORTED, "top_k is reserved and must be NULL");
+  if (a->batch == 0) return SPEC_OK;
+  if (!a->target_logits || !a->cu_gamma || !a->temperature || !a->committed_len ||
+      !a->out_tokens || !a->num_accepted)
+    return fail(SPEC_ERR_INVALID_ARG,
+                "target_logits, cu_gamma, temperature, committed_len, out_tokens and "
+                "num_accepted are required");
+  if (a->total_draft_rows > 0 && !a->draft_tokens)
+    return fail(SPEC_ERR_INVALID_ARG, "draft_tokens is required when total_draft_rows > 0");
+  if (!aligned16(a->target_logits) || (a->draft_logits && !aligned16(a->draft_logits)))
+    return fail(SPEC_ERR_INVALID_ARG, "logits base pointers must be 16-byte aligned");
+  if ((int64_t)a->batch * (a->max_gamma + 1) > 0x7FFFFFFFLL)
+    return fail(SPEC_ERR_INVALID_ARG, "batch * (max_gamma + 1) exceeds the grid limit");
+  const size_t need =
+      specv::chain_workspace_bytes(a->batch, a->total_draft_rows, a->vocab);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  hipError_t e = specv::launch_chain(*a, workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_chain launch");
+  return SPEC_OK;
+}
+
+size_t spec_verify_tree_workspace_size(int32_t batch, int32_t rows_per_seq) {
+  if (batch < 0 || rows_per_seq < 1 || rows_per_seq > 256) return 0;
+  return specv::tree_workspace_bytes(batch, rows_per_seq);
+}
+
+int spec_verify_tree(const spec_tree_args* a, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+  g_err[0] = '\0';
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "spec_verify_tree: args is NULL");
+  if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->vocab < 1 || a->vocab > kMaxVocab)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", kMaxVocab, a->vocab);
+  if (a->row_stride < a->vocab || a->row_stride % 8 != 0)
+    return fail(SPEC_ERR_INVALID_ARG, "row_stride must be >= vocab and a multiple of 8");
+  if (a->num_nodes < 1 || a->num_nodes > 256)
+    return fail(SPEC_ERR_INVALID_ARG, "num_nodes must be in [1, 256] (got %d)", a->num_nodes);
+  if (a->rows_per_seq < 1 || a->rows_per_seq > 256)
+    return fail(SPEC_ERR_INVALID_ARG, "rows_per_seq must be in [1, 256] (got %d)",
+                a->rows_per_seq);
+  if (a->max_depth < 1 || a->max_depth > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "max_depth must be in [1, 64] (got %d)", a->max_depth);
+  if (a->tree_stride != 0 && a->tree_stride < a->num_nodes)
+    return fail(SPEC_ERR_INVALID_ARG, "tree_stride must be 0 or >= num_nodes");
+  if (a->batch == 0) return SPEC_OK;
+  if (!a->target_logits || !a->parent || !a->node_row || !a->node_token || !a->path_nodes ||
+      !a->path_len || !a->out_tokens || !a->num_emitted)
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(a->target_logits))
+    return fail(SPEC_ERR_INVALID_ARG, "target_logits must be 16-byte aligned");
+  if ((int64_t)a->batch * a->rows_per_seq > 0x7FFFFFFFLL)
+    return fail(SPEC_ERR_INVALID_ARG, "batch * rows_per_seq exceeds the grid limit");
+  const size_t need = specv::tree_workspace_bytes(a->batch, a->rows_per_seq);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  hipError_t e = specv::launch_tree(*a, workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_tree launch");
+  return SPEC_OK;
+}
+
+int kv_commit_path(const spec_kv_args* a, void* hip_stream) {
+  g_err[0] = '\0';
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "kv_commit_path: args is NULL");
+  if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->num_layers < 1 || a->num_layers > 128)
+    return fail(SPEC_ERR_INVALID_ARG, "num_layers must be in [1, 128] (got %d)", a->num_layers);
+  if (a->num_kv_heads < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", a->num_kv_heads);
+  if (a->head_dim < 8 || a->head_dim % 8 != 0)
+    return fail(SPEC_ERR_INVALID_ARG,
+                "head_dim must be a positive multiple of 8 (16-byte rows; got %d)", a->head_dim);
+  if (a->seq_stride < 0 || a->slot_stride < 0 || a->head_stride < 0 ||
+      a->seq_stride % 8 || a->slot_stride % 8 || a->head_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
+  if (a->slot_capacity < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "slot_capacity must be >= 1");
+  if (a->lead_slots != 0 && a->lead_slots != 1)
+    return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
+  if (a->max_depth < 1 || a->max_depth > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "max_depth must be in [1, 64] (got %d)", a->max_depth);
+  if (a->batch == 0) return SPEC_OK;
+  if (!a->k_cache || !a->v_cache || !a->path_nodes || !a->path_len || !a->committed_len)
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  for (int l = 0; l < a->num_layers; ++l) {
+    if (!a->k_cache[l] || !a->v_cache[l])
+      return fail(SPEC_ERR_INVALID_ARG, "k_cache[%d] / v_cache[%d] is NULL", l, l);
+    if (!aligned16(a->k_cache[l]) || !aligned16(a->v_cache[l]))
+      return fail(SPEC_ERR_INVALID_ARG, "cache pointers of layer %d must be 16-byte aligned", l);
+  }
+  hipError_t e = specv::launch_kv(*a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_commit_path launch");
+  return SPEC_OK;
+}
+
+}  // extern "C"

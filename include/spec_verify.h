@@ -1,0 +1,229 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X speculative-sampling verification library
+ * (libspecv.so, gfx950).
+ *
+ * One round of speculative sampling: a drafter proposes d_1..d_gamma with laws q_1..q_gamma;
+ * the target scores [x, d_1..d_gamma] in one causal forward and yields p_1..p_{gamma+1};
+ * the verifier tests the drafts left to right, keeps the accepted prefix, and adds one
+ * token -- a residual draw at the first rejection or a bonus draw after a full accept; the
+ * KV cache keeps the accepted prefix and drops the rest. Sources (page title, section):
+ *   "10.6 投机解码：为什么'先猜后验'能加速" (llm_internals) §10.6.1 (the round in five
+ *     steps; greedy special case), §10.6.3 (the verify step's logits[B, gamma+1, n_vocab],
+ *     per-request start points, cache truncation after a rejection, tree drafts);
+ *   "KV Cache 优化（四）：Speculative Decoding 投机解码" §4 (eq. a(x) and eq. p'(x); the law
+ *     after temperature and top-k/top-p is the one to test), §5 (bonus token), §6 (reserved
+ *     slots and one committed-length pointer, the same in every layer);
+ *   "投机解码" (LLM glossary), exact acceptance section (q = 0 and zero-residual cases);
+ *   "投机推理：小模型搭树，大模型一次验证", validation and path-walk sections (tree).
+ *
+ * Conventions for every call
+ *  - Logits are bf16, passed as raw uint16 bit patterns, row-major with row_stride elements
+ *    per row (row_stride >= vocab, a multiple of 8; base pointers 16-byte aligned). A row
+ *    must hold at least one finite logit; NaN and +inf logits are not supported.
+ *  - All array arguments are DEVICE pointers owned by the caller, except where a field says
+ *    "host". The library allocates nothing, keeps no pointer after returning, and holds no
+ *    global state except a thread-local error string. Calls are thread-safe.
+ *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the default stream). Outputs are
+ *    valid after the stream is synchronised; inputs must stay alive until then.
+ *  - Host validation reads only host-visible fields and makes no HIP call before it passes.
+ *    On SPEC_ERR_INVALID_ARG / SPEC_ERR_UNSUPPORTED / SPEC_ERR_WORKSPACE nothing is enqueued
+ *    and no output is touched. spec_last_error() then describes the failure.
+ *  - Data errors only visible on the device set bits in seq_flags[b]; see SPEC_FLAG_*.
+ *  - Results are a pure function of the inputs and the seed: independent of batch
+ *    composition (uniforms are keyed by seq_id) and of launch geometry; repeated calls give
+ *    identical bits.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+/* ---- status codes ---------------------------------------------------------------------- */
+#define SPEC_OK 0
+#define SPEC_ERR_INVALID_ARG (-1)  /* a host-visible argument is out of range            */
+#define SPEC_ERR_UNSUPPORTED (-2)  /* a reserved feature was requested (e.g. top_k)       */
+#define SPEC_ERR_HIP (-3)          /* a HIP launch or event call failed                   */
+#define SPEC_ERR_WORKSPACE (-4)    /* workspace NULL, misaligned or smaller than required */
+
+/* ---- seq_flags bits -------------------------------------------------------------------- */
+#define SPEC_FLAG_BAD_TOKEN 1       /* a draft token is outside [0, vocab): no progress      */
+#define SPEC_FLAG_Q_ZERO 2          /* q_k(d_k) = 0 at a tested position (a = [p_k(d_k)>0]) */
+#define SPEC_FLAG_RESID_FALLBACK 4  /* residual mass was 0: the draw used p_k itself        */
+#define SPEC_FLAG_NO_ROW 8          /* tree walk stopped at a node without a target row     */
+#define SPEC_FLAG_SLOT_OOB 16       /* KV slot outside [0, slot_capacity): no progress      */
+#define SPEC_FLAG_BAD_TREE 32       /* parent/node_row malformed: no progress               */
+#define SPEC_FLAG_TOPP_SLOW 64      /* a top-p threshold needed the exact multi-pass search */
+#define SPEC_FLAG_BAD_PARAM 128     /* T < 0, top_p outside (0,1], gamma_b out of range, or
+                                       T > 0 with draft_logits NULL: no progress            */
+
+/* ---- uniform purposes (third word of the Philox counter) ------------------------------- */
+#define SPEC_PURPOSE_ACCEPT 0
+#define SPEC_PURPOSE_RESIDUAL 1
+#define SPEC_PURPOSE_BONUS 2
+
+/*
+ * Chain verification of a ragged batch ("10.6 投机解码" §10.6.1 steps 1-5; §10.6.3).
+ *
+ * Sequence b has gamma_b = cu_gamma[b+1] - cu_gamma[b] drafts (0 <= gamma_b <= max_gamma).
+ * Target row of (b, k), k = 1..gamma_b+1, is cu_gamma[b] + b + k - 1 (p_k predicts the k-th
+ * new token); draft row of (b, k), k = 1..gamma_b, is cu_gamma[b] + k - 1.
+ *
+ * Per sequence, with L = committed_len[b] on entry, T = temperature[b], P = top_p[b]:
+ *  - laws: p_k = top-p_P(softmax(target row / T)), q_k likewise from the draft row (the same
+ *    T and P; "KV Cache 优化（四）" §4). Top-p keeps every token whose logit is >= t*, t* the
+ *    largest logit value at which the mass of all tokens at or above it reaches P. T = 0 is
+ *    greedy: p_k is one-hot at the target argmax (lowest id on ties) and q is not read.
+ *  - test: a_k = min(1, p_k(d_k)/q_k(d_k)) (eq. a(x)); where q_k(d_k) = 0, a_k = [p_k(d_k) > 0]
+ *    and SPEC_FLAG_Q_ZERO is set; accept iff u_acc < a_k, u_acc = U(L+k, ACCEPT). Greedy:
+ *    accept iff d_k equals the target argmax.
+ *  - first rejection at k: the emitted token is the inverse-CDF draw (ascending token id)
+ *    from max(0, p_k - q_k) with u = U(L+k, RESIDUAL) (eq. p'(x)); if that mass is 0, from p_k
+ *    (SPEC_FLAG_RESID_FALLBACK). Greedy: the target argmax.
+ *  - all accepted: a bonus draw from p_{gamma_b+1} with u = U(L+gamma_b+1, BONUS) ("KV Cache
+ *    优化（四）" §5). Greedy: the argmax. gamma_b = 0 is allowed: the round is one draw from
+ *    p_1 -- which is also how a drafter can draw its own tokens through this call.
+ *  - outputs: out_tokens[target row (b, 1..n+1)] = d_1..d_n, y; num_accepted[b] = n;
+ *    committed_len[b] = L + lead_slots + n (pointer-only rollback, "KV Cache 优化（四）" §6:
+ *    no KV byte moves; the rejected drafts' slots are simply past the pointer).
+ *  U(pos, purpose) = Philox4x32-10 with key (seed low 32 bits, seed high 32 bits), counter
+ *  (seq_id[b], pos, purpose, 0); u = (first output word >> 8) * 2^-24.
+ */
+typedef struct spec_chain_args {
+  int32_t batch;            /* B >= 0 (0: nothing to do)                                    */
+  int32_t vocab;            /* V >= 1                                                        */
+  int32_t row_stride;       /* elements between rows; >= vocab, multiple of 8               */
+  int32_t max_gamma;        /* 0..64: bound on every gamma_b                                 */
+  int32_t total_draft_rows; /* = cu_gamma[B] (sum of gamma_b); >= 0                          */
+  int32_t lead_slots;       /* 0 or 1 (1: the round also wrote x's slot at L)                */
+  uint64_t seed;            /* Philox key                                                    */
+  const uint16_t* target_logits; /* [total_draft_rows + B][row_stride] bf16                 */
+  const uint16_t* draft_logits;  /* [total_draft_rows][row_stride] bf16; NULL iff all T = 0  */
+  const int32_t* cu_gamma;       /* [B+1], cu_gamma[0] = 0, non-decreasing                    */
+  const int32_t* draft_tokens;   /* [total_draft_rows]; may be NULL if total_draft_rows = 0  */
+  const float* temperature;      /* [B], >= 0                                                */
+  const float* top_p;            /* [B] in (0, 1], or NULL = no top-p                        */
+  const int32_t* top_k;          /* reserved: must be NULL (else SPEC_ERR_UNSUPPORTED)       */
+  const uint32_t* seq_id;        /* [B] Philox stream ids, or NULL = b                       */
+  int32_t* committed_len;        /* [B] in/out: L on entry, L + lead_slots + n on exit       */
+  int32_t* out_tokens;           /* [total_draft_rows + B]; entries past n+1 are untouched   */
+  int32_t* num_accepted;         /* [B]                                                      */
+  int32_t* seq_flags;            /* [B] or NULL                                              */
+  float* probe_rows;             /* [total_draft_rows][3] or NULL: {p_k(d_k), q_k(d_k), a_k}
+                                    for tested positions (greedy: {[d=argmax], NaN, accept}) */
+  float* probe_seq;              /* [B][2] or NULL: {residual mass R (NaN if no rejection),
+                                    probability of the emitted last token under its law}    */
+  const float* uniform_override; /* [total_draft_rows + B][2] or NULL (test hook): row (b,k)
+                                    supplies {u_acc for k, u for the residual/bonus draw at k}
+                                    in place of the Philox uniforms                          */
+  void* profile_events;          /* NULL, or a host array of 2 hipEvent_t recorded on the
+                                    stream just before and just after the row pass kernel   */
+} spec_chain_args;
+
+/*
+ * Greedy tree verification ("投机推理：小模型搭树，大模型一次验证", validation and path walk;
+ * "10.6 投机解码" §10.6.3 tree drafts).
+ *
+ * Node 0 is the root (the last committed token; never verified). Node i >= 1 has parent
+ * parent[i] < i and token node_token[b][i]. node_row[i] is the target row holding the
+ * target's next-token logits after node i, or -1. The walk starts at v = 0: if v has no row
+ * it stops (SPEC_FLAG_NO_ROW, no extra token); else t = argmax of v's row (lowest id on
+ * ties); the lowest-index child c of v with node_token[c] = t is appended to the path and
+ * the walk continues from c; if no child matches (or the path already holds max_depth
+ * nodes) t is emitted as the extra token and the walk ends. Matches on other branches are
+ * never counted.
+ *
+ * Outputs: path_nodes[b][0..D) (rest set to -1), path_len[b] = D,
+ * out_tokens[b][0..D) = tokens of the path, out_tokens[b][D] = the extra token if any,
+ * num_emitted[b] = D or D+1. A malformed tree (parent[0] != -1, parent[i] outside [0, i),
+ * node_row outside [-1, rows_per_seq)) sets SPEC_FLAG_BAD_TREE and emits nothing.
+ */
+typedef struct spec_tree_args {
+  int32_t batch;          /* B >= 0                                                        */
+  int32_t vocab;          /* V >= 1                                                        */
+  int32_t row_stride;     /* elements; >= vocab, multiple of 8                             */
+  int32_t num_nodes;      /* N+1 including the root; 1..256                                */
+  int32_t rows_per_seq;   /* target rows per sequence; 1..256                              */
+  int32_t max_depth;      /* path capacity; 1..64                                          */
+  int32_t tree_stride;    /* elements between sequences in parent/node_row; 0 = one
+                             topology for the whole batch, else >= num_nodes              */
+  const uint16_t* target_logits; /* [B][rows_per_seq][row_stride] bf16                    */
+  const int32_t* parent;         /* [B or 1][tree_stride or num_nodes]                    */
+  const int32_t* node_row;       /* same layout as parent                                 */
+  const int32_t* node_token;     /* [B][num_nodes]                                        */
+  int32_t* path_nodes;           /* [B][max_depth]                                        */
+  int32_t* path_len;             /* [B]                                                   */
+  int32_t* out_tokens;           /* [B][max_depth + 1]                                    */
+  int32_t* num_emitted;          /* [B]                                                   */
+  int32_t* seq_flags;            /* [B] or NULL                                           */
+} spec_tree_args;
+
+/*
+ * KV commit of an accepted path ("KV Cache 优化（四）" §6; "10.6 投机解码" §10.6.3).
+ *
+ * The verify forward wrote node i's K/V (i >= 1, tree node index or chain draft index) at
+ * slot base + i, base = L + lead_slots - 1, L = committed_len[b]. For j = 1..D (D =
+ * path_len[b], in increasing j) every layer's K and V rows of every KV head are copied from
+ * slot base + path_nodes[b][j-1] to slot base + j (skipped when equal), then committed_len[b]
+ * becomes L + lead_slots + D. Slots outside [0, slot_capacity) set SPEC_FLAG_SLOT_OOB
+ * (OR-ed into seq_flags) and leave that sequence untouched. A chain round's path is the
+ * identity (path[j-1] = j), which moves no byte: the commit is then a pointer update, which
+ * is also how a draft model's cache is rolled back.
+ *
+ * Element (b, slot, head, e) of layer l's K cache is k_cache[l][b*seq_stride +
+ * slot*slot_stride + head*head_stride + e], e < head_dim, bf16 (copied bit for bit).
+ */
+typedef struct spec_kv_args {
+  int32_t batch;          /* B >= 0                                                       */
+  int32_t num_layers;     /* 1..128                                                       */
+  int32_t num_kv_heads;   /* >= 1                                                         */
+  int32_t head_dim;       /* elements; head_dim * 2 bytes a multiple of 16                */
+  int64_t seq_stride;     /* elements; multiples of 8                                     */
+  int64_t slot_stride;
+  int64_t head_stride;
+  int32_t slot_capacity;  /* slots per sequence                                           */
+  int32_t lead_slots;     /* 0 or 1                                                       */
+  int32_t max_depth;      /* row length of path_nodes; 1..64                              */
+  uint16_t* const* k_cache; /* HOST array [num_layers] of device pointers (16-B aligned)   */
+  uint16_t* const* v_cache; /* HOST array [num_layers] of device pointers (16-B aligned)   */
+  const int32_t* path_nodes; /* [B][max_depth], node indices >= 1 in depth order           */
+  const int32_t* path_len;   /* [B], 0..max_depth                                          */
+  int32_t* committed_len;    /* [B] in/out                                                 */
+  int32_t* seq_flags;        /* [B] or NULL (bits OR-ed in)                                */
+} spec_kv_args;
+
+/* ABI revision of this header (SPEC_ABI_VERSION). */
+int spec_abi_version(void);
+
+/* Last error message of the calling thread ("" if none). Valid until the thread's next call. */
+const char* spec_last_error(void);
+
+/* Workspace bytes spec_verify_chain needs for this batch shape (device memory, 256-byte
+ * aligned, caller-owned, contents need not be initialised). Returns 0 for invalid sizes. */
+size_t spec_verify_chain_workspace_size(int32_t batch, int32_t total_draft_rows, int32_t vocab);
+
+/* Enqueue chain verification. Returns SPEC_OK or a negative status. */
+int spec_verify_chain(const spec_chain_args* args, void* workspace, size_t workspace_bytes,
+                      void* hip_stream);
+
+/* Workspace bytes spec_verify_tree needs (device memory, 256-byte aligned). */
+size_t spec_verify_tree_workspace_size(int32_t batch, int32_t rows_per_seq);
+
+/* Enqueue greedy tree verification. Returns SPEC_OK or a negative status. */
+int spec_verify_tree(const spec_tree_args* args, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
+
+/* Enqueue the KV path commit and pointer update. Returns SPEC_OK or a negative status. */
+int kv_commit_path(const spec_kv_args* args, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -191,8 +191,8 @@ int oracle_dist(const uint16_t* row, int V, double T, double P, double* pi, doub
 }
 
 /* Inverse-CDF draw from non-negative weights (reading R7). *margin receives the distance of
- * u*W from the nearer of the two cumulative sums that bracket the chosen token, in the
- * weights' own units. */
+ * the uniform u from the nearer of the two decision boundaries that bracket the chosen
+ * token, in u's own units: min(u - C_{y-1}/W, C_y/W - u). */
 int oracle_sample(const double* w, int V, double u, double* margin) {
   double W = 0.0;
   for (int v = 0; v < V; ++v) W += w[v];
@@ -202,7 +202,7 @@ int oracle_sample(const double* w, int V, double u, double* margin) {
     c += w[v];
     if (c > x) {
       double a = x - prev, b = c - x;
-      if (margin) *margin = a < b ? a : b;
+      if (margin) *margin = (a < b ? a : b) / W;
       return v;
     }
   }
@@ -216,7 +216,9 @@ int oracle_sample(const double* w, int V, double u, double* margin) {
  * §10.6.1 steps 3-4; [GL] exact acceptance and its q=0 / vanishing-residual cases).
  * Returns 1 if the draft token d is accepted, else 0 with *token set to the residual draw.
  * info[0] = a, info[1] = R (NaN when accepted), info[2] = the drawn token's probability
- * under the residual law (NaN when accepted), info[3] = smallest decision margin. */
+ * under the residual law (NaN when accepted), info[3] = smallest decision margin: the
+ * distance of a uniform from its decision boundary (|u - a|, and the draw's margin), 0 when
+ * R < 1e-5. */
 int oracle_position_step(const double* p, const double* q, int V, int d, double u_acc,
                          double u_res, int* token, int* flags, double* r_scratch,
                          double info[4]) {
@@ -244,6 +246,7 @@ int oracle_position_step(const double* p, const double* q, int V, int d, double 
   }
   info[1] = R;
   if (sm < info[3]) info[3] = sm;
+  if (R < 1e-5) info[3] = 0.0; /* a vanishing residual is itself a boundary case */
   *token = y;
   return 0;
 }

@@ -1,0 +1,203 @@
+"""C-ABI checks that need no GPU: the library loads and exports every function that
+include/spec_verify.h declares, the ctypes structs match the C layout, and host validation
+rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from draft_verification_03_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ["spec_abi_version", "spec_last_error", "spec_verify_chain_workspace_size",
+                 "spec_verify_chain", "spec_verify_tree_workspace_size", "spec_verify_tree",
+                 "kv_commit_path"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(declared_functions()) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    prog = tmp_path / "layout.c"
+    fields = {
+        "spec_chain_args": [f for f, _ in B.spec_chain_args._fields_],
+        "spec_tree_args": [f for f, _ in B.spec_tree_args._fields_],
+        "spec_kv_args": [f for f, _ in B.spec_kv_args._fields_],
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spec_verify.h"',
+             "int main(void){"]
+    for s, fs in fields.items():
+        lines.append(f'printf("{s} %zu\\n", sizeof({s}));')
+        for f in fs:
+            lines.append(f'printf("{s}.{f} %zu\\n", offsetof({s}, {f}));')
+    lines.append("return 0;}")
+    prog.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(prog), "-o",
+                    str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for s, fs in fields.items():
+        cls = getattr(B, s)
+        assert int(got[s]) == ctypes.sizeof(cls), s
+        for f in fs:
+            assert int(got[f"{s}.{f}"]) == getattr(cls, f).offset, f"{s}.{f}"
+
+
+def test_abi_version_and_workspace_sizes():
+    assert B.spec_abi_version() == 1
+    assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
+    assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
+    assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
+    assert B.spec_verify_tree_workspace_size(128, 5) >= 128 * 5 * 4
+    assert B.spec_verify_tree_workspace_size(1, 0) == 0
+
+
+def _chain(**kw):
+    a = B.spec_chain_args()
+    base = dict(batch=2, vocab=100, row_stride=104, max_gamma=4, total_draft_rows=4,
+                lead_slots=1, target_logits=0x1000, draft_logits=0x2000, cu_gamma=0x3000,
+                draft_tokens=0x4000, temperature=0x5000, committed_len=0x6000,
+                out_tokens=0x7000, num_accepted=0x8000)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call_chain(a, ws=0x100000, nbytes=1 << 30):
+    return B.lib().spec_verify_chain(ctypes.byref(a), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), B.SPEC_ERR_INVALID_ARG),
+    (dict(vocab=0), B.SPEC_ERR_INVALID_ARG),
+    (dict(vocab=(1 << 19) + 1, row_stride=(1 << 19) + 8), B.SPEC_ERR_INVALID_ARG),
+    (dict(row_stride=99), B.SPEC_ERR_INVALID_ARG),
+    (dict(row_stride=101), B.SPEC_ERR_INVALID_ARG),
+    (dict(max_gamma=65), B.SPEC_ERR_INVALID_ARG),
+    (dict(max_gamma=-1), B.SPEC_ERR_INVALID_ARG),
+    (dict(total_draft_rows=9), B.SPEC_ERR_INVALID_ARG),
+    (dict(lead_slots=2), B.SPEC_ERR_INVALID_ARG),
+    (dict(target_logits=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(cu_gamma=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(temperature=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(committed_len=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(out_tokens=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(num_accepted=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(draft_tokens=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(target_logits=0x1002), B.SPEC_ERR_INVALID_ARG),
+    (dict(top_k=0x9000), B.SPEC_ERR_UNSUPPORTED),
+])
+def test_chain_validation(kw, code):
+    assert _call_chain(_chain(**kw)) == code
+    assert B.spec_last_error() != ""
+
+
+def test_chain_workspace_validation():
+    a = _chain()
+    assert _call_chain(a, ws=None) == B.SPEC_ERR_WORKSPACE
+    assert _call_chain(a, ws=0x100010) == B.SPEC_ERR_WORKSPACE
+    assert _call_chain(a, nbytes=16) == B.SPEC_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op():
+    assert _call_chain(_chain(batch=0, total_draft_rows=0), ws=None, nbytes=0) == B.SPEC_OK
+    assert B.lib().spec_verify_chain(None, None, 0, None) == B.SPEC_ERR_INVALID_ARG
+
+
+def _tree(**kw):
+    a = B.spec_tree_args()
+    base = dict(batch=2, vocab=100, row_stride=104, num_nodes=13, rows_per_seq=5,
+                max_depth=3, tree_stride=0, target_logits=0x1000, parent=0x2000,
+                node_row=0x3000, node_token=0x4000, path_nodes=0x5000, path_len=0x6000,
+                out_tokens=0x7000, num_emitted=0x8000)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), B.SPEC_ERR_INVALID_ARG),
+    (dict(num_nodes=0), B.SPEC_ERR_INVALID_ARG),
+    (dict(num_nodes=257), B.SPEC_ERR_INVALID_ARG),
+    (dict(rows_per_seq=0), B.SPEC_ERR_INVALID_ARG),
+    (dict(max_depth=0), B.SPEC_ERR_INVALID_ARG),
+    (dict(max_depth=65), B.SPEC_ERR_INVALID_ARG),
+    (dict(tree_stride=5), B.SPEC_ERR_INVALID_ARG),
+    (dict(row_stride=100 + 4), B.SPEC_OK),
+    (dict(parent=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(target_logits=0x1004), B.SPEC_ERR_INVALID_ARG),
+])
+def test_tree_validation(kw, code):
+    a = _tree(**kw)
+    if code == B.SPEC_OK:  # valid arguments: only the workspace check remains on the host
+        assert B.lib().spec_verify_tree(ctypes.byref(a), None, 0, None) == B.SPEC_ERR_WORKSPACE
+    else:
+        assert B.lib().spec_verify_tree(ctypes.byref(a), 0x100000, 1 << 20, None) == code
+
+
+def _kv(**kw):
+    a = B.spec_kv_args()
+    ptrs = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    base = dict(batch=2, num_layers=2, num_kv_heads=8, head_dim=128, seq_stride=1024 * 1024,
+                slot_stride=1024, head_stride=128, slot_capacity=1024, lead_slots=1,
+                max_depth=3, k_cache=ctypes.cast(ptrs, ctypes.c_void_p).value,
+                v_cache=ctypes.cast(ptrs, ctypes.c_void_p).value, path_nodes=0x5000,
+                path_len=0x6000, committed_len=0x7000)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    a._keep = ptrs
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=-1), dict(num_layers=0), dict(num_layers=129), dict(num_kv_heads=0),
+    dict(head_dim=12), dict(slot_stride=1020), dict(slot_capacity=0), dict(lead_slots=3),
+    dict(max_depth=0), dict(path_nodes=None), dict(k_cache=None),
+])
+def test_kv_validation(kw):
+    a = _kv(**kw)
+    assert B.lib().kv_commit_path(ctypes.byref(a), None) == B.SPEC_ERR_INVALID_ARG
+
+
+def test_kv_validation_rejects_misaligned_layer_pointer():
+    ptrs = (ctypes.c_void_p * 2)(0x10000, 0x20008)
+    a = _kv(k_cache=ctypes.cast(ptrs, ctypes.c_void_p).value)
+    a._keep2 = ptrs
+    assert B.lib().kv_commit_path(ctypes.byref(a), None) == B.SPEC_ERR_INVALID_ARG
+
+
+def test_product_never_imports_the_oracle():
+    """The GPU library and its binding share nothing with oracle/."""
+    pkg = os.path.join(ROOT, "draft_verification_03_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "spec_oracle" not in text, f
