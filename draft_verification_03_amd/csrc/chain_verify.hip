@@ -11,8 +11,9 @@
 //     The wave streams the target row and (for k <= gamma_b) the draft row of the item
 //     together from HBM once, with 16-byte loads, 8 vectors per row in flight per lane:
 //       - per-lane online max / sum of exp2((l - m) * log2(e)/T) (one rescale per trip);
-//       - with top-p: every 8-logit vector whose max is within kCaptureK*T of the wave's
-//         running max is kept in LDS (a superset of the final window m - kCaptureK*T);
+//       - with top-p: the index of every 8-logit vector whose max is within kCaptureK*T of
+//         the wave's running max is kept in LDS (a superset of the final window
+//         m - kCaptureK*T); the end phase reads those few vectors again;
 //       - greedy rows (T = 0): max with the lowest index only.
 //     The end phase (wave reductions only) gives m, Z, the nucleus threshold t* (binary
 //     search over bf16 keys on fixed-point masses of the captured elements; an exact
@@ -36,7 +37,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Top-p capture window: logits within kCaptureK * T of the row max (weight >= e^-7 of the
 // largest). Rows whose nucleus reaches further down take the exact multi-pass search.
 constexpr float kCaptureK = 7.0f;
-constexpr int kCapV = 256;    // captured 8-logit vectors per row
+constexpr int kCapV = 1024;   // captured 8-logit vector indices per row
 constexpr int kCapEl = 256;   // captured logits inside the final window per row
 constexpr int kElPerLane = kCapEl / kWave;
 constexpr int kResolveThreads = 256;
@@ -64,15 +65,15 @@ struct ChainParams {
   uint32_t seed_lo, seed_hi;
 };
 
+// Indices of the captured vectors; the vectors themselves (about 1% of the row) are read
+// again in the end phase.
 struct CapBuf {
-  uint4 data[kCapV];
   int32_t vidx[kCapV];
 };
 
 struct ElBuf {
   uint32_t key[kCapEl];
   uint32_t idx[kCapEl];
-  uint64_t fw[kCapEl];
   uint32_t sidx[kWave];  // staging of a nucleus list before it is sorted
   float sw[kWave];
 };
@@ -155,10 +156,7 @@ __device__ __forceinline__ void accumulate_trip(const uint4 d[kU], int v0, int l
       const uint64_t mask = __ballot(want);
       if (mask) {
         const int slot = a.cnt + (int)lanes_below(mask);
-        if (want && slot < kCapV) {
-          cap->data[slot] = d[u];
-          cap->vidx[slot] = v0 + u * kWave + lane;
-        }
+        if (want && slot < kCapV) cap->vidx[slot] = v0 + u * kWave + lane;
         a.cnt += __popcll(mask);
       }
     }
@@ -288,8 +286,8 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
     float x[8];
     int vi = 0;
     if (i < nv) {
-      unpack8(cap->data[i], x);
       vi = cap->vidx[i];
+      unpack8(row[vi], x);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -299,7 +297,6 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
       if (in && slot < kCapEl) {
         el->key[slot] = key_of(x[e]);
         el->idx[slot] = (uint32_t)(vi * 8 + e);
-        el->fw[slot] = fixw(weight(x[e], c, nref));
       }
       nel += __popcll(mask);
     }
@@ -316,7 +313,7 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
     const bool have = ok && i < nel;
     k[j] = have ? el->key[i] : 0u;
     ix[j] = have ? el->idx[i] : 0u;
-    f[j] = have ? el->fw[i] : 0ull;
+    f[j] = have ? fixw(weight(value_of_key(k[j]), c, nref)) : 0ull;
     tot += f[j];
     if (have) {
       kmin = min(kmin, k[j]);

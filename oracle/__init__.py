@@ -175,7 +175,9 @@ def verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p=Non
         "seq_flags": np.zeros(B, dtype=np.int32),
         "probe_rows": np.full((max(n_draft, 1), 3), np.nan, dtype=np.float64),
         "probe_seq": np.full((B, 2), np.nan, dtype=np.float64),
-        "margin": np.full(B, np.inf, dtype=np.float64),
+        # [B][2]: distance to the nearest decision boundary among (0) the acceptance tests
+        # and the top-p cuts of their rows, (1) those and the final draw (and its row's cut)
+        "margin": np.full((B, 2), np.inf, dtype=np.float64),
     }
     rc = lib().oracle_verify_chain(
         B, V, stride, _ptr(target), _ptr(draft), _ptr(cu), _ptr(toks), _ptr(temp), _ptr(tp),

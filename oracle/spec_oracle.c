@@ -292,7 +292,9 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
       const double T = (double)temperature[b];
       const double P = top_p ? (double)top_p[b] : 1.0;
       int flags = 0, n_acc = 0, y = -1;
-      double margin = INFINITY, R_out = NAN, py_out = NAN;
+      /* margin: smallest distance to a decision boundary among the acceptance tests and the
+       * top-p cuts of the rows they use; dmargin: the same for the final draw. */
+      double margin = INFINITY, dmargin = INFINITY, R_out = NAN, py_out = NAN;
       for (int k = 0; k < g; ++k) {
         double* pr = probe_rows ? probe_rows + 3 * (size_t)(drow0 + k) : NULL;
         if (pr) pr[0] = pr[1] = pr[2] = NAN;
@@ -312,7 +314,7 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         committed_len_out[b] = L;
         if (seq_flags) seq_flags[b] = flags;
         if (probe_seq) { probe_seq[2 * b] = NAN; probe_seq[2 * b + 1] = NAN; }
-        if (margin_out) margin_out[b] = INFINITY;
+        if (margin_out) margin_out[2 * b] = margin_out[2 * b + 1] = INFINITY;
         continue;
       }
       orow_t ip, iq;
@@ -347,8 +349,10 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         int tok = -1;
         int acc = oracle_position_step(p, q, V, d, u_acc, u_res, &tok, &flags, r, info);
         if (pr) { pr[0] = p[d]; pr[1] = q[d]; pr[2] = info[0]; }
-        if (info[3] < margin) margin = info[3];
+        double am = fabs(u_acc - info[0]);
+        if (am < margin) margin = am;
         if (acc) { n_acc = k; continue; }
+        dmargin = info[3];
         y = tok;
         R_out = info[1];
         py_out = info[2];
@@ -365,12 +369,12 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
           py_out = 1.0;
         } else {
           oracle_dist(trow, V, T, P, p, scratch, &ip);
-          if (ip.topp_margin < margin) margin = ip.topp_margin;
+          if (ip.topp_margin < dmargin) dmargin = ip.topp_margin;
           double u = uniform_override ? (double)uniform_override[ovr + 1]
                                       : oracle_uniform(seed, id, (uint32_t)(L + g + 1), PURPOSE_BONUS);
           double sm;
           y = oracle_sample(p, V, u, &sm);
-          if (sm < margin) margin = sm;
+          if (sm < dmargin) dmargin = sm;
           py_out = p[y];
         }
         n_acc = g;
@@ -381,7 +385,10 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
       committed_len_out[b] = L + lead_slots + n_acc; /* reading R10 ([KV] §6 pointer) */
       if (seq_flags) seq_flags[b] = flags;
       if (probe_seq) { probe_seq[2 * b] = R_out; probe_seq[2 * b + 1] = py_out; }
-      if (margin_out) margin_out[b] = margin;
+      if (margin_out) {
+        margin_out[2 * b] = margin;
+        margin_out[2 * b + 1] = dmargin < margin ? dmargin : margin;
+      }
     }
     free(p); free(q); free(r); free(scratch);
   }

@@ -63,11 +63,12 @@ def markov_stream_gpu(T, D, n_tokens, gamma=4, seed=303, seed_draft=909):
         B.spec_verify_chain(a, workspace=ws)
         n_g = int(d_n.item())
         n = int(o["num_accepted"][0])
-        if o["margin"][0] >= MARGIN:
-            assert n_g == n
-            assert np.array_equal(d_out.cpu().numpy()[:n + 1], o["out_tokens"][:n + 1])
-            assert int(d_L.item()) == pos + 1 + n
-        else:
+        m_acc, m_all = o["margin"][0]
+        if m_acc >= MARGIN:
+            assert n_g == n and int(d_L.item()) == pos + 1 + n
+            k = n + 1 if m_all >= MARGIN else n
+            assert np.array_equal(d_out.cpu().numpy()[:k], o["out_tokens"][:k])
+        if m_all < MARGIN:
             boundary += 1
         em = list(o["out_tokens"][:n + 1])
         calls += 1

@@ -101,6 +101,15 @@ def test_tree_random_small(shared):
     tok = rng.integers(0, V, size=(Bn, N)).astype(np.int32)
     logits = np.full((Bn, R, stride), 0xFF80, np.uint16)
     logits[..., :V] = W.bf16_bits(np.round(rng.standard_normal((Bn, R, V)) * 2).astype(np.float32))
+    # make half of the children carry their parent's target argmax, so that long paths and
+    # duplicate matching siblings occur
+    am = W.bf16_to_f32(logits[..., :V]).argmax(-1)
+    for b in range(Bn):
+        s_ = 0 if shared else b
+        for i in range(1, N):
+            r = row[s_, par[s_, i]]
+            if r >= 0 and rng.random() < 0.5:
+                tok[b, i] = am[b, r]
     ts = 0 if shared else N
     say(f"[tree] random small shared={shared}")
     o = oracle.verify_tree(logits, np.broadcast_to(par, (Bn, N)).copy(),
