@@ -121,6 +121,15 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _keep(args, *objs):
+    """The structs carry raw device addresses: hold the tensors they came from for as long
+    as the struct lives, so that a tensor passed inline is not freed (and its memory reused,
+    e.g. by the workspace) before the kernels run."""
+    held = getattr(args, "_held", [])
+    held.extend(o for o in objs if o is not None and not isinstance(o, int))
+    args._held = held
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -167,6 +176,9 @@ def chain_args(*, target_logits, cu_gamma, temperature, committed_len, out_token
     a.probe_seq = _ptr(probe_seq)
     a.uniform_override = _ptr(uniform_override)
     a.profile_events = profile_events
+    _keep(a, target_logits, draft_logits, cu_gamma, draft_tokens, temperature, top_p, top_k,
+          seq_id, committed_len, out_tokens, num_accepted, seq_flags, probe_rows, probe_seq,
+          uniform_override)
     return a
 
 
@@ -203,6 +215,8 @@ def tree_args(*, target_logits, parent, node_row, node_token, path_nodes, path_l
     a.out_tokens = _ptr(out_tokens)
     a.num_emitted = _ptr(num_emitted)
     a.seq_flags = _ptr(seq_flags)
+    _keep(a, target_logits, parent, node_row, node_token, path_nodes, path_len, out_tokens,
+          num_emitted, seq_flags)
     return a
 
 
@@ -239,6 +253,7 @@ def kv_args(*, k_cache, v_cache, path_nodes, path_len, committed_len, num_kv_hea
     a.path_len = _ptr(path_len)
     a.committed_len = _ptr(committed_len)
     a.seq_flags = _ptr(seq_flags)
+    _keep(a, path_nodes, path_len, committed_len, seq_flags, *k_cache, *v_cache)
     return a
 
 

@@ -38,11 +38,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // largest). Rows whose nucleus reaches further down take the exact multi-pass search.
 constexpr float kCaptureK = 7.0f;
 constexpr int kCapV = 1024;   // captured 8-logit vector indices per row
-constexpr int kCapEl = 256;   // captured logits inside the final window per row
-constexpr int kElPerLane = kCapEl / kWave;
+constexpr int kHist = 512;    // key offsets below the row max resolved by the window search
 constexpr int kResolveThreads = 256;
 constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass (V <= 2^19)
 constexpr double kFix = 17592186044416.0;  // 2^44: fixed-point scale of masses
+// A trip whose weights, taken against the lane's previous maximum, may exceed 2^100 is
+// recomputed against its own maximum (first trip of a row, or a large jump at small T).
+constexpr float kTripBig = 1.2676506e30f;  // 2^100
 
 struct ChainParams {
   const uint16_t* target;
@@ -71,10 +73,12 @@ struct CapBuf {
   int32_t vidx[kCapV];
 };
 
-struct ElBuf {
-  uint32_t key[kCapEl];
-  uint32_t idx[kCapEl];
-  uint32_t sidx[kWave];  // staging of a nucleus list before it is sorted
+// Threshold search state: fixed-point mass per key offset below the row max (integer
+// additions, so the sums do not depend on the order of the atomics), and the staging area
+// of a nucleus list.
+struct SelBuf {
+  unsigned long long hist[kHist];
+  uint32_t sidx[kWave];
   float sw[kWave];
 };
 
@@ -85,6 +89,18 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t fixw(float w) {
   return (uint64_t)((double)w * kFix);
+}
+
+// Parameters checked on their bit patterns (NaN fails every test). T: >= 0 (or -0), not NaN;
+// +inf is allowed (a flat law).
+__device__ __forceinline__ bool temperature_ok(float T) {
+  const uint32_t b = __float_as_uint(T);
+  return (b & 0x80000000u) ? (b == 0x80000000u) : (b <= 0x7F800000u);
+}
+// top_p: 0 < P <= 1.
+__device__ __forceinline__ bool top_p_ok(float P) {
+  const uint32_t b = __float_as_uint(P);
+  return b != 0u && b <= 0x3F800000u;
 }
 
 // Sequence parameters shared by the two kernels.
@@ -109,8 +125,9 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
   s.T = P.temp[b];
   s.P = P.topp ? P.topp[b] : 1.0f;
   s.bad_param = !(s.g >= 0 && s.g <= P.max_gamma && c0 >= 0 && c1 <= P.n_draft) ||
-                !(s.T >= 0.0f) || !(s.P > 0.0f && s.P <= 1.0f) ||
-                (s.T > 0.0f && s.g > 0 && P.draft == nullptr);
+                !temperature_ok(s.T) || !top_p_ok(s.P) ||
+                (s.T != 0.0f && s.g > 0 && P.draft == nullptr);
+  if (s.T == 0.0f) s.T = 0.0f;  // -0 is greedy too
   return s;
 }
 
@@ -119,35 +136,57 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
 // ----------------------------------------------------------------------------------------
 
 struct LaneAcc {
-  float m = -INFINITY;  // running max of this lane's logits
-  float s = 0.0f;       // sum of exp2((l - m) * c) over this lane's logits
-  float wm = -INFINITY; // running max of the whole wave (capture threshold)
-  int cnt = 0;          // captured vectors (wave-uniform)
+  float m = -INFINITY;   // running max of this lane's logits
+  float s = 0.0f;        // sum of exp2((l - m) * c) over this lane's logits
+  float wm = -INFINITY;  // running max of the whole wave (capture threshold)
+  int cnt = 0;           // captured vectors (wave-uniform)
 };
 
+// Weight of one logit relative to a reference: the same expression everywhere, so that
+// masses and probabilities computed in different places agree bit for bit.
+__device__ __forceinline__ float weight(float l, float c, float nref) {
+  return __builtin_amdgcn_exp2f(fmaf(l, c, nref));
+}
+
+// One trip (kU vectors of one row) into the lane's running (m, s). The weights are taken
+// against the lane's previous maximum; only when the trip raises it (rare after the first
+// trips) is the trip's partial sum re-referenced, or recomputed when it may have overflowed.
 template <bool CAPTURE>
-__device__ __forceinline__ void accumulate_trip(const uint4 d[kU], int v0, int lane, float c,
-                                                float capw, LaneAcc& a, CapBuf* cap) {
+__device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane, float c,
+                                             float capw, LaneAcc& a, CapBuf* cap) {
+  const float ref = (a.m == -INFINITY) ? 0.0f : a.m;
+  const float nref = -ref * c;
   float vm[kU];
-  float s = a.s;
+  float st = 0.0f;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     float x[8];
     unpack8(d[u], x);
     vm[u] = max8(x);
-    if (vm[u] > a.m) {  // new lane maximum: rescale the running sum (rare after warm-up)
-      s *= __builtin_amdgcn_exp2f((a.m - vm[u]) * c);
-      a.m = vm[u];
-    }
-    const float nref = (a.m == -INFINITY) ? 0.0f : -a.m * c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], c, nref));
+    for (int e = 0; e < 8; ++e) st += weight(x[e], c, nref);
   }
-  a.s = s;
-  if (CAPTURE) {
-    float tm = vm[0];
+  static_assert(kU == 4, "trip max below assumes four vectors per trip");
+  const float tm = vmax3(vmax3(vm[0], vm[1], vm[2]), vm[3], vm[3]);
+  if (tm > a.m) {
+    if (st < kTripBig) {
+      st *= __builtin_amdgcn_exp2f((ref - tm) * c);
+    } else {
+      st = 0.0f;
+      const float nt = -tm * c;
 #pragma unroll
-    for (int u = 1; u < kU; ++u) tm = fmaxf(tm, vm[u]);
+      for (int u = 0; u < kU; ++u) {
+        float x[8];
+        unpack8(d[u], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st += weight(x[e], c, nt);
+      }
+    }
+    a.s *= __builtin_amdgcn_exp2f((a.m - tm) * c);  // 0 while a.m = -inf (a.s = 0 then)
+    a.m = tm;
+  }
+  a.s += st;
+  if (CAPTURE) {
     a.wm = fmaxf(a.wm, wave_max(tm));
     const float thr = a.wm - capw;
 #pragma unroll
@@ -171,12 +210,6 @@ __device__ __forceinline__ void finish_mz(const LaneAcc& a, float c, float& M, f
   Z = wave_sum(s);
 }
 
-// Weight of one logit relative to the row max: the same expression everywhere, so that
-// masses and probabilities computed in different places agree bit for bit.
-__device__ __forceinline__ float weight(float l, float c, float nref) {
-  return __builtin_amdgcn_exp2f(fmaf(l, c, nref));
-}
-
 struct TopP {
   float t;     // threshold logit (-inf: keep all)
   float zs;    // normaliser over the kept set
@@ -186,181 +219,202 @@ struct TopP {
 
 // Appends the flagged lanes' (idx, w) to the staging list in LDS, in lane order. Returns the
 // new length (a length above kWave means the list overflowed and is incomplete).
-__device__ __forceinline__ int stage_append(bool in, uint32_t idx, float w, int n, ElBuf* el) {
+__device__ __forceinline__ int stage_append(bool in, uint32_t idx, float w, int n, SelBuf* sb) {
   const uint64_t mask = __ballot(in);
   const int slot = n + (int)lanes_below(mask);
   if (in && slot < kWave) {
-    el->sidx[slot] = idx;
-    el->sw[slot] = w;
+    sb->sidx[slot] = idx;
+    sb->sw[slot] = w;
   }
   return n + __popcll(mask);
 }
 
 // Writes the staged list (n <= kNucMax entries) to the workspace sorted by token id.
-__device__ __forceinline__ void write_sorted_list(NucEntry* out, int n, const ElBuf* el,
+__device__ __forceinline__ void write_sorted_list(NucEntry* out, int n, const SelBuf* sb,
                                                   int lane) {
-  const uint32_t idx = lane < n ? el->sidx[lane] : 0xFFFFFFFFu;
-  const float w = lane < n ? el->sw[lane] : 0.0f;
+  const uint32_t idx = lane < n ? sb->sidx[lane] : 0xFFFFFFFFu;
+  const float w = lane < n ? sb->sw[lane] : 0.0f;
   int rank = 0;
   for (int j = 0; j < n; ++j) rank += (__shfl(idx, j, kWave) < idx) ? 1 : 0;
   if (lane < n) out[rank] = NucEntry{(int32_t)idx, w};
 }
 
-// Exact threshold search over the whole row (16 passes, fixed-point masses): the largest
-// bf16 key t with mass(key >= t) >= thrP. Used when the capture window missed the nucleus.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)v, o, kWave);
+    const uint32_t hi = __shfl_up((uint32_t)(v >> 32), o, kWave);
+    if (lane >= o) v += ((uint64_t)hi << 32) | lo;
+  }
+  return v;
+}
+
+// First bucket (in increasing index = decreasing logit) at which base + the cumulative mass
+// reaches thr; -1 if the buckets never get there. *cum receives the cumulative mass at that
+// bucket (or base + the total). nb is a multiple of 64; each lane scans nb/64 buckets.
+__device__ int hist_crossing(const unsigned long long* h, int nb, uint64_t thr, uint64_t base,
+                             uint64_t* cum, int lane) {
+  const int per = nb / kWave;
+  uint64_t mine = 0;
+  for (int j = 0; j < per; ++j) mine += h[lane * per + j];
+  const uint64_t incl = base + wave_incl_scan_u64(mine, lane);
+  const uint64_t hit = __ballot(incl >= thr);
+  if (!hit) {
+    *cum = __shfl(incl, kWave - 1, kWave);
+    return -1;
+  }
+  const int src = __ffsll((long long)hit) - 1;
+  int o = -1;
+  uint64_t c = 0;
+  if (lane == src) {
+    c = incl - mine;
+    for (int j = 0; j < per; ++j) {
+      c += h[lane * per + j];
+      if (c >= thr) {
+        o = lane * per + j;
+        break;
+      }
+    }
+  }
+  o = __shfl(o, src, kWave);
+  const uint32_t lo = __shfl((uint32_t)c, src, kWave), hi = __shfl((uint32_t)(c >> 32), src, kWave);
+  *cum = ((uint64_t)hi << 32) | lo;
+  return o;
+}
+
+// Nucleus list of a row once t is known: every logit >= t, from the given vectors.
+template <typename VecAt>
+__device__ int collect_list(VecAt vec_at, int nv, int V, float t, float c, float nref,
+                            SelBuf* sb, int lane) {
+  int n = 0;
+  for (int i0 = 0; i0 < nv && n <= kNucMax; i0 += kWave) {
+    const int i = i0 + lane;
+    float x[8];
+    int vi = 0;
+    if (i < nv) {
+      vi = vec_at(i);
+      unpack8(vec_at.load(vi), x);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool in = i < nv && (vi * 8 + e < V) && x[e] >= t;
+      n = stage_append(in, (uint32_t)(vi * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n, sb);
+    }
+  }
+  return n;
+}
+
+struct AllVecs {
+  const uint4* row;
+  __device__ int operator()(int i) const { return i; }
+  __device__ uint4 load(int vi) const { return row[vi]; }
+};
+struct CapVecs {
+  const uint4* row;
+  const CapBuf* cap;
+  __device__ int operator()(int i) const { return cap->vidx[i]; }
+  __device__ uint4 load(int vi) const { return row[vi]; }
+};
+
+__device__ void finish_list(TopP& r, int n, NucEntry* list, SelBuf* sb, int lane) {
+  __syncthreads();
+  if (n > kNucMax) {
+    r.nuc = -1;
+  } else {
+    r.nuc = n;
+    write_sorted_list(list, n, sb, lane);
+  }
+  __syncthreads();
+}
+
+// Exact threshold search over the whole row: the largest bf16 key t with
+// mass(key >= t) >= thrP, by a 256-bucket fixed-point histogram of the key offset's high byte
+// and then of its low byte inside the chosen bucket (two passes), plus one pass for the
+// nucleus list. Used when the capture window missed the nucleus.
 __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c,
-                              float M, uint64_t thrP, NucEntry* list, ElBuf* el, int lane) {
+                              float M, uint64_t thrP, NucEntry* list, SelBuf* sb, int lane) {
   const float nref = -M * c;
-  auto mass_at_or_above = [&](uint32_t tkey) -> uint64_t {
-    uint64_t acc = 0;
+  const uint32_t kM = key_of(M);
+  TopP r;
+  r.slow = true;
+  uint64_t cum = 0, base = 0;
+  int hi_b = -1, o_star = -1;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int j = lane; j < kHist; j += kWave) sb->hist[j] = 0ull;
+    __syncthreads();
     for (int v = lane; v < nvec; v += kWave) {
       float x[8];
       unpack8(row[v], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool in = (v * 8 + e < V) && key_of(x[e]) >= tkey;
-        acc += in ? fixw(weight(x[e], c, nref)) : 0ull;
+        if (v * 8 + e >= V) continue;
+        const uint32_t o = kM - key_of(x[e]);
+        if (pass == 1 && (int)(o >> 8) != hi_b) continue;
+        const uint64_t fw = fixw(weight(x[e], c, nref));
+        if (fw) atomicAdd(&sb->hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
       }
     }
-    return wave_sum_u64(acc);
-  };
-  TopP r;
-  r.slow = true;
-  const uint64_t total = mass_at_or_above(0u);
-  if (total < thrP) {  // rounding left the whole row just below P: keep everything
+    __syncthreads();
+    if (pass == 0) {
+      hi_b = hist_crossing(sb->hist, 256, thrP, 0, &cum, lane);
+      if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
+      base = cum - sb->hist[hi_b];
+    } else {
+      o_star = hi_b * 256 + hist_crossing(sb->hist, 256, thrP, base, &cum, lane);
+    }
+    __syncthreads();
+  }
+  if (hi_b < 0) {
     r.t = -INFINITY;
-    r.zs = (float)((double)total / kFix);
   } else {
-    uint32_t lo = 0, hi = 0x10000u;
-    uint64_t zs = total;
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) >> 1;
-      const uint64_t m = mass_at_or_above(mid);
-      if (m >= thrP) {
-        lo = mid;
-        zs = m;
-      } else {
-        hi = mid;
-      }
-    }
-    r.t = value_of_key(lo);
-    r.zs = (float)((double)zs / kFix);
+    r.t = value_of_key(kM - (uint32_t)o_star);
   }
-  __syncthreads();
-  int n = 0;
-  for (int v0 = 0; v0 < nvec && n <= kNucMax; v0 += kWave) {
-    const int v = v0 + lane;
-    float x[8];
-    if (v < nvec) unpack8(row[v], x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool in = v < nvec && (v * 8 + e < V) && x[e] >= r.t;
-      n = stage_append(in, (uint32_t)(v * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n, el);
-    }
-  }
-  __syncthreads();
-  if (n > kNucMax) {
-    r.nuc = -1;
-  } else {
-    r.nuc = n;
-    write_sorted_list(list, n, el, lane);
-  }
+  r.zs = (float)((double)cum / kFix);
+  const int n = collect_list(AllVecs{row}, nvec, V, r.t, c, nref, sb, lane);
+  finish_list(r, n, list, sb, lane);
   return r;
 }
 
-// Threshold search on the captured window. Falls back to the whole row when the window is
-// overfull or does not hold mass P.
+// Threshold search on the captured window: fixed-point masses of the captured logits in a
+// histogram over key offsets below the row max; the first offset at which the running mass
+// reaches P * Z is the threshold. Falls back to the whole row when the window overflowed or
+// does not reach mass P within kHist offsets.
 __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, float c, float P,
-                            float M, float Z, int cnt, const CapBuf* cap, ElBuf* el,
+                            float M, float Z, int cnt, const CapBuf* cap, SelBuf* sb,
                             NucEntry* list, int lane) {
   const float capw = kCaptureK * (kLog2e / c);  // kCaptureK * T in logit units
   const float theta = M - capw;
   const float nref = -M * c;
   const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
+  const uint32_t kM = key_of(M);
   const int nv = min(cnt, kCapV);
-  bool ok = cnt <= kCapV;
-  // expand captured vectors into the logits inside the final window
-  int nel = 0;
+  for (int j = lane; j < kHist; j += kWave) sb->hist[j] = 0ull;
+  __syncthreads();
   for (int i0 = 0; i0 < nv; i0 += kWave) {
     const int i = i0 + lane;
+    if (i >= nv) break;
+    const int vi = cap->vidx[i];
     float x[8];
-    int vi = 0;
-    if (i < nv) {
-      vi = cap->vidx[i];
-      unpack8(row[vi], x);
-    }
+    unpack8(row[vi], x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const bool in = i < nv && (vi * 8 + e < V) && x[e] >= theta;
-      const uint64_t mask = __ballot(in);
-      const int slot = nel + (int)lanes_below(mask);
-      if (in && slot < kCapEl) {
-        el->key[slot] = key_of(x[e]);
-        el->idx[slot] = (uint32_t)(vi * 8 + e);
-      }
-      nel += __popcll(mask);
+      if (vi * 8 + e >= V || !(x[e] >= theta)) continue;
+      const uint32_t o = kM - key_of(x[e]);
+      if (o < (uint32_t)kHist)
+        atomicAdd(&sb->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
     }
   }
   __syncthreads();
-  ok = ok && nel <= kCapEl && nel > 0;
-  uint32_t k[kElPerLane], ix[kElPerLane];
-  uint64_t f[kElPerLane];
-  uint64_t tot = 0;
-  uint32_t kmin = 0xFFFFu, kmax = 0;
-#pragma unroll
-  for (int j = 0; j < kElPerLane; ++j) {
-    const int i = j * kWave + lane;
-    const bool have = ok && i < nel;
-    k[j] = have ? el->key[i] : 0u;
-    ix[j] = have ? el->idx[i] : 0u;
-    f[j] = have ? fixw(weight(value_of_key(k[j]), c, nref)) : 0ull;
-    tot += f[j];
-    if (have) {
-      kmin = min(kmin, k[j]);
-      kmax = max(kmax, k[j]);
-    }
-  }
-  tot = wave_sum_u64(tot);
-  ok = ok && tot >= thrP;
+  uint64_t zs = 0;
+  const int o_star = (cnt <= kCapV) ? hist_crossing(sb->hist, kHist, thrP, 0, &zs, lane) : -1;
   __syncthreads();
-  if (!ok) return topp_full_row(row, nvec, V, c, M, thrP, list, el, lane);
-  kmin = (uint32_t)wave_min_i((int)kmin);
-  kmax = (uint32_t)wave_max_i((int)kmax);
-  // largest key t with mass(key >= t) >= thrP; mass(kmin) = tot >= thrP
-  uint32_t lo = kmin, hi = kmax + 1;
-  uint64_t zs = tot;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
-    uint64_t sm = 0;
-#pragma unroll
-    for (int j = 0; j < kElPerLane; ++j) sm += (k[j] >= mid) ? f[j] : 0ull;
-    sm = wave_sum_u64(sm);
-    if (sm >= thrP) {
-      lo = mid;
-      zs = sm;
-    } else {
-      hi = mid;
-    }
-  }
+  if (o_star < 0) return topp_full_row(row, nvec, V, c, M, thrP, list, sb, lane);
   TopP r;
   r.slow = false;
-  r.t = value_of_key(lo);
+  r.t = value_of_key(kM - (uint32_t)o_star);
   r.zs = (float)((double)zs / kFix);
-  int n = 0;
-#pragma unroll
-  for (int j = 0; j < kElPerLane; ++j) {
-    const int i = j * kWave + lane;
-    const bool in = i < nel && k[j] >= lo;
-    n = stage_append(in, ix[j], in ? weight(value_of_key(k[j]), c, nref) : 0.0f, n, el);
-  }
-  __syncthreads();
-  if (n > kNucMax) {
-    r.nuc = -1;
-  } else {
-    r.nuc = n;
-    write_sorted_list(list, n, el, lane);
-  }
-  __syncthreads();
+  const int n = collect_list(CapVecs{row, cap}, nv, V, r.t, c, nref, sb, lane);
+  finish_list(r, n, list, sb, lane);
   return r;
 }
 
@@ -372,7 +426,7 @@ template <bool TOPP>
 __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
   extern __shared__ uint4 smem_dyn[];
   CapBuf* cap = reinterpret_cast<CapBuf*>(smem_dyn);
-  ElBuf& el = *reinterpret_cast<ElBuf*>(cap + 2);
+  SelBuf* sb = reinterpret_cast<SelBuf*>(cap + 2);
   const int lane = lane_id();
   const int per = P.max_gamma + 1;
   const int b = blockIdx.x / per;
@@ -424,18 +478,35 @@ __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
   const uint4* rq = pair ? reinterpret_cast<const uint4*>(P.draft + (size_t)drow * P.stride)
                          : nullptr;
   LaneAcc ap, aq;
-  for (int v0 = 0; v0 < P.nvec; v0 += kU * kWave) {
-    uint4 dp[kU], dq[kU];
-    load_trip(rp, v0, P.nvec, lane, dp);
-    if (pair) load_trip(rq, v0, P.nvec, lane, dq);
+  // Double-buffered: the next trip's loads are in flight while this trip is consumed.
+  constexpr int kStep = kU * kWave;
+  uint4 p0[kU], q0[kU], p1[kU], q1[kU];
+  load_trip(rp, 0, P.nvec, lane, p0);
+  if (pair) load_trip(rq, 0, P.nvec, lane, q0);
+  auto consume = [&](uint4* dp, uint4* dq, int v0) {
     mask_tail(dp, v0, P.nvec, P.V, lane);
-    if (topp) accumulate_trip<true>(dp, v0, lane, c, capw, ap, &cap[0]);
-    else accumulate_trip<false>(dp, v0, lane, c, capw, ap, nullptr);
+    if (topp) consume_trip<true>(dp, v0, lane, c, capw, ap, &cap[0]);
+    else consume_trip<false>(dp, v0, lane, c, capw, ap, nullptr);
     if (pair) {
       mask_tail(dq, v0, P.nvec, P.V, lane);
-      if (topp) accumulate_trip<true>(dq, v0, lane, c, capw, aq, &cap[1]);
-      else accumulate_trip<false>(dq, v0, lane, c, capw, aq, nullptr);
+      if (topp) consume_trip<true>(dq, v0, lane, c, capw, aq, &cap[1]);
+      else consume_trip<false>(dq, v0, lane, c, capw, aq, nullptr);
     }
+  };
+  for (int v0 = 0; v0 < P.nvec; v0 += 2 * kStep) {
+    const int v1 = v0 + kStep;
+    if (v1 < P.nvec) {
+      load_trip(rp, v1, P.nvec, lane, p1);
+      if (pair) load_trip(rq, v1, P.nvec, lane, q1);
+    }
+    consume(p0, q0, v0);
+    if (v1 >= P.nvec) break;
+    const int v2 = v1 + kStep;
+    if (v2 < P.nvec) {
+      load_trip(rp, v2, P.nvec, lane, p0);
+      if (pair) load_trip(rq, v2, P.nvec, lane, q0);
+    }
+    consume(p1, q1, v1);
   }
   __syncthreads();
   float Mp, Zp, Mq = 0.0f, Zq = 1.0f;
@@ -443,12 +514,10 @@ __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
   if (pair) finish_mz(aq, c, Mq, Zq);
   TopP tp{-INFINITY, Zp, -1, false}, tq{-INFINITY, Zq, -1, false};
   if (topp) {
-    tp = topp_select(rp, P.nvec, P.V, c, s.P, Mp, Zp, ap.cnt, &cap[0], &el, lists, lane);
-    if (pair) {
-      __syncthreads();
-      tq = topp_select(rq, P.nvec, P.V, c, s.P, Mq, Zq, aq.cnt, &cap[1], &el,
-                       lists + kNucMax, lane);
-    }
+    tp = topp_select(rp, P.nvec, P.V, c, s.P, Mp, Zp, ap.cnt, &cap[0], sb, lists, lane);
+    if (pair)
+      tq = topp_select(rq, P.nvec, P.V, c, s.P, Mq, Zq, aq.cnt, &cap[1], sb, lists + kNucMax,
+                       lane);
     if (tp.slow || tq.slow) flags |= SPEC_FLAG_TOPP_SLOW;
   }
   float pd = NAN, qd = NAN, a = NAN;
@@ -886,7 +955,7 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   const unsigned grid = (unsigned)a.batch * (unsigned)(a.max_gamma + 1);
   if (a.top_p)
     hipLaunchKernelGGL(chain_row_kernel<true>, dim3(grid), dim3(kWave),
-                       2 * sizeof(CapBuf) + sizeof(ElBuf), st, P);
+                       2 * sizeof(CapBuf) + sizeof(SelBuf), st, P);
   else
     hipLaunchKernelGGL(chain_row_kernel<false>, dim3(grid), dim3(kWave), 0, st, P);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -41,30 +41,54 @@ __device__ __forceinline__ void mask_tail(uint4 d[kU], int v0, int nvec, int V, 
 }
 
 // ----------------------------------------------------------------------------------------
-// Greedy rows: argmax with the lowest index on ties.
+// Greedy rows: argmax with the lowest index on ties. Loads are double-buffered; the lane's
+// best is only revisited when a trip holds a larger value (rare after the first trips).
 // ----------------------------------------------------------------------------------------
+__device__ __forceinline__ void argmax_trip(uint4 d[kU], int v0, int nvec, int V, int lane,
+                                            float& bv, int& bi) {
+  mask_tail(d, v0, nvec, V, lane);
+  float vm[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    float x[8];
+    unpack8(d[u], x);
+    vm[u] = max8(x);
+  }
+  static_assert(kU == 4, "trip max below assumes four vectors per trip");
+  const float tm = vmax3(vmax3(vm[0], vm[1], vm[2]), vm[3], vm[3]);
+  if (tm > bv) {  // this lane's earliest occurrence of tm in the trip
+    int found = 0x7FFFFFFF;
+#pragma unroll
+    for (int u = kU - 1; u >= 0; --u) {
+      if (vm[u] == tm) {
+        float x[8];
+        unpack8(d[u], x);
+        int e = 7;
+#pragma unroll
+        for (int j = 7; j >= 0; --j)
+          if (x[j] == tm) e = j;
+        found = (v0 + u * kWave + lane) * 8 + e;
+      }
+    }
+    bv = tm;
+    bi = found;
+  }
+}
+
 __device__ __forceinline__ int row_argmax(const uint4* __restrict__ row, int nvec, int V,
                                           int lane) {
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int v0 = 0; v0 < nvec; v0 += kU * kWave) {
-    uint4 d[kU];
-    load_trip(row, v0, nvec, lane, d);
-    mask_tail(d, v0, nvec, V, lane);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      float x[8];
-      unpack8(d[u], x);
-      const float vm = max8(x);
-      if (vm > bv) {  // this lane's vectors come in increasing index order
-        int e = 7;
-#pragma unroll
-        for (int j = 7; j >= 0; --j)
-          if (x[j] == vm) e = j;
-        bv = vm;
-        bi = (v0 + u * kWave + lane) * 8 + e;
-      }
-    }
+  constexpr int kStep = kU * kWave;
+  uint4 a[kU], b[kU];
+  load_trip(row, 0, nvec, lane, a);
+  for (int v0 = 0; v0 < nvec; v0 += 2 * kStep) {
+    const int v1 = v0 + kStep;
+    if (v1 < nvec) load_trip(row, v1, nvec, lane, b);
+    argmax_trip(a, v0, nvec, V, lane, bv, bi);
+    if (v1 >= nvec) break;
+    if (v1 + kStep < nvec) load_trip(row, v1 + kStep, nvec, lane, a);
+    argmax_trip(b, v1, nvec, V, lane, bv, bi);
   }
   wave_argmax(bv, bi);
   return bi == 0x7FFFFFFF ? 0 : bi;
