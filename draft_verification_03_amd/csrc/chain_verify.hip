@@ -37,9 +37,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Top-p capture window: logits within kCaptureK * T of the row max (weight >= e^-7 of the
 // largest). Rows whose nucleus reaches further down take the exact multi-pass search.
 constexpr float kCaptureK = 7.0f;
-constexpr int kCapV = 1024;   // captured 8-logit vector indices per row
+constexpr int kCapLane = 32;  // captured vector ids per lane per row
+constexpr int kRefresh = 2;   // trips between refreshes of the capture threshold
+constexpr int kEndB = 8;      // captured vectors per lane the end phase holds in registers
 constexpr int kHist = 512;    // key offsets below the row max resolved by the window search
-constexpr int kResolveThreads = 256;
+constexpr int kResolveThreads = 1024;
+constexpr int kTilesPerIter = 4;  // row-pair tiles in flight per wave in the resolve pass
 constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass (V <= 2^19)
 constexpr double kFix = 17592186044416.0;  // 2^44: fixed-point scale of masses
 // A trip whose weights, taken against the lane's previous maximum, may exceed 2^100 is
@@ -67,20 +70,27 @@ struct ChainParams {
   uint32_t seed_lo, seed_hi;
 };
 
-// Indices of the captured vectors; the vectors themselves (about 1% of the row) are read
-// again in the end phase.
+// Ids of the captured vectors (16 bits: a row has at most 65536 vectors); the vectors
+// themselves (about 1% of the row) are read again in the end phase. During the stream each
+// lane appends to its own list, with no cross-lane traffic; the end phase compacts the lists
+// in lane order.
 struct CapBuf {
-  int32_t vidx[kCapV];
+  uint16_t lane[kCapLane][kWave];
 };
 
 // Threshold search state: fixed-point mass per key offset below the row max (integer
 // additions, so the sums do not depend on the order of the atomics), and the staging area
-// of a nucleus list.
-struct SelBuf {
+// of a nucleus list. The list is staged only after the threshold is known, behind a
+// barrier, so the two share their storage.
+union SelBuf {
   unsigned long long hist[kHist];
-  uint32_t sidx[kWave];
-  float sw[kWave];
+  struct {
+    uint32_t sidx[kNucMax];
+    float sw[kNucMax];
+  };
+  uint16_t flat[kCapLane * kWave];  // compacted capture ids, before the threshold search
 };
+static_assert(sizeof(SelBuf) == kHist * 8, "list staging fits in the histogram's storage");
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -138,8 +148,8 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
 struct LaneAcc {
   float m = -INFINITY;   // running max of this lane's logits
   float s = 0.0f;        // sum of exp2((l - m) * c) over this lane's logits
-  float wm = -INFINITY;  // running max of the whole wave (capture threshold)
-  int cnt = 0;           // captured vectors (wave-uniform)
+  float wm = -INFINITY;  // the wave's max at the last refresh (capture threshold)
+  int cnt = 0;           // vectors this lane captured (may exceed kCapLane: overflow)
 };
 
 // Weight of one logit relative to a reference: the same expression everywhere, so that
@@ -187,16 +197,17 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
   }
   a.s += st;
   if (CAPTURE) {
-    a.wm = fmaxf(a.wm, wave_max(tm));
-    const float thr = a.wm - capw;
+    // Threshold: the larger of the lane's own max and the wave's max at its last refresh,
+    // less the window. Both are lower bounds of the row max, so every vector within the
+    // final window is captured (with some extra ones).
+    if ((v0 / (kU * kWave)) % kRefresh == 0) a.wm = wave_max_dpp(a.m);
+    // finite, so a vector of -inf logits (past the row end included) is never captured
+    const float thr = vmax3(vmax3(a.wm, a.m, a.m) - capw, -3.4028235e38f, -3.4028235e38f);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool want = vm[u] >= thr;
-      const uint64_t mask = __ballot(want);
-      if (mask) {
-        const int slot = a.cnt + (int)lanes_below(mask);
-        if (want && slot < kCapV) cap->vidx[slot] = v0 + u * kWave + lane;
-        a.cnt += __popcll(mask);
+      if (vm[u] >= thr) {
+        if (a.cnt < kCapLane) cap->lane[a.cnt][lane] = (uint16_t)(v0 + u * kWave + lane);
+        ++a.cnt;
       }
     }
   }
@@ -218,25 +229,27 @@ struct TopP {
 };
 
 // Appends the flagged lanes' (idx, w) to the staging list in LDS, in lane order. Returns the
-// new length (a length above kWave means the list overflowed and is incomplete).
+// new length (a length above kNucMax means the list overflowed and is incomplete).
 __device__ __forceinline__ int stage_append(bool in, uint32_t idx, float w, int n, SelBuf* sb) {
   const uint64_t mask = __ballot(in);
   const int slot = n + (int)lanes_below(mask);
-  if (in && slot < kWave) {
+  if (in && slot < kNucMax) {
     sb->sidx[slot] = idx;
     sb->sw[slot] = w;
   }
   return n + __popcll(mask);
 }
 
-// Writes the staged list (n <= kNucMax entries) to the workspace sorted by token id.
+// Writes the staged list (n <= kNucMax entries, distinct token ids) to the workspace sorted
+// by token id: each entry's rank is the number of staged ids below it.
 __device__ __forceinline__ void write_sorted_list(NucEntry* out, int n, const SelBuf* sb,
                                                   int lane) {
-  const uint32_t idx = lane < n ? sb->sidx[lane] : 0xFFFFFFFFu;
-  const float w = lane < n ? sb->sw[lane] : 0.0f;
-  int rank = 0;
-  for (int j = 0; j < n; ++j) rank += (__shfl(idx, j, kWave) < idx) ? 1 : 0;
-  if (lane < n) out[rank] = NucEntry{(int32_t)idx, w};
+  for (int j = lane; j < n; j += kWave) {
+    const uint32_t idx = sb->sidx[j];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += (sb->sidx[i] < idx) ? 1 : 0;
+    out[rank] = NucEntry{(int32_t)idx, sb->sw[j]};
+  }
 }
 
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
@@ -309,12 +322,80 @@ struct AllVecs {
   __device__ int operator()(int i) const { return i; }
   __device__ uint4 load(int vi) const { return row[vi]; }
 };
-struct CapVecs {
-  const uint4* row;
-  const CapBuf* cap;
-  __device__ int operator()(int i) const { return cap->vidx[i]; }
-  __device__ uint4 load(int vi) const { return row[vi]; }
+
+// The captured vectors of a row as the end phase holds them: the lanes' lists compacted in
+// lane order, entry j * 64 + lane in d[j] with its vector id in vi[j] (-inf / 0 past n).
+struct Held {
+  uint4 d[kEndB];
+  int vi[kEndB];
+  int n = 0;          // entries in all lists
+  int cl = 0;         // entries in this lane's list
+  bool over = false;  // a lane's list overflowed: the search reads the whole row
 };
+
+// Compacts the lanes' lists (through flat, in LDS) and issues the loads of the first
+// kEndB * 64 captured vectors. Called for both rows of an item before either is used, so
+// the end phase waits for one round trip instead of one per 64 captured vectors.
+__device__ __forceinline__ void gather_captured(const uint4* __restrict__ row,
+                                                const CapBuf* cap, int cnt, uint16_t* flat,
+                                                int lane, Held& h) {
+  h.over = __ballot(cnt > kCapLane) != 0;
+  h.cl = min(cnt, kCapLane);
+  const int incl = (int)wave_incl_scan((float)h.cl, lane);  // counts <= 2048: exact in fp32
+  h.n = __shfl(incl, kWave - 1, kWave);
+  __syncthreads();  // flat's previous contents have been read
+  for (int j = 0, o = incl - h.cl; j < h.cl; ++j) flat[o + j] = cap->lane[j][lane];
+  __syncthreads();
+  const int nl = h.over ? 0 : min(h.n, kEndB * kWave);
+#pragma unroll
+  for (int j = 0; j < kEndB; ++j) {
+    const int i = j * kWave + lane;
+    h.vi[j] = i < nl ? (int)flat[i] : 0;
+    h.d[j] = i < nl ? row[h.vi[j]]
+                    : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+  }
+}
+
+// Nucleus list from held vectors (h.n <= kEndB * 64).
+__device__ __forceinline__ int collect_held(const Held& h, int V, float t, float c, float nref,
+                                            SelBuf* sb, int lane) {
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < kEndB; ++j) {  // fully unrolled: h.d[] stays in registers
+    if (j * kWave < h.n && n <= kNucMax) {
+      const int i = j * kWave + lane;
+      const int vi = h.vi[j];
+      float x[8];
+      unpack8(h.d[j], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in = i < h.n && (vi * 8 + e < V) && x[e] >= t;
+        n = stage_append(in, (uint32_t)(vi * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n,
+                         sb);
+      }
+    }
+  }
+  return n;
+}
+
+// Nucleus list straight from the lanes' lists (rows with more than kEndB * 64 captures).
+__device__ int collect_lanes(const uint4* __restrict__ row, const CapBuf* cap, int cl, int V,
+                             float t, float c, float nref, SelBuf* sb, int lane) {
+  int n = 0;
+  const int jmax = wave_max_i(cl);
+  for (int j = 0; j < jmax && n <= kNucMax; ++j) {
+    const bool has = j < cl;
+    const int vi = has ? (int)cap->lane[j][lane] : 0;
+    float x[8];
+    unpack8(has ? row[vi] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool in = has && (vi * 8 + e < V) && x[e] >= t;
+      n = stage_append(in, (uint32_t)(vi * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n, sb);
+    }
+  }
+  return n;
+}
 
 __device__ void finish_list(TopP& r, int n, NucEntry* list, SelBuf* sb, int lane) {
   __syncthreads();
@@ -379,23 +460,22 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
 // histogram over key offsets below the row max; the first offset at which the running mass
 // reaches P * Z is the threshold. Falls back to the whole row when the window overflowed or
 // does not reach mass P within kHist offsets.
-__device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, float c, float P,
-                            float M, float Z, int cnt, const CapBuf* cap, SelBuf* sb,
-                            NucEntry* list, int lane) {
+__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V,
+                                            float c, float P, float M, float Z,
+                                            const CapBuf* cap, const Held& h, SelBuf* sb,
+                                            NucEntry* list, int lane) {
   const float capw = kCaptureK * (kLog2e / c);  // kCaptureK * T in logit units
   const float theta = M - capw;
   const float nref = -M * c;
   const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
   const uint32_t kM = key_of(M);
-  const int nv = min(cnt, kCapV);
+  if (h.over) return topp_full_row(row, nvec, V, c, M, thrP, list, sb, lane);
+  const bool in_regs = h.n <= kEndB * kWave;
   for (int j = lane; j < kHist; j += kWave) sb->hist[j] = 0ull;
   __syncthreads();
-  for (int i0 = 0; i0 < nv; i0 += kWave) {
-    const int i = i0 + lane;
-    if (i >= nv) break;
-    const int vi = cap->vidx[i];
+  auto add = [&](const uint4& d, int vi) {
     float x[8];
-    unpack8(row[vi], x);
+    unpack8(d, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (vi * 8 + e >= V || !(x[e] >= theta)) continue;
@@ -403,23 +483,38 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
       if (o < (uint32_t)kHist)
         atomicAdd(&sb->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
     }
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kEndB; ++j)  // fully unrolled: h.d[] stays in registers
+      if (j * kWave + lane < h.n) add(h.d[j], h.vi[j]);
+  } else {
+    const int jmax = wave_max_i(h.cl);
+    for (int j = 0; j < jmax; ++j)
+      if (j < h.cl) {
+        const int vi = (int)cap->lane[j][lane];
+        add(row[vi], vi);
+      }
   }
   __syncthreads();
   uint64_t zs = 0;
-  const int o_star = (cnt <= kCapV) ? hist_crossing(sb->hist, kHist, thrP, 0, &zs, lane) : -1;
+  const int o_star = hist_crossing(sb->hist, kHist, thrP, 0, &zs, lane);
   __syncthreads();
   if (o_star < 0) return topp_full_row(row, nvec, V, c, M, thrP, list, sb, lane);
   TopP r;
   r.slow = false;
   r.t = value_of_key(kM - (uint32_t)o_star);
   r.zs = (float)((double)zs / kFix);
-  const int n = collect_list(CapVecs{row, cap}, nv, V, r.t, c, nref, sb, lane);
+  const int n = in_regs ? collect_held(h, V, r.t, c, nref, sb, lane)
+                        : collect_lanes(row, cap, h.cl, V, r.t, c, nref, sb, lane);
   finish_list(r, n, list, sb, lane);
   return r;
 }
 
 // ----------------------------------------------------------------------------------------
-// Kernel 1: one wave per (sequence, position) item.
+// Kernel 1: one wave per draft position (sequence b, k = 1..gamma_b): the target row p_k and
+// the draft row q_k. The bonus row p_{gamma_b+1} is only needed when every draft is
+// accepted, so the resolve step computes its law then, and only then.
 // ----------------------------------------------------------------------------------------
 // TOPP: the batch carries a top-p array, so capture buffers live in (dynamic) LDS.
 template <bool TOPP>
@@ -428,33 +523,33 @@ __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
   CapBuf* cap = reinterpret_cast<CapBuf*>(smem_dyn);
   SelBuf* sb = reinterpret_cast<SelBuf*>(cap + 2);
   const int lane = lane_id();
-  const int per = P.max_gamma + 1;
-  const int b = blockIdx.x / per;
-  const int k = blockIdx.x % per + 1;  // 1-based position
+  const int b = blockIdx.x / P.max_gamma;
+  const int k = blockIdx.x % P.max_gamma + 1;  // 1-based position
   const SeqInfo s = seq_info(P, b);
-  if (s.bad_param || k > s.g + 1) return;
+  if (s.bad_param || k > s.g) return;
   const int trow = s.t0 + k - 1;
-  const bool pair = k <= s.g;
   const int drow = s.d0 + k - 1;
   RowRec* rec = P.rec + trow;
   NucEntry* lists = P.nuc + (size_t)trow * 2 * kNucMax;
   const uint4* rp = reinterpret_cast<const uint4*>(P.target + (size_t)trow * P.stride);
   int flags = 0;
-  int d = -1;
-  if (pair) {
-    d = P.tokens[drow];
-    if (d < 0 || d >= P.V) flags |= SPEC_FLAG_BAD_TOKEN;
+  const int d = P.tokens[drow];
+  if (d < 0 || d >= P.V) flags |= SPEC_FLAG_BAD_TOKEN;
+  uint32_t lp_bits = 0, lq_bits = 0;  // the draft token's target and draft logits
+  if (!(flags & SPEC_FLAG_BAD_TOKEN) && s.T != 0.0f) {  // issued early, used last
+    lp_bits = P.target[(size_t)trow * P.stride + d];
+    lq_bits = P.draft[(size_t)drow * P.stride + d];
   }
 
   if (s.T == 0.0f) {  // greedy: argmax of the target row; q is not read
     const int am = row_argmax(rp, P.nvec, P.V, lane);
     if (lane == 0) {
-      const int acc = (pair && !(flags & SPEC_FLAG_BAD_TOKEN) && d == am) ? 1 : 0;
+      const int acc = (!(flags & SPEC_FLAG_BAD_TOKEN) && d == am) ? 1 : 0;
       RowRec r;
       r.m[0] = r.m[1] = 0.0f;
       r.z[0] = r.z[1] = 1.0f;
       r.t[0] = r.t[1] = -INFINITY;
-      r.pd = (pair && d == am) ? 1.0f : 0.0f;
+      r.pd = (d == am) ? 1.0f : 0.0f;
       r.qd = NAN;
       r.argmax = am;
       r.accept = acc;
@@ -463,7 +558,7 @@ __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
       r.valid = 1;
       r.pad[0] = r.pad[1] = 0;
       *rec = r;
-      if (pair && P.probe_rows) {
+      if (P.probe_rows) {
         P.probe_rows[(size_t)drow * 3 + 0] = r.pd;
         P.probe_rows[(size_t)drow * 3 + 1] = NAN;
         P.probe_rows[(size_t)drow * 3 + 2] = (float)acc;
@@ -475,58 +570,60 @@ __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
   const float c = kLog2e / s.T;
   const bool topp = TOPP && s.P < 1.0f;
   const float capw = kCaptureK * s.T;
-  const uint4* rq = pair ? reinterpret_cast<const uint4*>(P.draft + (size_t)drow * P.stride)
-                         : nullptr;
+  const uint4* rq = reinterpret_cast<const uint4*>(P.draft + (size_t)drow * P.stride);
   LaneAcc ap, aq;
   // Double-buffered: the next trip's loads are in flight while this trip is consumed.
   constexpr int kStep = kU * kWave;
   uint4 p0[kU], q0[kU], p1[kU], q1[kU];
   load_trip(rp, 0, P.nvec, lane, p0);
-  if (pair) load_trip(rq, 0, P.nvec, lane, q0);
+  load_trip(rq, 0, P.nvec, lane, q0);
   auto consume = [&](uint4* dp, uint4* dq, int v0) {
     mask_tail(dp, v0, P.nvec, P.V, lane);
-    if (topp) consume_trip<true>(dp, v0, lane, c, capw, ap, &cap[0]);
-    else consume_trip<false>(dp, v0, lane, c, capw, ap, nullptr);
-    if (pair) {
-      mask_tail(dq, v0, P.nvec, P.V, lane);
-      if (topp) consume_trip<true>(dq, v0, lane, c, capw, aq, &cap[1]);
-      else consume_trip<false>(dq, v0, lane, c, capw, aq, nullptr);
+    mask_tail(dq, v0, P.nvec, P.V, lane);
+    if (topp) {
+      consume_trip<true>(dp, v0, lane, c, capw, ap, &cap[0]);
+      consume_trip<true>(dq, v0, lane, c, capw, aq, &cap[1]);
+    } else {
+      consume_trip<false>(dp, v0, lane, c, capw, ap, nullptr);
+      consume_trip<false>(dq, v0, lane, c, capw, aq, nullptr);
     }
   };
   for (int v0 = 0; v0 < P.nvec; v0 += 2 * kStep) {
     const int v1 = v0 + kStep;
     if (v1 < P.nvec) {
       load_trip(rp, v1, P.nvec, lane, p1);
-      if (pair) load_trip(rq, v1, P.nvec, lane, q1);
+      load_trip(rq, v1, P.nvec, lane, q1);
     }
     consume(p0, q0, v0);
     if (v1 >= P.nvec) break;
     const int v2 = v1 + kStep;
     if (v2 < P.nvec) {
       load_trip(rp, v2, P.nvec, lane, p0);
-      if (pair) load_trip(rq, v2, P.nvec, lane, q0);
+      load_trip(rq, v2, P.nvec, lane, q0);
     }
     consume(p1, q1, v1);
   }
   __syncthreads();
-  float Mp, Zp, Mq = 0.0f, Zq = 1.0f;
+  Held hp, hq;
+  if (topp) {
+    gather_captured(rp, &cap[0], ap.cnt, sb->flat, lane, hp);
+    gather_captured(rq, &cap[1], aq.cnt, sb->flat, lane, hq);
+  }
+  __syncthreads();  // flat's storage is the threshold search's from here
+  float Mp, Zp, Mq, Zq;
   finish_mz(ap, c, Mp, Zp);
-  if (pair) finish_mz(aq, c, Mq, Zq);
+  finish_mz(aq, c, Mq, Zq);
   TopP tp{-INFINITY, Zp, -1, false}, tq{-INFINITY, Zq, -1, false};
   if (topp) {
-    tp = topp_select(rp, P.nvec, P.V, c, s.P, Mp, Zp, ap.cnt, &cap[0], sb, lists, lane);
-    if (pair)
-      tq = topp_select(rq, P.nvec, P.V, c, s.P, Mq, Zq, aq.cnt, &cap[1], sb, lists + kNucMax,
-                       lane);
+    tp = topp_select(rp, P.nvec, P.V, c, s.P, Mp, Zp, &cap[0], hp, sb, lists, lane);
+    tq = topp_select(rq, P.nvec, P.V, c, s.P, Mq, Zq, &cap[1], hq, sb, lists + kNucMax, lane);
     if (tp.slow || tq.slow) flags |= SPEC_FLAG_TOPP_SLOW;
   }
   float pd = NAN, qd = NAN, a = NAN;
   int acc = 0;
-  if (pair && !(flags & SPEC_FLAG_BAD_TOKEN)) {
-    const uint16_t* tr = P.target + (size_t)trow * P.stride;
-    const uint16_t* dr = P.draft + (size_t)drow * P.stride;
-    const float lp = __uint_as_float((uint32_t)tr[d] << 16);
-    const float lq = __uint_as_float((uint32_t)dr[d] << 16);
+  if (!(flags & SPEC_FLAG_BAD_TOKEN)) {
+    const float lp = __uint_as_float(lp_bits << 16);
+    const float lq = __uint_as_float(lq_bits << 16);
     pd = (lp >= tp.t) ? weight(lp, c, -Mp * c) / tp.zs : 0.0f;
     qd = (lq >= tq.t) ? weight(lq, c, -Mq * c) / tq.zs : 0.0f;
     if (qd > 0.0f) {
@@ -554,11 +651,11 @@ __global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
     r.accept = acc;
     r.flags = flags;
     r.nuc[0] = topp ? tp.nuc : -1;
-    r.nuc[1] = (topp && pair) ? tq.nuc : -1;
+    r.nuc[1] = topp ? tq.nuc : -1;
     r.valid = 1;
     r.pad[0] = r.pad[1] = 0;
     *rec = r;
-    if (pair && P.probe_rows) {
+    if (P.probe_rows) {
       P.probe_rows[(size_t)drow * 3 + 0] = pd;
       P.probe_rows[(size_t)drow * 3 + 1] = qd;
       P.probe_rows[(size_t)drow * 3 + 2] = a;
@@ -576,69 +673,114 @@ struct Draw {
   float wtok;   // weight of the drawn token
 };
 
-// One wave: inverse-CDF draw over a nucleus list sorted by token id (<= 64 entries).
-// residual: weights max(0, p - q) with q looked up in q's list; else p.
+// Weight of token id in a sorted nucleus list held in LDS (0 if absent): binary search.
+__device__ __forceinline__ float list_weight(const NucEntry* q, int nq, int id) {
+  int lo = 0, hi = nq;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (q[mid].idx < id) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < nq && q[lo].idx == id) ? q[lo].w : 0.0f;
+}
+
+constexpr int kPerLane = kNucMax / kWave;  // list entries per lane in a list draw
+
+// One wave: inverse-CDF draw over a nucleus list sorted by token id (<= kNucMax entries;
+// lane l holds entries kPerLane*l .. kPerLane*l + kPerLane-1, so the lanes' order is token
+// order). residual: weights max(0, p - q), q looked up in q's list (in LDS); else p.
 __device__ Draw draw_from_lists(const NucEntry* pl, int np, float zp, const NucEntry* ql,
                                 int nq, float zq, bool residual, float u, int lane) {
-  int idx = 0x7FFFFFFF;
-  float w = 0.0f;
-  if (lane < np) {
-    const NucEntry e = pl[lane];
-    idx = e.idx;
-    w = e.w / zp;
-  }
-  if (residual) {
-    const NucEntry eq = lane < nq ? ql[lane] : NucEntry{-1, 0.0f};
-    float wq = 0.0f;
-    for (int j = 0; j < nq; ++j) {
-      const int qi = __shfl(eq.idx, j, kWave);
-      const float qw = __shfl(eq.w, j, kWave);
-      if (qi == idx) wq = qw / zq;
+  int idx[kPerLane];
+  float w[kPerLane];
+  float ls = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) {
+    const int j = lane * kPerLane + e;
+    idx[e] = 0x7FFFFFFF;
+    w[e] = 0.0f;
+    if (j < np) {
+      const NucEntry en = pl[j];
+      idx[e] = en.idx;
+      w[e] = en.w / zp;
+      if (residual) w[e] = fmaxf(0.0f, w[e] - list_weight(ql, nq, en.idx) / zq);
     }
-    w = fmaxf(0.0f, w - wq);
+    ls += w[e];
   }
-  const float incl = wave_incl_scan(w, lane);
+  const float incl = wave_incl_scan(ls, lane);
   const float total = __shfl(incl, kWave - 1, kWave);
   const float x = u * total;
-  const uint64_t hit = __ballot(lane < np && incl > x);
+  const uint64_t hit = __ballot(incl > x && ls > 0.0f);
+  int tok = -1;
+  float wt = 0.0f;
   int src;
   if (hit) {
     src = __ffsll((long long)hit) - 1;
-  } else {  // rounding left u*total at or past the end: the last token with weight
-    const uint64_t pos = __ballot(lane < np && w > 0.0f);
+    float cum = incl - ls;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      cum += w[e];
+      if (tok < 0 && w[e] > 0.0f && cum > x) {
+        tok = idx[e];
+        wt = w[e];
+      }
+    }
+    if (tok < 0) {  // rounding inside the lane: its last entry with weight
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e)
+        if (w[e] > 0.0f) {
+          tok = idx[e];
+          wt = w[e];
+        }
+    }
+  } else {  // rounding left u*total at or past the end: the last entry with weight
+    const uint64_t pos = __ballot(ls > 0.0f);
     src = pos ? 63 - __clzll((long long)pos) : 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e)
+      if (w[e] > 0.0f) {
+        tok = idx[e];
+        wt = w[e];
+      }
   }
   Draw d;
-  d.token = __shfl(idx, src, kWave);
-  d.wtok = __shfl(w, src, kWave);
+  d.token = __shfl(tok, src, kWave);
+  d.wtok = __shfl(wt, src, kWave);
   d.total = total;
+  if (d.token < 0) {  // an empty list (no weight anywhere): token 0
+    d.token = 0;
+    d.wtok = 0.0f;
+  }
   return d;
 }
 
+// A row's filtered law: weight(l) = exp2(l*c + nref) * iz for l >= t, else 0 (iz = 1/Z).
 struct RowLaw {
   const uint4* row;
-  float c, nref, t, z;
+  float c, nref, t, iz;
 };
 
 __device__ __forceinline__ void law_weights(const RowLaw& L, const uint4& d, float w[8]) {
   float x[8];
   unpack8(d, x);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) w[e] = (x[e] >= L.t) ? weight(x[e], L.c, L.nref) / L.z : 0.0f;
+  for (int e = 0; e < 8; ++e) w[e] = (x[e] >= L.t) ? weight(x[e], L.c, L.nref) * L.iz : 0.0f;
 }
 
-// Weights of vector v: p, or max(0, p - q). Logits past V weigh 0.
-__device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, bool residual,
-                                            int v, int nvec, int V, float w[8]) {
+// Weights of vector v from its loaded p (and q) data: p, or max(0, p - q). Vectors past the
+// row and logits past V weigh 0.
+__device__ __forceinline__ void data_weights(const RowLaw& Lp, const RowLaw& Lq, bool residual,
+                                             int v, int nvec, int V, const uint4& dp,
+                                             const uint4& dq, float w[8]) {
   if (v >= nvec) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = 0.0f;
     return;
   }
-  law_weights(Lp, Lp.row[v], w);
+  law_weights(Lp, dp, w);
   if (residual) {
     float wq[8];
-    law_weights(Lq, Lq.row[v], wq);
+    law_weights(Lq, dq, wq);
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = fmaxf(0.0f, w[e] - wq[e]);
   }
@@ -646,29 +788,23 @@ __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, 
   for (int e = 0; e < 8; ++e)
     if (v * 8 + e >= V) w[e] = 0.0f;
 }
+__device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, bool residual,
+                                            int v, int nvec, int V, float w[8]) {
+  const uint4 z{0u, 0u, 0u, 0u};
+  const uint4 dp = v < nvec ? Lp.row[v] : z;
+  const uint4 dq = (residual && v < nvec) ? Lq.row[v] : z;
+  data_weights(Lp, Lq, residual, v, nvec, V, dp, dq, w);
+}
 
-// All threads of the workgroup: inverse-CDF draw over a whole row (pair) in token order.
-// Pass 1 stores per-tile sums (a tile = 64 vectors = 512 logits, one coalesced wave load);
-// wave 0 scans the tile sums, then re-reads the chosen tile and scans it.
-__device__ Draw draw_from_rows(const RowLaw& Lp, const RowLaw& Lq, bool residual, int nvec,
-                               int V, float u, float* tile_sum, int* sh_i, float* sh_f) {
+// Phase 2 of a row draw, once tile_sum holds every tile's sum and each lane knows the last
+// positive-weight token it saw: wave 0 scans the tile sums, then re-reads the chosen tile
+// and scans it.
+__device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool residual,
+                                          int nvec, int V, float u, int last, float* tile_sum,
+                                          int* sh_i, float* sh_f) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int nw = kResolveThreads / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
-  int last = -1;  // last token with positive weight seen by this lane
-  for (int g = wid; g < ntiles; g += nw) {
-    const int v = g * kWave + lane;
-    float w[8];
-    vec_weights(Lp, Lq, residual, v, nvec, V, w);
-    float ls = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ls += w[e];
-      if (w[e] > 0.0f) last = v * 8 + e;
-    }
-    const float ts = wave_sum(ls);
-    if (lane == 0) tile_sum[g] = ts;
-  }
   last = wave_max_i(last);
   if (lane == 0) sh_i[wid] = last;
   __syncthreads();
@@ -789,10 +925,421 @@ __device__ Draw draw_from_rows(const RowLaw& Lp, const RowLaw& Lq, bool residual
   return d;
 }
 
+// All threads of the workgroup: inverse-CDF draw over a whole row (pair) in token order.
+// Pass 1 stores per-tile sums (a tile = 64 vectors = 512 logits, one coalesced wave load;
+// each wave keeps kTilesPerIter tiles of p and of q in flight); draw_scan finishes.
+__device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq, bool residual,
+                                               int nvec, int V, float u, float* tile_sum,
+                                               int* sh_i, float* sh_f) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nw = kResolveThreads / kWave;
+  const int ntiles = (nvec + kWave - 1) / kWave;
+  int last = -1;  // last token with positive weight seen by this lane
+  const uint4 z{0u, 0u, 0u, 0u};
+  for (int g0 = wid * kTilesPerIter; g0 < ntiles; g0 += nw * kTilesPerIter) {
+    uint4 dp[kTilesPerIter], dq[kTilesPerIter];
+#pragma unroll
+    for (int t = 0; t < kTilesPerIter; ++t) {
+      const int v = (g0 + t) * kWave + lane;
+      dp[t] = v < nvec ? Lp.row[v] : z;
+      dq[t] = (residual && v < nvec) ? Lq.row[v] : z;
+    }
+#pragma unroll
+    for (int t = 0; t < kTilesPerIter; ++t) {
+      const int v = (g0 + t) * kWave + lane;
+      float w[8];
+      data_weights(Lp, Lq, residual, v, nvec, V, dp[t], dq[t], w);
+      float ls = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ls += w[e];
+        if (w[e] > 0.0f) last = v * 8 + e;
+      }
+      const float ts = wave_sum(ls);
+      if (lane == 0 && g0 + t < ntiles) tile_sum[g0 + t] = ts;
+    }
+  }
+  return draw_scan(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
+}
+
+// ---- the bonus row's law, by the whole resolve workgroup --------------------------------
+
+constexpr int kWgWaves = kResolveThreads / kWave;
+constexpr int kWgBatch = 4;  // vectors in flight per thread in a workgroup pass
+
+// Vector v of a row as fp32 logits, -inf past the vocabulary (and for v >= nvec).
+__device__ __forceinline__ void row_vec(const uint4& d, int v, int nvec, int V, float x[8]) {
+  unpack8(d, x);
+  if (v >= nvec) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
+  } else if (v == nvec - 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (v * 8 + e >= V) x[e] = -INFINITY;
+  }
+}
+
+// Calls f(v, x) for every vector of the row, thread tid taking v = tid + j * kResolveThreads,
+// with kWgBatch loads in flight per thread.
+template <typename F>
+__device__ __forceinline__ void wg_row_pass(const uint4* __restrict__ row, int nvec, int V,
+                                            F&& f) {
+  const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kWgBatch * kResolveThreads) {
+    uint4 d[kWgBatch];
+#pragma unroll
+    for (int j = 0; j < kWgBatch; ++j) {
+      const int v = v0 + j * kResolveThreads;
+      d[j] = v < nvec ? row[v] : ninf;
+    }
+#pragma unroll
+    for (int j = 0; j < kWgBatch; ++j) {
+      const int v = v0 + j * kResolveThreads;
+      float x[8];
+      row_vec(d[j], v, nvec, V, x);
+      f(v, x);
+    }
+  }
+}
+
+// Argmax of a row, lowest token id on ties (greedy bonus token).
+__device__ int wg_row_argmax(const uint4* __restrict__ row, int nvec, int V, float* sh_v,
+                             int* sh_i) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  wg_row_pass(row, nvec, V, [&](int v, const float* x) {
+    const float vm = max8(x);
+    if (vm > bv) {  // vectors arrive in increasing v per thread: the first hit is the lowest
+      bv = vm;
+#pragma unroll
+      for (int e = 7; e >= 0; --e)
+        if (x[e] == vm) bi = v * 8 + e;
+    }
+  });
+  wave_argmax(bv, bi);
+  if (lane == 0) {
+    sh_v[wid] = bv;
+    sh_i[wid] = bi;
+  }
+  __syncthreads();
+  float v = sh_v[0];
+  int i = sh_i[0];
+  for (int w = 1; w < kWgWaves; ++w)
+    if (sh_v[w] > v || (sh_v[w] == v && sh_i[w] < i)) {
+      v = sh_v[w];
+      i = sh_i[w];
+    }
+  __syncthreads();
+  return i == 0x7FFFFFFF ? 0 : i;
+}
+
+// Max M and normaliser Z = sum exp2((l - M) c) of a row: per-thread online (m, s), then the
+// waves' partials merged in wave order.
+__device__ void wg_row_mz(const uint4* __restrict__ row, int nvec, int V, float c, float* sh_v,
+                          float* sh_z, float& M, float& Z) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  LaneAcc a;
+  wg_row_pass(row, nvec, V, [&](int, const float* x) {
+    const float vm = max8(x);
+    if (vm == -INFINITY) return;
+    if (vm > a.m) {
+      a.s *= __builtin_amdgcn_exp2f((a.m - vm) * c);  // 0 while a.m = -inf (a.s = 0 then)
+      a.m = vm;
+    }
+    const float nref = -a.m * c;
+    float st = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st += weight(x[e], c, nref);
+    a.s += st;
+  });
+  float Mw, Zw;
+  finish_mz(a, c, Mw, Zw);
+  if (lane == 0) {
+    sh_v[wid] = Mw;
+    sh_z[wid] = Zw;
+  }
+  __syncthreads();
+  M = sh_v[0];
+  for (int w = 1; w < kWgWaves; ++w) M = fmaxf(M, sh_v[w]);
+  Z = 0.0f;
+  for (int w = 0; w < kWgWaves; ++w)
+    if (sh_v[w] != -INFINITY) Z += sh_z[w] * __builtin_amdgcn_exp2f((sh_v[w] - M) * c);
+  __syncthreads();
+}
+
+// Top-p threshold of a row whose (M, Z) are known, by the same rule as the row pass: a
+// fixed-point histogram of the weights over key offsets below M, first inside the window
+// M - kCaptureK*T (one pass), else over all keys by high byte then low byte (two passes).
+// Returns t* and the kept mass Zs; *slow is set when the window did not hold the nucleus.
+__device__ float wg_topp_threshold(const uint4* __restrict__ row, int nvec, int V, float c,
+                                   float P, float M, float Z, unsigned long long* hist,
+                                   int* sh_i, unsigned long long* sh_u, float* zs_out,
+                                   bool* slow) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const float theta = M - kCaptureK * (kLog2e / c);
+  const float nref = -M * c;
+  const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
+  const uint32_t kM = key_of(M);
+  for (int j = tid; j < kHist; j += kResolveThreads) hist[j] = 0ull;
+  __syncthreads();
+  wg_row_pass(row, nvec, V, [&](int, const float* x) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!(x[e] >= theta)) continue;
+      const uint32_t o = kM - key_of(x[e]);
+      if (o < (uint32_t)kHist) atomicAdd(&hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
+    }
+  });
+  __syncthreads();
+  if (wid == 0) {
+    uint64_t zs = 0;
+    const int o = hist_crossing(hist, kHist, thrP, 0, &zs, lane);
+    if (lane == 0) {
+      sh_i[0] = o;
+      sh_u[0] = zs;
+    }
+  }
+  __syncthreads();
+  int o_star = sh_i[0];
+  uint64_t zs = sh_u[0];
+  *slow = o_star < 0;
+  if (o_star < 0) {  // the nucleus reaches below the window: exact search over all keys
+    int hi_b = -1;
+    uint64_t base = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();
+      for (int j = tid; j < 256; j += kResolveThreads) hist[j] = 0ull;
+      __syncthreads();
+      wg_row_pass(row, nvec, V, [&](int, const float* x) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (x[e] == -INFINITY) continue;
+          const uint32_t o = kM - key_of(x[e]);
+          if (pass == 1 && (int)(o >> 8) != hi_b) continue;
+          const uint64_t fw = fixw(weight(x[e], c, nref));
+          if (fw) atomicAdd(&hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
+        }
+      });
+      __syncthreads();
+      if (wid == 0) {
+        uint64_t cum = 0;
+        const int b = hist_crossing(hist, 256, thrP, pass == 0 ? 0 : base, &cum, lane);
+        if (lane == 0) {
+          sh_i[0] = b;
+          sh_u[0] = cum;
+          sh_u[1] = b >= 0 ? cum - hist[b] : 0;
+        }
+      }
+      __syncthreads();
+      const int bsel = sh_i[0];
+      zs = sh_u[0];
+      if (bsel < 0) {  // rounding left the whole row just below P: keep everything
+        o_star = -1;
+        break;
+      }
+      if (pass == 0) {
+        hi_b = bsel;
+        base = sh_u[1];
+      } else {
+        o_star = hi_b * 256 + bsel;
+      }
+    }
+    __syncthreads();
+  }
+  *zs_out = (float)((double)zs / kFix);
+  return o_star < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o_star);
+}
+
+constexpr int kRowSlots = 16;  // vectors per thread when the workgroup holds a whole row
+
+// The packed vector itself, hidden from the optimiser: each pass over held vectors unpacks
+// again instead of keeping every unpacked logit of an earlier pass alive (twice the
+// registers of the packed data).
+__device__ __forceinline__ uint4 opaque(uint4 d) {
+  asm volatile("" : "+v"(d.x), "+v"(d.y), "+v"(d.z), "+v"(d.w));
+  return d;
+}
+
+// The bonus draw from p_{gamma+1} for a row of at most kRowSlots * kResolveThreads vectors,
+// loaded once into registers (thread tid holds vectors tid + j * kResolveThreads, so tile g
+// of 64 vectors is wave g % kWgWaves's slot g / kWgWaves). One exponential per logit: the
+// row max M first (no exponentials), then every weight against M, kept per slot; Z and the
+// tile sums follow from the slot sums. With top-p the kept tokens (at most kNucMax) are
+// collected from the registers into a sorted list and drawn from like a rejected row's
+// list. Returns false, with M and Z, when the top-p window did not hold the nucleus or the
+// nucleus is longer than a list (the caller then takes the streaming path).
+__device__ __forceinline__ bool bonus_draw_held(const uint4* __restrict__ row, int nvec, int V,
+                                                float c, bool topp, float P, float u,
+                                                float* tile_sum, unsigned long long* hist,
+                                                NucEntry* list, int* sh_i, float* sh_f,
+                                                float* sh_v, float* sh_z,
+                                                unsigned long long* sh_u, Draw* out,
+                                                float* Mout, float* Zout) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  // Masked once, as loaded: slots past the row hold -inf logits (their load re-reads the
+  // last vector, in bounds), and so do the logits of the last vector past V.
+  const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+  uint4 d[kRowSlots];
+#pragma unroll
+  for (int j = 0; j < kRowSlots; ++j) {
+    const int v = tid + j * kResolveThreads;
+    const uint4 q = row[min(v, nvec - 1)];
+    d[j] = v < nvec ? q : ninf;
+    if (v == nvec - 1 && (V & 7)) {  // one lane of the workgroup
+      uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e >= (V & 7)) w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | 0xFF800000u)
+                                              : ((w[e >> 1] & 0xFFFF0000u) | 0x0000FF80u);
+      d[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  // M: lane max, wave max, then the waves' maxima.
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kRowSlots; ++j) {
+    float x[8];
+    unpack8(opaque(d[j]), x);
+    m = vmax3(m, max8(x), max8(x));
+  }
+  m = wave_max_dpp(m);
+  if (lane == 0) sh_v[wid] = m;
+  __syncthreads();
+  float M = sh_v[0];
+  for (int w = 1; w < kWgWaves; ++w) M = fmaxf(M, sh_v[w]);
+  const float nref = -M * c;  // M is finite: a row holds a finite logit
+  // Weights against M, summed per slot; Z over the workgroup in wave order.
+  float sj[kRowSlots];
+  float lz = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kRowSlots; ++j) {
+    float x[8];
+    unpack8(opaque(d[j]), x);
+    float t = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t += weight(x[e], c, nref);
+    sj[j] = t;
+    lz += t;
+  }
+  lz = wave_sum(lz);
+  if (lane == 0) sh_z[wid] = lz;
+  __syncthreads();
+  float Z = 0.0f;
+  for (int w = 0; w < kWgWaves; ++w) Z += sh_z[w];
+  *Mout = M;
+  *Zout = Z;
+  if (topp) {
+    const float theta = M - kCaptureK * (kLog2e / c);
+    const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
+    const uint32_t kM = key_of(M);
+    for (int j = tid; j < kHist; j += kResolveThreads) hist[j] = 0ull;
+    if (tid == 0) sh_i[1] = 0;  // list length
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRowSlots; ++j) {
+      float x[8];
+      unpack8(opaque(d[j]), x);
+      if (!(max8(x) >= theta)) continue;  // most vectors: nothing inside the window
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!(x[e] >= theta)) continue;
+        const uint32_t o = kM - key_of(x[e]);
+        if (o < (uint32_t)kHist) atomicAdd(&hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      uint64_t z64 = 0;
+      const int o = hist_crossing(hist, kHist, thrP, 0, &z64, lane);
+      if (lane == 0) {
+        sh_i[0] = o;
+        sh_u[0] = z64;
+      }
+    }
+    __syncthreads();
+    const int o_star = sh_i[0];
+    if (o_star < 0) return false;
+    const float t = value_of_key(kM - (uint32_t)o_star);
+    const float zs = (float)((double)sh_u[0] / kFix);
+    // the kept tokens (logit >= t): appended to the list through an LDS counter
+#pragma unroll
+    for (int j = 0; j < kRowSlots; ++j) {
+      float x[8];
+      unpack8(opaque(d[j]), x);
+      if (!(max8(x) >= t)) continue;
+      const int v = tid + j * kResolveThreads;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!(x[e] >= t)) continue;
+        const int slot = atomicAdd(&sh_i[1], 1);
+        if (slot < kNucMax) list[slot] = NucEntry{v * 8 + e, weight(x[e], c, nref)};
+      }
+    }
+    __syncthreads();
+    const int n = sh_i[1];
+    if (n > kNucMax) return false;
+    // sort by token id: each entry's rank is the number of smaller ids (ids are distinct)
+    NucEntry mine{0, 0.0f};
+    int rank = 0;
+    if (tid < n) {
+      mine = list[tid];
+      for (int i = 0; i < n; ++i) rank += list[i].idx < mine.idx ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid < n) list[rank] = mine;
+    __syncthreads();
+    if (wid == 0) {
+      const Draw dr = draw_from_lists(list, n, zs, nullptr, 0, 1.0f, false, u, lane);
+      if (lane == 0) {
+        sh_i[0] = dr.token;
+        sh_f[0] = dr.total;
+        sh_f[1] = dr.wtok;
+      }
+    }
+    __syncthreads();
+    *out = Draw{sh_i[0], sh_f[0], sh_f[1]};
+    __syncthreads();
+    return true;
+  }
+  // No top-p: tile g's sum is wave g % kWgWaves's slot g / kWgWaves sum, normalised.
+  const float iz = 1.0f / Z;
+  const int ntiles = (nvec + kWave - 1) / kWave;
+  int jl = -1;  // this lane's last slot with weight (ids grow with the slot)
+  uint4 dl = ninf;
+#pragma unroll
+  for (int j = 0; j < kRowSlots; ++j) {
+    const float ts = wave_sum(sj[j]) * iz;
+    const int g = wid + j * kWgWaves;
+    if (lane == 0 && g < ntiles) tile_sum[g] = ts;
+    if (sj[j] > 0.0f) {
+      jl = j;
+      dl = d[j];
+    }
+  }
+  int last = -1;  // last token with positive weight seen by this lane
+  if (jl >= 0) {
+    float x[8];
+    unpack8(dl, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (weight(x[e], c, nref) > 0.0f) last = (tid + jl * kResolveThreads) * 8 + e;
+  }
+  const RowLaw L{row, c, nref, -INFINITY, iz};
+  *out = draw_scan(L, L, false, nvec, V, u, last, tile_sum, sh_i, sh_f);
+  return true;
+}
+
 __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainParams P) {
-  __shared__ float tile_sum[kMaxTiles];
-  __shared__ int sh_i[8];
-  __shared__ float sh_f[8];
+  __shared__ union {
+    float tile_sum[kMaxTiles];       // inverse-CDF draw over a row
+    unsigned long long hist[kHist];  // bonus row top-p threshold
+  } sbuf;
+  __shared__ int sh_i[kWgWaves];
+  __shared__ float sh_f[2], sh_v[kWgWaves], sh_z[kWgWaves];
+  __shared__ unsigned long long sh_u[2];
+  __shared__ NucEntry s_q[kNucMax];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const SeqInfo s = seq_info(P, b);
@@ -833,49 +1380,80 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
     flags = f & (SPEC_FLAG_Q_ZERO | SPEC_FLAG_TOPP_SLOW);
   }
   const int trow = s.t0 + kstar - 1;
-  const RowRec r = P.rec[trow];
-  flags |= r.flags & SPEC_FLAG_TOPP_SLOW;
+  const bool residual = kstar <= s.g;
+  const uint4* prow = reinterpret_cast<const uint4*>(P.target + (size_t)trow * P.stride);
   int y;
   float R = NAN, py;
-  if (s.T == 0.0f) {
+  if (!residual) {  // every draft accepted: the bonus token from p_{gamma+1}
+    if (s.T == 0.0f) {
+      y = wg_row_argmax(prow, P.nvec, P.V, sh_v, sh_i);
+      py = 1.0f;
+    } else {
+      const float u = P.ovr ? P.ovr[(size_t)trow * 2 + 1]
+                            : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
+                                        SPEC_PURPOSE_BONUS);
+      const float c = kLog2e / s.T;
+      const bool topp = P.topp && s.P < 1.0f;
+      bool slow = false;
+      Draw d;
+      float M, Z;
+      const bool held = P.nvec <= kRowSlots * kResolveThreads;
+      if (!held || !bonus_draw_held(prow, P.nvec, P.V, c, topp, s.P, u, sbuf.tile_sum,
+                                    sbuf.hist, s_q, sh_i, sh_f, sh_v, sh_z, sh_u, &d, &M,
+                                    &Z)) {
+        if (!held) wg_row_mz(prow, P.nvec, P.V, c, sh_v, sh_z, M, Z);
+        float t = -INFINITY, zs = Z;
+        if (topp)
+          t = wg_topp_threshold(prow, P.nvec, P.V, c, s.P, M, Z, sbuf.hist, sh_i, sh_u, &zs,
+                                &slow);
+        const RowLaw Lp{prow, c, -M * c, t, 1.0f / zs};
+        d = draw_from_rows(Lp, Lp, false, P.nvec, P.V, u, sbuf.tile_sum, sh_i, sh_f);
+      }
+      if (slow) flags |= SPEC_FLAG_TOPP_SLOW;
+      y = d.token;
+      py = d.wtok;
+    }
+  } else if (s.T == 0.0f) {
+    const RowRec r = P.rec[trow];
     y = r.argmax;
     py = 1.0f;
-  } else {
-    const bool residual = kstar <= s.g;
+  } else {  // first rejection at kstar: the residual max(0, p - q), or p if it has no mass
+    const RowRec r = P.rec[trow];
+    flags |= r.flags & SPEC_FLAG_TOPP_SLOW;
     const float u = P.ovr ? P.ovr[(size_t)trow * 2 + 1]
                           : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
-                                      residual ? SPEC_PURPOSE_RESIDUAL : SPEC_PURPOSE_BONUS);
+                                      SPEC_PURPOSE_RESIDUAL);
     const float c = kLog2e / s.T;
     const NucEntry* lists = P.nuc + (size_t)trow * 2 * kNucMax;
-    RowLaw Lp{reinterpret_cast<const uint4*>(P.target + (size_t)trow * P.stride), c,
-              -r.m[0] * c, r.t[0], r.z[0]};
-    RowLaw Lq{residual ? reinterpret_cast<const uint4*>(P.draft + (size_t)(s.d0 + kstar - 1) *
-                                                        P.stride)
-                       : nullptr,
-              c, -r.m[1] * c, r.t[1], r.z[1]};
+    const RowLaw Lp{prow, c, -r.m[0] * c, r.t[0], 1.0f / r.z[0]};
+    const RowLaw Lq{reinterpret_cast<const uint4*>(P.draft +
+                                                   (size_t)(s.d0 + kstar - 1) * P.stride),
+                    c, -r.m[1] * c, r.t[1], 1.0f / r.z[1]};
     Draw d;
     const bool lists_p = r.nuc[0] >= 0, lists_pq = lists_p && r.nuc[1] >= 0;
-    if (residual) {
-      if (lists_pq) {
-        if (wid == 0) {
-          d = draw_from_lists(lists, r.nuc[0], r.z[0], lists + kNucMax, r.nuc[1], r.z[1], true,
-                              u, lane);
-          if (lane == 0) {
-            sh_i[0] = d.token;
-            sh_f[0] = d.total;
-            sh_f[1] = d.wtok;
-          }
+    if (lists_pq) {
+      for (int j = tid; j < r.nuc[1]; j += kResolveThreads) s_q[j] = lists[kNucMax + j];
+      __syncthreads();
+      if (wid == 0) {
+        d = draw_from_lists(lists, r.nuc[0], r.z[0], s_q, r.nuc[1], r.z[1], true, u, lane);
+        if (lane == 0) {
+          sh_i[0] = d.token;
+          sh_f[0] = d.total;
+          sh_f[1] = d.wtok;
         }
-        __syncthreads();
-        d = Draw{sh_i[0], sh_f[0], sh_f[1]};
-        __syncthreads();
-      } else {
-        d = draw_from_rows(Lp, Lq, true, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
       }
-      R = d.total;
-      if (!(d.total > 0.0f)) flags |= SPEC_FLAG_RESID_FALLBACK;
+      __syncthreads();
+      d = Draw{sh_i[0], sh_f[0], sh_f[1]};
+      __syncthreads();
+    } else {
+      d = draw_from_rows(Lp, Lq, true, P.nvec, P.V, u, sbuf.tile_sum, sh_i, sh_f);
     }
-    if (!residual || !(d.total > 0.0f)) {
+    R = d.total;
+    if (d.total > 0.0f) {
+      y = d.token;
+      py = d.wtok / d.total;
+    } else {  // R = 0 means p = q: the draw from p has the same law
+      flags |= SPEC_FLAG_RESID_FALLBACK;
       if (lists_p) {
         if (wid == 0) {
           d = draw_from_lists(lists, r.nuc[0], r.z[0], nullptr, 0, 1.0f, false, u, lane);
@@ -888,13 +1466,10 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
         __syncthreads();
         d = Draw{sh_i[0], sh_f[0], sh_f[1]};
       } else {
-        d = draw_from_rows(Lp, Lq, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
+        d = draw_from_rows(Lp, Lq, false, P.nvec, P.V, u, sbuf.tile_sum, sh_i, sh_f);
       }
       y = d.token;
       py = d.wtok;
-    } else {
-      y = d.token;
-      py = d.wtok / d.total;
     }
   }
   if (wid == 0) {
@@ -952,13 +1527,15 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(a.profile_events);
   hipError_t e = hipSuccess;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  const unsigned grid = (unsigned)a.batch * (unsigned)(a.max_gamma + 1);
-  if (a.top_p)
-    hipLaunchKernelGGL(chain_row_kernel<true>, dim3(grid), dim3(kWave),
-                       2 * sizeof(CapBuf) + sizeof(SelBuf), st, P);
-  else
-    hipLaunchKernelGGL(chain_row_kernel<false>, dim3(grid), dim3(kWave), 0, st, P);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned grid = (unsigned)a.batch * (unsigned)a.max_gamma;  // draft positions
+  if (grid > 0) {
+    if (a.top_p)
+      hipLaunchKernelGGL(chain_row_kernel<true>, dim3(grid), dim3(kWave),
+                         2 * sizeof(CapBuf) + sizeof(SelBuf), st, P);
+    else
+      hipLaunchKernelGGL(chain_row_kernel<false>, dim3(grid), dim3(kWave), 0, st, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)a.batch), dim3(kResolveThreads), 0,
                      st, P);
@@ -966,3 +1543,4 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
 }
 
 }  // namespace specv
+

@@ -88,6 +88,24 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
+// Wave maximum through DPP moves (quad permutes, half-row and row mirrors, row broadcasts
+// 15 and 31), read back from lane 63: no LDS traffic. Lanes a masked DPP row does not write
+// keep their own value, which leaves the maximum unchanged.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
+                                            0xF, false);
+  return vmax3(v, __int_as_float(o), __int_as_float(o));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = dpp_max_step<0xB1>(v);         // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E>(v);         // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141>(v);        // row_half_mirror
+  v = dpp_max_step<0x140>(v);        // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

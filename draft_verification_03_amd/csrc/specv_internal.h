@@ -12,7 +12,7 @@ namespace specv {
 
 // Longest nucleus list a row record keeps for the resolve step; longer nuclei are re-read
 // from the logits instead.
-constexpr int kNucMax = 64;
+constexpr int kNucMax = 256;
 
 // Per-(sequence, position) record the row pass leaves for the resolve step. Index 0 is the
 // target row (p), index 1 the draft row (q).

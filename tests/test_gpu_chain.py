@@ -64,6 +64,50 @@ def test_top_p_flat_rows_take_the_exact_search():
     assert np.all(g["seq_flags"] & B.FLAG_TOPP_SLOW)
 
 
+def test_top_p_nuclei_across_list_sizes():
+    """Nuclei from tens to hundreds of tokens: plateaus of K boosted ids (+8 over N(0, 0.3^2)),
+    K chosen so that the kept lists cross the sizes at which the resolve step switches from
+    drawing over the lists to a pass over the row pair."""
+    rng = np.random.default_rng(41)
+    V, stride, gamma = 12000, 12000, 4
+    Ks = [40, 70, 150, 250, 290, 600]
+    Bn = len(Ks)
+    tgt = np.zeros((Bn * (gamma + 1), stride), np.float32)
+    drf = np.zeros((Bn * gamma, stride), np.float32)
+    for b, K in enumerate(Ks):
+        ids = rng.choice(V, size=K, replace=False)
+        for k in range(gamma + 1):
+            row = rng.normal(0.0, 0.3, V).astype(np.float32)
+            row[ids] += 8.0
+            tgt[b * (gamma + 1) + k] = row
+            if k < gamma:
+                drf[b * gamma + k] = row + rng.normal(0.0, 0.5, V).astype(np.float32)
+    x = dict(target=W.bf16_bits(tgt), draft=W.bf16_bits(drf),
+             cu_gamma=np.arange(Bn + 1, dtype=np.int32) * gamma,
+             temperature=np.ones(Bn, np.float32), top_p=np.full(Bn, 0.9, np.float32),
+             seq_id=np.arange(Bn, dtype=np.uint32),
+             committed_len=rng.integers(0, 4096, Bn).astype(np.int32), vocab=V, stride=stride)
+    sizes = [oracle.dist(x["target"][r, :V], 1.0, 0.9)[1]["nucleus"]
+             for r in range(0, Bn * (gamma + 1), gamma + 1)]
+    assert min(sizes) < 64 and any(64 < n <= 256 for n in sizes) and max(sizes) > 256, sizes
+    for seed in (42, 43, 44):
+        check_chain(x, seed=seed, label=f"top-p list sizes {sizes} seed {seed}")
+
+
+@pytest.mark.parametrize("V,topp", [(128256, 0.9), (128256, None), (200000, 0.9),
+                                    (200000, None)])
+def test_every_draft_accepted_bonus_draw(V, topp):
+    """Draft rows equal to target rows: every test accepts (p = q), so every sequence ends
+    with the bonus draw from p_{gamma+1}, whose law the resolve step computes itself -- from
+    registers up to 16384 vectors per row, by streaming passes beyond."""
+    x = W.chain_inputs("c3", B=12, V=V, gamma=(0, 6), top_p=topp, seed=45)
+    cu = x["cu_gamma"]
+    x["draft"] = x["target"][np.concatenate(
+        [np.arange(int(cu[b]) + b, int(cu[b + 1]) + b) for b in range(12)]).astype(int)].copy()
+    o, g, _ = check_chain(x, seed=46, label=f"all accepted V={V} top-p={topp}")
+    assert np.all(o["num_accepted"] == np.diff(cu))
+
+
 def test_mixed_temperatures_and_greedy():
     x = W.chain_inputs("c5", B=40, V=5000, seed=3)
     x["temperature"][::3] = 0.0
