@@ -7,23 +7,24 @@
 // committed-length pointer. See include/spec_verify.h for the exact contract.
 //
 // Structure
-//  1. chain_row_kernel -- one wave per (sequence b, position k) item, k = 1..gamma_b+1.
-//     The wave streams the target row and (for k <= gamma_b) the draft row of the item
-//     together from HBM once, with 16-byte loads, 8 vectors per row in flight per lane:
-//       - per-lane online max / sum of exp2((l - m) * log2(e)/T) (one rescale per trip);
-//       - with top-p: the index of every 8-logit vector whose max is within kCaptureK*T of
-//         the wave's running max is kept in LDS (a superset of the final window
-//         m - kCaptureK*T); the end phase reads those few vectors again;
+//  1. row_stats_kernel -- one wave per logits row of a draft position: the target row p_k
+//     or the draft row q_k, k = 1..gamma_b (the bonus row p_{gamma_b+1} is only needed after
+//     a full accept, so the resolve step reads it then). The wave streams its row from HBM
+//     once with 16-byte loads, double-buffered:
+//       - per-lane online max / sum of exp2((l - m) * log2(e)/T) (lazy rescaling);
+//       - with top-p: every 8-logit vector whose max is within kCaptureK*T of the running
+//         max is copied to LDS (a superset of the final window m - kCaptureK*T, pruned when
+//         the buffer fills), so the end phase touches no HBM;
 //       - greedy rows (T = 0): max with the lowest index only.
-//     The end phase (wave reductions only) gives m, Z, the nucleus threshold t* (binary
-//     search over bf16 keys on fixed-point masses of the captured elements; an exact
-//     16-pass search over the whole row if the window did not hold the nucleus), p_k(d_k),
-//     q_k(d_k), the acceptance decision, and a sorted nucleus list (<= kNucMax tokens) for
-//     the resolve step.
-//  2. chain_resolve_kernel -- one 256-thread workgroup per sequence: first rejection by a
-//     ballot over the items' decisions, then the residual or bonus draw -- from the nucleus
-//     lists when both are kept (no logits touched), else by one pass over the row pair with
-//     per-tile sums, a tile scan and an in-tile scan (ascending token id) -- and the outputs.
+//     The end phase gives m, Z, the nucleus threshold t* (fixed-point mass histogram over
+//     bf16 keys of the captured logits; an exact multi-pass search over the whole row if
+//     the window did not hold the nucleus), the draft token's weight, and the nucleus list
+//     in token order (<= kNucMax tokens) for the residual draw.
+//  2. chain_resolve_kernel -- one workgroup per sequence: p_k(d_k), q_k(d_k) and the
+//     acceptance decisions from the row statistics, the first rejection (one ballot), then
+//     the residual or bonus draw -- from the nucleus lists when both are kept (their heads
+//     are prefetched with the statistics), else by one pass over the row pair with per-tile
+//     sums, a tile scan and an in-tile scan (ascending token id) -- and the outputs.
 #include <math.h>
 
 #include "row_ops.h"
@@ -37,13 +38,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Top-p capture window: logits within kCaptureK * T of the row max (weight >= e^-7 of the
 // largest). Rows whose nucleus reaches further down take the exact multi-pass search.
 constexpr float kCaptureK = 7.0f;
-constexpr int kCapLane = 32;  // captured vector ids per lane per row
+constexpr int kCapV = 256;    // captured vectors per row held in LDS
+constexpr int kCapG = 1024;   // further captured vector ids per row spilled to the workspace
+constexpr int kDepth = 2;     // trips of loads in flight per wave in the row pass
 constexpr int kRefresh = 2;   // trips between refreshes of the capture threshold
-constexpr int kEndB = 8;      // captured vectors per lane the end phase holds in registers
 constexpr int kHist = 512;    // key offsets below the row max resolved by the window search
 constexpr int kResolveThreads = 1024;
 constexpr int kTilesPerIter = 4;  // row-pair tiles in flight per wave in the resolve pass
 constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass (V <= 2^19)
+constexpr int kPreRows = 8;      // draft positions whose list heads the resolve prefetches
+constexpr int kPre = 64;         // list entries prefetched per row
 constexpr double kFix = 17592186044416.0;  // 2^44: fixed-point scale of masses
 // A trip whose weights, taken against the lane's previous maximum, may exceed 2^100 is
 // recomputed against its own maximum (first trip of a row, or a large jump at small T).
@@ -64,33 +68,20 @@ struct ChainParams {
   float* probe_rows;
   float* probe_seq;
   const float* ovr;
-  RowRec* rec;
-  NucEntry* nuc;  // [n_items][2][kNucMax]
+  RowStat* stat;    // [n_draft][2]
+  NucEntry* nuc;    // [n_draft][2][kNucMax]
+  uint16_t* spill;  // [n_draft][2][kCapG]
   int32_t B, V, stride, nvec, max_gamma, n_draft, lead;
   uint32_t seed_lo, seed_hi;
 };
 
-// Ids of the captured vectors (16 bits: a row has at most 65536 vectors); the vectors
-// themselves (about 1% of the row) are read again in the end phase. During the stream each
-// lane appends to its own list, with no cross-lane traffic; the end phase compacts the lists
-// in lane order.
-struct CapBuf {
-  uint16_t lane[kCapLane][kWave];
-};
-
-// Threshold search state: fixed-point mass per key offset below the row max (integer
-// additions, so the sums do not depend on the order of the atomics), and the staging area
-// of a nucleus list. The list is staged only after the threshold is known, behind a
-// barrier, so the two share their storage.
-union SelBuf {
+// LDS of one top-p row: the captured vectors in increasing vector index (data and index),
+// and the threshold search's histogram.
+struct CapLds {
+  uint4 data[kCapV];
   unsigned long long hist[kHist];
-  struct {
-    uint32_t sidx[kNucMax];
-    float sw[kNucMax];
-  };
-  uint16_t flat[kCapLane * kWave];  // compacted capture ids, before the threshold search
+  uint16_t idx[kCapV];
 };
-static_assert(sizeof(SelBuf) == kHist * 8, "list staging fits in the histogram's storage");
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -99,6 +90,15 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t fixw(float w) {
   return (uint64_t)((double)w * kFix);
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
 }
 
 // Parameters checked on their bit patterns (NaN fails every test). T: >= 0 (or -0), not NaN;
@@ -149,7 +149,11 @@ struct LaneAcc {
   float m = -INFINITY;   // running max of this lane's logits
   float s = 0.0f;        // sum of exp2((l - m) * c) over this lane's logits
   float wm = -INFINITY;  // the wave's max at the last refresh (capture threshold)
-  int cnt = 0;           // vectors this lane captured (may exceed kCapLane: overflow)
+  // capture state (wave-uniform): vectors held in LDS, then ids spilled to the workspace
+  int ncap = 0;
+  int nspill = 0;
+  bool spilling = false;  // LDS stayed nearly full after pruning: later captures spill
+  bool over = false;      // the spill list overflowed too: exact search over the row
 };
 
 // Weight of one logit relative to a reference: the same expression everywhere, so that
@@ -158,12 +162,72 @@ __device__ __forceinline__ float weight(float l, float c, float nref) {
   return __builtin_amdgcn_exp2f(fmaf(l, c, nref));
 }
 
-// One trip (kU vectors of one row) into the lane's running (m, s). The weights are taken
+// Keeps the captured vectors whose max is still >= thr (in their order) and returns how
+// many remain. A chunk's entries are all read before any of them is written, and a kept
+// entry never moves up, so the compaction can work in place.
+__device__ int cap_compact(CapLds* cap, int n, float thr, int lane) {
+  int out = 0;
+  for (int j0 = 0; j0 < n; j0 += kWave) {
+    const int j = j0 + lane;
+    uint4 dv = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t id = 0;
+    bool keep = false;
+    if (j < n) {
+      dv = cap->data[j];
+      id = cap->idx[j];
+      float x[8];
+      unpack8(dv, x);
+      keep = max8(x) >= thr;
+    }
+    const uint64_t m = __ballot(keep);
+    if (keep) {
+      const int pos = out + (int)lanes_below(m);
+      cap->data[pos] = dv;
+      cap->idx[pos] = (uint16_t)id;
+    }
+    out += __popcll(m);
+  }
+  return out;
+}
+
+// Appends the flagged lanes' vectors to the capture buffer in lane order (= increasing
+// vector index within a trip slot). A full buffer is first pruned against the wave's
+// current threshold; if it stays more than 3/4 full, this and every later capture of the row
+// only records the vector id in the workspace spill list (read back in the end phase), so
+// the captures stay in increasing vector order: LDS entries, then spilled ones.
+__device__ __forceinline__ void cap_push(CapLds* cap, uint16_t* spill, LaneAcc& a,
+                                         const uint4& dv, bool in, int vid, float capw,
+                                         int lane) {
+  const uint64_t mask = __ballot(in);
+  if (mask == 0) return;
+  const int n = __popcll(mask);
+  if (!a.spilling && a.ncap + n > kCapV) {
+    a.wm = wave_max_dpp(a.m);
+    a.ncap = cap_compact(cap, a.ncap, a.wm - capw, lane);
+    a.spilling = a.ncap > kCapV * 3 / 4;
+  }
+  const int pos = (int)lanes_below(mask);
+  if (!a.spilling) {
+    if (in) {
+      cap->data[a.ncap + pos] = dv;
+      cap->idx[a.ncap + pos] = (uint16_t)vid;
+    }
+    a.ncap += n;
+  } else if (a.nspill + n <= kCapG) {
+    if (in) spill[a.nspill + pos] = (uint16_t)vid;
+    a.nspill += n;
+  } else {
+    a.over = true;
+  }
+}
+
+// One trip (kU vectors of the row) into the lane's running (m, s). The weights are taken
 // against the lane's previous maximum; only when the trip raises it (rare after the first
 // trips) is the trip's partial sum re-referenced, or recomputed when it may have overflowed.
 template <bool CAPTURE>
 __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane, float c,
-                                             float capw, LaneAcc& a, CapBuf* cap) {
+                                             float capw, LaneAcc& a, CapLds* cap,
+                                             uint16_t* spill) {
   const float ref = (a.m == -INFINITY) ? 0.0f : a.m;
   const float nref = -ref * c;
   float vm[kU];
@@ -196,7 +260,7 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
     a.m = tm;
   }
   a.s += st;
-  if (CAPTURE) {
+  if (CAPTURE && !a.over) {
     // Threshold: the larger of the lane's own max and the wave's max at its last refresh,
     // less the window. Both are lower bounds of the row max, so every vector within the
     // final window is captured (with some extra ones).
@@ -205,10 +269,8 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
     const float thr = vmax3(vmax3(a.wm, a.m, a.m) - capw, -3.4028235e38f, -3.4028235e38f);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      if (vm[u] >= thr) {
-        if (a.cnt < kCapLane) cap->lane[a.cnt][lane] = (uint16_t)(v0 + u * kWave + lane);
-        ++a.cnt;
-      }
+      if (a.over) break;
+      cap_push(cap, spill, a, d[u], vm[u] >= thr, v0 + u * kWave + lane, capw, lane);
     }
   }
 }
@@ -227,30 +289,6 @@ struct TopP {
   int nuc;     // kept count if the list was written, else -1
   bool slow;   // exact multi-pass search ran
 };
-
-// Appends the flagged lanes' (idx, w) to the staging list in LDS, in lane order. Returns the
-// new length (a length above kNucMax means the list overflowed and is incomplete).
-__device__ __forceinline__ int stage_append(bool in, uint32_t idx, float w, int n, SelBuf* sb) {
-  const uint64_t mask = __ballot(in);
-  const int slot = n + (int)lanes_below(mask);
-  if (in && slot < kNucMax) {
-    sb->sidx[slot] = idx;
-    sb->sw[slot] = w;
-  }
-  return n + __popcll(mask);
-}
-
-// Writes the staged list (n <= kNucMax entries, distinct token ids) to the workspace sorted
-// by token id: each entry's rank is the number of staged ids below it.
-__device__ __forceinline__ void write_sorted_list(NucEntry* out, int n, const SelBuf* sb,
-                                                  int lane) {
-  for (int j = lane; j < n; j += kWave) {
-    const uint32_t idx = sb->sidx[j];
-    int rank = 0;
-    for (int i = 0; i < n; ++i) rank += (sb->sidx[i] < idx) ? 1 : 0;
-    out[rank] = NucEntry{(int32_t)idx, sb->sw[j]};
-  }
-}
 
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
 #pragma unroll
@@ -295,125 +333,74 @@ __device__ int hist_crossing(const unsigned long long* h, int nb, uint64_t thr, 
   return o;
 }
 
-// Nucleus list of a row once t is known: every logit >= t, from the given vectors.
-template <typename VecAt>
-__device__ int collect_list(VecAt vec_at, int nv, int V, float t, float c, float nref,
-                            SelBuf* sb, int lane) {
-  int n = 0;
-  for (int i0 = 0; i0 < nv && n <= kNucMax; i0 += kWave) {
-    const int i = i0 + lane;
+// Nucleus list of a row once t is known: every kept logit (>= t, token < V) of the given
+// vectors, written to the workspace in token order -- the vectors come in increasing index
+// and each lane's kept elements are placed after all lower lanes' by a wave scan of the
+// counts. Returns the kept count; a count above kNucMax means the list is incomplete.
+template <typename Src>
+__device__ int collect_ordered(Src src, int n, int V, float t, float c, float nref,
+                               NucEntry* list, int lane) {
+  int total = 0;
+  for (int j0 = 0; j0 < n && total <= kNucMax; j0 += kWave) {
+    const int j = j0 + lane;
     float x[8];
     int vi = 0;
-    if (i < nv) {
-      vi = vec_at(i);
-      unpack8(vec_at.load(vi), x);
+    uint32_t keep = 0;
+    if (j < n) {
+      uint4 dv;
+      src(j, vi, dv);
+      unpack8(dv, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (vi * 8 + e < V && x[e] >= t) keep |= 1u << e;
     }
+    const int cnt = __popc(keep);
+    const int incl = wave_incl_scan_i(cnt, lane);
+    int pos = total + incl - cnt;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const bool in = i < nv && (vi * 8 + e < V) && x[e] >= t;
-      n = stage_append(in, (uint32_t)(vi * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n, sb);
-    }
-  }
-  return n;
-}
-
-struct AllVecs {
-  const uint4* row;
-  __device__ int operator()(int i) const { return i; }
-  __device__ uint4 load(int vi) const { return row[vi]; }
-};
-
-// The captured vectors of a row as the end phase holds them: the lanes' lists compacted in
-// lane order, entry j * 64 + lane in d[j] with its vector id in vi[j] (-inf / 0 past n).
-struct Held {
-  uint4 d[kEndB];
-  int vi[kEndB];
-  int n = 0;          // entries in all lists
-  int cl = 0;         // entries in this lane's list
-  bool over = false;  // a lane's list overflowed: the search reads the whole row
-};
-
-// Compacts the lanes' lists (through flat, in LDS) and issues the loads of the first
-// kEndB * 64 captured vectors. Called for both rows of an item before either is used, so
-// the end phase waits for one round trip instead of one per 64 captured vectors.
-__device__ __forceinline__ void gather_captured(const uint4* __restrict__ row,
-                                                const CapBuf* cap, int cnt, uint16_t* flat,
-                                                int lane, Held& h) {
-  h.over = __ballot(cnt > kCapLane) != 0;
-  h.cl = min(cnt, kCapLane);
-  const int incl = (int)wave_incl_scan((float)h.cl, lane);  // counts <= 2048: exact in fp32
-  h.n = __shfl(incl, kWave - 1, kWave);
-  __syncthreads();  // flat's previous contents have been read
-  for (int j = 0, o = incl - h.cl; j < h.cl; ++j) flat[o + j] = cap->lane[j][lane];
-  __syncthreads();
-  const int nl = h.over ? 0 : min(h.n, kEndB * kWave);
-#pragma unroll
-  for (int j = 0; j < kEndB; ++j) {
-    const int i = j * kWave + lane;
-    h.vi[j] = i < nl ? (int)flat[i] : 0;
-    h.d[j] = i < nl ? row[h.vi[j]]
-                    : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-  }
-}
-
-// Nucleus list from held vectors (h.n <= kEndB * 64).
-__device__ __forceinline__ int collect_held(const Held& h, int V, float t, float c, float nref,
-                                            SelBuf* sb, int lane) {
-  int n = 0;
-#pragma unroll
-  for (int j = 0; j < kEndB; ++j) {  // fully unrolled: h.d[] stays in registers
-    if (j * kWave < h.n && n <= kNucMax) {
-      const int i = j * kWave + lane;
-      const int vi = h.vi[j];
-      float x[8];
-      unpack8(h.d[j], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool in = i < h.n && (vi * 8 + e < V) && x[e] >= t;
-        n = stage_append(in, (uint32_t)(vi * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n,
-                         sb);
+      if ((keep >> e) & 1u) {
+        if (pos < kNucMax) list[pos] = NucEntry{vi * 8 + e, weight(x[e], c, nref)};
+        ++pos;
       }
     }
+    total += __shfl(incl, kWave - 1, kWave);
   }
-  return n;
+  return total;
 }
 
-// Nucleus list straight from the lanes' lists (rows with more than kEndB * 64 captures).
-__device__ int collect_lanes(const uint4* __restrict__ row, const CapBuf* cap, int cl, int V,
-                             float t, float c, float nref, SelBuf* sb, int lane) {
-  int n = 0;
-  const int jmax = wave_max_i(cl);
-  for (int j = 0; j < jmax && n <= kNucMax; ++j) {
-    const bool has = j < cl;
-    const int vi = has ? (int)cap->lane[j][lane] : 0;
-    float x[8];
-    unpack8(has ? row[vi] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u), x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool in = has && (vi * 8 + e < V) && x[e] >= t;
-      n = stage_append(in, (uint32_t)(vi * 8 + e), in ? weight(x[e], c, nref) : 0.0f, n, sb);
+// The captured vectors in increasing index: the LDS entries, then the spilled ids (whose
+// vectors are read again from the row).
+struct CapSrc {
+  const CapLds* cap;
+  const uint16_t* spill;
+  const uint4* row;
+  int ncap;
+  __device__ void operator()(int j, int& vi, uint4& dv) const {
+    if (j < ncap) {
+      vi = cap->idx[j];
+      dv = cap->data[j];
+    } else {
+      vi = spill[j - ncap];
+      dv = row[vi];
     }
   }
-  return n;
-}
-
-__device__ void finish_list(TopP& r, int n, NucEntry* list, SelBuf* sb, int lane) {
-  __syncthreads();
-  if (n > kNucMax) {
-    r.nuc = -1;
-  } else {
-    r.nuc = n;
-    write_sorted_list(list, n, sb, lane);
+};
+struct RowSrc {
+  const uint4* row;
+  __device__ void operator()(int j, int& vi, uint4& dv) const {
+    vi = j;
+    dv = row[j];
   }
-  __syncthreads();
-}
+};
 
 // Exact threshold search over the whole row: the largest bf16 key t with
 // mass(key >= t) >= thrP, by a 256-bucket fixed-point histogram of the key offset's high byte
 // and then of its low byte inside the chosen bucket (two passes), plus one pass for the
 // nucleus list. Used when the capture window missed the nucleus.
 __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c,
-                              float M, uint64_t thrP, NucEntry* list, SelBuf* sb, int lane) {
+                              float M, uint64_t thrP, NucEntry* list, unsigned long long* hist,
+                              int lane) {
   const float nref = -M * c;
   const uint32_t kM = key_of(M);
   TopP r;
@@ -421,7 +408,8 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
   uint64_t cum = 0, base = 0;
   int hi_b = -1, o_star = -1;
   for (int pass = 0; pass < 2; ++pass) {
-    for (int j = lane; j < kHist; j += kWave) sb->hist[j] = 0ull;
+    __syncthreads();
+    for (int j = lane; j < 256; j += kWave) hist[j] = 0ull;
     __syncthreads();
     for (int v = lane; v < nvec; v += kWave) {
       float x[8];
@@ -432,235 +420,134 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
         const uint32_t o = kM - key_of(x[e]);
         if (pass == 1 && (int)(o >> 8) != hi_b) continue;
         const uint64_t fw = fixw(weight(x[e], c, nref));
-        if (fw) atomicAdd(&sb->hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
+        if (fw) atomicAdd(&hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
       }
     }
     __syncthreads();
     if (pass == 0) {
-      hi_b = hist_crossing(sb->hist, 256, thrP, 0, &cum, lane);
+      hi_b = hist_crossing(hist, 256, thrP, 0, &cum, lane);
       if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
-      base = cum - sb->hist[hi_b];
+      base = cum - hist[hi_b];
     } else {
-      o_star = hi_b * 256 + hist_crossing(sb->hist, 256, thrP, base, &cum, lane);
+      o_star = hi_b * 256 + hist_crossing(hist, 256, thrP, base, &cum, lane);
     }
-    __syncthreads();
   }
-  if (hi_b < 0) {
-    r.t = -INFINITY;
-  } else {
-    r.t = value_of_key(kM - (uint32_t)o_star);
-  }
+  r.t = hi_b < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o_star);
   r.zs = (float)((double)cum / kFix);
-  const int n = collect_list(AllVecs{row}, nvec, V, r.t, c, nref, sb, lane);
-  finish_list(r, n, list, sb, lane);
+  const int n = collect_ordered(RowSrc{row}, nvec, V, r.t, c, nref, list, lane);
+  r.nuc = n <= kNucMax ? n : -1;
   return r;
 }
 
 // Threshold search on the captured window: fixed-point masses of the captured logits in a
 // histogram over key offsets below the row max; the first offset at which the running mass
-// reaches P * Z is the threshold. Falls back to the whole row when the window overflowed or
-// does not reach mass P within kHist offsets.
-__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V,
-                                            float c, float P, float M, float Z,
-                                            const CapBuf* cap, const Held& h, SelBuf* sb,
-                                            NucEntry* list, int lane) {
+// reaches P * Z is the threshold. Falls back to the whole row when the capture buffer
+// overflowed or the window does not reach mass P within kHist offsets.
+__device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, float c, float P,
+                            float M, float Z, CapLds* cap, const uint16_t* spill,
+                            const LaneAcc& a, NucEntry* list, int lane) {
   const float capw = kCaptureK * (kLog2e / c);  // kCaptureK * T in logit units
   const float theta = M - capw;
   const float nref = -M * c;
   const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
   const uint32_t kM = key_of(M);
-  if (h.over) return topp_full_row(row, nvec, V, c, M, thrP, list, sb, lane);
-  const bool in_regs = h.n <= kEndB * kWave;
-  for (int j = lane; j < kHist; j += kWave) sb->hist[j] = 0ull;
+  if (a.over) return topp_full_row(row, nvec, V, c, M, thrP, list, cap->hist, lane);
+  for (int j = lane; j < kHist; j += kWave) cap->hist[j] = 0ull;
   __syncthreads();
-  auto add = [&](const uint4& d, int vi) {
+  const CapSrc src{cap, spill, row, a.ncap};
+  const int ntot = a.ncap + a.nspill;
+  for (int j0 = 0; j0 < ntot; j0 += kWave) {
+    const int j = j0 + lane;
+    if (j >= ntot) continue;
+    int vi;
+    uint4 dv;
+    src(j, vi, dv);
     float x[8];
-    unpack8(d, x);
+    unpack8(dv, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (vi * 8 + e >= V || !(x[e] >= theta)) continue;
       const uint32_t o = kM - key_of(x[e]);
       if (o < (uint32_t)kHist)
-        atomicAdd(&sb->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
+        atomicAdd(&cap->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
     }
-  };
-  if (in_regs) {
-#pragma unroll
-    for (int j = 0; j < kEndB; ++j)  // fully unrolled: h.d[] stays in registers
-      if (j * kWave + lane < h.n) add(h.d[j], h.vi[j]);
-  } else {
-    const int jmax = wave_max_i(h.cl);
-    for (int j = 0; j < jmax; ++j)
-      if (j < h.cl) {
-        const int vi = (int)cap->lane[j][lane];
-        add(row[vi], vi);
-      }
   }
   __syncthreads();
   uint64_t zs = 0;
-  const int o_star = hist_crossing(sb->hist, kHist, thrP, 0, &zs, lane);
-  __syncthreads();
-  if (o_star < 0) return topp_full_row(row, nvec, V, c, M, thrP, list, sb, lane);
+  const int o_star = hist_crossing(cap->hist, kHist, thrP, 0, &zs, lane);
+  if (o_star < 0) return topp_full_row(row, nvec, V, c, M, thrP, list, cap->hist, lane);
   TopP r;
   r.slow = false;
   r.t = value_of_key(kM - (uint32_t)o_star);
   r.zs = (float)((double)zs / kFix);
-  const int n = in_regs ? collect_held(h, V, r.t, c, nref, sb, lane)
-                        : collect_lanes(row, cap, h.cl, V, r.t, c, nref, sb, lane);
-  finish_list(r, n, list, sb, lane);
+  const int n = collect_ordered(src, ntot, V, r.t, c, nref, list, lane);
+  r.nuc = n <= kNucMax ? n : -1;
   return r;
 }
 
+// The streaming pass over one row: running (m, s) per lane and, with CAPTURE, the top-p
+// window captures.
+template <bool CAPTURE>
+__device__ __forceinline__ void row_pass(const uint4* __restrict__ rp, int nvec, int V, float c,
+                                         float T, LaneAcc& acc, CapLds* cap, uint16_t* spill,
+                                         int lane) {
+  const float capw = kCaptureK * T;
+  stream_row<kDepth>(rp, nvec, lane, [&](uint4* d, int v0, bool maybe_last) {
+    if (maybe_last) mask_tail(d, v0, nvec, V, lane);
+    consume_trip<CAPTURE>(d, v0, lane, c, capw, acc, cap, spill);
+  });
+}
+
 // ----------------------------------------------------------------------------------------
-// Kernel 1: one wave per draft position (sequence b, k = 1..gamma_b): the target row p_k and
-// the draft row q_k. The bonus row p_{gamma_b+1} is only needed when every draft is
-// accepted, so the resolve step computes its law then, and only then.
-// ----------------------------------------------------------------------------------------
+// Kernel 1: one wave per logits row of a draft position (sequence b, k = 1..gamma_b): block
+// 2i is the target row p_k of draft position i = (b, k), block 2i+1 its draft row q_k.
 // TOPP: the batch carries a top-p array, so capture buffers live in (dynamic) LDS.
+// ----------------------------------------------------------------------------------------
 template <bool TOPP>
-__global__ __launch_bounds__(kWave) void chain_row_kernel(ChainParams P) {
+__global__ __launch_bounds__(kWave) void row_stats_kernel(ChainParams P) {
   extern __shared__ uint4 smem_dyn[];
-  CapBuf* cap = reinterpret_cast<CapBuf*>(smem_dyn);
-  SelBuf* sb = reinterpret_cast<SelBuf*>(cap + 2);
+  CapLds* cap = reinterpret_cast<CapLds*>(smem_dyn);
   const int lane = lane_id();
-  const int b = blockIdx.x / P.max_gamma;
-  const int k = blockIdx.x % P.max_gamma + 1;  // 1-based position
+  const int item = blockIdx.x >> 1, r = blockIdx.x & 1;
+  const int b = item / P.max_gamma;
+  const int k = item % P.max_gamma + 1;  // 1-based position
   const SeqInfo s = seq_info(P, b);
   if (s.bad_param || k > s.g) return;
-  const int trow = s.t0 + k - 1;
+  if (r == 1 && s.T == 0.0f) return;  // greedy: q is not read
   const int drow = s.d0 + k - 1;
-  RowRec* rec = P.rec + trow;
-  NucEntry* lists = P.nuc + (size_t)trow * 2 * kNucMax;
-  const uint4* rp = reinterpret_cast<const uint4*>(P.target + (size_t)trow * P.stride);
-  int flags = 0;
+  const uint16_t* base = r == 0 ? P.target + (size_t)(s.t0 + k - 1) * P.stride
+                                : P.draft + (size_t)drow * P.stride;
+  const uint4* rp = reinterpret_cast<const uint4*>(base);
+  RowStat* st = P.stat + (size_t)drow * 2 + r;
+  NucEntry* list = P.nuc + ((size_t)drow * 2 + r) * kNucMax;
   const int d = P.tokens[drow];
-  if (d < 0 || d >= P.V) flags |= SPEC_FLAG_BAD_TOKEN;
-  uint32_t lp_bits = 0, lq_bits = 0;  // the draft token's target and draft logits
-  if (!(flags & SPEC_FLAG_BAD_TOKEN) && s.T != 0.0f) {  // issued early, used last
-    lp_bits = P.target[(size_t)trow * P.stride + d];
-    lq_bits = P.draft[(size_t)drow * P.stride + d];
-  }
-
-  if (s.T == 0.0f) {  // greedy: argmax of the target row; q is not read
-    const int am = row_argmax(rp, P.nvec, P.V, lane);
-    if (lane == 0) {
-      const int acc = (!(flags & SPEC_FLAG_BAD_TOKEN) && d == am) ? 1 : 0;
-      RowRec r;
-      r.m[0] = r.m[1] = 0.0f;
-      r.z[0] = r.z[1] = 1.0f;
-      r.t[0] = r.t[1] = -INFINITY;
-      r.pd = (d == am) ? 1.0f : 0.0f;
-      r.qd = NAN;
-      r.argmax = am;
-      r.accept = acc;
-      r.flags = flags;
-      r.nuc[0] = r.nuc[1] = -1;
-      r.valid = 1;
-      r.pad[0] = r.pad[1] = 0;
-      *rec = r;
-      if (P.probe_rows) {
-        P.probe_rows[(size_t)drow * 3 + 0] = r.pd;
-        P.probe_rows[(size_t)drow * 3 + 1] = NAN;
-        P.probe_rows[(size_t)drow * 3 + 2] = (float)acc;
-      }
-    }
+  if (d < 0 || d >= P.V) {  // the resolve step flags the sequence; nothing to compute
+    if (lane == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, 0.0f, 0, -1, 0, 1};
     return;
   }
 
+  if (s.T == 0.0f) {  // greedy: argmax of the target row
+    const int am = row_argmax(rp, P.nvec, P.V, lane);
+    if (lane == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, d == am ? 1.0f : 0.0f, am, -1, 0, 1};
+    return;
+  }
+
+  const uint32_t ld_bits = base[d];  // the draft token's logit: issued early, used last
   const float c = kLog2e / s.T;
   const bool topp = TOPP && s.P < 1.0f;
-  const float capw = kCaptureK * s.T;
-  const uint4* rq = reinterpret_cast<const uint4*>(P.draft + (size_t)drow * P.stride);
-  LaneAcc ap, aq;
-  // Double-buffered: the next trip's loads are in flight while this trip is consumed.
-  constexpr int kStep = kU * kWave;
-  uint4 p0[kU], q0[kU], p1[kU], q1[kU];
-  load_trip(rp, 0, P.nvec, lane, p0);
-  load_trip(rq, 0, P.nvec, lane, q0);
-  auto consume = [&](uint4* dp, uint4* dq, int v0) {
-    mask_tail(dp, v0, P.nvec, P.V, lane);
-    mask_tail(dq, v0, P.nvec, P.V, lane);
-    if (topp) {
-      consume_trip<true>(dp, v0, lane, c, capw, ap, &cap[0]);
-      consume_trip<true>(dq, v0, lane, c, capw, aq, &cap[1]);
-    } else {
-      consume_trip<false>(dp, v0, lane, c, capw, ap, nullptr);
-      consume_trip<false>(dq, v0, lane, c, capw, aq, nullptr);
-    }
-  };
-  for (int v0 = 0; v0 < P.nvec; v0 += 2 * kStep) {
-    const int v1 = v0 + kStep;
-    if (v1 < P.nvec) {
-      load_trip(rp, v1, P.nvec, lane, p1);
-      load_trip(rq, v1, P.nvec, lane, q1);
-    }
-    consume(p0, q0, v0);
-    if (v1 >= P.nvec) break;
-    const int v2 = v1 + kStep;
-    if (v2 < P.nvec) {
-      load_trip(rp, v2, P.nvec, lane, p0);
-      load_trip(rq, v2, P.nvec, lane, q0);
-    }
-    consume(p1, q1, v1);
-  }
-  __syncthreads();
-  Held hp, hq;
-  if (topp) {
-    gather_captured(rp, &cap[0], ap.cnt, sb->flat, lane, hp);
-    gather_captured(rq, &cap[1], aq.cnt, sb->flat, lane, hq);
-  }
-  __syncthreads();  // flat's storage is the threshold search's from here
-  float Mp, Zp, Mq, Zq;
-  finish_mz(ap, c, Mp, Zp);
-  finish_mz(aq, c, Mq, Zq);
-  TopP tp{-INFINITY, Zp, -1, false}, tq{-INFINITY, Zq, -1, false};
-  if (topp) {
-    tp = topp_select(rp, P.nvec, P.V, c, s.P, Mp, Zp, &cap[0], hp, sb, lists, lane);
-    tq = topp_select(rq, P.nvec, P.V, c, s.P, Mq, Zq, &cap[1], hq, sb, lists + kNucMax, lane);
-    if (tp.slow || tq.slow) flags |= SPEC_FLAG_TOPP_SLOW;
-  }
-  float pd = NAN, qd = NAN, a = NAN;
-  int acc = 0;
-  if (!(flags & SPEC_FLAG_BAD_TOKEN)) {
-    const float lp = __uint_as_float(lp_bits << 16);
-    const float lq = __uint_as_float(lq_bits << 16);
-    pd = (lp >= tp.t) ? weight(lp, c, -Mp * c) / tp.zs : 0.0f;
-    qd = (lq >= tq.t) ? weight(lq, c, -Mq * c) / tq.zs : 0.0f;
-    if (qd > 0.0f) {
-      a = fminf(1.0f, pd / qd);
-    } else {
-      a = pd > 0.0f ? 1.0f : 0.0f;
-      flags |= SPEC_FLAG_Q_ZERO;
-    }
-    const float u = P.ovr ? P.ovr[(size_t)trow * 2]
-                          : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + k),
-                                      SPEC_PURPOSE_ACCEPT);
-    acc = (u < a) ? 1 : 0;
-  }
-  if (lane == 0) {
-    RowRec r;
-    r.m[0] = Mp;
-    r.m[1] = Mq;
-    r.z[0] = tp.zs;
-    r.z[1] = tq.zs;
-    r.t[0] = tp.t;
-    r.t[1] = tq.t;
-    r.pd = pd;
-    r.qd = qd;
-    r.argmax = -1;
-    r.accept = acc;
-    r.flags = flags;
-    r.nuc[0] = topp ? tp.nuc : -1;
-    r.nuc[1] = topp ? tq.nuc : -1;
-    r.valid = 1;
-    r.pad[0] = r.pad[1] = 0;
-    *rec = r;
-    if (P.probe_rows) {
-      P.probe_rows[(size_t)drow * 3 + 0] = pd;
-      P.probe_rows[(size_t)drow * 3 + 1] = qd;
-      P.probe_rows[(size_t)drow * 3 + 2] = a;
-    }
-  }
+  uint16_t* spill = P.spill + ((size_t)drow * 2 + r) * kCapG;
+  LaneAcc acc;
+  if (topp) row_pass<true>(rp, P.nvec, P.V, c, s.T, acc, cap, spill, lane);
+  else row_pass<false>(rp, P.nvec, P.V, c, s.T, acc, nullptr, nullptr, lane);
+  float M, Z;
+  finish_mz(acc, c, M, Z);
+  TopP tp{-INFINITY, Z, -1, false};
+  if (topp) tp = topp_select(rp, P.nvec, P.V, c, s.P, M, Z, cap, spill, acc, list, lane);
+  const float ld = __uint_as_float(ld_bits << 16);
+  const float wd = (ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;
+  if (lane == 0)
+    *st = RowStat{M, tp.zs, tp.t, wd, -1, topp ? tp.nuc : -1,
+                  tp.slow ? SPEC_FLAG_TOPP_SLOW : 0, 1};
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1331,6 +1218,15 @@ __device__ __forceinline__ bool bonus_draw_held(const uint4* __restrict__ row, i
   return true;
 }
 
+
+// Per-sequence decision state the resolve step shares through LDS.
+struct SeqDecision {
+  int n_acc;
+  int flags;
+  int bad;  // SPEC_FLAG_BAD_TOKEN / SPEC_FLAG_BAD_PARAM bits: no progress
+  RowStat sp, sq;  // statistics of the rows at the first rejection (if any)
+};
+
 __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainParams P) {
   __shared__ union {
     float tile_sum[kMaxTiles];       // inverse-CDF draw over a row
@@ -1339,24 +1235,85 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   __shared__ int sh_i[kWgWaves];
   __shared__ float sh_f[2], sh_v[kWgWaves], sh_z[kWgWaves];
   __shared__ unsigned long long sh_u[2];
-  __shared__ NucEntry s_q[kNucMax];
+  __shared__ NucEntry s_lp[kNucMax], s_lq[kNucMax];
+  __shared__ NucEntry s_pre[kPreRows][2][kPre];
+  __shared__ SeqDecision sd;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const SeqInfo s = seq_info(P, b);
   __syncthreads();  // every thread has read committed_len[b] before thread 0 rewrites it
-  // gamma_b and cu_gamma in range: the draft tokens of the sequence can be read
+  // gamma_b and cu_gamma in range: the draft tokens and statistics of the sequence exist
   const int c0 = P.cu[b], c1 = P.cu[b + 1];
   const bool cu_ok = c1 - c0 >= 0 && c1 - c0 <= P.max_gamma && c0 >= 0 && c1 <= P.n_draft;
-  const bool in_g = cu_ok && lane < s.g;
-  int tok = 0, acc = 1, rflags = 0;
-  if (in_g) tok = P.tokens[s.d0 + lane];
-  const bool bad_tok = __ballot(in_g && (tok < 0 || tok >= P.V)) != 0;
-  if (s.bad_param || bad_tok) {  // no progress: nothing emitted, pointer unchanged
+  const bool stochastic = !s.bad_param && s.T != 0.0f;
+  // The heads of the candidate positions' nucleus lists, fetched together with the
+  // statistics: the first rejection is not known yet, and the residual draw of a rejected
+  // position usually needs nothing more.
+  if (cu_ok && stochastic && P.topp) {
+    const int kk = tid / (2 * kPre), rr = (tid / kPre) & 1, j = tid % kPre;
+    if (kk < kPreRows && kk < s.g)
+      s_pre[kk][rr][j] = P.nuc[((size_t)(s.d0 + kk) * 2 + rr) * kNucMax + j];
+  }
+  if (wid == 0) {
+    const bool in_g = cu_ok && lane < s.g;
+    int tok = 0;
+    RowStat sp{}, sq{};
+    if (in_g) {
+      tok = P.tokens[s.d0 + lane];
+      sp = P.stat[(size_t)(s.d0 + lane) * 2];
+      if (stochastic) sq = P.stat[(size_t)(s.d0 + lane) * 2 + 1];
+    }
+    const bool bad_tok = __ballot(in_g && (tok < 0 || tok >= P.V)) != 0;
+    int acc = 1, rflags = 0;
+    if (in_g && !s.bad_param && !bad_tok) {
+      float pd, qd, a;
+      if (s.T == 0.0f) {  // greedy: accept iff the draft is the target argmax
+        acc = tok == sp.argmax ? 1 : 0;
+        pd = (float)acc;
+        qd = NAN;
+        a = (float)acc;
+      } else {
+        pd = sp.wd / sp.z;
+        qd = sq.wd / sq.z;
+        if (qd > 0.0f) {
+          a = fminf(1.0f, pd / qd);
+        } else {
+          a = pd > 0.0f ? 1.0f : 0.0f;
+          rflags |= SPEC_FLAG_Q_ZERO;
+        }
+        const float u = P.ovr ? P.ovr[(size_t)(s.t0 + lane) * 2]
+                              : uniform24(P.seed_lo, P.seed_hi, s.id,
+                                          (uint32_t)(s.L + lane + 1), SPEC_PURPOSE_ACCEPT);
+        acc = (u < a) ? 1 : 0;
+        rflags |= (sp.flags | sq.flags) & SPEC_FLAG_TOPP_SLOW;
+      }
+      if (P.probe_rows) {
+        P.probe_rows[(size_t)(s.d0 + lane) * 3 + 0] = pd;
+        P.probe_rows[(size_t)(s.d0 + lane) * 3 + 1] = qd;
+        P.probe_rows[(size_t)(s.d0 + lane) * 3 + 2] = a;
+      }
+    }
+    const uint64_t rej = __ballot(in_g && acc == 0);
+    const int n_acc = rej ? __ffsll((long long)rej) - 1 : s.g;
+    int f = (lane < min(n_acc + 1, s.g)) ? rflags : 0;
+    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
+    if (lane == 0) {
+      sd.n_acc = n_acc;
+      sd.flags = f;
+      sd.bad = (bad_tok ? SPEC_FLAG_BAD_TOKEN : 0) | (s.bad_param ? SPEC_FLAG_BAD_PARAM : 0);
+    }
+    if (in_g && lane == n_acc) {  // the first rejected position
+      sd.sp = sp;
+      sd.sq = sq;
+    }
+  }
+  __syncthreads();
+  const int n_acc = sd.n_acc;
+  int flags = sd.flags;
+  if (sd.bad) {  // no progress: nothing emitted, pointer unchanged
     if (tid == 0) {
       P.num_acc[b] = 0;
-      if (P.flags_out)
-        P.flags_out[b] = (bad_tok ? SPEC_FLAG_BAD_TOKEN : 0) |
-                         (s.bad_param ? SPEC_FLAG_BAD_PARAM : 0);
+      if (P.flags_out) P.flags_out[b] = sd.bad;
       if (P.probe_seq) {
         P.probe_seq[2 * b] = NAN;
         P.probe_seq[2 * b + 1] = NAN;
@@ -1364,21 +1321,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
     }
     return;
   }
-  // decisions and first rejection (gamma_b <= 64: one wave ballot)
-  if (in_g) {
-    const RowRec& r = P.rec[s.t0 + lane];
-    acc = r.accept;
-    rflags = r.flags;
-  }
-  const uint64_t rej = __ballot(in_g && acc == 0);
-  const int n_acc = rej ? __ffsll((long long)rej) - 1 : s.g;
   const int kstar = n_acc + 1;
-  int flags = 0;
-  {
-    int f = (lane < min(kstar, s.g)) ? rflags : 0;
-    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
-    flags = f & (SPEC_FLAG_Q_ZERO | SPEC_FLAG_TOPP_SLOW);
-  }
   const int trow = s.t0 + kstar - 1;
   const bool residual = kstar <= s.g;
   const uint4* prow = reinterpret_cast<const uint4*>(P.target + (size_t)trow * P.stride);
@@ -1399,7 +1342,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
       float M, Z;
       const bool held = P.nvec <= kRowSlots * kResolveThreads;
       if (!held || !bonus_draw_held(prow, P.nvec, P.V, c, topp, s.P, u, sbuf.tile_sum,
-                                    sbuf.hist, s_q, sh_i, sh_f, sh_v, sh_z, sh_u, &d, &M,
+                                    sbuf.hist, s_lp, sh_i, sh_f, sh_v, sh_z, sh_u, &d, &M,
                                     &Z)) {
         if (!held) wg_row_mz(prow, P.nvec, P.V, c, sh_v, sh_z, M, Z);
         float t = -INFINITY, zs = Z;
@@ -1414,28 +1357,38 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
       py = d.wtok;
     }
   } else if (s.T == 0.0f) {
-    const RowRec r = P.rec[trow];
-    y = r.argmax;
+    y = sd.sp.argmax;
     py = 1.0f;
   } else {  // first rejection at kstar: the residual max(0, p - q), or p if it has no mass
-    const RowRec r = P.rec[trow];
-    flags |= r.flags & SPEC_FLAG_TOPP_SLOW;
+    const RowStat sp = sd.sp, sq = sd.sq;
     const float u = P.ovr ? P.ovr[(size_t)trow * 2 + 1]
                           : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
                                       SPEC_PURPOSE_RESIDUAL);
     const float c = kLog2e / s.T;
-    const NucEntry* lists = P.nuc + (size_t)trow * 2 * kNucMax;
-    const RowLaw Lp{prow, c, -r.m[0] * c, r.t[0], 1.0f / r.z[0]};
+    const RowLaw Lp{prow, c, -sp.m * c, sp.t, 1.0f / sp.z};
     const RowLaw Lq{reinterpret_cast<const uint4*>(P.draft +
                                                    (size_t)(s.d0 + kstar - 1) * P.stride),
-                    c, -r.m[1] * c, r.t[1], 1.0f / r.z[1]};
+                    c, -sq.m * c, sq.t, 1.0f / sq.z};
     Draw d;
-    const bool lists_p = r.nuc[0] >= 0, lists_pq = lists_p && r.nuc[1] >= 0;
+    const bool lists_p = sp.nuc >= 0, lists_pq = lists_p && sq.nuc >= 0;
+    const NucEntry* lp = s_lp;
+    const NucEntry* lq = s_lq;
+    if (lists_p) {
+      const bool pre = kstar - 1 < kPreRows && sp.nuc <= kPre && sq.nuc <= kPre;
+      if (pre) {
+        lp = s_pre[kstar - 1][0];
+        lq = s_pre[kstar - 1][1];
+      } else {
+        const NucEntry* gl = P.nuc + (size_t)(s.d0 + kstar - 1) * 2 * kNucMax;
+        for (int j = tid; j < sp.nuc; j += kResolveThreads) s_lp[j] = gl[j];
+        if (lists_pq)
+          for (int j = tid; j < sq.nuc; j += kResolveThreads) s_lq[j] = gl[kNucMax + j];
+        __syncthreads();
+      }
+    }
     if (lists_pq) {
-      for (int j = tid; j < r.nuc[1]; j += kResolveThreads) s_q[j] = lists[kNucMax + j];
-      __syncthreads();
       if (wid == 0) {
-        d = draw_from_lists(lists, r.nuc[0], r.z[0], s_q, r.nuc[1], r.z[1], true, u, lane);
+        d = draw_from_lists(lp, sp.nuc, sp.z, lq, sq.nuc, sq.z, true, u, lane);
         if (lane == 0) {
           sh_i[0] = d.token;
           sh_f[0] = d.total;
@@ -1456,7 +1409,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
       flags |= SPEC_FLAG_RESID_FALLBACK;
       if (lists_p) {
         if (wid == 0) {
-          d = draw_from_lists(lists, r.nuc[0], r.z[0], nullptr, 0, 1.0f, false, u, lane);
+          d = draw_from_lists(lp, sp.nuc, sp.z, nullptr, 0, 1.0f, false, u, lane);
           if (lane == 0) {
             sh_i[0] = d.token;
             sh_f[0] = d.total;
@@ -1473,7 +1426,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
     }
   }
   if (wid == 0) {
-    if (lane < n_acc) P.out_tokens[s.t0 + lane] = tok;
+    if (lane < n_acc) P.out_tokens[s.t0 + lane] = P.tokens[s.d0 + lane];
     if (lane == 0) {
       P.out_tokens[s.t0 + n_acc] = y;
       P.num_acc[b] = n_acc;
@@ -1490,9 +1443,12 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
 }  // namespace
 
 size_t chain_workspace_bytes(int32_t batch, int32_t total_draft_rows, int32_t vocab) {
+  (void)batch;
   (void)vocab;
-  const size_t items = (size_t)total_draft_rows + (size_t)batch;
-  return align256(items * sizeof(RowRec)) + align256(items * 2 * kNucMax * sizeof(NucEntry));
+  const size_t rows = 2 * (size_t)total_draft_rows;
+  const size_t n = align256(rows * sizeof(RowStat)) + align256(rows * kNucMax * sizeof(NucEntry)) +
+                   align256(rows * kCapG * sizeof(uint16_t));
+  return n > 256 ? n : 256;  // never 0: a batch without drafts still passes a workspace
 }
 
 hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
@@ -1511,10 +1467,11 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   P.probe_rows = a.probe_rows;
   P.probe_seq = a.probe_seq;
   P.ovr = a.uniform_override;
-  const size_t items = (size_t)a.total_draft_rows + (size_t)a.batch;
-  P.rec = reinterpret_cast<RowRec*>(ws);
-  P.nuc = reinterpret_cast<NucEntry*>(reinterpret_cast<char*>(ws) +
-                                      align256(items * sizeof(RowRec)));
+  const size_t rows = 2 * (size_t)a.total_draft_rows;
+  P.stat = reinterpret_cast<RowStat*>(ws);
+  char* w = reinterpret_cast<char*>(ws) + align256(rows * sizeof(RowStat));
+  P.nuc = reinterpret_cast<NucEntry*>(w);
+  P.spill = reinterpret_cast<uint16_t*>(w + align256(rows * kNucMax * sizeof(NucEntry)));
   P.B = a.batch;
   P.V = a.vocab;
   P.stride = a.row_stride;
@@ -1527,13 +1484,14 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(a.profile_events);
   hipError_t e = hipSuccess;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  const unsigned grid = (unsigned)a.batch * (unsigned)a.max_gamma;  // draft positions
+  // two rows (target, draft) per draft position slot (b, k <= max_gamma)
+  const unsigned grid = 2u * (unsigned)a.batch * (unsigned)a.max_gamma;
   if (grid > 0) {
     if (a.top_p)
-      hipLaunchKernelGGL(chain_row_kernel<true>, dim3(grid), dim3(kWave),
-                         2 * sizeof(CapBuf) + sizeof(SelBuf), st, P);
+      hipLaunchKernelGGL(row_stats_kernel<true>, dim3(grid), dim3(kWave), sizeof(CapLds), st,
+                         P);
     else
-      hipLaunchKernelGGL(chain_row_kernel<false>, dim3(grid), dim3(kWave), 0, st, P);
+      hipLaunchKernelGGL(row_stats_kernel<false>, dim3(grid), dim3(kWave), 0, st, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
@@ -1543,4 +1501,3 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
 }
 
 }  // namespace specv
-

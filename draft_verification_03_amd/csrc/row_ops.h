@@ -27,6 +27,53 @@ __device__ __forceinline__ void load_trip(const uint4* __restrict__ row, int v0,
   }
 }
 
+// Loads one full trip (every vector exists): no predication.
+__device__ __forceinline__ void load_full(const uint4* __restrict__ row, int v0, int lane,
+                                          uint4 d[kU]) {
+  const uint4* base = row + v0;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) d[u] = base[u * kWave + lane];
+}
+
+// Streams vectors [0, nvec) of a row through consume(d, v0, maybe_last), one trip of kU
+// vectors per lane at a time, with DEPTH trips of loads in flight. The steady-state loop
+// loads full trips only, unpredicated, so that the compiler can keep the younger trips'
+// loads outstanding while it consumes the oldest; the last few full trips and the partial
+// trip follow it. maybe_last is true only where the trip may hold vector nvec - 1.
+template <int DEPTH, typename F>
+__device__ __forceinline__ void stream_row(const uint4* __restrict__ row, int nvec, int lane,
+                                           F&& consume) {
+  constexpr int kStep = kU * kWave;
+  const int nfull = nvec / kStep;
+  int t = 0;
+  if (nfull >= DEPTH) {
+    uint4 buf[DEPTH][kU];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load_full(row, s * kStep, lane, buf[s]);
+    for (; t + 2 * DEPTH <= nfull; t += DEPTH) {  // trips t .. t+DEPTH-1; none is the last
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        consume(buf[s], (t + s) * kStep, false);
+        load_full(row, (t + s + DEPTH) * kStep, lane, buf[s]);
+      }
+    }
+    // DEPTH .. 2*DEPTH-1 full trips remain; the first DEPTH of them are loaded
+#pragma unroll
+    for (int s = 0; s < 2 * DEPTH - 1; ++s) {
+      if (t + s < nfull) {
+        consume(buf[s % DEPTH], (t + s) * kStep, true);
+        if (t + s + DEPTH < nfull) load_full(row, (t + s + DEPTH) * kStep, lane, buf[s % DEPTH]);
+      }
+    }
+    t = nfull;
+  }
+  for (; t * kStep < nvec; ++t) {  // short rows, and the partial trip
+    uint4 d[kU];
+    load_trip(row, t * kStep, nvec, lane, d);
+    consume(d, t * kStep, true);
+  }
+}
+
 // Masks the logits of the last, partial vector (V not a multiple of 8) to -inf; only the
 // last trip of a row can hold it.
 __device__ __forceinline__ void mask_tail(uint4 d[kU], int v0, int nvec, int V, int lane) {
@@ -84,44 +131,13 @@ __device__ __forceinline__ void argmax_trip(uint4 d[kU], int v0, int nvec, int V
   }
 }
 
-// Argmax of vectors [cv0, cv1) of a row (cv0 a multiple of the trip): the wave's largest
-// value and its lowest index.
-__device__ __forceinline__ void row_argmax_range(const uint4* __restrict__ row, int cv0,
-                                                 int cv1, int nvec, int V, int lane, float& v,
-                                                 int& i) {
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  constexpr int kStep = kU * kWave;
-  uint4 a[kU], b[kU];
-  load_trip(row, cv0, cv1, lane, a);
-  for (int v0 = cv0; v0 < cv1; v0 += 2 * kStep) {
-    const int v1 = v0 + kStep;
-    if (v1 < cv1) load_trip(row, v1, cv1, lane, b);
-    argmax_trip(a, v0, nvec, V, lane, bv, bi);
-    if (v1 >= cv1) break;
-    if (v1 + kStep < cv1) load_trip(row, v1 + kStep, cv1, lane, a);
-    argmax_trip(b, v1, nvec, V, lane, bv, bi);
-  }
-  wave_argmax(bv, bi);
-  v = bv;
-  i = bi == 0x7FFFFFFF ? cv0 * 8 : bi;
-}
-
 __device__ __forceinline__ int row_argmax(const uint4* __restrict__ row, int nvec, int V,
                                           int lane) {
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  constexpr int kStep = kU * kWave;
-  uint4 a[kU], b[kU];
-  load_trip(row, 0, nvec, lane, a);
-  for (int v0 = 0; v0 < nvec; v0 += 2 * kStep) {
-    const int v1 = v0 + kStep;
-    if (v1 < nvec) load_trip(row, v1, nvec, lane, b);
-    argmax_trip(a, v0, nvec, V, lane, bv, bi);
-    if (v1 >= nvec) break;
-    if (v1 + kStep < nvec) load_trip(row, v1 + kStep, nvec, lane, a);
-    argmax_trip(b, v1, nvec, V, lane, bv, bi);
-  }
+  stream_row<2>(row, nvec, lane, [&](uint4* d, int v0, bool) {
+    argmax_trip(d, v0, nvec, V, lane, bv, bi);
+  });
   wave_argmax(bv, bi);
   return bi == 0x7FFFFFFF ? 0 : bi;
 }

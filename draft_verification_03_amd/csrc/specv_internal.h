@@ -10,25 +10,24 @@
 
 namespace specv {
 
-// Longest nucleus list a row record keeps for the resolve step; longer nuclei are re-read
+// Longest nucleus list a row statistic keeps for the resolve step; longer nuclei are re-read
 // from the logits instead.
 constexpr int kNucMax = 256;
 
-// Per-(sequence, position) record the row pass leaves for the resolve step. Index 0 is the
-// target row (p), index 1 the draft row (q).
-struct RowRec {
-  float m[2];      // largest logit of the row
-  float z[2];      // normaliser of the kept set, in units of exp((m - m)/T) = 1
-  float t[2];      // nucleus threshold logit (-inf: every token kept)
-  float pd, qd;    // p_k(d_k), q_k(d_k)
-  int32_t argmax;  // target-row argmax (greedy rows)
-  int32_t accept;  // 1 accepted, 0 rejected
-  int32_t flags;   // SPEC_FLAG_* seen by this item
-  int32_t nuc[2];  // entries in the nucleus list (-1: list not kept, re-read the row)
-  int32_t valid;   // 1 once the item ran
-  int32_t pad[2];
+// Statistics the row pass leaves for one logits row of a draft position: its target row
+// (index 0) or its draft row (index 1). Weights are exp2((l - m) * log2(e) / T), so the
+// row's largest logit weighs 1.
+struct RowStat {
+  float m;         // largest logit of the row (T > 0)
+  float z;         // normaliser: summed weight of the kept set
+  float t;         // nucleus threshold logit (-inf: every token kept)
+  float wd;        // weight of the draft token if kept, else 0 (T = 0: [token == argmax])
+  int32_t argmax;  // greedy rows: argmax, lowest id on ties
+  int32_t nuc;     // entries in the row's nucleus list (-1: no list, re-read the row)
+  int32_t flags;   // SPEC_FLAG_TOPP_SLOW
+  int32_t valid;   // 1 once written
 };
-static_assert(sizeof(RowRec) == 64, "RowRec must stay 64 bytes");
+static_assert(sizeof(RowStat) == 32, "RowStat must stay 32 bytes");
 
 struct NucEntry {
   int32_t idx;  // token id
