@@ -49,21 +49,17 @@ def kernel_source_hash() -> str:
 def algorithmic_bytes(x) -> dict:
     """Bytes the verification must move at least once, per call.
 
-    The row kernel covers the draft positions only: per position its p row and its q row,
-    each read once (2 * V * 2 B), and the draft token (4 B). A bonus row p_{gamma+1}
-    (V * 2 B) is read by the resolve step, and only for a sequence whose drafts were all
-    accepted; ``call`` counts it for every sequence (the upper bound), plus the outputs
-    (tokens, accepted counts, committed lengths)."""
+    The row kernel reads every logits row once: per draft position its p row and its q row
+    (2 * V * 2 B) plus the draft token (4 B), and per sequence the bonus row p_{gamma+1}
+    (V * 2 B). The call adds the outputs (tokens, accepted counts, committed lengths)."""
     import numpy as np
     cu = x["cu_gamma"]
     B = len(cu) - 1
     nd = int(cu[-1])
     V = x["vocab"]
-    tokens_in = nd * 4
-    row_pass = 2 * nd * V * 2 + tokens_in
+    row_pass = (2 * nd + B) * V * 2 + nd * 4
     outputs = (nd + B) * 4 + B * 4 * 2
-    return dict(row_pass=row_pass, row_units=nd, bytes_per_unit=2 * V * 2 + 4,
-                call=row_pass + B * V * 2 + outputs, rows=int(np.sum(np.diff(cu) + 1)))
+    return dict(row_pass=row_pass, call=row_pass + outputs, rows=int(np.sum(np.diff(cu) + 1)))
 
 
 def read_traffic(src_hash):

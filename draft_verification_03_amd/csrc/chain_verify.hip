@@ -41,6 +41,7 @@ constexpr float kCaptureK = 7.0f;
 constexpr int kCapV = 256;    // captured vectors per row held in LDS
 constexpr int kCapG = 1024;   // further captured vector ids per row spilled to the workspace
 constexpr int kDepth = 2;     // trips of loads in flight per wave in the row pass
+constexpr int kRowWaves = 2;  // rows (one per wave) per row-pass workgroup
 constexpr int kRefresh = 2;   // trips between refreshes of the capture threshold
 constexpr int kHist = 512;    // key offsets below the row max resolved by the window search
 constexpr int kResolveThreads = 1024;
@@ -82,6 +83,14 @@ struct CapLds {
   unsigned long long hist[kHist];
   uint16_t idx[kCapV];
 };
+
+// Orders one wave's own LDS accesses around a phase boundary (a row's LDS area belongs to
+// one wave, so the row pass never needs a workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -408,9 +417,9 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
   uint64_t cum = 0, base = 0;
   int hi_b = -1, o_star = -1;
   for (int pass = 0; pass < 2; ++pass) {
-    __syncthreads();
+    wave_sync();
     for (int j = lane; j < 256; j += kWave) hist[j] = 0ull;
-    __syncthreads();
+    wave_sync();
     for (int v = lane; v < nvec; v += kWave) {
       float x[8];
       unpack8(row[v], x);
@@ -423,7 +432,7 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
         if (fw) atomicAdd(&hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
       }
     }
-    __syncthreads();
+    wave_sync();
     if (pass == 0) {
       hi_b = hist_crossing(hist, 256, thrP, 0, &cum, lane);
       if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
@@ -453,7 +462,7 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
   const uint32_t kM = key_of(M);
   if (a.over) return topp_full_row(row, nvec, V, c, M, thrP, list, cap->hist, lane);
   for (int j = lane; j < kHist; j += kWave) cap->hist[j] = 0ull;
-  __syncthreads();
+  wave_sync();
   const CapSrc src{cap, spill, row, a.ncap};
   const int ntot = a.ncap + a.nspill;
   for (int j0 = 0; j0 < ntot; j0 += kWave) {
@@ -472,7 +481,7 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
         atomicAdd(&cap->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
     }
   }
-  __syncthreads();
+  wave_sync();
   uint64_t zs = 0;
   const int o_star = hist_crossing(cap->hist, kHist, thrP, 0, &zs, lane);
   if (o_star < 0) return topp_full_row(row, nvec, V, c, M, thrP, list, cap->hist, lane);
@@ -499,31 +508,48 @@ __device__ __forceinline__ void row_pass(const uint4* __restrict__ rp, int nvec,
 }
 
 // ----------------------------------------------------------------------------------------
-// Kernel 1: one wave per logits row of a draft position (sequence b, k = 1..gamma_b): block
-// 2i is the target row p_k of draft position i = (b, k), block 2i+1 its draft row q_k.
+// Kernel 1: one wave per logits row, kRowWaves independent waves per workgroup (a workgroup
+// that holds LDS takes one of a CU's 16 workgroup slots; pairing rows lets a CU hold more
+// than 16 rows at once). Sequence b owns row ids b*(2G+1) .. b*(2G+1)+2G (G = max_gamma):
+// id 2(k-1) is the target row p_k of draft position k, id 2(k-1)+1 its draft row q_k, and
+// the last one the bonus row p_{gamma_b+1} (needed only after a full accept, but read with
+// the rest: one workgroup cannot pull a row from HBM fast enough to do it later without
+// stalling the whole resolve step).
 // TOPP: the batch carries a top-p array, so capture buffers live in (dynamic) LDS.
 // ----------------------------------------------------------------------------------------
+// Five waves per SIMD (<= 102 VGPRs): 20 rows resident per CU, so a batch of up to 20 rows
+// per CU (B=256, gamma=8: 17) streams in one round.
 template <bool TOPP>
-__global__ __launch_bounds__(kWave) void row_stats_kernel(ChainParams P) {
+__global__ __launch_bounds__(kRowWaves * kWave) __attribute__((amdgpu_waves_per_eu(5)))
+void row_stats_kernel(ChainParams P) {
   extern __shared__ uint4 smem_dyn[];
-  CapLds* cap = reinterpret_cast<CapLds*>(smem_dyn);
-  const int lane = lane_id();
-  const int item = blockIdx.x >> 1, r = blockIdx.x & 1;
-  const int b = item / P.max_gamma;
-  const int k = item % P.max_gamma + 1;  // 1-based position
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  CapLds* cap = reinterpret_cast<CapLds*>(smem_dyn) + w;
+  const int per = 2 * P.max_gamma + 1;
+  const int row_id = blockIdx.x * kRowWaves + w;
+  if (row_id >= P.B * per) return;
+  const int b = row_id / per, j = row_id % per;
+  const bool bonus = j == 2 * P.max_gamma;
+  const int r = bonus ? 0 : (j & 1);
   const SeqInfo s = seq_info(P, b);
-  if (s.bad_param || k > s.g) return;
+  if (s.bad_param) return;
+  const int k = bonus ? s.g + 1 : (j >> 1) + 1;  // 1-based position
+  if (!bonus && k > s.g) return;
   if (r == 1 && s.T == 0.0f) return;  // greedy: q is not read
-  const int drow = s.d0 + k - 1;
+  const int drow = s.d0 + k - 1;       // draft row (draft positions only)
   const uint16_t* base = r == 0 ? P.target + (size_t)(s.t0 + k - 1) * P.stride
                                 : P.draft + (size_t)drow * P.stride;
   const uint4* rp = reinterpret_cast<const uint4*>(base);
-  RowStat* st = P.stat + (size_t)drow * 2 + r;
-  NucEntry* list = P.nuc + ((size_t)drow * 2 + r) * kNucMax;
-  const int d = P.tokens[drow];
-  if (d < 0 || d >= P.V) {  // the resolve step flags the sequence; nothing to compute
-    if (lane == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, 0.0f, 0, -1, 0, 1};
-    return;
+  const size_t slot = bonus ? 2 * (size_t)P.n_draft + (size_t)b : (size_t)drow * 2 + r;
+  RowStat* st = P.stat + slot;
+  NucEntry* list = P.nuc + slot * kNucMax;
+  int d = -1;  // the draft token (none for the bonus row)
+  if (!bonus) {
+    d = P.tokens[drow];
+    if (d < 0 || d >= P.V) {  // the resolve step flags the sequence; nothing to compute
+      if (lane == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, 0.0f, 0, -1, 0, 1};
+      return;
+    }
   }
 
   if (s.T == 0.0f) {  // greedy: argmax of the target row
@@ -532,10 +558,10 @@ __global__ __launch_bounds__(kWave) void row_stats_kernel(ChainParams P) {
     return;
   }
 
-  const uint32_t ld_bits = base[d];  // the draft token's logit: issued early, used last
+  const uint32_t ld_bits = d >= 0 ? base[d] : 0u;  // the draft token's logit: issued early
   const float c = kLog2e / s.T;
   const bool topp = TOPP && s.P < 1.0f;
-  uint16_t* spill = P.spill + ((size_t)drow * 2 + r) * kCapG;
+  uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
   if (topp) row_pass<true>(rp, P.nvec, P.V, c, s.T, acc, cap, spill, lane);
   else row_pass<false>(rp, P.nvec, P.V, c, s.T, acc, nullptr, nullptr, lane);
@@ -544,7 +570,7 @@ __global__ __launch_bounds__(kWave) void row_stats_kernel(ChainParams P) {
   TopP tp{-INFINITY, Z, -1, false};
   if (topp) tp = topp_select(rp, P.nvec, P.V, c, s.P, M, Z, cap, spill, acc, list, lane);
   const float ld = __uint_as_float(ld_bits << 16);
-  const float wd = (ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;
+  const float wd = (d >= 0 && ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;
   if (lane == 0)
     *st = RowStat{M, tp.zs, tp.t, wd, -1, topp ? tp.nuc : -1,
                   tp.slow ? SPEC_FLAG_TOPP_SLOW : 0, 1};
@@ -849,375 +875,7 @@ __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq,
   return draw_scan(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
 }
 
-// ---- the bonus row's law, by the whole resolve workgroup --------------------------------
-
 constexpr int kWgWaves = kResolveThreads / kWave;
-constexpr int kWgBatch = 4;  // vectors in flight per thread in a workgroup pass
-
-// Vector v of a row as fp32 logits, -inf past the vocabulary (and for v >= nvec).
-__device__ __forceinline__ void row_vec(const uint4& d, int v, int nvec, int V, float x[8]) {
-  unpack8(d, x);
-  if (v >= nvec) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
-  } else if (v == nvec - 1) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (v * 8 + e >= V) x[e] = -INFINITY;
-  }
-}
-
-// Calls f(v, x) for every vector of the row, thread tid taking v = tid + j * kResolveThreads,
-// with kWgBatch loads in flight per thread.
-template <typename F>
-__device__ __forceinline__ void wg_row_pass(const uint4* __restrict__ row, int nvec, int V,
-                                            F&& f) {
-  const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kWgBatch * kResolveThreads) {
-    uint4 d[kWgBatch];
-#pragma unroll
-    for (int j = 0; j < kWgBatch; ++j) {
-      const int v = v0 + j * kResolveThreads;
-      d[j] = v < nvec ? row[v] : ninf;
-    }
-#pragma unroll
-    for (int j = 0; j < kWgBatch; ++j) {
-      const int v = v0 + j * kResolveThreads;
-      float x[8];
-      row_vec(d[j], v, nvec, V, x);
-      f(v, x);
-    }
-  }
-}
-
-// Argmax of a row, lowest token id on ties (greedy bonus token).
-__device__ int wg_row_argmax(const uint4* __restrict__ row, int nvec, int V, float* sh_v,
-                             int* sh_i) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  wg_row_pass(row, nvec, V, [&](int v, const float* x) {
-    const float vm = max8(x);
-    if (vm > bv) {  // vectors arrive in increasing v per thread: the first hit is the lowest
-      bv = vm;
-#pragma unroll
-      for (int e = 7; e >= 0; --e)
-        if (x[e] == vm) bi = v * 8 + e;
-    }
-  });
-  wave_argmax(bv, bi);
-  if (lane == 0) {
-    sh_v[wid] = bv;
-    sh_i[wid] = bi;
-  }
-  __syncthreads();
-  float v = sh_v[0];
-  int i = sh_i[0];
-  for (int w = 1; w < kWgWaves; ++w)
-    if (sh_v[w] > v || (sh_v[w] == v && sh_i[w] < i)) {
-      v = sh_v[w];
-      i = sh_i[w];
-    }
-  __syncthreads();
-  return i == 0x7FFFFFFF ? 0 : i;
-}
-
-// Max M and normaliser Z = sum exp2((l - M) c) of a row: per-thread online (m, s), then the
-// waves' partials merged in wave order.
-__device__ void wg_row_mz(const uint4* __restrict__ row, int nvec, int V, float c, float* sh_v,
-                          float* sh_z, float& M, float& Z) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  LaneAcc a;
-  wg_row_pass(row, nvec, V, [&](int, const float* x) {
-    const float vm = max8(x);
-    if (vm == -INFINITY) return;
-    if (vm > a.m) {
-      a.s *= __builtin_amdgcn_exp2f((a.m - vm) * c);  // 0 while a.m = -inf (a.s = 0 then)
-      a.m = vm;
-    }
-    const float nref = -a.m * c;
-    float st = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st += weight(x[e], c, nref);
-    a.s += st;
-  });
-  float Mw, Zw;
-  finish_mz(a, c, Mw, Zw);
-  if (lane == 0) {
-    sh_v[wid] = Mw;
-    sh_z[wid] = Zw;
-  }
-  __syncthreads();
-  M = sh_v[0];
-  for (int w = 1; w < kWgWaves; ++w) M = fmaxf(M, sh_v[w]);
-  Z = 0.0f;
-  for (int w = 0; w < kWgWaves; ++w)
-    if (sh_v[w] != -INFINITY) Z += sh_z[w] * __builtin_amdgcn_exp2f((sh_v[w] - M) * c);
-  __syncthreads();
-}
-
-// Top-p threshold of a row whose (M, Z) are known, by the same rule as the row pass: a
-// fixed-point histogram of the weights over key offsets below M, first inside the window
-// M - kCaptureK*T (one pass), else over all keys by high byte then low byte (two passes).
-// Returns t* and the kept mass Zs; *slow is set when the window did not hold the nucleus.
-__device__ float wg_topp_threshold(const uint4* __restrict__ row, int nvec, int V, float c,
-                                   float P, float M, float Z, unsigned long long* hist,
-                                   int* sh_i, unsigned long long* sh_u, float* zs_out,
-                                   bool* slow) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const float theta = M - kCaptureK * (kLog2e / c);
-  const float nref = -M * c;
-  const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
-  const uint32_t kM = key_of(M);
-  for (int j = tid; j < kHist; j += kResolveThreads) hist[j] = 0ull;
-  __syncthreads();
-  wg_row_pass(row, nvec, V, [&](int, const float* x) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (!(x[e] >= theta)) continue;
-      const uint32_t o = kM - key_of(x[e]);
-      if (o < (uint32_t)kHist) atomicAdd(&hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
-    }
-  });
-  __syncthreads();
-  if (wid == 0) {
-    uint64_t zs = 0;
-    const int o = hist_crossing(hist, kHist, thrP, 0, &zs, lane);
-    if (lane == 0) {
-      sh_i[0] = o;
-      sh_u[0] = zs;
-    }
-  }
-  __syncthreads();
-  int o_star = sh_i[0];
-  uint64_t zs = sh_u[0];
-  *slow = o_star < 0;
-  if (o_star < 0) {  // the nucleus reaches below the window: exact search over all keys
-    int hi_b = -1;
-    uint64_t base = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      __syncthreads();
-      for (int j = tid; j < 256; j += kResolveThreads) hist[j] = 0ull;
-      __syncthreads();
-      wg_row_pass(row, nvec, V, [&](int, const float* x) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (x[e] == -INFINITY) continue;
-          const uint32_t o = kM - key_of(x[e]);
-          if (pass == 1 && (int)(o >> 8) != hi_b) continue;
-          const uint64_t fw = fixw(weight(x[e], c, nref));
-          if (fw) atomicAdd(&hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
-        }
-      });
-      __syncthreads();
-      if (wid == 0) {
-        uint64_t cum = 0;
-        const int b = hist_crossing(hist, 256, thrP, pass == 0 ? 0 : base, &cum, lane);
-        if (lane == 0) {
-          sh_i[0] = b;
-          sh_u[0] = cum;
-          sh_u[1] = b >= 0 ? cum - hist[b] : 0;
-        }
-      }
-      __syncthreads();
-      const int bsel = sh_i[0];
-      zs = sh_u[0];
-      if (bsel < 0) {  // rounding left the whole row just below P: keep everything
-        o_star = -1;
-        break;
-      }
-      if (pass == 0) {
-        hi_b = bsel;
-        base = sh_u[1];
-      } else {
-        o_star = hi_b * 256 + bsel;
-      }
-    }
-    __syncthreads();
-  }
-  *zs_out = (float)((double)zs / kFix);
-  return o_star < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o_star);
-}
-
-constexpr int kRowSlots = 16;  // vectors per thread when the workgroup holds a whole row
-
-// The packed vector itself, hidden from the optimiser: each pass over held vectors unpacks
-// again instead of keeping every unpacked logit of an earlier pass alive (twice the
-// registers of the packed data).
-__device__ __forceinline__ uint4 opaque(uint4 d) {
-  asm volatile("" : "+v"(d.x), "+v"(d.y), "+v"(d.z), "+v"(d.w));
-  return d;
-}
-
-// The bonus draw from p_{gamma+1} for a row of at most kRowSlots * kResolveThreads vectors,
-// loaded once into registers (thread tid holds vectors tid + j * kResolveThreads, so tile g
-// of 64 vectors is wave g % kWgWaves's slot g / kWgWaves). One exponential per logit: the
-// row max M first (no exponentials), then every weight against M, kept per slot; Z and the
-// tile sums follow from the slot sums. With top-p the kept tokens (at most kNucMax) are
-// collected from the registers into a sorted list and drawn from like a rejected row's
-// list. Returns false, with M and Z, when the top-p window did not hold the nucleus or the
-// nucleus is longer than a list (the caller then takes the streaming path).
-__device__ __forceinline__ bool bonus_draw_held(const uint4* __restrict__ row, int nvec, int V,
-                                                float c, bool topp, float P, float u,
-                                                float* tile_sum, unsigned long long* hist,
-                                                NucEntry* list, int* sh_i, float* sh_f,
-                                                float* sh_v, float* sh_z,
-                                                unsigned long long* sh_u, Draw* out,
-                                                float* Mout, float* Zout) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  // Masked once, as loaded: slots past the row hold -inf logits (their load re-reads the
-  // last vector, in bounds), and so do the logits of the last vector past V.
-  const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-  uint4 d[kRowSlots];
-#pragma unroll
-  for (int j = 0; j < kRowSlots; ++j) {
-    const int v = tid + j * kResolveThreads;
-    const uint4 q = row[min(v, nvec - 1)];
-    d[j] = v < nvec ? q : ninf;
-    if (v == nvec - 1 && (V & 7)) {  // one lane of the workgroup
-      uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e >= (V & 7)) w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0x0000FFFFu) | 0xFF800000u)
-                                              : ((w[e >> 1] & 0xFFFF0000u) | 0x0000FF80u);
-      d[j] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-  // M: lane max, wave max, then the waves' maxima.
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kRowSlots; ++j) {
-    float x[8];
-    unpack8(opaque(d[j]), x);
-    m = vmax3(m, max8(x), max8(x));
-  }
-  m = wave_max_dpp(m);
-  if (lane == 0) sh_v[wid] = m;
-  __syncthreads();
-  float M = sh_v[0];
-  for (int w = 1; w < kWgWaves; ++w) M = fmaxf(M, sh_v[w]);
-  const float nref = -M * c;  // M is finite: a row holds a finite logit
-  // Weights against M, summed per slot; Z over the workgroup in wave order.
-  float sj[kRowSlots];
-  float lz = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kRowSlots; ++j) {
-    float x[8];
-    unpack8(opaque(d[j]), x);
-    float t = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t += weight(x[e], c, nref);
-    sj[j] = t;
-    lz += t;
-  }
-  lz = wave_sum(lz);
-  if (lane == 0) sh_z[wid] = lz;
-  __syncthreads();
-  float Z = 0.0f;
-  for (int w = 0; w < kWgWaves; ++w) Z += sh_z[w];
-  *Mout = M;
-  *Zout = Z;
-  if (topp) {
-    const float theta = M - kCaptureK * (kLog2e / c);
-    const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
-    const uint32_t kM = key_of(M);
-    for (int j = tid; j < kHist; j += kResolveThreads) hist[j] = 0ull;
-    if (tid == 0) sh_i[1] = 0;  // list length
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kRowSlots; ++j) {
-      float x[8];
-      unpack8(opaque(d[j]), x);
-      if (!(max8(x) >= theta)) continue;  // most vectors: nothing inside the window
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (!(x[e] >= theta)) continue;
-        const uint32_t o = kM - key_of(x[e]);
-        if (o < (uint32_t)kHist) atomicAdd(&hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
-      }
-    }
-    __syncthreads();
-    if (wid == 0) {
-      uint64_t z64 = 0;
-      const int o = hist_crossing(hist, kHist, thrP, 0, &z64, lane);
-      if (lane == 0) {
-        sh_i[0] = o;
-        sh_u[0] = z64;
-      }
-    }
-    __syncthreads();
-    const int o_star = sh_i[0];
-    if (o_star < 0) return false;
-    const float t = value_of_key(kM - (uint32_t)o_star);
-    const float zs = (float)((double)sh_u[0] / kFix);
-    // the kept tokens (logit >= t): appended to the list through an LDS counter
-#pragma unroll
-    for (int j = 0; j < kRowSlots; ++j) {
-      float x[8];
-      unpack8(opaque(d[j]), x);
-      if (!(max8(x) >= t)) continue;
-      const int v = tid + j * kResolveThreads;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (!(x[e] >= t)) continue;
-        const int slot = atomicAdd(&sh_i[1], 1);
-        if (slot < kNucMax) list[slot] = NucEntry{v * 8 + e, weight(x[e], c, nref)};
-      }
-    }
-    __syncthreads();
-    const int n = sh_i[1];
-    if (n > kNucMax) return false;
-    // sort by token id: each entry's rank is the number of smaller ids (ids are distinct)
-    NucEntry mine{0, 0.0f};
-    int rank = 0;
-    if (tid < n) {
-      mine = list[tid];
-      for (int i = 0; i < n; ++i) rank += list[i].idx < mine.idx ? 1 : 0;
-    }
-    __syncthreads();
-    if (tid < n) list[rank] = mine;
-    __syncthreads();
-    if (wid == 0) {
-      const Draw dr = draw_from_lists(list, n, zs, nullptr, 0, 1.0f, false, u, lane);
-      if (lane == 0) {
-        sh_i[0] = dr.token;
-        sh_f[0] = dr.total;
-        sh_f[1] = dr.wtok;
-      }
-    }
-    __syncthreads();
-    *out = Draw{sh_i[0], sh_f[0], sh_f[1]};
-    __syncthreads();
-    return true;
-  }
-  // No top-p: tile g's sum is wave g % kWgWaves's slot g / kWgWaves sum, normalised.
-  const float iz = 1.0f / Z;
-  const int ntiles = (nvec + kWave - 1) / kWave;
-  int jl = -1;  // this lane's last slot with weight (ids grow with the slot)
-  uint4 dl = ninf;
-#pragma unroll
-  for (int j = 0; j < kRowSlots; ++j) {
-    const float ts = wave_sum(sj[j]) * iz;
-    const int g = wid + j * kWgWaves;
-    if (lane == 0 && g < ntiles) tile_sum[g] = ts;
-    if (sj[j] > 0.0f) {
-      jl = j;
-      dl = d[j];
-    }
-  }
-  int last = -1;  // last token with positive weight seen by this lane
-  if (jl >= 0) {
-    float x[8];
-    unpack8(dl, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (weight(x[e], c, nref) > 0.0f) last = (tid + jl * kResolveThreads) * 8 + e;
-  }
-  const RowLaw L{row, c, nref, -INFINITY, iz};
-  *out = draw_scan(L, L, false, nvec, V, u, last, tile_sum, sh_i, sh_f);
-  return true;
-}
-
 
 // Per-sequence decision state the resolve step shares through LDS.
 struct SeqDecision {
@@ -1227,16 +885,37 @@ struct SeqDecision {
   RowStat sp, sq;  // statistics of the rows at the first rejection (if any)
 };
 
+// One wave: a list draw, published to the workgroup through LDS.
+__device__ __forceinline__ Draw wg_list_draw(const NucEntry* pl, int np, float zp,
+                                             const NucEntry* ql, int nq, float zq,
+                                             bool residual, float u, int* sh_i, float* sh_f) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  if (tid < kWave) {
+    const Draw d = draw_from_lists(pl, np, zp, ql, nq, zq, residual, u, lane);
+    if (lane == 0) {
+      sh_i[0] = d.token;
+      sh_f[0] = d.total;
+      sh_f[1] = d.wtok;
+    }
+  }
+  __syncthreads();
+  const Draw d{sh_i[0], sh_f[0], sh_f[1]};
+  __syncthreads();
+  return d;
+}
+
+// Index of the bonus row's statistics (and list, spill area) after the draft rows' ones.
+__device__ __forceinline__ size_t bonus_slot(const ChainParams& P, int b) {
+  return 2 * (size_t)P.n_draft + (size_t)b;
+}
+
 __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainParams P) {
-  __shared__ union {
-    float tile_sum[kMaxTiles];       // inverse-CDF draw over a row
-    unsigned long long hist[kHist];  // bonus row top-p threshold
-  } sbuf;
+  __shared__ float tile_sum[kMaxTiles];  // inverse-CDF draw over a row (pair)
   __shared__ int sh_i[kWgWaves];
-  __shared__ float sh_f[2], sh_v[kWgWaves], sh_z[kWgWaves];
-  __shared__ unsigned long long sh_u[2];
+  __shared__ float sh_f[2];
   __shared__ NucEntry s_lp[kNucMax], s_lq[kNucMax];
   __shared__ NucEntry s_pre[kPreRows][2][kPre];
+  __shared__ NucEntry s_preb[kPre];
   __shared__ SeqDecision sd;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -1246,14 +925,16 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   const int c0 = P.cu[b], c1 = P.cu[b + 1];
   const bool cu_ok = c1 - c0 >= 0 && c1 - c0 <= P.max_gamma && c0 >= 0 && c1 <= P.n_draft;
   const bool stochastic = !s.bad_param && s.T != 0.0f;
-  // The heads of the candidate positions' nucleus lists, fetched together with the
-  // statistics: the first rejection is not known yet, and the residual draw of a rejected
-  // position usually needs nothing more.
+  // The heads of the candidate rows' nucleus lists, fetched together with the statistics:
+  // where the first rejection falls is not known yet, and the draw usually needs no more.
   if (cu_ok && stochastic && P.topp) {
     const int kk = tid / (2 * kPre), rr = (tid / kPre) & 1, j = tid % kPre;
     if (kk < kPreRows && kk < s.g)
       s_pre[kk][rr][j] = P.nuc[((size_t)(s.d0 + kk) * 2 + rr) * kNucMax + j];
+    if (tid < kPre) s_preb[tid] = P.nuc[bonus_slot(P, b) * kNucMax + tid];
   }
+  RowStat sbon{};
+  if (!s.bad_param) sbon = P.stat[bonus_slot(P, b)];
   if (wid == 0) {
     const bool in_g = cu_ok && lane < s.g;
     int tok = 0;
@@ -1325,34 +1006,32 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   const int trow = s.t0 + kstar - 1;
   const bool residual = kstar <= s.g;
   const uint4* prow = reinterpret_cast<const uint4*>(P.target + (size_t)trow * P.stride);
+  const float c = s.T == 0.0f ? 0.0f : kLog2e / s.T;
   int y;
   float R = NAN, py;
   if (!residual) {  // every draft accepted: the bonus token from p_{gamma+1}
     if (s.T == 0.0f) {
-      y = wg_row_argmax(prow, P.nvec, P.V, sh_v, sh_i);
+      y = sbon.argmax;
       py = 1.0f;
     } else {
       const float u = P.ovr ? P.ovr[(size_t)trow * 2 + 1]
                             : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
                                         SPEC_PURPOSE_BONUS);
-      const float c = kLog2e / s.T;
-      const bool topp = P.topp && s.P < 1.0f;
-      bool slow = false;
+      flags |= sbon.flags & SPEC_FLAG_TOPP_SLOW;
       Draw d;
-      float M, Z;
-      const bool held = P.nvec <= kRowSlots * kResolveThreads;
-      if (!held || !bonus_draw_held(prow, P.nvec, P.V, c, topp, s.P, u, sbuf.tile_sum,
-                                    sbuf.hist, s_lp, sh_i, sh_f, sh_v, sh_z, sh_u, &d, &M,
-                                    &Z)) {
-        if (!held) wg_row_mz(prow, P.nvec, P.V, c, sh_v, sh_z, M, Z);
-        float t = -INFINITY, zs = Z;
-        if (topp)
-          t = wg_topp_threshold(prow, P.nvec, P.V, c, s.P, M, Z, sbuf.hist, sh_i, sh_u, &zs,
-                                &slow);
-        const RowLaw Lp{prow, c, -M * c, t, 1.0f / zs};
-        d = draw_from_rows(Lp, Lp, false, P.nvec, P.V, u, sbuf.tile_sum, sh_i, sh_f);
+      if (sbon.nuc >= 0) {
+        const NucEntry* lb = s_preb;
+        if (sbon.nuc > kPre) {
+          const NucEntry* gl = P.nuc + bonus_slot(P, b) * kNucMax;
+          for (int j = tid; j < sbon.nuc; j += kResolveThreads) s_lp[j] = gl[j];
+          __syncthreads();
+          lb = s_lp;
+        }
+        d = wg_list_draw(lb, sbon.nuc, sbon.z, nullptr, 0, 1.0f, false, u, sh_i, sh_f);
+      } else {
+        const RowLaw Lp{prow, c, -sbon.m * c, sbon.t, 1.0f / sbon.z};
+        d = draw_from_rows(Lp, Lp, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
       }
-      if (slow) flags |= SPEC_FLAG_TOPP_SLOW;
       y = d.token;
       py = d.wtok;
     }
@@ -1364,7 +1043,6 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
     const float u = P.ovr ? P.ovr[(size_t)trow * 2 + 1]
                           : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
                                       SPEC_PURPOSE_RESIDUAL);
-    const float c = kLog2e / s.T;
     const RowLaw Lp{prow, c, -sp.m * c, sp.t, 1.0f / sp.z};
     const RowLaw Lq{reinterpret_cast<const uint4*>(P.draft +
                                                    (size_t)(s.d0 + kstar - 1) * P.stride),
@@ -1374,8 +1052,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
     const NucEntry* lp = s_lp;
     const NucEntry* lq = s_lq;
     if (lists_p) {
-      const bool pre = kstar - 1 < kPreRows && sp.nuc <= kPre && sq.nuc <= kPre;
-      if (pre) {
+      if (kstar - 1 < kPreRows && sp.nuc <= kPre && sq.nuc <= kPre) {
         lp = s_pre[kstar - 1][0];
         lq = s_pre[kstar - 1][1];
       } else {
@@ -1386,41 +1063,16 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
         __syncthreads();
       }
     }
-    if (lists_pq) {
-      if (wid == 0) {
-        d = draw_from_lists(lp, sp.nuc, sp.z, lq, sq.nuc, sq.z, true, u, lane);
-        if (lane == 0) {
-          sh_i[0] = d.token;
-          sh_f[0] = d.total;
-          sh_f[1] = d.wtok;
-        }
-      }
-      __syncthreads();
-      d = Draw{sh_i[0], sh_f[0], sh_f[1]};
-      __syncthreads();
-    } else {
-      d = draw_from_rows(Lp, Lq, true, P.nvec, P.V, u, sbuf.tile_sum, sh_i, sh_f);
-    }
+    if (lists_pq) d = wg_list_draw(lp, sp.nuc, sp.z, lq, sq.nuc, sq.z, true, u, sh_i, sh_f);
+    else d = draw_from_rows(Lp, Lq, true, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
     R = d.total;
     if (d.total > 0.0f) {
       y = d.token;
       py = d.wtok / d.total;
     } else {  // R = 0 means p = q: the draw from p has the same law
       flags |= SPEC_FLAG_RESID_FALLBACK;
-      if (lists_p) {
-        if (wid == 0) {
-          d = draw_from_lists(lp, sp.nuc, sp.z, nullptr, 0, 1.0f, false, u, lane);
-          if (lane == 0) {
-            sh_i[0] = d.token;
-            sh_f[0] = d.total;
-            sh_f[1] = d.wtok;
-          }
-        }
-        __syncthreads();
-        d = Draw{sh_i[0], sh_f[0], sh_f[1]};
-      } else {
-        d = draw_from_rows(Lp, Lq, false, P.nvec, P.V, u, sbuf.tile_sum, sh_i, sh_f);
-      }
+      if (lists_p) d = wg_list_draw(lp, sp.nuc, sp.z, nullptr, 0, 1.0f, false, u, sh_i, sh_f);
+      else d = draw_from_rows(Lp, Lq, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
       y = d.token;
       py = d.wtok;
     }
@@ -1442,13 +1094,14 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
 
 }  // namespace
 
+// Row statistics, nucleus lists and spill lists for the 2 * total_draft_rows draft-position
+// rows and the batch's bonus rows.
 size_t chain_workspace_bytes(int32_t batch, int32_t total_draft_rows, int32_t vocab) {
-  (void)batch;
   (void)vocab;
-  const size_t rows = 2 * (size_t)total_draft_rows;
+  const size_t rows = 2 * (size_t)total_draft_rows + (size_t)batch;
   const size_t n = align256(rows * sizeof(RowStat)) + align256(rows * kNucMax * sizeof(NucEntry)) +
                    align256(rows * kCapG * sizeof(uint16_t));
-  return n > 256 ? n : 256;  // never 0: a batch without drafts still passes a workspace
+  return n > 256 ? n : 256;
 }
 
 hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
@@ -1467,7 +1120,7 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   P.probe_rows = a.probe_rows;
   P.probe_seq = a.probe_seq;
   P.ovr = a.uniform_override;
-  const size_t rows = 2 * (size_t)a.total_draft_rows;
+  const size_t rows = 2 * (size_t)a.total_draft_rows + (size_t)a.batch;
   P.stat = reinterpret_cast<RowStat*>(ws);
   char* w = reinterpret_cast<char*>(ws) + align256(rows * sizeof(RowStat));
   P.nuc = reinterpret_cast<NucEntry*>(w);
@@ -1484,16 +1137,16 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(a.profile_events);
   hipError_t e = hipSuccess;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  // two rows (target, draft) per draft position slot (b, k <= max_gamma)
-  const unsigned grid = 2u * (unsigned)a.batch * (unsigned)a.max_gamma;
-  if (grid > 0) {
-    if (a.top_p)
-      hipLaunchKernelGGL(row_stats_kernel<true>, dim3(grid), dim3(kWave), sizeof(CapLds), st,
-                         P);
-    else
-      hipLaunchKernelGGL(row_stats_kernel<false>, dim3(grid), dim3(kWave), 0, st, P);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  // per sequence: two rows (target, draft) per draft position slot k <= max_gamma, then the
+  // bonus row
+  const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
+  const unsigned grid = (nrows + kRowWaves - 1) / kRowWaves;
+  if (a.top_p)
+    hipLaunchKernelGGL(row_stats_kernel<true>, dim3(grid), dim3(kRowWaves * kWave),
+                       kRowWaves * sizeof(CapLds), st, P);
+  else
+    hipLaunchKernelGGL(row_stats_kernel<false>, dim3(grid), dim3(kRowWaves * kWave), 0, st, P);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)a.batch), dim3(kResolveThreads), 0,
                      st, P);
