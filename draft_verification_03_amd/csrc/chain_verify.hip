@@ -97,18 +97,18 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// floor(w * 2^44) for 0 <= w < 2^19 (a weight relative to the row max is <= 1): the exact
+// fixed-point value, by integer shifts of the mantissa.
 __device__ __forceinline__ uint64_t fixw(float w) {
-  return (uint64_t)((double)w * kFix);
+  const uint32_t b = __float_as_uint(w);
+  const int e = (int)(b >> 23) - 127;  // w = m * 2^(e - 23), m = 24-bit mantissa
+  if (e < -44) return 0;               // below the fixed-point resolution (zero included)
+  const uint64_t m = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
+  const int sh = e + 44 - 23;
+  return sh >= 0 ? (m << sh) : (m >> -sh);
 }
 
-__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
+__device__ __forceinline__ int wave_incl_scan_i(int v, int) { return wave_incl_scan_dpp(v); }
 
 // Parameters checked on their bit patterns (NaN fails every test). T: >= 0 (or -0), not NaN;
 // +inf is allowed (a flat law).
@@ -286,10 +286,10 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
 
 // Wave-wide (m, Z) of a row from the lanes' running (m, s).
 __device__ __forceinline__ void finish_mz(const LaneAcc& a, float c, float& M, float& Z) {
-  M = wave_max(a.m);
+  M = wave_max_dpp(a.m);
   const float ref = (M == -INFINITY) ? 0.0f : M;
   const float s = (a.m == -INFINITY) ? 0.0f : a.s * __builtin_amdgcn_exp2f((a.m - ref) * c);
-  Z = wave_sum(s);
+  Z = wave_sum_dpp(s);
 }
 
 struct TopP {
@@ -299,14 +299,8 @@ struct TopP {
   bool slow;   // exact multi-pass search ran
 };
 
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t lo = __shfl_up((uint32_t)v, o, kWave);
-    const uint32_t hi = __shfl_up((uint32_t)(v >> 32), o, kWave);
-    if (lane >= o) v += ((uint64_t)hi << 32) | lo;
-  }
-  return v;
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int) {
+  return wave_incl_scan_dpp_u64(v);
 }
 
 // First bucket (in increasing index = decreasing logit) at which base + the cumulative mass

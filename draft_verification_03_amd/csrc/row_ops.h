@@ -50,7 +50,14 @@ __device__ __forceinline__ void stream_row(const uint4* __restrict__ row, int nv
     uint4 buf[DEPTH][kU];
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) load_full(row, s * kStep, lane, buf[s]);
+    // Issue priority falls with progress (quarters of the row): of the waves sharing a SIMD,
+    // the one furthest behind is served first, which narrows the spread of finish times.
+    __builtin_amdgcn_s_setprio(3);
     for (; t + 2 * DEPTH <= nfull; t += DEPTH) {  // trips t .. t+DEPTH-1; none is the last
+      const int lvl = (4 * t) / nfull;
+      if (lvl == 1) __builtin_amdgcn_s_setprio(2);
+      else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
+      else if (lvl == 3) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int s = 0; s < DEPTH; ++s) {
         consume(buf[s], (t + s) * kStep, false);
@@ -66,6 +73,7 @@ __device__ __forceinline__ void stream_row(const uint4* __restrict__ row, int nv
       }
     }
     t = nfull;
+    __builtin_amdgcn_s_setprio(0);
   }
   for (; t * kStep < nvec; ++t) {  // short rows, and the partial trip
     uint4 d[kU];

@@ -106,6 +106,50 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   v = dpp_max_step<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// DPP move with 0 for lanes that have no source (row edges, rows outside ROW_MASK).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+// Wave sum through DPP (the same tree as wave_max_dpp), read back from lane 63; fixed order.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(dpp_or_zero<0xB1>(__float_as_int(v)));        // quad_perm [1,0,3,2]
+  v += __int_as_float(dpp_or_zero<0x4E>(__float_as_int(v)));        // quad_perm [2,3,0,1]
+  v += __int_as_float(dpp_or_zero<0x141>(__float_as_int(v)));       // row_half_mirror
+  v += __int_as_float(dpp_or_zero<0x140>(__float_as_int(v)));       // row_mirror
+  v += __int_as_float(dpp_or_zero<0x142, 0xA>(__float_as_int(v)));  // row_bcast:15
+  v += __int_as_float(dpp_or_zero<0x143, 0xC>(__float_as_int(v)));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// Inclusive prefix sum over the wave through DPP: shifts by 1, 2, 4, 8 inside each row of 16
+// lanes, then the row totals carried by row broadcasts 15 and 31.
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += dpp_or_zero<0x111>(v);       // row_shr:1
+  v += dpp_or_zero<0x112>(v);       // row_shr:2
+  v += dpp_or_zero<0x114>(v);       // row_shr:4
+  v += dpp_or_zero<0x118>(v);       // row_shr:8
+  v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+// The same for 64-bit values (the two halves moved separately, added with carry).
+__device__ __forceinline__ uint64_t dpp_add_u64_step(uint64_t v, uint32_t lo, uint32_t hi) {
+  return v + (((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t wave_incl_scan_dpp_u64(uint64_t v) {
+#define SPECV_SCAN_STEP(CTRL, MASK)                                                          \
+  v = dpp_add_u64_step(v, (uint32_t)dpp_or_zero<CTRL, MASK>((int)(uint32_t)v),              \
+                       (uint32_t)dpp_or_zero<CTRL, MASK>((int)(uint32_t)(v >> 32)));
+  SPECV_SCAN_STEP(0x111, 0xF)
+  SPECV_SCAN_STEP(0x112, 0xF)
+  SPECV_SCAN_STEP(0x114, 0xF)
+  SPECV_SCAN_STEP(0x118, 0xF)
+  SPECV_SCAN_STEP(0x142, 0xA)
+  SPECV_SCAN_STEP(0x143, 0xC)
+#undef SPECV_SCAN_STEP
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
