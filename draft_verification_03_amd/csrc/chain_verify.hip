@@ -580,8 +580,17 @@ struct Draw {
   float wtok;   // weight of the drawn token
 };
 
-// Weight of token id in a sorted nucleus list held in LDS (0 if absent): binary search.
+// Weight of token id in a sorted nucleus list held in LDS (0 if absent): a scan of a short
+// list (independent broadcast reads), else a binary search.
 __device__ __forceinline__ float list_weight(const NucEntry* q, int nq, int id) {
+  if (nq <= kWave) {
+    float r = 0.0f;
+    for (int i = 0; i < nq; ++i) {
+      const NucEntry e = q[i];
+      r = e.idx == id ? e.w : r;
+    }
+    return r;
+  }
   int lo = 0, hi = nq;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -594,65 +603,90 @@ __device__ __forceinline__ float list_weight(const NucEntry* q, int nq, int id) 
 constexpr int kPerLane = kNucMax / kWave;  // list entries per lane in a list draw
 
 // One wave: inverse-CDF draw over a nucleus list sorted by token id (<= kNucMax entries;
-// lane l holds entries kPerLane*l .. kPerLane*l + kPerLane-1, so the lanes' order is token
-// order). residual: weights max(0, p - q), q looked up in q's list (in LDS); else p.
-__device__ Draw draw_from_lists(const NucEntry* pl, int np, float zp, const NucEntry* ql,
-                                int nq, float zq, bool residual, float u, int lane) {
+// entry j sits in lane j % 64, slot j / 64, so token order is slot-major, then lane order).
+// residual: weights max(0, p - q) with q looked up in q's list -- held in registers and
+// scanned with lane reads when it has at most 64 entries, else searched in memory; else p.
+__device__ __forceinline__ Draw draw_from_lists(const NucEntry* pl, int np, float zp,
+                                                const NucEntry* ql, int nq, float zq,
+                                                bool residual, float u, int lane) {
+  const bool qregs = residual && nq <= kWave;
+  int qidx = 0x7FFFFFFF;
+  float qw = 0.0f;
+  if (qregs && lane < nq) {
+    const NucEntry e = ql[lane];
+    qidx = e.idx;
+    qw = e.w;
+  }
   int idx[kPerLane];
   float w[kPerLane];
-  float ls = 0.0f;
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) {
-    const int j = lane * kPerLane + e;
-    idx[e] = 0x7FFFFFFF;
-    w[e] = 0.0f;
-    if (j < np) {
-      const NucEntry en = pl[j];
-      idx[e] = en.idx;
-      w[e] = en.w / zp;
-      if (residual) w[e] = fmaxf(0.0f, w[e] - list_weight(ql, nq, en.idx) / zq);
+  for (int s = 0; s < kPerLane; ++s) {
+    const int j = s * kWave + lane;
+    idx[s] = 0x7FFFFFFF;
+    w[s] = 0.0f;
+    if (s * kWave < np) {  // wave-uniform: the lane reads below stay in converged code
+      if (j < np) {
+        const NucEntry en = pl[j];
+        idx[s] = en.idx;
+        w[s] = en.w / zp;
+      }
+      if (residual) {
+        float wq = 0.0f;
+        if (qregs) {
+          for (int i = 0; i < nq; ++i) {
+            const int qi = __builtin_amdgcn_readlane(qidx, i);
+            const float qv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qw), i));
+            wq = qi == idx[s] ? qv : wq;
+          }
+        } else if (j < np) {
+          wq = list_weight(ql, nq, idx[s]);
+        }
+        w[s] = fmaxf(0.0f, w[s] - wq / zq);
+      }
     }
-    ls += w[e];
   }
-  const float incl = wave_incl_scan(ls, lane);
-  const float total = __shfl(incl, kWave - 1, kWave);
+  // slot totals (uniform), then the slot holding x and the lane inside it
+  float incl[kPerLane], tot[kPerLane];
+  float total = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kPerLane; ++s) {
+    incl[s] = wave_incl_scan_dpp_f(w[s]);
+    tot[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl[s]), 63));
+    total += tot[s];
+  }
   const float x = u * total;
-  const uint64_t hit = __ballot(incl > x && ls > 0.0f);
   int tok = -1;
   float wt = 0.0f;
-  int src;
-  if (hit) {
-    src = __ffsll((long long)hit) - 1;
-    float cum = incl - ls;
+  float base = 0.0f;
+  bool found = false;
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) {
-      cum += w[e];
-      if (tok < 0 && w[e] > 0.0f && cum > x) {
-        tok = idx[e];
-        wt = w[e];
+  for (int s = 0; s < kPerLane; ++s) {
+    if (!found) {
+      const uint64_t hit = __ballot(base + incl[s] > x && w[s] > 0.0f);
+      if (hit) {
+        const int src = __ffsll((long long)hit) - 1;
+        tok = __builtin_amdgcn_readlane(idx[s], src);
+        wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[s]), src));
+        found = true;
+      }
+      base += tot[s];
+    }
+  }
+  if (!found) {  // rounding left u*total at or past the end: the last entry with weight
+#pragma unroll
+    for (int s = kPerLane - 1; s >= 0; --s) {
+      const uint64_t pos = __ballot(w[s] > 0.0f);
+      if (!found && pos) {
+        const int src = 63 - __clzll((long long)pos);
+        tok = __builtin_amdgcn_readlane(idx[s], src);
+        wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[s]), src));
+        found = true;
       }
     }
-    if (tok < 0) {  // rounding inside the lane: its last entry with weight
-#pragma unroll
-      for (int e = 0; e < kPerLane; ++e)
-        if (w[e] > 0.0f) {
-          tok = idx[e];
-          wt = w[e];
-        }
-    }
-  } else {  // rounding left u*total at or past the end: the last entry with weight
-    const uint64_t pos = __ballot(ls > 0.0f);
-    src = pos ? 63 - __clzll((long long)pos) : 0;
-#pragma unroll
-    for (int e = 0; e < kPerLane; ++e)
-      if (w[e] > 0.0f) {
-        tok = idx[e];
-        wt = w[e];
-      }
   }
   Draw d;
-  d.token = __shfl(tok, src, kWave);
-  d.wtok = __shfl(wt, src, kWave);
+  d.token = tok;
+  d.wtok = wt;
   d.total = total;
   if (d.token < 0) {  // an empty list (no weight anywhere): token 0
     d.token = 0;

@@ -132,6 +132,15 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int v) {
   v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31
   return v;
 }
+__device__ __forceinline__ float wave_incl_scan_dpp_f(float v) {
+  v += __int_as_float(dpp_or_zero<0x111>(__float_as_int(v)));
+  v += __int_as_float(dpp_or_zero<0x112>(__float_as_int(v)));
+  v += __int_as_float(dpp_or_zero<0x114>(__float_as_int(v)));
+  v += __int_as_float(dpp_or_zero<0x118>(__float_as_int(v)));
+  v += __int_as_float(dpp_or_zero<0x142, 0xA>(__float_as_int(v)));
+  v += __int_as_float(dpp_or_zero<0x143, 0xC>(__float_as_int(v)));
+  return v;
+}
 // The same for 64-bit values (the two halves moved separately, added with carry).
 __device__ __forceinline__ uint64_t dpp_add_u64_step(uint64_t v, uint32_t lo, uint32_t hi) {
   return v + (((uint64_t)hi << 32) | lo);
