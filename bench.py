@@ -9,7 +9,7 @@ sum(gamma_b+1) per call), the row-pass kernel's achieved HBM bandwidth against 8
 (timed live with HIP events on the launch stream), and the fp64 CPU oracle timed on a
 bounded sample of the same workload as a reported baseline.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--warmup-seconds S] [--gpus 1] [--no-cpu-baseline]
   python bench.py --copy-calibration     # a plain copy of known size, for counter scaling
 """
 from __future__ import annotations
@@ -29,8 +29,8 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "verify rows/sec at B=256 γ=8 V=128k; achieved HBM GB/s vs peak"
 SEED = 2024
 SEED_DRAFT = 9090
-ROW_KERNEL = "chain_row_kernel"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "chain_row_kernel_c3.md")
+ROW_KERNEL = "row_stats_kernel"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "row_stats_kernel_c3.md")
 
 
 def log(msg):
@@ -122,8 +122,9 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -182,9 +183,16 @@ def main():
                      row_stride=x["stride"])
     ws = torch.empty(B.spec_verify_chain_workspace_size(Bn, nd, V), dtype=torch.uint8,
                      device="cuda")
-    for _ in range(args.warmup):
-        B.spec_verify_chain(a, workspace=ws)
-    torch.cuda.synchronize()
+    # Warm-up: the W steps, continued until --warmup-seconds have passed, so that the timed
+    # steps run at the GPU's settled clocks (the first few hundred milliseconds of a burst
+    # of work run measurably slower).
+    t_warm = time.time()
+    done = 0
+    while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        for _ in range(10):
+            B.spec_verify_chain(a, workspace=ws)
+        done += 10
+        torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     # Headline: the steps back to back with nothing between them (an event recorded between
     # the row pass and the resolve step delays the resolve by a few microseconds).

@@ -7,19 +7,21 @@
 // committed-length pointer. See include/spec_verify.h for the exact contract.
 //
 // Structure
-//  1. row_stats_kernel -- one wave per logits row of a draft position: the target row p_k
-//     or the draft row q_k, k = 1..gamma_b (the bonus row p_{gamma_b+1} is only needed after
-//     a full accept, so the resolve step reads it then). The wave streams its row from HBM
-//     once with 16-byte loads, double-buffered:
+//  1. row_stats_kernel -- one workgroup of kRowWgWaves waves per logits row: the target row
+//     p_k or the draft row q_k of draft position k = 1..gamma_b, and the bonus row
+//     p_{gamma_b+1}. The waves take the row's trips in turn (16-byte loads, two trips in
+//     flight per wave), so the row streams from HBM once as one wide sequential read, and
+//     the hardware hands rows to CUs as they free up:
 //       - per-lane online max / sum of exp2((l - m) * log2(e)/T) (lazy rescaling);
-//       - with top-p: every 8-logit vector whose max is within kCaptureK*T of the running
-//         max is copied to LDS (a superset of the final window m - kCaptureK*T, pruned when
-//         the buffer fills), so the end phase touches no HBM;
+//       - with top-p: every 8-logit vector whose max is within kCaptureK*T of the best known
+//         lower bound of the row max (the waves share theirs through LDS) is copied to LDS
+//         (a superset of the final window m - kCaptureK*T; past kCapN vectors only their
+//         indexes are kept, in the workspace), so the end phase touches no HBM;
 //       - greedy rows (T = 0): max with the lowest index only.
-//     The end phase gives m, Z, the nucleus threshold t* (fixed-point mass histogram over
-//     bf16 keys of the captured logits; an exact multi-pass search over the whole row if
-//     the window did not hold the nucleus), the draft token's weight, and the nucleus list
-//     in token order (<= kNucMax tokens) for the residual draw.
+//     After a workgroup barrier the end phase gives m, Z, the nucleus threshold t*
+//     (fixed-point mass histogram over bf16 keys of the captured logits; an exact multi-pass
+//     search over the whole row if the window did not hold the nucleus), the draft token's
+//     weight, and the nucleus list in token order (<= kNucMax tokens) for the residual draw.
 //  2. chain_resolve_kernel -- one workgroup per sequence: p_k(d_k), q_k(d_k) and the
 //     acceptance decisions from the row statistics, the first rejection (one ballot), then
 //     the residual or bonus draw -- from the nucleus lists when both are kept (their heads
@@ -38,12 +40,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Top-p capture window: logits within kCaptureK * T of the row max (weight >= e^-7 of the
 // largest). Rows whose nucleus reaches further down take the exact multi-pass search.
 constexpr float kCaptureK = 7.0f;
-constexpr int kCapV = 256;    // captured vectors per row held in LDS
-constexpr int kCapG = 1024;   // further captured vector ids per row spilled to the workspace
-constexpr int kDepth = 2;     // trips of loads in flight per wave in the row pass
-constexpr int kRowWaves = 2;  // rows (one per wave) per row-pass workgroup
-constexpr int kRefresh = 2;   // trips between refreshes of the capture threshold
-constexpr int kHist = 512;    // key offsets below the row max resolved by the window search
+constexpr int kCapN = 512;         // captured vectors per row held in LDS
+constexpr int kCapG = 1024;        // further captured vector ids per row spilled to the workspace
+constexpr int kDepth = 2;          // trips of loads in flight per wave in the row pass
+constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per workgroup)
+constexpr int kRowThreads = kRowWgWaves * kWave;
+constexpr int kHist = 512;         // key offsets below the row max resolved by the window search
 constexpr int kResolveThreads = 1024;
 constexpr int kTilesPerIter = 4;  // row-pair tiles in flight per wave in the resolve pass
 constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass (V <= 2^19)
@@ -75,22 +77,6 @@ struct ChainParams {
   int32_t B, V, stride, nvec, max_gamma, n_draft, lead;
   uint32_t seed_lo, seed_hi;
 };
-
-// LDS of one top-p row: the captured vectors in increasing vector index (data and index),
-// and the threshold search's histogram.
-struct CapLds {
-  uint4 data[kCapV];
-  unsigned long long hist[kHist];
-  uint16_t idx[kCapV];
-};
-
-// Orders one wave's own LDS accesses around a phase boundary (a row's LDS area belongs to
-// one wave, so the row pass never needs a workgroup barrier).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -157,12 +143,8 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
 struct LaneAcc {
   float m = -INFINITY;   // running max of this lane's logits
   float s = 0.0f;        // sum of exp2((l - m) * c) over this lane's logits
-  float wm = -INFINITY;  // the wave's max at the last refresh (capture threshold)
-  // capture state (wave-uniform): vectors held in LDS, then ids spilled to the workspace
-  int ncap = 0;
-  int nspill = 0;
-  bool spilling = false;  // LDS stayed nearly full after pruning: later captures spill
-  bool over = false;      // the spill list overflowed too: exact search over the row
+  float wm = -INFINITY;  // capture reference: a lower bound of the row max known to the wave
+  int wg = 0;            // lane 0: the workgroup maximum read back at the last publication
 };
 
 // Weight of one logit relative to a reference: the same expression everywhere, so that
@@ -171,72 +153,75 @@ __device__ __forceinline__ float weight(float l, float c, float nref) {
   return __builtin_amdgcn_exp2f(fmaf(l, c, nref));
 }
 
-// Keeps the captured vectors whose max is still >= thr (in their order) and returns how
-// many remain. A chunk's entries are all read before any of them is written, and a kept
-// entry never moves up, so the compaction can work in place.
-__device__ int cap_compact(CapLds* cap, int n, float thr, int lane) {
-  int out = 0;
-  for (int j0 = 0; j0 < n; j0 += kWave) {
-    const int j = j0 + lane;
-    uint4 dv = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t id = 0;
-    bool keep = false;
-    if (j < n) {
-      dv = cap->data[j];
-      id = cap->idx[j];
-      float x[8];
-      unpack8(dv, x);
-      keep = max8(x) >= thr;
-    }
-    const uint64_t m = __ballot(keep);
-    if (keep) {
-      const int pos = out + (int)lanes_below(m);
-      cap->data[pos] = dv;
-      cap->idx[pos] = (uint16_t)id;
-    }
-    out += __popcll(m);
-  }
-  return out;
+// Order-preserving int image of a float (for LDS atomic max), and its inverse.
+__device__ __forceinline__ int ord_key(float f) {
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : (b ^ 0x7FFFFFFF);
 }
+__device__ __forceinline__ float ord_val(int k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7FFFFFFF)); }
 
-// Appends the flagged lanes' vectors to the capture buffer in lane order (= increasing
-// vector index within a trip slot). A full buffer is first pruned against the wave's
-// current threshold; if it stays more than 3/4 full, this and every later capture of the row
-// only records the vector id in the workspace spill list (read back in the end phase), so
-// the captures stay in increasing vector order: LDS entries, then spilled ones.
-__device__ __forceinline__ void cap_push(CapLds* cap, uint16_t* spill, LaneAcc& a,
-                                         const uint4& dv, bool in, int vid, float capw,
-                                         int lane) {
-  const uint64_t mask = __ballot(in);
-  if (mask == 0) return;
-  const int n = __popcll(mask);
-  if (!a.spilling && a.ncap + n > kCapV) {
-    a.wm = wave_max_dpp(a.m);
-    a.ncap = cap_compact(cap, a.ncap, a.wm - capw, lane);
-    a.spilling = a.ncap > kCapV * 3 / 4;
+// LDS of one row's workgroup.
+struct RowLds {
+  uint4 data[kCapN];               // captured vectors, in claim order
+  unsigned long long hist[kHist];  // fixed-point masses by key offset below the row max
+  NucEntry kept[kNucMax];          // nucleus entries before they are put in token order
+  uint16_t idx[kCapN];             // vector index of each captured vector
+  float pm[kRowWgWaves];           // per-wave max (value of the argmax for greedy rows)
+  float pz[kRowWgWaves];           // per-wave sum of weights relative to the wave max
+  int pa[kRowWgWaves];             // per-wave argmax (greedy rows)
+  int ncap;                        // capture slots claimed: LDS slots, then spill slots
+  int wgmax;                       // ord_key of the largest wave maximum published so far
+  int nkept;                       // nucleus entries claimed
+  int ostar;                       // threshold search: key offset of t (-1: not found)
+  unsigned long long zs;           // threshold search: fixed-point mass of the kept set
+};
+
+// Claims slots for the trip's flagged vectors (one LDS atomic per wave) and writes them:
+// slots below kCapN hold the vector and its index in LDS, the next kCapG only the index in
+// the row's workspace spill list; claims past both are only counted (the end phase then
+// searches the whole row).
+__device__ __forceinline__ void capture_trip(RowLds* L, uint16_t* spill, const uint4 d[kU],
+                                             const float vm[kU], float thr, int v0, int lane) {
+  uint64_t bm[kU];
+  int n[kU], tot = 0;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    bm[u] = __ballot(vm[u] >= thr);
+    n[u] = __popcll(bm[u]);
+    tot += n[u];
   }
-  const int pos = (int)lanes_below(mask);
-  if (!a.spilling) {
-    if (in) {
-      cap->data[a.ncap + pos] = dv;
-      cap->idx[a.ncap + pos] = (uint16_t)vid;
+  if (tot == 0) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(&L->ncap, tot);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if (vm[u] >= thr) {
+      const int pos = base + (int)lanes_below(bm[u]);
+      const int vid = v0 + u * kWave + lane;
+      if (pos < kCapN) {
+        L->data[pos] = d[u];
+        L->idx[pos] = (uint16_t)vid;
+      } else if (pos < kCapN + kCapG) {
+        spill[pos - kCapN] = (uint16_t)vid;
+      }
     }
-    a.ncap += n;
-  } else if (a.nspill + n <= kCapG) {
-    if (in) spill[a.nspill + pos] = (uint16_t)vid;
-    a.nspill += n;
-  } else {
-    a.over = true;
+    base += n[u];
   }
 }
 
 // One trip (kU vectors of the row) into the lane's running (m, s). The weights are taken
 // against the lane's previous maximum; only when the trip raises it (rare after the first
 // trips) is the trip's partial sum re-referenced, or recomputed when it may have overflowed.
+// With CAPTURE, the vectors whose max is within capw of the best known lower bound of the
+// row max are captured (a superset of the final window), and the wave publishes its max to
+// the workgroup and picks up the other waves' (the read-back is used from the next trip on,
+// after this trip's reload has issued).
 template <bool CAPTURE>
 __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane, float c,
-                                             float capw, LaneAcc& a, CapLds* cap,
+                                             float capw, LaneAcc& a, RowLds* L,
                                              uint16_t* spill) {
+  if (CAPTURE) a.wm = fmaxf(a.wm, ord_val(__builtin_amdgcn_readfirstlane(a.wg)));
   const float ref = (a.m == -INFINITY) ? 0.0f : a.m;
   const float nref = -ref * c;
   float vm[kU];
@@ -269,27 +254,33 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
     a.m = tm;
   }
   a.s += st;
-  if (CAPTURE && !a.over) {
-    // Threshold: the larger of the lane's own max and the wave's max at its last refresh,
-    // less the window. Both are lower bounds of the row max, so every vector within the
-    // final window is captured (with some extra ones).
-    if ((v0 / (kU * kWave)) % kRefresh == 0) a.wm = wave_max_dpp(a.m);
-    // finite, so a vector of -inf logits (past the row end included) is never captured
-    const float thr = vmax3(vmax3(a.wm, a.m, a.m) - capw, -3.4028235e38f, -3.4028235e38f);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (a.over) break;
-      cap_push(cap, spill, a, d[u], vm[u] >= thr, v0 + u * kWave + lane, capw, lane);
-    }
+  if (CAPTURE) {
+    a.wm = fmaxf(a.wm, wave_max_dpp(a.m));
+    // kept finite, so a vector of -inf logits (past the row end included) is never captured
+    const float thr = vmax3(a.wm - capw, -3.4028235e38f, -3.4028235e38f);
+    capture_trip(L, spill, d, vm, thr, v0, lane);
+    if (lane == 0) a.wg = atomicMax(&L->wgmax, ord_key(a.wm));
   }
 }
 
-// Wave-wide (m, Z) of a row from the lanes' running (m, s).
+// Wave-wide (m, Z) of the lanes' running (m, s).
 __device__ __forceinline__ void finish_mz(const LaneAcc& a, float c, float& M, float& Z) {
   M = wave_max_dpp(a.m);
   const float ref = (M == -INFINITY) ? 0.0f : M;
   const float s = (a.m == -INFINITY) ? 0.0f : a.s * __builtin_amdgcn_exp2f((a.m - ref) * c);
   Z = wave_sum_dpp(s);
+}
+
+// (m, Z) of the row from the waves' partials (every thread computes the same values, in the
+// same order).
+__device__ __forceinline__ void row_mz(const RowLds* L, float c, float& M, float& Z) {
+  M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kRowWgWaves; ++i) M = fmaxf(M, L->pm[i]);
+  Z = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRowWgWaves; ++i)
+    if (L->pm[i] != -INFINITY) Z += L->pz[i] * __builtin_amdgcn_exp2f((L->pm[i] - M) * c);
 }
 
 struct TopP {
@@ -336,15 +327,39 @@ __device__ int hist_crossing(const unsigned long long* h, int nb, uint64_t thr, 
   return o;
 }
 
-// Nucleus list of a row once t is known: every kept logit (>= t, token < V) of the given
-// vectors, written to the workspace in token order -- the vectors come in increasing index
-// and each lane's kept elements are placed after all lower lanes' by a wave scan of the
-// counts. Returns the kept count; a count above kNucMax means the list is incomplete.
+// The captured vectors: LDS slots, then spilled indexes (whose vectors are read again from
+// the row).
+struct CapSrc {
+  const RowLds* L;
+  const uint16_t* spill;
+  const uint4* row;
+  __device__ void operator()(int j, int& vi, uint4& dv) const {
+    if (j < kCapN) {
+      vi = L->idx[j];
+      dv = L->data[j];
+    } else {
+      vi = spill[j - kCapN];
+      dv = row[vi];
+    }
+  }
+};
+struct RowSrc {
+  const uint4* row;
+  __device__ void operator()(int j, int& vi, uint4& dv) const {
+    vi = j;
+    dv = row[j];
+  }
+};
+
+// Nucleus list of a row once t is known: every kept logit (>= t, token < V) of the n source
+// vectors, claimed into LDS by a wave-aggregated atomic, then written to the workspace in
+// token order (each entry's position is the number of kept tokens below it). Returns the
+// kept count; above kNucMax the list is not written.
 template <typename Src>
-__device__ int collect_ordered(Src src, int n, int V, float t, float c, float nref,
-                               NucEntry* list, int lane) {
-  int total = 0;
-  for (int j0 = 0; j0 < n && total <= kNucMax; j0 += kWave) {
+__device__ int collect_wg(Src src, int n, int V, float t, float c, float nref, RowLds* L,
+                          NucEntry* list, int tid) {
+  const int lane = tid % kWave;
+  for (int j0 = tid - lane; j0 < n; j0 += kRowThreads) {
     const int j = j0 + lane;
     float x[8];
     int vi = 0;
@@ -359,51 +374,39 @@ __device__ int collect_ordered(Src src, int n, int V, float t, float c, float nr
     }
     const int cnt = __popc(keep);
     const int incl = wave_incl_scan_i(cnt, lane);
-    int pos = total + incl - cnt;
+    const int tot = __shfl(incl, kWave - 1, kWave);
+    if (tot == 0) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&L->nkept, tot);
+    int pos = __builtin_amdgcn_readfirstlane(base) + incl - cnt;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if ((keep >> e) & 1u) {
-        if (pos < kNucMax) list[pos] = NucEntry{vi * 8 + e, weight(x[e], c, nref)};
+        if (pos < kNucMax) L->kept[pos] = NucEntry{vi * 8 + e, weight(x[e], c, nref)};
         ++pos;
       }
     }
-    total += __shfl(incl, kWave - 1, kWave);
   }
-  return total;
-}
-
-// The captured vectors in increasing index: the LDS entries, then the spilled ids (whose
-// vectors are read again from the row).
-struct CapSrc {
-  const CapLds* cap;
-  const uint16_t* spill;
-  const uint4* row;
-  int ncap;
-  __device__ void operator()(int j, int& vi, uint4& dv) const {
-    if (j < ncap) {
-      vi = cap->idx[j];
-      dv = cap->data[j];
-    } else {
-      vi = spill[j - ncap];
-      dv = row[vi];
+  __syncthreads();
+  const int K = L->nkept;
+  if (K <= kNucMax) {
+    for (int i = tid; i < K; i += kRowThreads) {
+      const NucEntry e = L->kept[i];
+      int r = 0;
+      for (int k = 0; k < K; ++k) r += L->kept[k].idx < e.idx;
+      list[r] = e;
     }
   }
-};
-struct RowSrc {
-  const uint4* row;
-  __device__ void operator()(int j, int& vi, uint4& dv) const {
-    vi = j;
-    dv = row[j];
-  }
-};
+  return K;
+}
 
 // Exact threshold search over the whole row: the largest bf16 key t with
 // mass(key >= t) >= thrP, by a 256-bucket fixed-point histogram of the key offset's high byte
 // and then of its low byte inside the chosen bucket (two passes), plus one pass for the
-// nucleus list. Used when the capture window missed the nucleus.
-__device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c,
-                              float M, uint64_t thrP, NucEntry* list, unsigned long long* hist,
-                              int lane) {
+// nucleus list. Used when the captures missed the nucleus or overflowed.
+__device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c, float M,
+                              uint64_t thrP, RowLds* L, NucEntry* list, int tid) {
+  const int lane = tid % kWave, w = tid / kWave;
   const float nref = -M * c;
   const uint32_t kM = key_of(M);
   TopP r;
@@ -411,10 +414,9 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
   uint64_t cum = 0, base = 0;
   int hi_b = -1, o_star = -1;
   for (int pass = 0; pass < 2; ++pass) {
-    wave_sync();
-    for (int j = lane; j < 256; j += kWave) hist[j] = 0ull;
-    wave_sync();
-    for (int v = lane; v < nvec; v += kWave) {
+    for (int j = tid; j < 256; j += kRowThreads) L->hist[j] = 0ull;
+    __syncthreads();
+    for (int v = tid; v < nvec; v += kRowThreads) {
       float x[8];
       unpack8(row[v], x);
 #pragma unroll
@@ -423,45 +425,55 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
         const uint32_t o = kM - key_of(x[e]);
         if (pass == 1 && (int)(o >> 8) != hi_b) continue;
         const uint64_t fw = fixw(weight(x[e], c, nref));
-        if (fw) atomicAdd(&hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
+        if (fw) atomicAdd(&L->hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
       }
     }
-    wave_sync();
-    if (pass == 0) {
-      hi_b = hist_crossing(hist, 256, thrP, 0, &cum, lane);
-      if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
-      base = cum - hist[hi_b];
-    } else {
-      o_star = hi_b * 256 + hist_crossing(hist, 256, thrP, base, &cum, lane);
+    __syncthreads();
+    if (w == 0) {
+      uint64_t cm = 0;
+      const int o = hist_crossing(L->hist, 256, thrP, pass == 0 ? 0 : base, &cm, lane);
+      if (lane == 0) {
+        L->ostar = o;
+        L->zs = cm;
+      }
     }
+    __syncthreads();
+    const int o = L->ostar;
+    cum = L->zs;
+    if (pass == 0) {
+      hi_b = o;
+      if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
+      base = cum - L->hist[hi_b];
+    } else {
+      o_star = hi_b * 256 + o;
+    }
+    __syncthreads();  // the histogram is cleared again only after every thread has read it
   }
   r.t = hi_b < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o_star);
   r.zs = (float)((double)cum / kFix);
-  const int n = collect_ordered(RowSrc{row}, nvec, V, r.t, c, nref, list, lane);
+  const int n = collect_wg(RowSrc{row}, nvec, V, r.t, c, nref, L, list, tid);
   r.nuc = n <= kNucMax ? n : -1;
   return r;
 }
 
 // Threshold search on the captured window: fixed-point masses of the captured logits in a
 // histogram over key offsets below the row max; the first offset at which the running mass
-// reaches P * Z is the threshold. Falls back to the whole row when the capture buffer
-// overflowed or the window does not reach mass P within kHist offsets.
-__device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, float c, float P,
-                            float M, float Z, CapLds* cap, const uint16_t* spill,
-                            const LaneAcc& a, NucEntry* list, int lane) {
-  const float capw = kCaptureK * (kLog2e / c);  // kCaptureK * T in logit units
+// reaches P * Z is the threshold. Falls back to the whole row when the captures overflowed
+// or the window does not reach mass P within kHist offsets.
+__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, float c, float P,
+                            float capw, float M, float Z, RowLds* L, const uint16_t* spill,
+                            NucEntry* list, int tid) {
+  const int lane = tid % kWave, w = tid / kWave;
   const float theta = M - capw;
   const float nref = -M * c;
   const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
   const uint32_t kM = key_of(M);
-  if (a.over) return topp_full_row(row, nvec, V, c, M, thrP, list, cap->hist, lane);
-  for (int j = lane; j < kHist; j += kWave) cap->hist[j] = 0ull;
-  wave_sync();
-  const CapSrc src{cap, spill, row, a.ncap};
-  const int ntot = a.ncap + a.nspill;
-  for (int j0 = 0; j0 < ntot; j0 += kWave) {
-    const int j = j0 + lane;
-    if (j >= ntot) continue;
+  const int ntot = L->ncap;
+  if (ntot > kCapN + kCapG) return topp_full_row(row, nvec, V, c, M, thrP, L, list, tid);
+  for (int j = tid; j < kHist; j += kRowThreads) L->hist[j] = 0ull;
+  __syncthreads();
+  const CapSrc src{L, spill, row};
+  for (int j = tid; j < ntot; j += kRowThreads) {
     int vi;
     uint4 dv;
     src(j, vi, dv);
@@ -472,55 +484,51 @@ __device__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, floa
       if (vi * 8 + e >= V || !(x[e] >= theta)) continue;
       const uint32_t o = kM - key_of(x[e]);
       if (o < (uint32_t)kHist)
-        atomicAdd(&cap->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
+        atomicAdd(&L->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
     }
   }
-  wave_sync();
-  uint64_t zs = 0;
-  const int o_star = hist_crossing(cap->hist, kHist, thrP, 0, &zs, lane);
-  if (o_star < 0) return topp_full_row(row, nvec, V, c, M, thrP, list, cap->hist, lane);
+  __syncthreads();
+  if (w == 0) {
+    uint64_t zs = 0;
+    const int o = hist_crossing(L->hist, kHist, thrP, 0, &zs, lane);
+    if (lane == 0) {
+      L->ostar = o;
+      L->zs = zs;
+    }
+  }
+  __syncthreads();
+  const int o_star = L->ostar;
+  if (o_star < 0) {
+    __syncthreads();  // every thread has read ostar before the fallback overwrites it
+    return topp_full_row(row, nvec, V, c, M, thrP, L, list, tid);
+  }
   TopP r;
   r.slow = false;
   r.t = value_of_key(kM - (uint32_t)o_star);
-  r.zs = (float)((double)zs / kFix);
-  const int n = collect_ordered(src, ntot, V, r.t, c, nref, list, lane);
+  r.zs = (float)((double)L->zs / kFix);
+  const int n = collect_wg(src, ntot, V, r.t, c, nref, L, list, tid);
   r.nuc = n <= kNucMax ? n : -1;
   return r;
 }
 
-// The streaming pass over one row: running (m, s) per lane and, with CAPTURE, the top-p
-// window captures.
-template <bool CAPTURE>
-__device__ __forceinline__ void row_pass(const uint4* __restrict__ rp, int nvec, int V, float c,
-                                         float T, LaneAcc& acc, CapLds* cap, uint16_t* spill,
-                                         int lane) {
-  const float capw = kCaptureK * T;
-  stream_row<kDepth>(rp, nvec, lane, [&](uint4* d, int v0, bool maybe_last) {
-    if (maybe_last) mask_tail(d, v0, nvec, V, lane);
-    consume_trip<CAPTURE>(d, v0, lane, c, capw, acc, cap, spill);
-  });
-}
-
 // ----------------------------------------------------------------------------------------
-// Kernel 1: one wave per logits row, kRowWaves independent waves per workgroup (a workgroup
-// that holds LDS takes one of a CU's 16 workgroup slots; pairing rows lets a CU hold more
-// than 16 rows at once). Sequence b owns row ids b*(2G+1) .. b*(2G+1)+2G (G = max_gamma):
-// id 2(k-1) is the target row p_k of draft position k, id 2(k-1)+1 its draft row q_k, and
-// the last one the bonus row p_{gamma_b+1} (needed only after a full accept, but read with
-// the rest: one workgroup cannot pull a row from HBM fast enough to do it later without
-// stalling the whole resolve step).
-// TOPP: the batch carries a top-p array, so capture buffers live in (dynamic) LDS.
+// Kernel 1: one workgroup of kRowWgWaves waves per logits row. The waves take the row's
+// trips in turn (wave w: trips w, w + kRowWgWaves, ...), so a row streams as one wide
+// sequential read and the hardware hands out rows to CUs as they free up (which evens out
+// the speed differences between CUs and XCDs that a fixed row-to-CU split would expose).
+// Sequence b owns row ids b*(2G+1) .. b*(2G+1)+2G (G = max_gamma): id 2(k-1) is the target
+// row p_k of draft position k, id 2(k-1)+1 its draft row q_k, and the last one the bonus row
+// p_{gamma_b+1} (needed only after a full accept, but read with the rest: one workgroup
+// cannot pull a row from HBM fast enough to do it later without stalling the resolve step).
+// TOPP: the batch carries a top-p array.
 // ----------------------------------------------------------------------------------------
-// Five waves per SIMD (<= 102 VGPRs): 20 rows resident per CU, so a batch of up to 20 rows
-// per CU (B=256, gamma=8: 17) streams in one round.
 template <bool TOPP>
-__global__ __launch_bounds__(kRowWaves * kWave) __attribute__((amdgpu_waves_per_eu(5)))
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void row_stats_kernel(ChainParams P) {
-  extern __shared__ uint4 smem_dyn[];
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  CapLds* cap = reinterpret_cast<CapLds*>(smem_dyn) + w;
+  __shared__ RowLds L;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int per = 2 * P.max_gamma + 1;
-  const int row_id = blockIdx.x * kRowWaves + w;
+  const int row_id = blockIdx.x;
   if (row_id >= P.B * per) return;
   const int b = row_id / per, j = row_id % per;
   const bool bonus = j == 2 * P.max_gamma;
@@ -541,33 +549,79 @@ void row_stats_kernel(ChainParams P) {
   if (!bonus) {
     d = P.tokens[drow];
     if (d < 0 || d >= P.V) {  // the resolve step flags the sequence; nothing to compute
-      if (lane == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, 0.0f, 0, -1, 0, 1};
+      if (tid == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, 0.0f, 0, -1, 0, 1};
       return;
     }
   }
 
-  if (s.T == 0.0f) {  // greedy: argmax of the target row
-    const int am = row_argmax(rp, P.nvec, P.V, lane);
-    if (lane == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, d == am ? 1.0f : 0.0f, am, -1, 0, 1};
+  if (s.T == 0.0f) {  // greedy: argmax of the target row, lowest index on ties
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    stream_row_strided<kDepth>(rp, P.nvec, lane, w, kRowWgWaves, [&](uint4* dd, int v0, bool) {
+      argmax_trip(dd, v0, P.nvec, P.V, lane, bv, bi);
+    });
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      L.pm[w] = bv;
+      L.pa[w] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {  // starts from wave 0's (bv, bi)
+      for (int i = 1; i < kRowWgWaves; ++i)
+        if (L.pm[i] > bv || (L.pm[i] == bv && L.pa[i] < bi)) {
+          bv = L.pm[i];
+          bi = L.pa[i];
+        }
+      const int am = bi == 0x7FFFFFFF ? 0 : bi;
+      *st = RowStat{0.0f, 1.0f, -INFINITY, d == am ? 1.0f : 0.0f, am, -1, 0, 1};
+    }
     return;
   }
 
-  const uint32_t ld_bits = d >= 0 ? base[d] : 0u;  // the draft token's logit: issued early
+  const uint32_t ld_bits = (tid == 0 && d >= 0) ? base[d] : 0u;  // the draft token's logit
   const float c = kLog2e / s.T;
+  const float capw = kCaptureK * s.T;
   const bool topp = TOPP && s.P < 1.0f;
   uint16_t* spill = P.spill + slot * kCapG;
+  if (topp) {
+    if (tid == 0) {
+      L.ncap = 0;
+      L.nkept = 0;
+      L.wgmax = ord_key(-INFINITY);
+    }
+    __syncthreads();
+  }
   LaneAcc acc;
-  if (topp) row_pass<true>(rp, P.nvec, P.V, c, s.T, acc, cap, spill, lane);
-  else row_pass<false>(rp, P.nvec, P.V, c, s.T, acc, nullptr, nullptr, lane);
+  acc.wg = ord_key(-INFINITY);
+  if (topp)
+    stream_row_strided<kDepth>(rp, P.nvec, lane, w, kRowWgWaves, [&](uint4* dd, int v0, bool ml) {
+      if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
+      consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
+    });
+  else
+    stream_row_strided<kDepth>(rp, P.nvec, lane, w, kRowWgWaves, [&](uint4* dd, int v0, bool ml) {
+      if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
+      consume_trip<false>(dd, v0, lane, c, capw, acc, nullptr, nullptr);
+    });
+  {
+    float Mw, Zw;
+    finish_mz(acc, c, Mw, Zw);
+    if (lane == 0) {
+      L.pm[w] = Mw;
+      L.pz[w] = Zw;
+    }
+  }
+  __syncthreads();
   float M, Z;
-  finish_mz(acc, c, M, Z);
+  row_mz(&L, c, M, Z);
   TopP tp{-INFINITY, Z, -1, false};
-  if (topp) tp = topp_select(rp, P.nvec, P.V, c, s.P, M, Z, cap, spill, acc, list, lane);
-  const float ld = __uint_as_float(ld_bits << 16);
-  const float wd = (d >= 0 && ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;
-  if (lane == 0)
+  if (topp) tp = topp_select(rp, P.nvec, P.V, c, s.P, capw, M, Z, &L, spill, list, tid);
+  if (tid == 0) {
+    const float ld = __uint_as_float(ld_bits << 16);
+    const float wd = (d >= 0 && ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;
     *st = RowStat{M, tp.zs, tp.t, wd, -1, topp ? tp.nuc : -1,
                   tp.slow ? SPEC_FLAG_TOPP_SLOW : 0, 1};
+  }
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1168,12 +1222,10 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   // per sequence: two rows (target, draft) per draft position slot k <= max_gamma, then the
   // bonus row
   const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
-  const unsigned grid = (nrows + kRowWaves - 1) / kRowWaves;
   if (a.top_p)
-    hipLaunchKernelGGL(row_stats_kernel<true>, dim3(grid), dim3(kRowWaves * kWave),
-                       kRowWaves * sizeof(CapLds), st, P);
+    hipLaunchKernelGGL(row_stats_kernel<true>, dim3(nrows), dim3(kRowThreads), 0, st, P);
   else
-    hipLaunchKernelGGL(row_stats_kernel<false>, dim3(grid), dim3(kRowWaves * kWave), 0, st, P);
+    hipLaunchKernelGGL(row_stats_kernel<false>, dim3(nrows), dim3(kRowThreads), 0, st, P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)a.batch), dim3(kResolveThreads), 0,

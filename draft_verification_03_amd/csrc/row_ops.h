@@ -82,6 +82,60 @@ __device__ __forceinline__ void stream_row(const uint4* __restrict__ row, int nv
   }
 }
 
+// Streams the trips first, first + step, first + 2*step, ... of a row (a trip is kU vectors
+// per lane at kU * kWave vectors apart from the next trip) through consume(d, v0,
+// maybe_last), with DEPTH of this wave's trips of loads in flight: the waves of a workgroup
+// pass first = 0 .. step-1 and together cover the row once, each wave's stream a regular
+// stride of full trips (unpredicated loads) plus, for one of them, the row's partial trip.
+// Issue priority falls with the wave's progress, as in stream_row.
+template <int DEPTH, typename F>
+__device__ __forceinline__ void stream_row_strided(const uint4* __restrict__ row, int nvec,
+                                                   int lane, int first, int step, F&& consume) {
+  constexpr int kStep = kU * kWave;
+  const int nfull = nvec / kStep;
+  const int nf = first < nfull ? (nfull - 1 - first) / step + 1 : 0;  // this wave's full trips
+  auto v0_of = [&](int i) { return (first + i * step) * kStep; };
+  int i = 0;
+  if (nf >= DEPTH) {
+    uint4 buf[DEPTH][kU];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) load_full(row, v0_of(s), lane, buf[s]);
+    const int q1 = nf / 4, q2 = nf / 2, q3 = (3 * nf) / 4;
+    __builtin_amdgcn_s_setprio(3);
+    for (; i + 2 * DEPTH <= nf; i += DEPTH) {  // trips i .. i+DEPTH-1; none is the row's last
+      if (i >= q3) __builtin_amdgcn_s_setprio(0);
+      else if (i >= q2) __builtin_amdgcn_s_setprio(1);
+      else if (i >= q1) __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        consume(buf[s], v0_of(i + s), false);
+        load_full(row, v0_of(i + s + DEPTH), lane, buf[s]);
+        __builtin_amdgcn_sched_barrier(0);  // the reload issues before the next trip's waits
+      }
+    }
+    // DEPTH .. 2*DEPTH-1 full trips remain; the first DEPTH of them are loaded
+#pragma unroll
+    for (int s = 0; s < 2 * DEPTH - 1; ++s) {
+      if (i + s < nf) {
+        consume(buf[s % DEPTH], v0_of(i + s), true);
+        if (i + s + DEPTH < nf) load_full(row, v0_of(i + s + DEPTH), lane, buf[s % DEPTH]);
+      }
+    }
+    i = nf;
+    __builtin_amdgcn_s_setprio(0);
+  }
+  for (; i < nf; ++i) {  // fewer than DEPTH full trips
+    uint4 d[kU];
+    load_full(row, v0_of(i), lane, d);
+    consume(d, v0_of(i), true);
+  }
+  if (nfull * kStep < nvec && nfull >= first && (nfull - first) % step == 0) {  // partial trip
+    uint4 d[kU];
+    load_trip(row, nfull * kStep, nvec, lane, d);
+    consume(d, nfull * kStep, true);
+  }
+}
+
 // Masks the logits of the last, partial vector (V not a multiple of 8) to -inf; only the
 // last trip of a row can hold it.
 __device__ __forceinline__ void mask_tail(uint4 d[kU], int v0, int nvec, int V, int lane) {

@@ -75,8 +75,8 @@ int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspac
     return fail(SPEC_ERR_INVALID_ARG, "draft_tokens is required when total_draft_rows > 0");
   if (!aligned16(a->target_logits) || (a->draft_logits && !aligned16(a->draft_logits)))
     return fail(SPEC_ERR_INVALID_ARG, "logits base pointers must be 16-byte aligned");
-  if ((int64_t)a->batch * (a->max_gamma + 1) > 0x7FFFFFFFLL)
-    return fail(SPEC_ERR_INVALID_ARG, "batch * (max_gamma + 1) exceeds the grid limit");
+  if ((int64_t)a->batch * (2 * a->max_gamma + 1) > 0x7FFFFFFFLL)
+    return fail(SPEC_ERR_INVALID_ARG, "batch * (2 * max_gamma + 1) exceeds the grid limit");
   const size_t need =
       specv::chain_workspace_bytes(a->batch, a->total_draft_rows, a->vocab);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
