@@ -2,7 +2,10 @@
 
 All HIP code is compiled with packed-FP32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass warns that it does
-not know the feature, which is harmless.
+not know the feature, which is harmless. The atomic optimizer is off
+(``-amdgpu-atomic-optimizer-strategy=None``): the kernels' atomics are already issued by one
+lane, and the optimizer's rewrite reads each result back right after the atomic, which puts
+the LDS round trip of the row pass's trip claims in front of its loads.
 """
 from __future__ import annotations
 
@@ -33,6 +36,7 @@ def build(force: bool = True, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-I", INCLUDE, "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
            "-Wall", "-o", tmp] + sources()
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()

@@ -144,7 +144,6 @@ struct LaneAcc {
   float m = -INFINITY;   // running max of this lane's logits
   float s = 0.0f;        // sum of exp2((l - m) * c) over this lane's logits
   float wm = -INFINITY;  // capture reference: a lower bound of the row max known to the wave
-  int wg = 0;            // lane 0: the workgroup maximum read back at the last publication
 };
 
 // Weight of one logit relative to a reference: the same expression everywhere, so that
@@ -152,13 +151,6 @@ struct LaneAcc {
 __device__ __forceinline__ float weight(float l, float c, float nref) {
   return __builtin_amdgcn_exp2f(fmaf(l, c, nref));
 }
-
-// Order-preserving int image of a float (for LDS atomic max), and its inverse.
-__device__ __forceinline__ int ord_key(float f) {
-  const int b = __float_as_int(f);
-  return b >= 0 ? b : (b ^ 0x7FFFFFFF);
-}
-__device__ __forceinline__ float ord_val(int k) { return __int_as_float(k >= 0 ? k : (k ^ 0x7FFFFFFF)); }
 
 // LDS of one row's workgroup.
 struct RowLds {
@@ -169,11 +161,9 @@ struct RowLds {
   float pm[kRowWgWaves];           // per-wave max (value of the argmax for greedy rows)
   float pz[kRowWgWaves];           // per-wave sum of weights relative to the wave max
   int pa[kRowWgWaves];             // per-wave argmax (greedy rows)
+  int trip;                        // trips of the row claimed by the waves
   int ncap;                        // capture slots claimed: LDS slots, then spill slots
-  int wgmax;                       // ord_key of the largest wave maximum published so far
   int nkept;                       // nucleus entries claimed
-  int ostar;                       // threshold search: key offset of t (-1: not found)
-  unsigned long long zs;           // threshold search: fixed-point mass of the kept set
 };
 
 // Claims slots for the trip's flagged vectors (one LDS atomic per wave) and writes them:
@@ -213,15 +203,12 @@ __device__ __forceinline__ void capture_trip(RowLds* L, uint16_t* spill, const u
 // One trip (kU vectors of the row) into the lane's running (m, s). The weights are taken
 // against the lane's previous maximum; only when the trip raises it (rare after the first
 // trips) is the trip's partial sum re-referenced, or recomputed when it may have overflowed.
-// With CAPTURE, the vectors whose max is within capw of the best known lower bound of the
-// row max are captured (a superset of the final window), and the wave publishes its max to
-// the workgroup and picks up the other waves' (the read-back is used from the next trip on,
-// after this trip's reload has issued).
+// With CAPTURE, the vectors whose max is within capw of the wave's max so far (a lower bound
+// of the row max) are captured: a superset of the final window.
 template <bool CAPTURE>
 __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane, float c,
                                              float capw, LaneAcc& a, RowLds* L,
                                              uint16_t* spill) {
-  if (CAPTURE) a.wm = fmaxf(a.wm, ord_val(__builtin_amdgcn_readfirstlane(a.wg)));
   const float ref = (a.m == -INFINITY) ? 0.0f : a.m;
   const float nref = -ref * c;
   float vm[kU];
@@ -259,7 +246,6 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
     // kept finite, so a vector of -inf logits (past the row end included) is never captured
     const float thr = vmax3(a.wm - capw, -3.4028235e38f, -3.4028235e38f);
     capture_trip(L, spill, d, vm, thr, v0, lane);
-    if (lane == 0) a.wg = atomicMax(&L->wgmax, ord_key(a.wm));
   }
 }
 
@@ -403,10 +389,11 @@ __device__ int collect_wg(Src src, int n, int V, float t, float c, float nref, R
 // Exact threshold search over the whole row: the largest bf16 key t with
 // mass(key >= t) >= thrP, by a 256-bucket fixed-point histogram of the key offset's high byte
 // and then of its low byte inside the chosen bucket (two passes), plus one pass for the
-// nucleus list. Used when the captures missed the nucleus or overflowed.
+// nucleus list. Used when the captures missed the nucleus or overflowed. Every wave reads the
+// crossings from the shared histograms.
 __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c, float M,
                               uint64_t thrP, RowLds* L, NucEntry* list, int tid) {
-  const int lane = tid % kWave, w = tid / kWave;
+  const int lane = tid % kWave;
   const float nref = -M * c;
   const uint32_t kM = key_of(M);
   TopP r;
@@ -429,25 +416,14 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
       }
     }
     __syncthreads();
-    if (w == 0) {
-      uint64_t cm = 0;
-      const int o = hist_crossing(L->hist, 256, thrP, pass == 0 ? 0 : base, &cm, lane);
-      if (lane == 0) {
-        L->ostar = o;
-        L->zs = cm;
-      }
-    }
-    __syncthreads();
-    const int o = L->ostar;
-    cum = L->zs;
     if (pass == 0) {
-      hi_b = o;
+      hi_b = hist_crossing(L->hist, 256, thrP, 0, &cum, lane);
       if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
       base = cum - L->hist[hi_b];
     } else {
-      o_star = hi_b * 256 + o;
+      o_star = hi_b * 256 + hist_crossing(L->hist, 256, thrP, base, &cum, lane);
     }
-    __syncthreads();  // the histogram is cleared again only after every thread has read it
+    __syncthreads();  // the histogram is cleared again only after every wave has read it
   }
   r.t = hi_b < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o_star);
   r.zs = (float)((double)cum / kFix);
@@ -457,21 +433,22 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
 }
 
 // Threshold search on the captured window: fixed-point masses of the captured logits in a
-// histogram over key offsets below the row max; the first offset at which the running mass
-// reaches P * Z is the threshold. Falls back to the whole row when the captures overflowed
-// or the window does not reach mass P within kHist offsets.
-__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V, float c, float P,
-                            float capw, float M, float Z, RowLds* L, const uint16_t* spill,
-                            NucEntry* list, int tid) {
-  const int lane = tid % kWave, w = tid / kWave;
+// histogram over key offsets below the row max (cleared before the stream); the first offset
+// at which the running mass reaches P * Z is the threshold, found by every wave from the
+// same histogram (the same integer sums, so the same answer, with no barrier to hand it
+// out). Falls back to the whole row when the captures overflowed or the window does not
+// reach mass P within kHist offsets.
+__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V,
+                                            float c, float P, float capw, float M, float Z,
+                                            RowLds* L, const uint16_t* spill, NucEntry* list,
+                                            int tid) {
+  const int lane = tid % kWave;
   const float theta = M - capw;
   const float nref = -M * c;
   const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
   const uint32_t kM = key_of(M);
   const int ntot = L->ncap;
   if (ntot > kCapN + kCapG) return topp_full_row(row, nvec, V, c, M, thrP, L, list, tid);
-  for (int j = tid; j < kHist; j += kRowThreads) L->hist[j] = 0ull;
-  __syncthreads();
   const CapSrc src{L, spill, row};
   for (int j = tid; j < ntot; j += kRowThreads) {
     int vi;
@@ -488,24 +465,16 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
     }
   }
   __syncthreads();
-  if (w == 0) {
-    uint64_t zs = 0;
-    const int o = hist_crossing(L->hist, kHist, thrP, 0, &zs, lane);
-    if (lane == 0) {
-      L->ostar = o;
-      L->zs = zs;
-    }
-  }
-  __syncthreads();
-  const int o_star = L->ostar;
+  uint64_t zs = 0;
+  const int o_star = hist_crossing(L->hist, kHist, thrP, 0, &zs, lane);
   if (o_star < 0) {
-    __syncthreads();  // every thread has read ostar before the fallback overwrites it
+    __syncthreads();  // every wave has read the histogram before the fallback clears it
     return topp_full_row(row, nvec, V, c, M, thrP, L, list, tid);
   }
   TopP r;
   r.slow = false;
   r.t = value_of_key(kM - (uint32_t)o_star);
-  r.zs = (float)((double)L->zs / kFix);
+  r.zs = (float)((double)zs / kFix);
   const int n = collect_wg(src, ntot, V, r.t, c, nref, L, list, tid);
   r.nuc = n <= kNucMax ? n : -1;
   return r;
@@ -554,10 +523,20 @@ void row_stats_kernel(ChainParams P) {
     }
   }
 
+  const bool topp = TOPP && s.T != 0.0f && s.P < 1.0f;
+  if (tid == 0) {
+    L.trip = 0;
+    L.ncap = 0;
+    L.nkept = 0;
+  }
+  if (topp)
+    for (int i = tid; i < kHist; i += kRowThreads) L.hist[i] = 0ull;
+  __syncthreads();
+
   if (s.T == 0.0f) {  // greedy: argmax of the target row, lowest index on ties
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    stream_row_strided<kDepth>(rp, P.nvec, lane, w, kRowWgWaves, [&](uint4* dd, int v0, bool) {
+    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
       argmax_trip(dd, v0, P.nvec, P.V, lane, bv, bi);
     });
     wave_argmax(bv, bi);
@@ -581,25 +560,15 @@ void row_stats_kernel(ChainParams P) {
   const uint32_t ld_bits = (tid == 0 && d >= 0) ? base[d] : 0u;  // the draft token's logit
   const float c = kLog2e / s.T;
   const float capw = kCaptureK * s.T;
-  const bool topp = TOPP && s.P < 1.0f;
   uint16_t* spill = P.spill + slot * kCapG;
-  if (topp) {
-    if (tid == 0) {
-      L.ncap = 0;
-      L.nkept = 0;
-      L.wgmax = ord_key(-INFINITY);
-    }
-    __syncthreads();
-  }
   LaneAcc acc;
-  acc.wg = ord_key(-INFINITY);
   if (topp)
-    stream_row_strided<kDepth>(rp, P.nvec, lane, w, kRowWgWaves, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
     });
   else
-    stream_row_strided<kDepth>(rp, P.nvec, lane, w, kRowWgWaves, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<false>(dd, v0, lane, c, capw, acc, nullptr, nullptr);
     });

@@ -136,6 +136,59 @@ __device__ __forceinline__ void stream_row_strided(const uint4* __restrict__ row
   }
 }
 
+// Spare load target: a claim past a row's full trips loads these 4 KB instead (data never
+// used), so that the row streams' loads are all issued unconditionally.
+static __device__ uint4 g_spare_trip[kU * kWave];
+
+// Streams the full trips of a row that this wave claims from a counter shared by the
+// workgroup's waves (one LDS atomic per trip, issued before the consume so that its latency
+// hides behind it), DEPTH trips of loads in flight: a wave that runs faster takes more trips,
+// so the waves of a row finish together. The wave that claims index nfull also streams the
+// row's partial trip, if there is one. consume(d, v0, maybe_last) as in stream_row.
+template <int DEPTH, typename F>
+__device__ __forceinline__ void stream_row_claimed(const uint4* __restrict__ row, int nvec,
+                                                   int lane, int* ctr, F&& consume) {
+  constexpr int kStep = kU * kWave;
+  const int nfull = nvec / kStep;
+  // A claim is issued by lane 0 and read back (readfirstlane) only where it is needed, so
+  // that the consume between the two hides the atomic's latency.
+  auto claim_issue = [&]() {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(ctr, 1);
+    return t;  // the claim in lane 0
+  };
+  auto claim = [&]() { return __builtin_amdgcn_readfirstlane(claim_issue()); };
+  auto src = [&](int t) { return t < nfull ? row + t * kStep : g_spare_trip; };
+  bool partial = false;  // this wave claimed index nfull
+  uint4 buf[DEPTH][kU];
+  int tc[DEPTH];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) {
+    tc[s] = claim();
+    partial |= tc[s] == nfull;
+    load_full(src(tc[s]), 0, lane, buf[s]);
+  }
+  // Each wave's claims grow and its buffers hold them in claim order (tc[0] < tc[1] < ...):
+  // once tc[0] is past the full trips, so are the others.
+  while (tc[0] < nfull) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      const int tq = claim_issue();
+      if (tc[s] < nfull) consume(buf[s], tc[s] * kStep, tc[s] == nfull - 1);
+      const int tn = __builtin_amdgcn_readfirstlane(tq);
+      partial |= tn == nfull;
+      load_full(src(tn), 0, lane, buf[s]);
+      __builtin_amdgcn_sched_barrier(0);  // the reload issues before the next trip's waits
+      tc[s] = tn;
+    }
+  }
+  if (partial && nfull * kStep < nvec) {
+    uint4 d[kU];
+    load_trip(row, nfull * kStep, nvec, lane, d);
+    consume(d, nfull * kStep, true);
+  }
+}
+
 // Masks the logits of the last, partial vector (V not a multiple of 8) to -inf; only the
 // last trip of a row can hold it.
 __device__ __forceinline__ void mask_tail(uint4 d[kU], int v0, int nvec, int V, int lane) {
