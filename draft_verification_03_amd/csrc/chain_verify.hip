@@ -158,6 +158,7 @@ struct RowLds {
   unsigned long long hist[kHist];  // fixed-point masses by key offset below the row max
   NucEntry kept[kNucMax];          // nucleus entries before they are put in token order
   uint16_t idx[kCapN];             // vector index of each captured vector
+  float wmax[kRowWgWaves];         // each wave's max so far, published for the others
   float pm[kRowWgWaves];           // per-wave max (value of the argmax for greedy rows)
   float pz[kRowWgWaves];           // per-wave sum of weights relative to the wave max
   int pa[kRowWgWaves];             // per-wave argmax (greedy rows)
@@ -203,12 +204,20 @@ __device__ __forceinline__ void capture_trip(RowLds* L, uint16_t* spill, const u
 // One trip (kU vectors of the row) into the lane's running (m, s). The weights are taken
 // against the lane's previous maximum; only when the trip raises it (rare after the first
 // trips) is the trip's partial sum re-referenced, or recomputed when it may have overflowed.
-// With CAPTURE, the vectors whose max is within capw of the wave's max so far (a lower bound
-// of the row max) are captured: a superset of the final window.
+// With CAPTURE, the vectors whose max is within capw of the best lower bound of the row max
+// the wave knows (its own max so far, and the maxima the other waves published in LDS) are
+// captured: a superset of the final window.
 template <bool CAPTURE>
 __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane, float c,
                                              float capw, LaneAcc& a, RowLds* L,
                                              uint16_t* spill) {
+  // the other waves' published maxima, read now and used after the trip's arithmetic
+  float wg = -INFINITY;
+  if (CAPTURE) {
+#pragma unroll
+    for (int i = 0; i < kRowWgWaves; ++i)
+      wg = fmaxf(wg, __hip_atomic_load(&L->wmax[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  }
   const float ref = (a.m == -INFINITY) ? 0.0f : a.m;
   const float nref = -ref * c;
   float vm[kU];
@@ -242,10 +251,12 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
   }
   a.s += st;
   if (CAPTURE) {
-    a.wm = fmaxf(a.wm, wave_max_dpp(a.m));
+    a.wm = vmax3(a.wm, wave_max_dpp(a.m), wg);
     // kept finite, so a vector of -inf logits (past the row end included) is never captured
     const float thr = vmax3(a.wm - capw, -3.4028235e38f, -3.4028235e38f);
     capture_trip(L, spill, d, vm, thr, v0, lane);
+    if (lane == 0)
+      __hip_atomic_store(&L->wmax[threadIdx.x / kWave], a.wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -529,6 +540,7 @@ void row_stats_kernel(ChainParams P) {
     L.ncap = 0;
     L.nkept = 0;
   }
+  if (tid < kRowWgWaves) L.wmax[tid] = -INFINITY;
   if (topp)
     for (int i = tid; i < kHist; i += kRowThreads) L.hist[i] = 0ull;
   __syncthreads();
