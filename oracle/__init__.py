@@ -22,7 +22,7 @@ _LIB = os.path.join(_HERE, "libspec_oracle.so")
 
 PURPOSE_ACCEPT, PURPOSE_RESIDUAL, PURPOSE_BONUS = 0, 1, 2
 F_BAD_TOKEN, F_Q_ZERO, F_RESID_FALLBACK, F_NO_ROW = 1, 2, 4, 8
-F_SLOT_OOB, F_BAD_TREE, F_BAD_PARAM = 16, 32, 128
+F_SLOT_OOB, F_BAD_TREE, F_BAD_PARAM, F_EOS, F_LEN_CAP = 16, 32, 128, 256, 512
 
 
 def build(force: bool = True) -> str:
@@ -55,15 +55,16 @@ def _declare(L):
     L.oracle_philox4x32_10.argtypes = [_P, _P, _P]
     L.oracle_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
     L.oracle_uniform.restype = ctypes.c_double
-    L.oracle_dist.argtypes = [_P, _I, ctypes.c_double, ctypes.c_double, _P, _P, _P]
+    L.oracle_dist.argtypes = [_P, _I, ctypes.c_double, ctypes.c_double, _I, _P, _P, _P]
     L.oracle_dist.restype = _I
     L.oracle_sample.argtypes = [_P, _I, ctypes.c_double, _P]
     L.oracle_sample.restype = _I
     L.oracle_position_step.argtypes = [_P, _P, _I, _I, ctypes.c_double, ctypes.c_double,
                                        _P, _P, _P, _P]
     L.oracle_position_step.restype = _I
-    L.oracle_verify_chain.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
-                                      ctypes.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _I]
+    L.oracle_verify_chain.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _I, ctypes.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _I]
     L.oracle_verify_chain.restype = _I
     L.oracle_verify_tree.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _I]
@@ -75,8 +76,8 @@ def _declare(L):
 
 class _RowInfo(ctypes.Structure):
     _fields_ = [("argmax", ctypes.c_int), ("nucleus", ctypes.c_int), ("m", ctypes.c_double),
-                ("tstar", ctypes.c_double), ("z", ctypes.c_double), ("zs", ctypes.c_double),
-                ("topp_margin", ctypes.c_double)]
+                ("tk", ctypes.c_double), ("tstar", ctypes.c_double), ("z", ctypes.c_double),
+                ("zs", ctypes.c_double), ("topp_margin", ctypes.c_double)]
 
 
 def _ptr(a):
@@ -99,14 +100,15 @@ def uniform(seed, id_, pos, purpose):
     return lib().oracle_uniform(int(seed), int(id_), int(pos), int(purpose))
 
 
-def dist(row_bits, T, P=1.0):
-    """Filtered, normalised law of one bf16 row. Returns (pi, info dict)."""
+def dist(row_bits, T, P=1.0, K=0):
+    """Filtered (top-k K, then top-p P), normalised law of one bf16 row. Returns (pi, info
+    dict)."""
     row = _c(row_bits, np.uint16)
     V = row.shape[0]
     pi = np.zeros(V, dtype=np.float64)
     scratch = np.zeros(V, dtype=np.float64)
     info = _RowInfo()
-    rc = lib().oracle_dist(_ptr(row), V, float(T), float(P), _ptr(pi), _ptr(scratch),
+    rc = lib().oracle_dist(_ptr(row), V, float(T), float(P), int(K), _ptr(pi), _ptr(scratch),
                            ctypes.addressof(info))
     d = {f: getattr(info, f) for f, _ in _RowInfo._fields_}
     d["rc"] = rc
@@ -136,7 +138,8 @@ def position_step(p, q, d, u_acc, u_res):
 
 
 def verify_chain(target, draft, cu_gamma, draft_tokens, temperature, top_p=None, seq_id=None,
-                 committed_len=None, lead_slots=1, seed=0, uniform_override=None, nthreads=0):
+                 committed_len=None, lead_slots=1, seed=0, uniform_override=None, nthreads=0,
+                 top_k=None, eos_token=None, max_emit=None):
     """Chain verification of a ragged batch on host arrays.
 
     target: uint16 [sum(gamma_b+1), row_stride]; draft: uint16 [sum(gamma_b), row_stride] or
@@ -145,12 +148,13 @@ def verify_chain(target, draft, cu_gamma, draft_tokens, temperature, top_p=None,
     """
     return verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p, seq_id,
                           committed_len, lead_slots, seed, uniform_override, nthreads,
-                          vocab=None)
+                          vocab=None, top_k=top_k, eos_token=eos_token, max_emit=max_emit)
 
 
 def verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p=None,
                    seq_id=None, committed_len=None, lead_slots=1, seed=0,
-                   uniform_override=None, nthreads=0, vocab=None):
+                   uniform_override=None, nthreads=0, vocab=None, top_k=None, eos_token=None,
+                   max_emit=None):
     target = _c(target, np.uint16)
     draft = _c(draft, np.uint16)
     cu = _c(cu_gamma, np.int32)
@@ -165,12 +169,16 @@ def verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p=Non
         toks = np.zeros(max(n_draft, 1), dtype=np.int32)
     temp = _c(temperature, np.float32)
     tp = _c(top_p, np.float32)
+    tk = _c(top_k, np.int32)
+    eos = _c(eos_token, np.int32)
+    cap = _c(max_emit, np.int32)
     sid = _c(seq_id, np.uint32)
     L = _c(committed_len if committed_len is not None else np.zeros(B), np.int32)
     ovr = _c(uniform_override, np.float32)
     out = {
         "out_tokens": np.full(max(n_target, 1), -1, dtype=np.int32),
         "num_accepted": np.zeros(B, dtype=np.int32),
+        "num_emitted": np.zeros(B, dtype=np.int32),
         "committed_len": np.zeros(B, dtype=np.int32),
         "seq_flags": np.zeros(B, dtype=np.int32),
         "probe_rows": np.full((max(n_draft, 1), 3), np.nan, dtype=np.float64),
@@ -181,8 +189,9 @@ def verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p=Non
     }
     rc = lib().oracle_verify_chain(
         B, V, stride, _ptr(target), _ptr(draft), _ptr(cu), _ptr(toks), _ptr(temp), _ptr(tp),
-        _ptr(sid), _ptr(L), int(lead_slots), int(seed), _ptr(ovr), _ptr(out["out_tokens"]),
-        _ptr(out["num_accepted"]), _ptr(out["committed_len"]), _ptr(out["seq_flags"]),
+        _ptr(tk), _ptr(eos), _ptr(cap), _ptr(sid), _ptr(L), int(lead_slots), int(seed),
+        _ptr(ovr), _ptr(out["out_tokens"]), _ptr(out["num_accepted"]), _ptr(out["num_emitted"]),
+        _ptr(out["committed_len"]), _ptr(out["seq_flags"]),
         _ptr(out["probe_rows"]), _ptr(out["probe_seq"]), _ptr(out["margin"]), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_verify_chain failed")
@@ -191,7 +200,8 @@ def verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p=Non
     return out
 
 
-def draw_tokens(rows, temperature, top_p, seed, ids, start_pos, vocab=None, nthreads=0):
+def draw_tokens(rows, temperature, top_p, seed, ids, start_pos, vocab=None, nthreads=0,
+                top_k=None):
     """One token per row from the row's filtered law: a round with gamma = 0 per row.
 
     Row i is a one-row sequence with id ``ids[i]`` and committed length ``start_pos[i]``, so
@@ -203,7 +213,8 @@ def draw_tokens(rows, temperature, top_p, seed, ids, start_pos, vocab=None, nthr
     if n == 0:
         return np.zeros(0, dtype=np.int32)
     r = verify_chain_v(rows, None, np.zeros(n + 1, dtype=np.int32), None, temperature, top_p,
-                       ids, start_pos, lead_slots=1, seed=seed, nthreads=nthreads, vocab=vocab)
+                       ids, start_pos, lead_slots=1, seed=seed, nthreads=nthreads, vocab=vocab,
+                       top_k=top_k)
     return r["out_tokens"].copy()
 
 

@@ -39,6 +39,19 @@
  *       the argmax at the stopping node and is emitted only if that node has a row.
  *   R12 tree KV commit copies, in depth order, slot base+path[j] to slot base+j,
  *       base = L + lead_slots - 1, for every layer, K and V, and head.
+ *   R18 top-k is a value threshold too: t_k is the K-th largest logit counting repeats, and
+ *       every token with logit >= t_k is kept (ties at the boundary included, so the kept
+ *       set can exceed K). K <= 0 or K >= V switches it off. Top-k comes first and top-p
+ *       then applies to the top-k law (mass measured within the top-k set), in the order
+ *       the pages name them ([KV] §4, "top-k/top-p"); both apply to p and q alike.
+ *   R19 early stop ([KV] §5: EOS and the length cap end a round early): the round's
+ *       emitted tokens are the accepted drafts in order, then the correction or bonus token.
+ *       Emission stops after the first emitted token equal to the sequence's EOS id
+ *       (flag EOS), and after max_emit tokens (flag LEN_CAP when that cuts the round short).
+ *       A stop inside the accepted drafts ends the round there: later positions are not
+ *       tested and no correction or bonus token is drawn; n_acc counts the emitted drafts
+ *       and the committed length follows R10 with that n_acc. eos < 0 and max_emit <= 0
+ *       switch the respective stop off.
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +71,8 @@
 #define OF_SLOT_OOB 16
 #define OF_BAD_TREE 32
 #define OF_BAD_PARAM 128
+#define OF_EOS 256
+#define OF_LEN_CAP 512
 
 #define PURPOSE_ACCEPT 0u
 #define PURPOSE_RESIDUAL 1u
@@ -114,10 +129,12 @@ typedef struct {
   int argmax;          /* lowest token id holding the maximum logit            */
   int nucleus;         /* |S|                                                  */
   double m;            /* maximum logit                                        */
-  double tstar;        /* nucleus threshold logit; -inf when top-p is off      */
+  double tk;           /* top-k threshold logit; -inf when top-k is off        */
+  double tstar;        /* kept-set threshold logit; -inf when no filter is on  */
   double z;            /* sum over all tokens of exp((l-m)/T)                  */
   double zs;           /* the same sum over S                                  */
-  double topp_margin;  /* min(|mass(S)-P|, |mass(S minus lowest group)-P|)     */
+  double topp_margin;  /* min(|mass(S)-P|, |mass(S minus lowest group)-P|),
+                          masses relative to the top-k set                     */
 } orow_t;
 
 static int cmp_desc(const void* a, const void* b) {
@@ -125,10 +142,11 @@ static int cmp_desc(const void* a, const void* b) {
   return (x < y) - (x > y);
 }
 
-/* Fills pi[0..V) with the filtered, normalised law of one bf16 logits row.
- * scratch must hold V doubles. Returns 0, or -1 if the row has no finite maximum. */
-int oracle_dist(const uint16_t* row, int V, double T, double P, double* pi, double* scratch,
-                orow_t* info) {
+/* Fills pi[0..V) with the filtered, normalised law of one bf16 logits row (top-k K, then
+ * top-p P on the top-k law; readings R1-R3, R18). scratch must hold V doubles. Returns 0,
+ * or -1 if the row has no finite maximum. */
+int oracle_dist(const uint16_t* row, int V, double T, double P, int K, double* pi,
+                double* scratch, orow_t* info) {
   double m = -INFINITY;
   int am = 0;
   for (int v = 0; v < V; ++v) {
@@ -137,6 +155,7 @@ int oracle_dist(const uint16_t* row, int V, double T, double P, double* pi, doub
   }
   info->argmax = am;
   info->m = m;
+  info->tk = -INFINITY;
   info->tstar = -INFINITY;
   info->topp_margin = INFINITY;
   if (!(m > -INFINITY) || isinf(m) || isnan(m)) return -1;
@@ -153,28 +172,45 @@ int oracle_dist(const uint16_t* row, int V, double T, double P, double* pi, doub
     z += pi[v];
   }
   info->z = z;
+  const int use_k = K >= 1 && K < V, use_p = P < 1.0;
   double tstar = -INFINITY;
-  if (P < 1.0) {
-    /* Walk the distinct logit values from the largest down; the first value at which the
-     * mass of all tokens at or above it reaches P is the threshold. */
+  if (use_k || use_p) {
     for (int v = 0; v < V; ++v) scratch[v] = oracle_bf16_to_double(row[v]);
     qsort(scratch, (size_t)V, sizeof(double), cmp_desc);
-    double cum = 0.0, above = 0.0;
-    for (int i = 0; i < V; ++i) {
-      cum += exp((scratch[i] - m) / T);
-      int group_end = (i + 1 == V) || (scratch[i + 1] != scratch[i]);
-      if (!group_end) continue;
-      if (cum / z >= P) {
-        tstar = scratch[i];
-        double d1 = fabs(cum / z - P), d2 = fabs(above / z - P);
-        info->topp_margin = d1 < d2 ? d1 : d2;
-        break;
-      }
-      above = cum;
+    /* Top-k: the K-th largest value, repeats counted; the top-k set is every token at or
+     * above it, and its mass zk is the reference mass for top-p. */
+    double tk = -INFINITY, zk = z;
+    if (use_k) {
+      tk = scratch[K - 1];
+      zk = 0.0;
+      for (int v = 0; v < V; ++v)
+        if (oracle_bf16_to_double(row[v]) >= tk) zk += pi[v];
     }
-    if (tstar == -INFINITY) { /* rounding kept the total just below P: keep everything */
-      tstar = scratch[V - 1];
-      info->topp_margin = 0.0;
+    info->tk = tk;
+    tstar = tk;
+    if (use_p) {
+      /* Walk the distinct logit values of the top-k set from the largest down; the first
+       * value at which the mass of all tokens at or above it reaches P * zk is the
+       * threshold. */
+      double cum = 0.0, above = 0.0;
+      int found = 0;
+      for (int i = 0; i < V && scratch[i] >= tk; ++i) {
+        cum += exp((scratch[i] - m) / T);
+        int group_end = (i + 1 == V) || (scratch[i + 1] != scratch[i]);
+        if (!group_end) continue;
+        if (cum / zk >= P) {
+          tstar = scratch[i];
+          double d1 = fabs(cum / zk - P), d2 = fabs(above / zk - P);
+          info->topp_margin = d1 < d2 ? d1 : d2;
+          found = 1;
+          break;
+        }
+        above = cum;
+      }
+      if (!found) { /* rounding kept the total just below P: keep the whole top-k set */
+        tstar = use_k ? tk : scratch[V - 1];
+        info->topp_margin = 0.0;
+      }
     }
   }
   info->tstar = tstar;
@@ -260,12 +296,13 @@ int oracle_position_step(const double* p, const double* q, int V, int d, double 
 int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
                         const uint16_t* draft, const int32_t* cu_gamma,
                         const int32_t* draft_tokens, const float* temperature,
-                        const float* top_p, const uint32_t* seq_id,
+                        const float* top_p, const int32_t* top_k, const int32_t* eos_token,
+                        const int32_t* max_emit, const uint32_t* seq_id,
                         const int32_t* committed_len_in, int lead_slots, uint64_t seed,
                         const float* uniform_override, int32_t* out_tokens,
-                        int32_t* num_accepted, int32_t* committed_len_out, int32_t* seq_flags,
-                        double* probe_rows, double* probe_seq, double* margin_out,
-                        int nthreads) {
+                        int32_t* num_accepted, int32_t* num_emitted, int32_t* committed_len_out,
+                        int32_t* seq_flags, double* probe_rows, double* probe_seq,
+                        double* margin_out, int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -291,6 +328,9 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
       const uint32_t id = seq_id ? seq_id[b] : (uint32_t)b;
       const double T = (double)temperature[b];
       const double P = top_p ? (double)top_p[b] : 1.0;
+      const int K = top_k ? top_k[b] : 0;
+      const int eos = eos_token ? eos_token[b] : -1;
+      const int cap = max_emit ? max_emit[b] : 0;
       int flags = 0, n_acc = 0, y = -1;
       /* margin: smallest distance to a decision boundary among the acceptance tests and the
        * top-p cuts of the rows they use; dmargin: the same for the final draw. */
@@ -311,6 +351,7 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
       }
       if (bad) {
         num_accepted[b] = 0;
+        if (num_emitted) num_emitted[b] = 0;
         committed_len_out[b] = L;
         if (seq_flags) seq_flags[b] = flags;
         if (probe_seq) { probe_seq[2 * b] = NAN; probe_seq[2 * b + 1] = NAN; }
@@ -318,7 +359,7 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         continue;
       }
       orow_t ip, iq;
-      int stopped = 0;
+      int stopped = 0, drawn = 1; /* drawn: the round ends with a correction/bonus token */
       for (int k = 1; k <= g && !stopped; ++k) {
         const uint16_t* trow = target + (size_t)(trow0 + k - 1) * row_stride;
         const int d = draft_tokens[drow0 + k - 1];
@@ -327,18 +368,24 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         if (T == 0.0) {
           /* Greedy: accept iff the draft token is the target argmax; at the first mismatch
            * the target's argmax is emitted ([LI] §10.6.1 greedy special case; [KV] §4). */
-          oracle_dist(trow, V, 0.0, 1.0, p, scratch, &ip);
+          oracle_dist(trow, V, 0.0, 1.0, 0, p, scratch, &ip);
           int acc = (d == ip.argmax);
           if (pr) { pr[0] = acc ? 1.0 : 0.0; pr[1] = NAN; pr[2] = acc ? 1.0 : 0.0; }
-          if (acc) { n_acc = k; continue; }
+          if (acc) {
+            n_acc = k;
+            /* reading R19: an emitted EOS, or the emission cap, ends the round here */
+            if (d == eos) { flags |= OF_EOS; stopped = 1; drawn = 0; break; }
+            if (cap > 0 && k >= cap) { flags |= OF_LEN_CAP; stopped = 1; drawn = 0; break; }
+            continue;
+          }
           y = ip.argmax;
           py_out = 1.0;
           stopped = 1;
           break;
         }
         const uint16_t* drow = draft + (size_t)(drow0 + k - 1) * row_stride;
-        oracle_dist(trow, V, T, P, p, scratch, &ip);
-        oracle_dist(drow, V, T, P, q, scratch, &iq);
+        oracle_dist(trow, V, T, P, K, p, scratch, &ip);
+        oracle_dist(drow, V, T, P, K, q, scratch, &iq);
         if (ip.topp_margin < margin) margin = ip.topp_margin;
         if (iq.topp_margin < margin) margin = iq.topp_margin;
         double u_acc = uniform_override ? (double)uniform_override[ovr]
@@ -351,7 +398,12 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         if (pr) { pr[0] = p[d]; pr[1] = q[d]; pr[2] = info[0]; }
         double am = fabs(u_acc - info[0]);
         if (am < margin) margin = am;
-        if (acc) { n_acc = k; continue; }
+        if (acc) {
+          n_acc = k;
+          if (d == eos) { flags |= OF_EOS; stopped = 1; drawn = 0; break; }
+          if (cap > 0 && k >= cap) { flags |= OF_LEN_CAP; stopped = 1; drawn = 0; break; }
+          continue;
+        }
         dmargin = info[3];
         y = tok;
         R_out = info[1];
@@ -364,11 +416,11 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         const uint16_t* trow = target + (size_t)(trow0 + g) * row_stride;
         const size_t ovr = (size_t)(trow0 + g) * 2;
         if (T == 0.0) {
-          oracle_dist(trow, V, 0.0, 1.0, p, scratch, &ip);
+          oracle_dist(trow, V, 0.0, 1.0, 0, p, scratch, &ip);
           y = ip.argmax;
           py_out = 1.0;
         } else {
-          oracle_dist(trow, V, T, P, p, scratch, &ip);
+          oracle_dist(trow, V, T, P, K, p, scratch, &ip);
           if (ip.topp_margin < dmargin) dmargin = ip.topp_margin;
           double u = uniform_override ? (double)uniform_override[ovr + 1]
                                       : oracle_uniform(seed, id, (uint32_t)(L + g + 1), PURPOSE_BONUS);
@@ -380,8 +432,12 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         n_acc = g;
       }
       for (int k = 0; k < n_acc; ++k) out_tokens[trow0 + k] = draft_tokens[drow0 + k];
-      out_tokens[trow0 + n_acc] = y;
+      if (drawn) {
+        out_tokens[trow0 + n_acc] = y;
+        if (y == eos) flags |= OF_EOS;
+      }
       num_accepted[b] = n_acc;
+      if (num_emitted) num_emitted[b] = n_acc + drawn;
       committed_len_out[b] = L + lead_slots + n_acc; /* reading R10 ([KV] §6 pointer) */
       if (seq_flags) seq_flags[b] = flags;
       if (probe_seq) { probe_seq[2 * b] = R_out; probe_seq[2 * b + 1] = py_out; }
