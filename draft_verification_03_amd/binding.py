@@ -26,6 +26,7 @@ SPEC_ERR_WORKSPACE = -4
 
 FLAG_BAD_TOKEN, FLAG_Q_ZERO, FLAG_RESID_FALLBACK, FLAG_NO_ROW = 1, 2, 4, 8
 FLAG_SLOT_OOB, FLAG_BAD_TREE, FLAG_TOPP_SLOW, FLAG_BAD_PARAM = 16, 32, 64, 128
+FLAG_EOS, FLAG_LEN_CAP = 256, 512
 
 
 class spec_chain_args(ctypes.Structure):
@@ -36,7 +37,7 @@ class spec_chain_args(ctypes.Structure):
         ("temperature", _P), ("top_p", _P), ("top_k", _P), ("seq_id", _P),
         ("committed_len", _P), ("out_tokens", _P), ("num_accepted", _P), ("seq_flags", _P),
         ("probe_rows", _P), ("probe_seq", _P), ("uniform_override", _P),
-        ("profile_events", _P),
+        ("profile_events", _P), ("eos_token", _P), ("max_emit", _P), ("num_emitted", _P),
     ]
 
 
@@ -149,7 +150,8 @@ def chain_args(*, target_logits, cu_gamma, temperature, committed_len, out_token
                num_accepted, vocab, max_gamma, total_draft_rows, draft_logits=None,
                draft_tokens=None, top_p=None, seq_id=None, seq_flags=None, probe_rows=None,
                probe_seq=None, uniform_override=None, seed=0, lead_slots=1, row_stride=None,
-               profile_events=None, top_k=None):
+               profile_events=None, top_k=None, eos_token=None, max_emit=None,
+               num_emitted=None):
     """Fills a spec_chain_args from tensors (device) or raw pointers."""
     B = int(cu_gamma.shape[0]) - 1 if hasattr(cu_gamma, "shape") else None
     a = spec_chain_args()
@@ -176,9 +178,12 @@ def chain_args(*, target_logits, cu_gamma, temperature, committed_len, out_token
     a.probe_seq = _ptr(probe_seq)
     a.uniform_override = _ptr(uniform_override)
     a.profile_events = profile_events
+    a.eos_token = _ptr(eos_token)
+    a.max_emit = _ptr(max_emit)
+    a.num_emitted = _ptr(num_emitted)
     _keep(a, target_logits, draft_logits, cu_gamma, draft_tokens, temperature, top_p, top_k,
           seq_id, committed_len, out_tokens, num_accepted, seq_flags, probe_rows, probe_seq,
-          uniform_override)
+          uniform_override, eos_token, max_emit, num_emitted)
     return a
 
 

@@ -63,10 +63,14 @@ struct ChainParams {
   const int32_t* tokens;
   const float* temp;
   const float* topp;
+  const int32_t* topk;
+  const int32_t* eos;
+  const int32_t* cap;
   const uint32_t* sid;
   int32_t* committed;
   int32_t* out_tokens;
   int32_t* num_acc;
+  int32_t* num_emit;
   int32_t* flags_out;
   float* probe_rows;
   float* probe_seq;
@@ -116,6 +120,10 @@ struct SeqInfo {
   int32_t L;       // committed length on entry
   uint32_t id;     // Philox stream id
   float T, P;
+  int32_t K;       // top-k (<= 0 or >= V: off)
+  int32_t eos;     // EOS id (< 0: none)
+  int32_t cap;     // emission cap (<= 0: none)
+  bool filter;     // a top-k or top-p cut applies to this sequence's laws
   bool bad_param;
 };
 
@@ -129,10 +137,14 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
   s.id = P.sid ? P.sid[b] : (uint32_t)b;
   s.T = P.temp[b];
   s.P = P.topp ? P.topp[b] : 1.0f;
+  s.K = P.topk ? P.topk[b] : 0;
+  s.eos = P.eos ? P.eos[b] : -1;
+  s.cap = P.cap ? P.cap[b] : 0;
   s.bad_param = !(s.g >= 0 && s.g <= P.max_gamma && c0 >= 0 && c1 <= P.n_draft) ||
                 !temperature_ok(s.T) || !top_p_ok(s.P) ||
                 (s.T != 0.0f && s.g > 0 && P.draft == nullptr);
   if (s.T == 0.0f) s.T = 0.0f;  // -0 is greedy too
+  s.filter = s.T != 0.0f && (s.P < 1.0f || (s.K >= 1 && s.K < P.V));
   return s;
 }
 
@@ -156,6 +168,7 @@ __device__ __forceinline__ float weight(float l, float c, float nref) {
 struct RowLds {
   uint4 data[kCapN];               // captured vectors, in claim order
   unsigned long long hist[kHist];  // fixed-point masses by key offset below the row max
+  uint32_t hcnt[kHist];            // logits by key offset below the row max (top-k)
   NucEntry kept[kNucMax];          // nucleus entries before they are put in token order
   uint16_t idx[kCapN];             // vector index of each captured vector
   float wmax[kRowWgWaves];         // each wave's max so far, published for the others
@@ -291,14 +304,16 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int) {
   return wave_incl_scan_dpp_u64(v);
 }
 
-// First bucket (in increasing index = decreasing logit) at which base + the cumulative mass
-// reaches thr; -1 if the buckets never get there. *cum receives the cumulative mass at that
-// bucket (or base + the total). nb is a multiple of 64; each lane scans nb/64 buckets.
-__device__ int hist_crossing(const unsigned long long* h, int nb, uint64_t thr, uint64_t base,
-                             uint64_t* cum, int lane) {
-  const int per = nb / kWave;
+// The first bin, in increasing bin index (= decreasing logit), at which base + the running
+// sum of v reaches thr, over the wave's bins (PER per lane, bin = lane * PER + j); -1 if it
+// never does. *cum receives the running sum at that bin (or base + the total). Every lane
+// returns the same values.
+template <int PER>
+__device__ int lane_bins_crossing(const uint64_t v[PER], uint64_t base, uint64_t thr,
+                                  uint64_t* cum, int lane) {
   uint64_t mine = 0;
-  for (int j = 0; j < per; ++j) mine += h[lane * per + j];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) mine += v[j];
   const uint64_t incl = base + wave_incl_scan_u64(mine, lane);
   const uint64_t hit = __ballot(incl >= thr);
   if (!hit) {
@@ -307,21 +322,58 @@ __device__ int hist_crossing(const unsigned long long* h, int nb, uint64_t thr, 
   }
   const int src = __ffsll((long long)hit) - 1;
   int o = -1;
-  uint64_t c = 0;
-  if (lane == src) {
-    c = incl - mine;
-    for (int j = 0; j < per; ++j) {
-      c += h[lane * per + j];
-      if (c >= thr) {
-        o = lane * per + j;
-        break;
-      }
+  uint64_t c = incl - mine;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (o < 0) {
+      c += v[j];
+      if (c >= thr) o = lane * PER + j;
     }
   }
   o = __shfl(o, src, kWave);
   const uint32_t lo = __shfl((uint32_t)c, src, kWave), hi = __shfl((uint32_t)(c >> 32), src, kWave);
   *cum = ((uint64_t)hi << 32) | lo;
   return o;
+}
+
+// Sum over the wave of the lane's bins at or below bin index o.
+template <int PER>
+__device__ __forceinline__ uint64_t bins_upto(const uint64_t v[PER], int o, int lane) {
+  uint64_t s = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (lane * PER + j <= o) s += v[j];
+  return wave_sum_u64(s);
+}
+
+// The cut of a row's law: t = the logit of key offset o below the row max (o < 0: keep
+// every token), zs = the fixed-point mass of the kept set.
+struct Cut {
+  int o;
+  uint64_t zs;
+};
+
+// Top-k, then top-p, over per-bin counts and fixed-point masses held by the wave's lanes:
+// with top-k, the first bin at which the running count reaches K (the K-th largest logit,
+// repeats counted) and the mass up to it; then, with top-p, the first bin at which the
+// running mass reaches P times that mass (P times the row's mass without top-k). o < 0: a
+// crossing was not reached within the bins.
+template <int PER>
+__device__ Cut bins_cut(const uint64_t cnt[PER], const uint64_t ms[PER], bool use_k, int K,
+                        bool use_p, float P, float Z, int lane) {
+  Cut r{-1, 0};
+  uint64_t cum = 0;
+  if (use_k) {
+    r.o = lane_bins_crossing<PER>(cnt, 0, (uint64_t)K, &cum, lane);
+    if (r.o < 0) return r;
+    r.zs = bins_upto<PER>(ms, r.o, lane);
+  }
+  if (!use_p) return r;
+  const uint64_t thr = use_k ? (uint64_t)((double)P * (double)r.zs)
+                             : (uint64_t)((double)P * (double)Z * kFix);
+  r.o = lane_bins_crossing<PER>(ms, 0, thr, &cum, lane);
+  r.zs = cum;
+  return r;
 }
 
 // The captured vectors: LDS slots, then spilled indexes (whose vectors are read again from
@@ -397,22 +449,23 @@ __device__ int collect_wg(Src src, int n, int V, float t, float c, float nref, R
   return K;
 }
 
-// Exact threshold search over the whole row: the largest bf16 key t with
-// mass(key >= t) >= thrP, by a 256-bucket fixed-point histogram of the key offset's high byte
-// and then of its low byte inside the chosen bucket (two passes), plus one pass for the
-// nucleus list. Used when the captures missed the nucleus or overflowed. Every wave reads the
-// crossings from the shared histograms.
-__device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c, float M,
-                              uint64_t thrP, RowLds* L, NucEntry* list, int tid) {
+// Exact search over the whole row, by a radix over the key offset below the row max (its
+// high byte, then its low byte inside the chosen bucket; two passes): the first offset at
+// which the running count (by_count) or fixed-point mass of the tokens at or above it
+// reaches thr. *mass_at receives the running mass there (the row's whole mass if thr is not
+// reached; the return value is then -1). Every thread returns the same values.
+__device__ int radix_cut(const uint4* __restrict__ row, int nvec, int V, float c, float nref,
+                         uint32_t kM, bool by_count, uint64_t thr, uint64_t* mass_at,
+                         RowLds* L, int tid) {
   const int lane = tid % kWave;
-  const float nref = -M * c;
-  const uint32_t kM = key_of(M);
-  TopP r;
-  r.slow = true;
-  uint64_t cum = 0, base = 0;
-  int hi_b = -1, o_star = -1;
+  constexpr int PER = 256 / kWave;
+  int hi = -1;
+  uint64_t base_c = 0, base_m = 0;
   for (int pass = 0; pass < 2; ++pass) {
-    for (int j = tid; j < 256; j += kRowThreads) L->hist[j] = 0ull;
+    for (int j = tid; j < 256; j += kRowThreads) {
+      L->hist[j] = 0ull;
+      L->hcnt[j] = 0u;
+    }
     __syncthreads();
     for (int v = tid; v < nvec; v += kRowThreads) {
       float x[8];
@@ -421,45 +474,87 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
       for (int e = 0; e < 8; ++e) {
         if (v * 8 + e >= V) continue;
         const uint32_t o = kM - key_of(x[e]);
-        if (pass == 1 && (int)(o >> 8) != hi_b) continue;
+        if (pass == 1 && (int)(o >> 8) != hi) continue;
+        const uint32_t bin = pass == 0 ? (o >> 8) : (o & 255u);
+        atomicAdd(&L->hcnt[bin], 1u);
         const uint64_t fw = fixw(weight(x[e], c, nref));
-        if (fw) atomicAdd(&L->hist[pass == 0 ? (o >> 8) : (o & 255u)], (unsigned long long)fw);
+        if (fw) atomicAdd(&L->hist[bin], (unsigned long long)fw);
       }
     }
     __syncthreads();
-    if (pass == 0) {
-      hi_b = hist_crossing(L->hist, 256, thrP, 0, &cum, lane);
-      if (hi_b < 0) break;  // rounding left the whole row just below P: keep everything
-      base = cum - L->hist[hi_b];
-    } else {
-      o_star = hi_b * 256 + hist_crossing(L->hist, 256, thrP, base, &cum, lane);
+    uint64_t cnt[PER], ms[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      cnt[j] = L->hcnt[lane * PER + j];
+      ms[j] = L->hist[lane * PER + j];
     }
-    __syncthreads();  // the histogram is cleared again only after every wave has read it
+    __syncthreads();  // the bins are cleared again only after every wave has read them
+    uint64_t cum = 0;
+    const int o = lane_bins_crossing<PER>(by_count ? cnt : ms, by_count ? base_c : base_m, thr,
+                                          &cum, lane);
+    if (o < 0) {
+      *mass_at = base_m + (by_count ? bins_upto<PER>(ms, 255, lane) : cum - base_m);
+      return -1;
+    }
+    if (pass == 0) {
+      hi = o;
+      base_c += bins_upto<PER>(cnt, o - 1, lane);
+      base_m += bins_upto<PER>(ms, o - 1, lane);
+    } else {
+      *mass_at = base_m + bins_upto<PER>(ms, o, lane);
+      return hi * 256 + o;
+    }
   }
-  r.t = hi_b < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o_star);
-  r.zs = (float)((double)cum / kFix);
+  return -1;
+}
+
+// Exact top-k / top-p cut over the whole row (radix_cut for the K-th largest logit, then for
+// the top-p crossing), plus one pass for the nucleus list. Used when the captures missed the
+// cut or overflowed. A top-p crossing that rounding leaves unreached keeps the top-k set
+// (every token without top-k).
+__device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, float c, float M,
+                              bool use_k, int K, bool use_p, float P, float Z, RowLds* L,
+                              NucEntry* list, int tid) {
+  const float nref = -M * c;
+  const uint32_t kM = key_of(M);
+  TopP r;
+  r.slow = true;
+  int o = -1;
+  uint64_t zs = 0;
+  if (use_k) o = radix_cut(row, nvec, V, c, nref, kM, true, (uint64_t)K, &zs, L, tid);
+  if (use_p) {
+    const uint64_t thr = use_k ? (uint64_t)((double)P * (double)zs)
+                               : (uint64_t)((double)P * (double)Z * kFix);
+    uint64_t zp = 0;
+    const int op = radix_cut(row, nvec, V, c, nref, kM, false, thr, &zp, L, tid);
+    if (op >= 0 || !use_k) {
+      o = op;
+      zs = zp;
+    }
+  }
+  r.t = o < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o);
+  r.zs = (float)((double)zs / kFix);
   const int n = collect_wg(RowSrc{row}, nvec, V, r.t, c, nref, L, list, tid);
   r.nuc = n <= kNucMax ? n : -1;
   return r;
 }
 
-// Threshold search on the captured window: fixed-point masses of the captured logits in a
-// histogram over key offsets below the row max (cleared before the stream); the first offset
-// at which the running mass reaches P * Z is the threshold, found by every wave from the
-// same histogram (the same integer sums, so the same answer, with no barrier to hand it
-// out). Falls back to the whole row when the captures overflowed or the window does not
-// reach mass P within kHist offsets.
+// The cut on the captured window: fixed-point masses (and, with top-k, counts) of the
+// captured logits by key offset below the row max, in LDS bins cleared before the stream;
+// top-k and then top-p cross those bins, found by every wave from the same integer sums (so
+// the same answer, with no barrier to hand it out). Falls back to the whole row when the
+// captures overflowed or a crossing is not reached within the window's kHist offsets.
 __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V,
-                                            float c, float P, float capw, float M, float Z,
-                                            RowLds* L, const uint16_t* spill, NucEntry* list,
-                                            int tid) {
+                                            float c, bool use_k, int K, bool use_p, float P,
+                                            float capw, float M, float Z, RowLds* L,
+                                            const uint16_t* spill, NucEntry* list, int tid) {
   const int lane = tid % kWave;
   const float theta = M - capw;
   const float nref = -M * c;
-  const uint64_t thrP = (uint64_t)((double)P * (double)Z * kFix);
   const uint32_t kM = key_of(M);
   const int ntot = L->ncap;
-  if (ntot > kCapN + kCapG) return topp_full_row(row, nvec, V, c, M, thrP, L, list, tid);
+  if (ntot > kCapN + kCapG)
+    return topp_full_row(row, nvec, V, c, M, use_k, K, use_p, P, Z, L, list, tid);
   const CapSrc src{L, spill, row};
   for (int j = tid; j < ntot; j += kRowThreads) {
     int vi;
@@ -471,21 +566,29 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
     for (int e = 0; e < 8; ++e) {
       if (vi * 8 + e >= V || !(x[e] >= theta)) continue;
       const uint32_t o = kM - key_of(x[e]);
-      if (o < (uint32_t)kHist)
+      if (o < (uint32_t)kHist) {
+        if (use_k) atomicAdd(&L->hcnt[o], 1u);
         atomicAdd(&L->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
+      }
     }
   }
   __syncthreads();
-  uint64_t zs = 0;
-  const int o_star = hist_crossing(L->hist, kHist, thrP, 0, &zs, lane);
-  if (o_star < 0) {
-    __syncthreads();  // every wave has read the histogram before the fallback clears it
-    return topp_full_row(row, nvec, V, c, M, thrP, L, list, tid);
+  constexpr int PER = kHist / kWave;
+  uint64_t cnt[PER], ms[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    cnt[j] = use_k ? L->hcnt[lane * PER + j] : 0u;
+    ms[j] = L->hist[lane * PER + j];
+  }
+  const Cut cut = bins_cut<PER>(cnt, ms, use_k, K, use_p, P, Z, lane);
+  if (cut.o < 0) {
+    __syncthreads();  // every wave has read the bins before the fallback reuses them
+    return topp_full_row(row, nvec, V, c, M, use_k, K, use_p, P, Z, L, list, tid);
   }
   TopP r;
   r.slow = false;
-  r.t = value_of_key(kM - (uint32_t)o_star);
-  r.zs = (float)((double)zs / kFix);
+  r.t = value_of_key(kM - (uint32_t)cut.o);
+  r.zs = (float)((double)cut.zs / kFix);
   const int n = collect_wg(src, ntot, V, r.t, c, nref, L, list, tid);
   r.nuc = n <= kNucMax ? n : -1;
   return r;
@@ -500,7 +603,7 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
 // row p_k of draft position k, id 2(k-1)+1 its draft row q_k, and the last one the bonus row
 // p_{gamma_b+1} (needed only after a full accept, but read with the rest: one workgroup
 // cannot pull a row from HBM fast enough to do it later without stalling the resolve step).
-// TOPP: the batch carries a top-p array.
+// TOPP: the batch carries a top-p or top-k array (the captures and the cut are compiled in).
 // ----------------------------------------------------------------------------------------
 template <bool TOPP>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -534,15 +637,18 @@ void row_stats_kernel(ChainParams P) {
     }
   }
 
-  const bool topp = TOPP && s.T != 0.0f && s.P < 1.0f;
+  const bool filt = TOPP && s.filter;
   if (tid == 0) {
     L.trip = 0;
     L.ncap = 0;
     L.nkept = 0;
   }
   if (tid < kRowWgWaves) L.wmax[tid] = -INFINITY;
-  if (topp)
-    for (int i = tid; i < kHist; i += kRowThreads) L.hist[i] = 0ull;
+  if (filt)
+    for (int i = tid; i < kHist; i += kRowThreads) {
+      L.hist[i] = 0ull;
+      L.hcnt[i] = 0u;
+    }
   __syncthreads();
 
   if (s.T == 0.0f) {  // greedy: argmax of the target row, lowest index on ties
@@ -574,7 +680,7 @@ void row_stats_kernel(ChainParams P) {
   const float capw = kCaptureK * s.T;
   uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
-  if (topp)
+  if (filt)
     stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
@@ -596,11 +702,13 @@ void row_stats_kernel(ChainParams P) {
   float M, Z;
   row_mz(&L, c, M, Z);
   TopP tp{-INFINITY, Z, -1, false};
-  if (topp) tp = topp_select(rp, P.nvec, P.V, c, s.P, capw, M, Z, &L, spill, list, tid);
+  if (filt)
+    tp = topp_select(rp, P.nvec, P.V, c, s.K >= 1 && s.K < P.V, s.K, s.P < 1.0f, s.P, capw, M, Z,
+                     &L, spill, list, tid);
   if (tid == 0) {
     const float ld = __uint_as_float(ld_bits << 16);
     const float wd = (d >= 0 && ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;
-    *st = RowStat{M, tp.zs, tp.t, wd, -1, topp ? tp.nuc : -1,
+    *st = RowStat{M, tp.zs, tp.t, wd, -1, filt ? tp.nuc : -1,
                   tp.slow ? SPEC_FLAG_TOPP_SLOW : 0, 1};
   }
 }
@@ -943,6 +1051,7 @@ constexpr int kWgWaves = kResolveThreads / kWave;
 // Per-sequence decision state the resolve step shares through LDS.
 struct SeqDecision {
   int n_acc;
+  int drawn;  // the round ends with a residual or bonus token (no early stop)
   int flags;
   int bad;  // SPEC_FLAG_BAD_TOKEN / SPEC_FLAG_BAD_PARAM bits: no progress
   RowStat sp, sq;  // statistics of the rows at the first rejection (if any)
@@ -990,7 +1099,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   const bool stochastic = !s.bad_param && s.T != 0.0f;
   // The heads of the candidate rows' nucleus lists, fetched together with the statistics:
   // where the first rejection falls is not known yet, and the draw usually needs no more.
-  if (cu_ok && stochastic && P.topp) {
+  if (cu_ok && stochastic && (P.topp || P.topk)) {
     const int kk = tid / (2 * kPre), rr = (tid / kPre) & 1, j = tid % kPre;
     if (kk < kPreRows && kk < s.g)
       s_pre[kk][rr][j] = P.nuc[((size_t)(s.d0 + kk) * 2 + rr) * kNucMax + j];
@@ -1038,12 +1147,25 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
       }
     }
     const uint64_t rej = __ballot(in_g && acc == 0);
-    const int n_acc = rej ? __ffsll((long long)rej) - 1 : s.g;
-    int f = (lane < min(n_acc + 1, s.g)) ? rflags : 0;
+    int n_acc = rej ? __ffsll((long long)rej) - 1 : s.g;
+    // Early stop ("KV Cache 优化（四）" §5): emission ends after an accepted draft equal to
+    // the EOS id, or once the cap's worth of accepted drafts is out; the round then ends
+    // there, with no later test and no residual or bonus draw.
+    const uint64_t eos_at = __ballot(in_g && s.eos >= 0 && tok == s.eos && lane < n_acc);
+    int stop = eos_at ? __ffsll((long long)eos_at) : 0x7FFFFFFF;  // 1-based position
+    int stop_flag = SPEC_FLAG_EOS;
+    if (s.cap > 0 && s.cap < stop) {
+      stop = s.cap;
+      stop_flag = SPEC_FLAG_LEN_CAP;
+    }
+    const bool early = stop <= n_acc;
+    if (early) n_acc = stop;
+    int f = (lane < (early ? n_acc : min(n_acc + 1, s.g))) ? rflags : 0;  // tested positions
     for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
     if (lane == 0) {
       sd.n_acc = n_acc;
-      sd.flags = f;
+      sd.drawn = early ? 0 : 1;
+      sd.flags = f | (early ? stop_flag : 0);
       sd.bad = (bad_tok ? SPEC_FLAG_BAD_TOKEN : 0) | (s.bad_param ? SPEC_FLAG_BAD_PARAM : 0);
     }
     if (in_g && lane == n_acc) {  // the first rejected position
@@ -1057,10 +1179,27 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   if (sd.bad) {  // no progress: nothing emitted, pointer unchanged
     if (tid == 0) {
       P.num_acc[b] = 0;
+      if (P.num_emit) P.num_emit[b] = 0;
       if (P.flags_out) P.flags_out[b] = sd.bad;
       if (P.probe_seq) {
         P.probe_seq[2 * b] = NAN;
         P.probe_seq[2 * b + 1] = NAN;
+      }
+    }
+    return;
+  }
+  if (!sd.drawn) {  // stopped inside the accepted drafts: they are the round's output
+    if (wid == 0) {
+      if (lane < n_acc) P.out_tokens[s.t0 + lane] = P.tokens[s.d0 + lane];
+      if (lane == 0) {
+        P.num_acc[b] = n_acc;
+        if (P.num_emit) P.num_emit[b] = n_acc;
+        P.committed[b] = s.L + P.lead + n_acc;
+        if (P.flags_out) P.flags_out[b] = flags;
+        if (P.probe_seq) {
+          P.probe_seq[2 * b] = NAN;
+          P.probe_seq[2 * b + 1] = NAN;
+        }
       }
     }
     return;
@@ -1143,8 +1282,10 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   if (wid == 0) {
     if (lane < n_acc) P.out_tokens[s.t0 + lane] = P.tokens[s.d0 + lane];
     if (lane == 0) {
+      if (s.eos >= 0 && y == s.eos) flags |= SPEC_FLAG_EOS;
       P.out_tokens[s.t0 + n_acc] = y;
       P.num_acc[b] = n_acc;
+      if (P.num_emit) P.num_emit[b] = n_acc + 1;
       P.committed[b] = s.L + P.lead + n_acc;
       if (P.flags_out) P.flags_out[b] = flags;
       if (P.probe_seq) {
@@ -1175,10 +1316,14 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   P.tokens = a.draft_tokens;
   P.temp = a.temperature;
   P.topp = a.top_p;
+  P.topk = a.top_k;
+  P.eos = a.eos_token;
+  P.cap = a.max_emit;
   P.sid = a.seq_id;
   P.committed = a.committed_len;
   P.out_tokens = a.out_tokens;
   P.num_acc = a.num_accepted;
+  P.num_emit = a.num_emitted;
   P.flags_out = a.seq_flags;
   P.probe_rows = a.probe_rows;
   P.probe_seq = a.probe_seq;
@@ -1203,7 +1348,7 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   // per sequence: two rows (target, draft) per draft position slot k <= max_gamma, then the
   // bonus row
   const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
-  if (a.top_p)
+  if (a.top_p || a.top_k)
     hipLaunchKernelGGL(row_stats_kernel<true>, dim3(nrows), dim3(kRowThreads), 0, st, P);
   else
     hipLaunchKernelGGL(row_stats_kernel<false>, dim3(nrows), dim3(kRowThreads), 0, st, P);

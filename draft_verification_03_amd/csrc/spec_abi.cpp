@@ -64,7 +64,6 @@ int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspac
                 a->total_draft_rows);
   if (a->lead_slots != 0 && a->lead_slots != 1)
     return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
-  if (a->top_k) return fail(SPEC_ERR_UNSUPPORTED, "top_k is reserved and must be NULL");
   if (a->batch == 0) return SPEC_OK;
   if (!a->target_logits || !a->cu_gamma || !a->temperature || !a->committed_len ||
       !a->out_tokens || !a->num_accepted)

@@ -43,12 +43,12 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
 #define SPEC_ERR_INVALID_ARG (-1)  /* a host-visible argument is out of range            */
-#define SPEC_ERR_UNSUPPORTED (-2)  /* a reserved feature was requested (e.g. top_k)       */
+#define SPEC_ERR_UNSUPPORTED (-2)  /* a reserved feature was requested                   */
 #define SPEC_ERR_HIP (-3)          /* a HIP launch or event call failed                   */
 #define SPEC_ERR_WORKSPACE (-4)    /* workspace NULL, misaligned or smaller than required */
 
@@ -59,9 +59,12 @@ extern "C" {
 #define SPEC_FLAG_NO_ROW 8          /* tree walk stopped at a node without a target row     */
 #define SPEC_FLAG_SLOT_OOB 16       /* KV slot outside [0, slot_capacity): no progress      */
 #define SPEC_FLAG_BAD_TREE 32       /* parent/node_row malformed: no progress               */
-#define SPEC_FLAG_TOPP_SLOW 64      /* a top-p threshold needed the exact multi-pass search */
+#define SPEC_FLAG_TOPP_SLOW 64      /* a top-k/top-p threshold needed the exact multi-pass
+                                       search over the whole row                           */
 #define SPEC_FLAG_BAD_PARAM 128     /* T < 0, top_p outside (0,1], gamma_b out of range, or
                                        T > 0 with draft_logits NULL: no progress            */
+#define SPEC_FLAG_EOS 256           /* the round's last emitted token is the EOS id         */
+#define SPEC_FLAG_LEN_CAP 512       /* the emission cap cut the round short                 */
 
 /* ---- uniform purposes (third word of the Philox counter) ------------------------------- */
 #define SPEC_PURPOSE_ACCEPT 0
@@ -75,11 +78,15 @@ extern "C" {
  * Target row of (b, k), k = 1..gamma_b+1, is cu_gamma[b] + b + k - 1 (p_k predicts the k-th
  * new token); draft row of (b, k), k = 1..gamma_b, is cu_gamma[b] + k - 1.
  *
- * Per sequence, with L = committed_len[b] on entry, T = temperature[b], P = top_p[b]:
- *  - laws: p_k = top-p_P(softmax(target row / T)), q_k likewise from the draft row (the same
- *    T and P; "KV Cache 优化（四）" §4). Top-p keeps every token whose logit is >= t*, t* the
- *    largest logit value at which the mass of all tokens at or above it reaches P. T = 0 is
- *    greedy: p_k is one-hot at the target argmax (lowest id on ties) and q is not read.
+ * Per sequence, with L = committed_len[b] on entry, T = temperature[b], P = top_p[b],
+ * K = top_k[b]:
+ *  - laws: p_k = top-p_P(top-k_K(softmax(target row / T))), q_k likewise from the draft row
+ *    (the same T, K and P; "KV Cache 优化（四）" §4 names top-k/top-p). Top-k keeps every token
+ *    whose logit is >= the K-th largest logit (repeats counted, so ties at the boundary are
+ *    kept); K <= 0 or K >= V keeps all. Top-p then keeps every token whose logit is >= t*,
+ *    t* the largest logit value at which the mass of all kept tokens at or above it reaches
+ *    P of the top-k set's mass. T = 0 is greedy: p_k is one-hot at the target argmax (lowest
+ *    id on ties) and q is not read.
  *  - test: a_k = min(1, p_k(d_k)/q_k(d_k)) (eq. a(x)); where q_k(d_k) = 0, a_k = [p_k(d_k) > 0]
  *    and SPEC_FLAG_Q_ZERO is set; accept iff u_acc < a_k, u_acc = U(L+k, ACCEPT). Greedy:
  *    accept iff d_k equals the target argmax.
@@ -89,7 +96,13 @@ extern "C" {
  *  - all accepted: a bonus draw from p_{gamma_b+1} with u = U(L+gamma_b+1, BONUS) ("KV Cache
  *    优化（四）" §5). Greedy: the argmax. gamma_b = 0 is allowed: the round is one draw from
  *    p_1 -- which is also how a drafter can draw its own tokens through this call.
- *  - outputs: out_tokens[target row (b, 1..n+1)] = d_1..d_n, y; num_accepted[b] = n;
+ *  - early stop ("KV Cache 优化（四）" §5: EOS and the length cap end a round early): the
+ *    round emits the accepted drafts in order, then y; emission stops after the first
+ *    emitted token equal to eos_token[b] (SPEC_FLAG_EOS) and after max_emit[b] tokens
+ *    (SPEC_FLAG_LEN_CAP when that cuts the round short). A stop inside the accepted drafts
+ *    ends the round there: no later position is tested and no y is drawn.
+ *  - outputs: out_tokens[target row (b, 1..m)] = the m emitted tokens (d_1..d_n, then y if
+ *    drawn); num_accepted[b] = n (accepted drafts emitted); num_emitted[b] = m (n or n+1);
  *    committed_len[b] = L + lead_slots + n (pointer-only rollback, "KV Cache 优化（四）" §6:
  *    no KV byte moves; the rejected drafts' slots are simply past the pointer).
  *  U(pos, purpose) = Philox4x32-10 with key (seed low 32 bits, seed high 32 bits), counter
@@ -109,10 +122,11 @@ typedef struct spec_chain_args {
   const int32_t* draft_tokens;   /* [total_draft_rows]; may be NULL if total_draft_rows = 0  */
   const float* temperature;      /* [B], >= 0                                                */
   const float* top_p;            /* [B] in (0, 1], or NULL = no top-p                        */
-  const int32_t* top_k;          /* reserved: must be NULL (else SPEC_ERR_UNSUPPORTED)       */
+  const int32_t* top_k;          /* [B] or NULL = no top-k; K <= 0 or K >= vocab: off        */
   const uint32_t* seq_id;        /* [B] Philox stream ids, or NULL = b                       */
   int32_t* committed_len;        /* [B] in/out: L on entry, L + lead_slots + n on exit       */
-  int32_t* out_tokens;           /* [total_draft_rows + B]; entries past n+1 are untouched   */
+  int32_t* out_tokens;           /* [total_draft_rows + B]; entries past the m emitted tokens
+                                    of a sequence are untouched                              */
   int32_t* num_accepted;         /* [B]                                                      */
   int32_t* seq_flags;            /* [B] or NULL                                              */
   float* probe_rows;             /* [total_draft_rows][3] or NULL: {p_k(d_k), q_k(d_k), a_k}
@@ -124,6 +138,9 @@ typedef struct spec_chain_args {
                                     in place of the Philox uniforms                          */
   void* profile_events;          /* NULL, or a host array of 2 hipEvent_t recorded on the
                                     stream just before and just after the row pass kernel   */
+  const int32_t* eos_token;      /* [B] or NULL: a sequence's EOS id (< 0: none)              */
+  const int32_t* max_emit;       /* [B] or NULL: most tokens the round may emit (<= 0: no cap) */
+  int32_t* num_emitted;          /* [B] or NULL: tokens emitted this round                   */
 } spec_chain_args;
 
 /*

@@ -50,9 +50,10 @@ def draft_tokens_oracle(x, seed_draft=9090):
     k_of = np.arange(n) - cu[b_of]
     T = x["temperature"][b_of]
     P = None if x["top_p"] is None else x["top_p"][b_of]
+    K = None if x.get("top_k") is None else x["top_k"][b_of]
     return oracle.draw_tokens(x["draft"][:, :x["stride"]], T, P, seed_draft,
                               x["seq_id"][b_of], x["committed_len"][b_of] + k_of,
-                              vocab=x["vocab"])
+                              vocab=x["vocab"], top_k=K)
 
 
 def run_oracle_chain(x, tokens, seed, override=None, lead=1, nthreads=0):
@@ -60,7 +61,8 @@ def run_oracle_chain(x, tokens, seed, override=None, lead=1, nthreads=0):
                                  x["temperature"], x["top_p"], x["seq_id"],
                                  x["committed_len"], lead_slots=lead, seed=seed,
                                  uniform_override=override, nthreads=nthreads,
-                                 vocab=x["vocab"])
+                                 vocab=x["vocab"], top_k=x.get("top_k"),
+                                 eos_token=x.get("eos_token"), max_emit=x.get("max_emit"))
 
 
 def run_gpu_chain(x, tokens, seed, override=None, lead=1, probes=True, no_draft=False,
@@ -75,6 +77,10 @@ def run_gpu_chain(x, tokens, seed, override=None, lead=1, probes=True, no_draft=
         cu=dev(cu), tok=dev(tokens if n_d else np.zeros(1, np.int32)),
         temp=dev(x["temperature"]),
         topp=None if x["top_p"] is None else dev(x["top_p"]),
+        topk=None if x.get("top_k") is None else dev(x["top_k"]),
+        eos=None if x.get("eos_token") is None else dev(x["eos_token"]),
+        cap=None if x.get("max_emit") is None else dev(x["max_emit"]),
+        nemit=torch.full((Bn,), -7, dtype=torch.int32, device="cuda"),
         sid=dev(x["seq_id"]), L=dev(x["committed_len"]),
         out=torch.full((max(n_t, 1),), -1, dtype=torch.int32, device="cuda"),
         nacc=torch.full((Bn,), -7, dtype=torch.int32, device="cuda"),
@@ -89,10 +95,12 @@ def run_gpu_chain(x, tokens, seed, override=None, lead=1, probes=True, no_draft=
                      num_accepted=t["nacc"], seq_flags=t["flags"], probe_rows=t["pr"],
                      probe_seq=t["ps"], uniform_override=t["ovr"], seed=seed, lead_slots=lead,
                      vocab=x["vocab"], max_gamma=max(int(np.diff(cu).max()) if Bn else 0, 0),
-                     total_draft_rows=n_d, row_stride=x["stride"])
+                     total_draft_rows=n_d, row_stride=x["stride"], top_k=t["topk"],
+                     eos_token=t["eos"], max_emit=t["cap"], num_emitted=t["nemit"])
     B.spec_verify_chain(a, workspace=workspace)
     torch.cuda.synchronize()
     return dict(out_tokens=t["out"].cpu().numpy()[:n_t], num_accepted=t["nacc"].cpu().numpy(),
+                num_emitted=t["nemit"].cpu().numpy(),
                 committed_len=t["L"].cpu().numpy(), seq_flags=t["flags"].cpu().numpy(),
                 probe_rows=None if not probes else t["pr"].cpu().numpy()[:n_d].astype(np.float64),
                 probe_seq=None if not probes else t["ps"].cpu().numpy().astype(np.float64))
@@ -128,11 +136,15 @@ def compare_chain(x, o, g, exact=False, probes=True):
         if o["seq_flags"][b] & (B.FLAG_BAD_TOKEN | B.FLAG_BAD_PARAM):
             continue
         t0 = int(cu[b]) + b
-        m = n + 1 if full else n
+        ne = int(o["num_emitted"][b])
+        drawn = ne == n + 1  # no early stop inside the accepted drafts
+        if full:
+            assert g["num_emitted"][b] == ne, ctx
+        m = ne if full else n
         assert np.array_equal(g["out_tokens"][t0:t0 + m], o["out_tokens"][t0:t0 + m]), ctx
         if probes and g["probe_rows"] is not None:
             gb = int(cu[b + 1] - cu[b])
-            tested = min(n + 1, gb)
+            tested = min(n + 1, gb) if drawn else n
             d0 = int(cu[b])
             tol = 0.0 if exact else PROB_TOL
             assert _close(g["probe_rows"][d0:d0 + tested], o["probe_rows"][d0:d0 + tested],

@@ -67,7 +67,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_abi_version_and_workspace_sizes():
-    assert B.spec_abi_version() == 1
+    assert B.spec_abi_version() == 2
     assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
     assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
     assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
@@ -109,7 +109,6 @@ def _call_chain(a, ws=0x100000, nbytes=1 << 30):
     (dict(num_accepted=None), B.SPEC_ERR_INVALID_ARG),
     (dict(draft_tokens=None), B.SPEC_ERR_INVALID_ARG),
     (dict(target_logits=0x1002), B.SPEC_ERR_INVALID_ARG),
-    (dict(top_k=0x9000), B.SPEC_ERR_UNSUPPORTED),
 ])
 def test_chain_validation(kw, code):
     assert _call_chain(_chain(**kw)) == code
