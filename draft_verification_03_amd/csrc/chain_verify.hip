@@ -40,6 +40,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Top-p capture window: logits within kCaptureK * T of the row max (weight >= e^-7 of the
 // largest). Rows whose nucleus reaches further down take the exact multi-pass search.
 constexpr float kCaptureK = 7.0f;
+// With top-k the window is wider (the K-th largest logit often lies below 7 * T); rows whose
+// window still holds fewer than K logits capture again from a lower bound of the K-th largest.
+constexpr float kCaptureKTopK = 10.0f;
 constexpr int kCapN = 512;         // captured vectors per row held in LDS
 constexpr int kCapG = 1024;        // further captured vector ids per row spilled to the workspace
 constexpr int kDepth = 2;          // trips of loads in flight per wave in the row pass
@@ -172,6 +175,7 @@ struct RowLds {
   NucEntry kept[kNucMax];          // nucleus entries before they are put in token order
   uint16_t idx[kCapN];             // vector index of each captured vector
   float wmax[kRowWgWaves];         // each wave's max so far, published for the others
+  float lmax[kRowThreads];         // every lane's max at the end of the stream
   float pm[kRowWgWaves];           // per-wave max (value of the argmax for greedy rows)
   float pz[kRowWgWaves];           // per-wave sum of weights relative to the wave max
   int pa[kRowWgWaves];             // per-wave argmax (greedy rows)
@@ -539,22 +543,19 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
   return r;
 }
 
-// The cut on the captured window: fixed-point masses (and, with top-k, counts) of the
-// captured logits by key offset below the row max, in LDS bins cleared before the stream;
-// top-k and then top-p cross those bins, found by every wave from the same integer sums (so
-// the same answer, with no barrier to hand it out). Falls back to the whole row when the
-// captures overflowed or a crossing is not reached within the window's kHist offsets.
-__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V,
-                                            float c, bool use_k, int K, bool use_p, float P,
-                                            float capw, float M, float Z, RowLds* L,
-                                            const uint16_t* spill, NucEntry* list, int tid) {
+// The cut on the captured vectors, which hold every logit >= theta of the row: fixed-point
+// masses (and, with top-k, counts) of those logits by key offset below the row max, in LDS
+// bins cleared beforehand; top-k and then top-p cross those bins, found by every wave from
+// the same integer sums (so the same answer, with no barrier to hand it out). o < 0: a
+// crossing is not reached within the kHist offsets (or the logits >= theta).
+__device__ __forceinline__ Cut capture_cut(const uint4* __restrict__ row, int V, float c,
+                                           float theta, float M, bool use_k, int K, bool use_p,
+                                           float P, float Z, RowLds* L, const uint16_t* spill,
+                                           int tid) {
   const int lane = tid % kWave;
-  const float theta = M - capw;
   const float nref = -M * c;
   const uint32_t kM = key_of(M);
   const int ntot = L->ncap;
-  if (ntot > kCapN + kCapG)
-    return topp_full_row(row, nvec, V, c, M, use_k, K, use_p, P, Z, L, list, tid);
   const CapSrc src{L, spill, row};
   for (int j = tid; j < ntot; j += kRowThreads) {
     int vi;
@@ -580,18 +581,90 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
     cnt[j] = use_k ? L->hcnt[lane * PER + j] : 0u;
     ms[j] = L->hist[lane * PER + j];
   }
-  const Cut cut = bins_cut<PER>(cnt, ms, use_k, K, use_p, P, Z, lane);
-  if (cut.o < 0) {
-    __syncthreads();  // every wave has read the bins before the fallback reuses them
-    return topp_full_row(row, nvec, V, c, M, use_k, K, use_p, P, Z, L, list, tid);
-  }
-  TopP r;
-  r.slow = false;
-  r.t = value_of_key(kM - (uint32_t)cut.o);
-  r.zs = (float)((double)cut.zs / kFix);
-  const int n = collect_wg(src, ntot, V, r.t, c, nref, L, list, tid);
-  r.nuc = n <= kNucMax ? n : -1;
+  return bins_cut<PER>(cnt, ms, use_k, K, use_p, P, Z, lane);
+}
+
+// The K-th largest of the workgroup's lane maxima (K <= kRowThreads): K distinct logits of
+// the row are at or above it, so it is a lower bound of the row's K-th largest logit.
+__device__ float lane_max_kth(RowLds* L, int K, int tid) {
+  const int lane = tid % kWave, w = tid / kWave;
+  const float v = L->lmax[tid];
+  int n = 0;
+  for (int i = 0; i < kRowThreads; ++i) n += L->lmax[i] >= v;
+  const float best = wave_max_dpp(n >= K ? v : -INFINITY);
+  if (lane == 0) L->pm[w] = best;  // the waves' partials are no longer needed
+  __syncthreads();
+  float r = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kRowWgWaves; ++i) r = fmaxf(r, L->pm[i]);
   return r;
+}
+
+// A second capture of the row: every vector whose max is >= vk, in the same LDS slots and
+// spill list (cleared first, as are the bins).
+__device__ void recapture(const uint4* __restrict__ row, int nvec, int V, float vk, RowLds* L,
+                          uint16_t* spill, int tid) {
+  const int lane = tid % kWave;
+  __syncthreads();  // every thread is done with the first capture and its bins
+  if (tid == 0) L->ncap = 0;
+  for (int i = tid; i < kHist; i += kRowThreads) {
+    L->hist[i] = 0ull;
+    L->hcnt[i] = 0u;
+  }
+  __syncthreads();
+  for (int v0 = tid - lane; v0 < nvec; v0 += kRowThreads) {
+    const int v = v0 + lane;
+    uint4 d[kU] = {};
+    float vm[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) vm[u] = -INFINITY;
+    if (v < nvec) {
+      d[0] = row[v];
+      float x[8];
+      unpack8(d[0], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (v * 8 + e >= V) x[e] = -INFINITY;
+      vm[0] = max8(x);
+    }
+    // one vector per lane: the trip layout's first slot (vid = v0 + lane)
+    capture_trip(L, spill, d, vm, vmax3(vk, -3.4028235e38f, -3.4028235e38f), v0, lane);
+  }
+  __syncthreads();
+}
+
+// Threshold search for a row with a top-k and/or top-p cut: on the captured window; with
+// top-k and too few logits in the window, on a second capture from a lower bound of the
+// K-th largest logit; else (captures overflowed, or a crossing past the bins) over the whole
+// row.
+__device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int nvec, int V,
+                                            float c, bool use_k, int K, bool use_p, float P,
+                                            float capw, float M, float Z, RowLds* L,
+                                            uint16_t* spill, NucEntry* list, int tid) {
+  const float nref = -M * c;
+  const uint32_t kM = key_of(M);
+  bool held = L->ncap <= kCapN + kCapG, again = false;
+  if (held) {
+    Cut cut = capture_cut(row, V, c, M - capw, M, use_k, K, use_p, P, Z, L, spill, tid);
+    if (cut.o < 0 && use_k && K <= kRowThreads) {
+      again = true;
+      const float vk = lane_max_kth(L, K, tid);
+      recapture(row, nvec, V, vk, L, spill, tid);
+      held = L->ncap <= kCapN + kCapG;
+      if (held) cut = capture_cut(row, V, c, vk, M, use_k, K, use_p, P, Z, L, spill, tid);
+    }
+    if (held && cut.o >= 0) {
+      TopP r;
+      r.slow = again;  // a second read of the row
+      r.t = value_of_key(kM - (uint32_t)cut.o);
+      r.zs = (float)((double)cut.zs / kFix);
+      const int n = collect_wg(CapSrc{L, spill, row}, L->ncap, V, r.t, c, nref, L, list, tid);
+      r.nuc = n <= kNucMax ? n : -1;
+      return r;
+    }
+    __syncthreads();  // every wave has read the bins before the whole-row search reuses them
+  }
+  return topp_full_row(row, nvec, V, c, M, use_k, K, use_p, P, Z, L, list, tid);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -677,7 +750,8 @@ void row_stats_kernel(ChainParams P) {
 
   const uint32_t ld_bits = (tid == 0 && d >= 0) ? base[d] : 0u;  // the draft token's logit
   const float c = kLog2e / s.T;
-  const float capw = kCaptureK * s.T;
+  const bool use_k = s.K >= 1 && s.K < P.V;
+  const float capw = (use_k ? kCaptureKTopK : kCaptureK) * s.T;
   uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
   if (filt)
@@ -697,14 +771,15 @@ void row_stats_kernel(ChainParams P) {
       L.pm[w] = Mw;
       L.pz[w] = Zw;
     }
+    if (filt) L.lmax[tid] = acc.m;
   }
   __syncthreads();
   float M, Z;
   row_mz(&L, c, M, Z);
   TopP tp{-INFINITY, Z, -1, false};
   if (filt)
-    tp = topp_select(rp, P.nvec, P.V, c, s.K >= 1 && s.K < P.V, s.K, s.P < 1.0f, s.P, capw, M, Z,
-                     &L, spill, list, tid);
+    tp = topp_select(rp, P.nvec, P.V, c, use_k, s.K, s.P < 1.0f, s.P, capw, M, Z, &L, spill,
+                     list, tid);
   if (tid == 0) {
     const float ld = __uint_as_float(ld_bits << 16);
     const float wd = (d >= 0 && ld >= tp.t) ? weight(ld, c, -M * c) : 0.0f;

@@ -59,8 +59,8 @@ extern "C" {
 #define SPEC_FLAG_NO_ROW 8          /* tree walk stopped at a node without a target row     */
 #define SPEC_FLAG_SLOT_OOB 16       /* KV slot outside [0, slot_capacity): no progress      */
 #define SPEC_FLAG_BAD_TREE 32       /* parent/node_row malformed: no progress               */
-#define SPEC_FLAG_TOPP_SLOW 64      /* a top-k/top-p threshold needed the exact multi-pass
-                                       search over the whole row                           */
+#define SPEC_FLAG_TOPP_SLOW 64      /* a top-k/top-p threshold needed another read of a row
+                                       (a second capture, or the exact multi-pass search)   */
 #define SPEC_FLAG_BAD_PARAM 128     /* T < 0, top_p outside (0,1], gamma_b out of range, or
                                        T > 0 with draft_logits NULL: no progress            */
 #define SPEC_FLAG_EOS 256           /* the round's last emitted token is the EOS id         */
