@@ -43,7 +43,7 @@ constexpr float kCaptureK = 7.0f;
 // With top-k the window is wider (the K-th largest logit often lies below 7 * T); rows whose
 // window still holds fewer than K logits capture again from a lower bound of the K-th largest.
 constexpr float kCaptureKTopK = 10.0f;
-constexpr int kCapN = 512;         // captured vectors per row held in LDS
+constexpr int kCapN = 1024;        // captured vectors per row held in LDS
 constexpr int kCapG = 1024;        // further captured vector ids per row spilled to the workspace
 constexpr int kDepth = 2;          // trips of loads in flight per wave in the row pass
 constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per workgroup)
