@@ -69,6 +69,9 @@ class SpecError(RuntimeError):
 
 _lib = None
 
+# Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
+ABI_VERSION = 2
+
 
 def lib_path() -> str:
     return _build.LIB
@@ -94,6 +97,9 @@ def lib():
         L.spec_verify_tree.restype = ctypes.c_int
         L.kv_commit_path.argtypes = [ctypes.POINTER(spec_kv_args), _P]
         L.kv_commit_path.restype = ctypes.c_int
+        if L.spec_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{_build.LIB} has ABI version {L.spec_abi_version()}, the "
+                               f"binding expects {ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 
