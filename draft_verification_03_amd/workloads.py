@@ -20,6 +20,10 @@ draft tree of "投机推理：小模型搭树，大模型一次验证"):
 * ``tree``    -- B=128, V=151936, 13-node tree (root + [6], [2,2], [1,1]), 5 target rows per
   sequence, target N(0, 2^2), draft rows = target + N(0, 0.5^2); KV cache 32 layers x 8 KV
   heads x head_dim 128, 1024 slots.
+* ``tree_draft`` -- the drafting side of the same tree: top_head [1, 2, 2], top_k_spec [[6],
+  [2, 2], [1, 1]] ("投机推理" tree configuration section), B=128, V=151936; step s has
+  B * top_head[s] draft rows of N(0, 2^2) logits; root tokens uniform, root positions
+  L_b ~ U{0..1010}.
 
 Every chain workload has committed lengths L_b ~ U{0..4095} and seq_id = b.
 """
@@ -63,7 +67,7 @@ CHAIN_CONFIGS = {
                noise=(0.3, 1.5), T=(0.5, 1.2), top_p=None),
 }
 
-SEEDS = {"markov": 101, "c2": 202, "c3": 303, "tree": 404, "c5": 505}
+SEEDS = {"markov": 101, "c2": 202, "c3": 303, "tree": 404, "c5": 505, "tree_draft": 606}
 
 
 def _pool_map(fn, n):
@@ -250,6 +254,33 @@ def tree_inputs(seed: int | None = None, B: int = 128, V: int = 151936,
     return dict(logits=logits, parent=parent, node_row=node_row, node_token=node_token,
                 rows_per_seq=R, num_nodes=N, max_depth=3, vocab=V, stride=st,
                 committed_len=L)
+
+
+TREE_SHAPE = dict(top_head=(1, 2, 2), top_k_spec=((6,), (2, 2), (1, 1)))
+
+
+def tree_draft_inputs(seed: int | None = None, B: int = 128, V: int = 151936,
+                      top_head=TREE_SHAPE["top_head"], top_k_spec=TREE_SHAPE["top_k_spec"],
+                      sigma: float = 2.0, quant: float | None = None, stride: int | None = None,
+                      max_len: int = 1010) -> dict:
+    """Draft rows of one tree-drafting round: for step s, ``B * top_head[s]`` rows of
+    N(0, sigma^2) logits (row b * top_head[s] + j follows the j-th node expanded for sequence
+    b). ``quant`` rounds the logits to multiples of 1/quant first (many exact ties). Root
+    tokens are uniform over the vocabulary, root positions L_b ~ U{0..max_len}."""
+    rng = np.random.default_rng(SEEDS["tree_draft"] if seed is None else seed)
+    st = round_up(V, 8) if stride is None else stride
+    rows = []
+    for h in top_head:
+        x = rng.standard_normal((B * h, V), dtype=np.float32) * np.float32(sigma)
+        if quant:
+            x = np.round(x * quant) / np.float32(quant)
+        r = np.zeros((B * h, st), dtype=np.uint16)
+        r[:, :V] = bf16_bits(x)
+        rows.append(r)
+    return dict(rows=rows, top_head=tuple(top_head), top_k_spec=tuple(map(tuple, top_k_spec)),
+                root_token=rng.integers(0, V, size=B).astype(np.int32),
+                pos_base=rng.integers(0, max_len + 1, size=B).astype(np.int32), vocab=V,
+                stride=st, batch=B)
 
 
 # --------------------------------------------------------------------------------------

@@ -72,6 +72,9 @@ def _declare(L):
     L.oracle_kv_commit.argtypes = [_I, _I, _I, _I, _P, _P, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, _I, _I, _I, _P, _P, _P, _P]
     L.oracle_kv_commit.restype = _I
+    L.oracle_tree_draft.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                                    _P, _P, _P, _I, _P, _I]
+    L.oracle_tree_draft.restype = _I
 
 
 class _RowInfo(ctypes.Structure):
@@ -259,3 +262,49 @@ def kv_commit(k_layers, v_layers, path_nodes, path_len, committed_len, lead_slot
                            int(S if slot_capacity is None else slot_capacity), int(lead_slots),
                            int(max_depth), _ptr(pn), _ptr(pl), _ptr(cl), _ptr(fl))
     return cl, fl
+
+
+def tree_nodes(top_head, top_k_spec):
+    """Number of nodes (root included) of a tree with this configuration."""
+    return 1 + sum(sum(k) for k in top_k_spec[:len(top_head)])
+
+
+def tree_draft(rows_by_step, top_head, top_k_spec, root_token, pos_base=None, tree_stride=None,
+               vocab=None, nthreads=0):
+    """Builds the draft trees of a batch (reading R20 of spec_oracle.c).
+
+    rows_by_step[s]: uint16 [B * top_head[s], row_stride], row b * top_head[s] + j holding the
+    draft logits after the j-th node expanded at step s. top_k_spec[s]: top_head[s] child
+    counts. Returns parent, node_token, node_row, node_logp (fp64), position_ids, ancestor
+    (uint8 [B, n, n]), expand ([depth, B, max head]) and select_margin ([depth, B]); raises
+    ValueError for an invalid configuration.
+    """
+    depth = len(top_head)
+    rows = np.concatenate([_c(r, np.uint16) for r in rows_by_step[:depth]], axis=0)
+    rt = _c(root_token, np.int32)
+    B = rt.shape[0]
+    stride = rows.shape[1]
+    V = stride if vocab is None else int(vocab)
+    n = tree_nodes(top_head, top_k_spec)
+    ts = n if tree_stride is None else int(tree_stride)
+    th = np.asarray(top_head, np.int32)
+    ks = np.asarray([k for s in range(depth) for k in top_k_spec[s]], np.int32)
+    es = int(th.max())
+    out = {
+        "parent": np.zeros((B, ts), np.int32), "node_token": np.zeros((B, ts), np.int32),
+        "node_row": np.zeros((B, ts), np.int32), "node_logp": np.zeros((B, ts), np.float64),
+        "position_ids": np.zeros((B, ts), np.int32),
+        "ancestor": np.zeros((B, ts, ts), np.uint8),
+        "expand": np.full((depth, B, es), -1, np.int32),
+        "select_margin": np.zeros((depth, B), np.float64),
+    }
+    rc = lib().oracle_tree_draft(B, V, stride, depth, _ptr(th), _ptr(ks), _ptr(rows), _ptr(rt),
+                                 _ptr(_c(pos_base, np.int32)), ts, _ptr(out["parent"]),
+                                 _ptr(out["node_token"]), _ptr(out["node_row"]),
+                                 _ptr(out["node_logp"]), _ptr(out["position_ids"]),
+                                 _ptr(out["ancestor"]), _ptr(out["expand"]), es,
+                                 _ptr(out["select_margin"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("invalid tree configuration")
+    out["num_nodes"] = n
+    return out

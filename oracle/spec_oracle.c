@@ -52,6 +52,19 @@
  *       tested and no correction or bonus token is drawn; n_acc counts the emitted drafts
  *       and the committed length follows R10 with that n_acc. eos < 0 and max_emit <= 0
  *       switch the respective stop off.
+ *   R20 tree drafting ([TR] tree configuration and draft steps): an expanded node's children
+ *       are the K tokens of largest draft logit, ties to the lower token id (a rank cut:
+ *       exactly K children, as the page's node counts 6 + 4 + 2 require). A node's path
+ *       probability is the product of the draft softmax probabilities (temperature 1, no
+ *       filter) of the tokens on its path below the root. The nodes expanded at the next
+ *       step are the top_head[s+1] nodes of the newest layer with the largest path
+ *       probability, ties to the lower node index, in descending order; the j-th of them
+ *       gets top_k_spec[s+1][j] children. Nodes are numbered root 0, then layer by layer,
+ *       within a layer by the rank of the parent and then of the child. Target rows belong
+ *       to the expanded nodes in expansion order (root row 0). The ancestor mask lets node
+ *       i see node j iff j is i or an ancestor of i, and a node's position is the root's
+ *       plus its depth ([LI] §10.6.3, Table 10-17). The selection compares path
+ *       log-probabilities rounded to binary32, the precision the GPU library decides in.
  */
 #include <math.h>
 #include <stdint.h>
@@ -550,6 +563,168 @@ int oracle_kv_commit(int B, int num_layers, int num_kv_heads, int head_dim,
         }
     }
     committed_len[b] = L + lead_slots + D;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Tree drafting ([TR] sections on the tree configuration and on the three draft steps;   */
+/* [LI] §10.6.3 tree drafts and Table 10-17). Reading R20.                                 */
+/* rows holds the draft rows of steps 0..depth-1 in order; step s contributes B*top_head[s] */
+/* rows, row (b, j) being the draft model's logits after the j-th node expanded at step s.  */
+/* top_k_spec concatenates top_k_spec[s][0..top_head[s]) over s. Per sequence (tree_stride  */
+/* entries apart): parent, node_token, node_row, node_logp (natural log of the path        */
+/* probability), position_ids, and ancestor[i*tree_stride + j] = 1 iff node i sees node j. */
+/* expand[(s*B + b)*expand_stride + j] = the j-th node expanded at step s; select_margin   */
+/* [s*B + b] = the smallest nonzero gap between neighbouring path log-probabilities among  */
+/* the first top_head[s]+1 of the ranked layer (+inf for step 0: the root is fixed).       */
+/* Returns 0, or -1 for an invalid configuration.                                          */
+/* ------------------------------------------------------------------------------------ */
+typedef struct {
+  double l;
+  int id;
+} otok_t;
+
+static int cmp_tok(const void* a, const void* b) {
+  const otok_t* x = (const otok_t*)a;
+  const otok_t* y = (const otok_t*)b;
+  if (x->l != y->l) return x->l > y->l ? -1 : 1;
+  return (x->id > y->id) - (x->id < y->id);
+}
+
+typedef struct {
+  double lp;
+  float lp32;
+  int node;
+} onode_t;
+
+static int cmp_node(const void* a, const void* b) {
+  const onode_t* x = (const onode_t*)a;
+  const onode_t* y = (const onode_t*)b;
+  if (x->lp32 != y->lp32) return x->lp32 > y->lp32 ? -1 : 1;
+  return (x->node > y->node) - (x->node < y->node);
+}
+
+int oracle_tree_draft(int B, int V, int row_stride, int depth, const int32_t* top_head,
+                      const int32_t* top_k_spec, const uint16_t* rows,
+                      const int32_t* root_token, const int32_t* pos_base, int tree_stride,
+                      int32_t* parent, int32_t* node_token, int32_t* node_row,
+                      double* node_logp, int32_t* position_ids, uint8_t* ancestor,
+                      int32_t* expand, int expand_stride, double* select_margin,
+                      int nthreads) {
+  /* configuration: the root alone at step 0, every expansion within its layer */
+  if (depth < 1 || top_head[0] != 1) return -1;
+  int nodes = 1, kofs = 0, layer = 1;
+  for (int s = 0; s < depth; ++s) {
+    if (top_head[s] < 1 || top_head[s] > layer || top_head[s] > expand_stride) return -1;
+    layer = 0;
+    for (int j = 0; j < top_head[s]; ++j) {
+      const int k = top_k_spec[kofs + j];
+      if (k < 1 || k > V) return -1;
+      layer += k;
+    }
+    kofs += top_head[s];
+    nodes += layer;
+  }
+  if (nodes > tree_stride) return -1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    otok_t* tok = (otok_t*)malloc(sizeof(otok_t) * (size_t)V);
+    onode_t* lay = (onode_t*)malloc(sizeof(onode_t) * (size_t)tree_stride);
+#pragma omp for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+      int32_t* par = parent + (size_t)b * tree_stride;
+      int32_t* ntok = node_token + (size_t)b * tree_stride;
+      int32_t* nrow = node_row + (size_t)b * tree_stride;
+      double* lp = node_logp + (size_t)b * tree_stride;
+      int32_t* pos = position_ids + (size_t)b * tree_stride;
+      uint8_t* anc = ancestor + (size_t)b * tree_stride * tree_stride;
+      for (int i = 0; i < tree_stride; ++i) {
+        par[i] = -1;
+        ntok[i] = -1;
+        nrow[i] = -1;
+        lp[i] = -INFINITY;
+        pos[i] = -1;
+      }
+      memset(anc, 0, (size_t)tree_stride * tree_stride);
+      /* the root: the round's last confirmed token */
+      ntok[0] = root_token[b];
+      lp[0] = 0.0;
+      pos[0] = pos_base ? pos_base[b] : 0;
+      nrow[0] = 0;
+      int32_t exp_now[256];
+      exp_now[0] = 0;
+      int n = 1;          /* nodes so far            */
+      int rows_done = 0;  /* rows before this step's */
+      size_t row_base = 0;
+      int ko = 0;
+      for (int s = 0; s < depth; ++s) {
+        const int h = top_head[s];
+        for (int j = 0; j < h; ++j) expand[((size_t)s * B + b) * expand_stride + j] = exp_now[j];
+        if (s == 0) select_margin[b] = INFINITY;
+        const int first = n; /* first node of the new layer */
+        for (int j = 0; j < h; ++j) {
+          const int pnode = exp_now[j];
+          const uint16_t* row = rows + (row_base + (size_t)b * h + j) * row_stride;
+          /* log of the draft softmax: log pi(v) = l_v - m - log(sum_u exp(l_u - m)) */
+          double m = -INFINITY;
+          for (int v = 0; v < V; ++v) {
+            const double l = oracle_bf16_to_double(row[v]);
+            if (l > m) m = l;
+          }
+          double z = 0.0;
+          for (int v = 0; v < V; ++v) z += exp(oracle_bf16_to_double(row[v]) - m);
+          const double logz = m + log(z);
+          /* the K largest logits, ties to the lower id: sort all tokens */
+          for (int v = 0; v < V; ++v) {
+            tok[v].l = oracle_bf16_to_double(row[v]);
+            tok[v].id = v;
+          }
+          qsort(tok, (size_t)V, sizeof(otok_t), cmp_tok);
+          const int K = top_k_spec[ko + j];
+          for (int r = 0; r < K; ++r) {
+            const int c = n++;
+            par[c] = pnode;
+            ntok[c] = tok[r].id;
+            lp[c] = lp[pnode] + (tok[r].l - logz);
+            pos[c] = pos[pnode] + 1;
+          }
+        }
+        ko += h;
+        row_base += (size_t)B * h;
+        rows_done += h;
+        if (s + 1 < depth) {
+          /* the next step expands the newest layer's most probable nodes */
+          const int cnt = n - first, hn = top_head[s + 1];
+          for (int i = 0; i < cnt; ++i) {
+            lay[i].lp = lp[first + i];
+            lay[i].lp32 = (float)lp[first + i];
+            lay[i].node = first + i;
+          }
+          qsort(lay, (size_t)cnt, sizeof(onode_t), cmp_node);
+          double mg = INFINITY;
+          for (int i = 0; i < hn && i + 1 < cnt; ++i) {
+            const double d = fabs(lay[i].lp - lay[i + 1].lp);
+            if (d > 0.0 && d < mg) mg = d;
+          }
+          select_margin[(size_t)(s + 1) * B + b] = mg;
+          for (int j = 0; j < hn; ++j) {
+            exp_now[j] = lay[j].node;
+            nrow[lay[j].node] = rows_done + j;
+          }
+        }
+      }
+      /* ancestor mask: each node sees itself and every node on its path to the root */
+      for (int i = 0; i < n; ++i)
+        for (int a = i; a >= 0; a = par[a]) anc[(size_t)i * tree_stride + a] = 1;
+    }
+    free(tok);
+    free(lay);
   }
   return 0;
 }

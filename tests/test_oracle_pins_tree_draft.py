@@ -1,0 +1,244 @@
+"""Pins of the oracle's tree drafting (reading R20 of oracle/spec_oracle.c).
+
+Pinned against:
+  * the page's drafting dump ("投机推理：小模型搭树，大模型一次验证", the tree configuration
+    section and the real dump example): draft rows whose ranked tops are the page's lists
+    must give the page's 12-node tree, its expansions and its five target rows, and the
+    oracle's tree verification then accepts the page's path;
+  * Table 10-17 of "10.6 投机解码" §10.6.3 (the five-node ancestor mask; positions by depth);
+  * brute force written here with library routines (scipy's log_softmax, numpy lexsort,
+    boolean transitive closure) on random and tie-heavy rows;
+  * invariants (path probability = product of softmax probabilities along the path,
+    expanded nodes at least as probable as the rest of their layer);
+  * invalid configurations.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.special import log_softmax, softmax
+
+from draft_verification_03_amd import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _row_with_top(V, top, rng, hi=10.0, step=0.5, floor=-4.0):
+    """A bf16 row whose largest logits are ``top`` in order (hi, hi - step, ...), every other
+    logit well below them."""
+    x = floor + 0.5 * rng.standard_normal(V).astype(np.float32)
+    x = np.minimum(x, floor + 2.0)
+    for r, t in enumerate(top):
+        x[t] = hi - step * r
+    return W.bf16_bits(x)
+
+
+def test_page_dump_builds_the_page_tree(orc):
+    g = _load("tree_draft_worked_example.json")
+    t = _load("tree_worked_example.json")
+    V = t["vocab"]
+    rng = np.random.default_rng(5)
+    th = g["config"]["topHead"]
+    ks = g["config"]["topKSpec"]
+    # A1 is the root's best candidate and A2 the second (values 10 and 9.5); under A2 the
+    # first child sits one logit above A1's second child, so that B21 outranks B12 by path
+    # probability (e^{1} against e^{0.5}), as the page's choice of B11 and B21 requires.
+    rows = []
+    for st in g["draft_top"]:
+        rows.append(np.stack([_row_with_top(V, r["top"], rng, hi=8.0 if st["step"] else 10.0,
+                                            step=1.0 if st["step"] else 0.5)
+                              for r in st["rows"]]))
+    o = orc.tree_draft(rows, th, ks, np.array([g["root_token"]], np.int32), vocab=V)
+    names = [n["name"] for n in t["nodes"]]
+    assert o["num_nodes"] == 1 + g["total_speculative_nodes"] == len(names)
+    assert list(o["parent"][0]) == [n["parent"] for n in t["nodes"]]
+    assert list(o["node_token"][0]) == [n["token"] for n in t["nodes"]]
+    depth = np.array([0] + [1] * 6 + [2] * 4 + [3] * 2)
+    assert [int((depth == d).sum()) for d in (1, 2, 3)] == g["layer_sizes"]
+    # expansions: step 1 expands A1, A2; step 2 expands B11, B21 (in that order)
+    assert [names[i] for i in o["expand"][1, 0]] == [r["node"] for r in g["draft_top"][1]["rows"]]
+    assert [names[i] for i in o["expand"][2, 0]] == [r["node"] for r in g["draft_top"][2]["rows"]]
+    # the five target rows belong to R, A1, A2, B11, B21, in that order
+    want_rows = {r["node"]: i for i, r in enumerate(t["rows"])}
+    for i, nm in enumerate(names):
+        assert o["node_row"][0, i] == want_rows.get(nm, -1), nm
+    assert np.array_equal(o["position_ids"][0], depth)
+    # the tree feeds the verifier: target rows with the page's top-1 accept A1, B11, C111
+    trows = np.stack([_row_with_top(V, [r["target_top1"]], rng) for r in t["rows"]])[None]
+    r = orc.verify_tree(trows, o["parent"], o["node_row"], o["node_token"], len(t["rows"]),
+                        3, o["num_nodes"], vocab=V)
+    assert [names[i] for i in r["path_nodes"][0]] == t["expected"]["path_names"]
+    assert r["num_emitted"][0] == t["expected"]["accepted"]
+
+
+def test_table_10_17_mask_and_depth_positions(orc):
+    g = _load("tree_mask_table_10_17.json")
+    rng = np.random.default_rng(6)
+    V = 64
+    # root expands to a (best) and b; a expands to c and d
+    rows = [_row_with_top(V, [5, 9], rng)[None], _row_with_top(V, [17, 3], rng)[None]]
+    base = np.array([40], np.int32)
+    o = orc.tree_draft(rows, [1, 1], [[2], [2]], np.array([11], np.int32), pos_base=base,
+                       vocab=V)
+    assert list(o["parent"][0]) == g["parent"]
+    assert o["ancestor"][0].tolist() == g["mask"]
+    assert list(o["position_ids"][0]) == [40 + d for d in g["depth"]]
+    assert list(o["node_token"][0]) == [11, 5, 9, 17, 3]
+
+
+def _brute_tree(rows_by_step, top_head, top_k_spec, root_token, pos_base, V):
+    """Library-routine tree builder: log_softmax for path probabilities, lexsort for the
+    ranked children, Python sort for the expansions, boolean closure for the mask."""
+    B = len(root_token)
+    n = 1 + sum(sum(k) for k in top_k_spec)
+    par = np.full((B, n), -1, np.int64)
+    tok = np.full((B, n), -1, np.int64)
+    lp = np.full((B, n), -np.inf)
+    nrow = np.full((B, n), -1, np.int64)
+    exps = []
+    for b in range(B):
+        tok[b, 0] = root_token[b]
+        lp[b, 0] = 0.0
+        nrow[b, 0] = 0
+        cur = [0]
+        nxt = 1
+        rows_before = 0
+        ex_b = []
+        for s, h in enumerate(top_head):
+            ex_b.append(list(cur))
+            first = nxt
+            for j, pnode in enumerate(cur):
+                l = W.bf16_to_f32(rows_by_step[s][b * h + j][:V]).astype(np.float64)
+                ls = log_softmax(l)
+                order = np.lexsort((np.arange(V), -l))  # logit desc, then id asc
+                for v in order[:top_k_spec[s][j]]:
+                    par[b, nxt] = pnode
+                    tok[b, nxt] = v
+                    lp[b, nxt] = lp[b, pnode] + ls[v]
+                    nxt += 1
+            rows_before += h
+            if s + 1 < len(top_head):
+                layer = list(range(first, nxt))
+                ranked = sorted(layer, key=lambda i: (-np.float32(lp[b, i]), i))
+                cur = ranked[:top_head[s + 1]]
+                for j, node in enumerate(cur):
+                    nrow[b, node] = rows_before + j
+        exps.append(ex_b)
+    # ancestor-or-self by transitive closure of the child -> parent relation
+    anc = np.zeros((B, n, n), bool)
+    for b in range(B):
+        A = np.zeros((n, n), bool)
+        for i in range(1, n):
+            A[i, par[b, i]] = True
+        C = np.eye(n, dtype=bool)
+        P = np.eye(n, dtype=bool)
+        for _ in range(n):
+            P = (P.astype(np.int64) @ A.astype(np.int64)) > 0
+            C |= P
+        anc[b] = C
+    depth = anc.sum(axis=2) - 1
+    pos = depth + (0 if pos_base is None else np.asarray(pos_base)[:, None])
+    return dict(parent=par, node_token=tok, node_logp=lp, node_row=nrow, ancestor=anc,
+                position_ids=pos, expand=exps)
+
+
+CONFIGS = [
+    ((1, 2, 2), ((6,), (2, 2), (1, 1))),
+    ((1, 3, 2), ((3,), (3, 2, 1), (2, 2))),
+    ((1,), ((5,),)),
+    ((1, 1, 1, 1), ((1,), (1,), (1,), (1,))),
+    ((1, 4), ((4,), (2, 1, 3, 1))),
+]
+
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("quant", [None, 2])
+def test_bruteforce(orc, cfg, quant):
+    th, ks = CONFIGS[cfg]
+    x = W.tree_draft_inputs(seed=70 + cfg, B=6, V=300, top_head=th, top_k_spec=ks, quant=quant)
+    o = orc.tree_draft(x["rows"], th, ks, x["root_token"], pos_base=x["pos_base"],
+                       vocab=x["vocab"])
+    r = _brute_tree(x["rows"], th, ks, x["root_token"], x["pos_base"], x["vocab"])
+    for k in ("parent", "node_token", "node_row", "position_ids"):
+        assert np.array_equal(o[k], r[k]), k
+    assert np.array_equal(o["ancestor"].astype(bool), r["ancestor"])
+    assert np.max(np.abs(o["node_logp"] - r["node_logp"])) < 1e-12
+    for s in range(len(th)):
+        for b in range(6):
+            assert list(o["expand"][s, b, :th[s]]) == r["expand"][b][s]
+
+
+def test_ties_go_to_the_lower_id_and_the_lower_node(orc):
+    """Equal logits: the lower token id ranks first; equal path probabilities (children of
+    one parent with equal logits): the lower node index is expanded first."""
+    V = 50
+    x = np.full(V, -3.0, np.float32)
+    x[[7, 3, 40, 12]] = 2.0  # four equal maxima
+    r0 = W.bf16_bits(x)[None]
+    y = np.full(V, -3.0, np.float32)
+    y[[30, 20]] = 1.0
+    r1 = np.stack([W.bf16_bits(y)] * 2)
+    o = orc.tree_draft([r0, r1], [1, 2], [[3], [1, 1]], np.array([0], np.int32), vocab=V)
+    assert list(o["node_token"][0, 1:4]) == [3, 7, 12]
+    assert list(o["expand"][1, 0, :2]) == [1, 2]  # nodes 1..3 tie: lowest two indexes
+    assert list(o["node_token"][0, 4:6]) == [20, 20]
+    # the exact ties are no decision boundary: the margin skips zero gaps
+    assert o["select_margin"][1, 0] == np.inf
+
+
+def test_path_probability_and_expansion_invariants(orc):
+    x = W.tree_draft_inputs(seed=77, B=8, V=2000)
+    th, ks = x["top_head"], x["top_k_spec"]
+    o = orc.tree_draft(x["rows"], th, ks, x["root_token"], vocab=x["vocab"])
+    n = o["num_nodes"]
+    for b in range(8):
+        # exp(logp) is the product of the draft softmax probabilities along the path
+        expanded_rows = {}
+        for s, h in enumerate(th):
+            for j in range(h):
+                expanded_rows[int(o["expand"][s, b, j])] = x["rows"][s][b * h + j][:2000]
+        for i in range(1, n):
+            prob, v = 1.0, i
+            while v != 0:
+                p = int(o["parent"][b, v])
+                pr = softmax(W.bf16_to_f32(expanded_rows[p]).astype(np.float64))
+                prob *= pr[o["node_token"][b, v]]
+                v = p
+            assert abs(np.exp(o["node_logp"][b, i]) - prob) <= 1e-12 * max(prob, 1e-300)
+        # expanded nodes are at least as probable as their unexpanded layer-mates
+        depth = o["position_ids"][b]
+        for s in range(1, len(th)):
+            layer = [i for i in range(n) if depth[i] == s]
+            chosen = set(int(c) for c in o["expand"][s, b, :th[s]])
+            lo = min(np.float32(o["node_logp"][b, c]) for c in chosen)
+            assert all(np.float32(o["node_logp"][b, i]) <= lo for i in layer if i not in chosen)
+        # the mask rows count depth + 1 visible nodes
+        assert np.array_equal(o["ancestor"][b].sum(axis=1), depth + 1)
+
+
+@pytest.mark.parametrize("th,ks,why", [
+    ((2, 1), ((2, 2), (1,)), "top_head[0] must be 1"),
+    ((1, 3), ((2,), (1, 1, 1)), "more parents than the layer holds"),
+    ((1,), ((0,),), "K = 0"),
+    ((1,), ((65,),), "K > V"),
+])
+def test_invalid_configurations(orc, th, ks, why):
+    x = W.tree_draft_inputs(seed=1, B=2, V=64, top_head=(1,) * len(th),
+                            top_k_spec=((1,),) * len(th))
+    rows = [np.zeros((2 * h, 64), np.uint16) for h in th]
+    with pytest.raises(ValueError):
+        orc.tree_draft(rows, th, ks, x["root_token"], vocab=64)
+
+
+def test_tree_stride_too_small_is_rejected(orc):
+    x = W.tree_draft_inputs(seed=2, B=2, V=64, top_head=(1,), top_k_spec=((5,),))
+    with pytest.raises(ValueError):
+        orc.tree_draft(x["rows"], (1,), ((5,),), x["root_token"], tree_stride=5, vocab=64)
+    o = orc.tree_draft(x["rows"], (1,), ((5,),), x["root_token"], tree_stride=9, vocab=64)
+    assert list(o["parent"][0, 6:]) == [-1, -1, -1] and list(o["node_row"][0, 6:]) == [-1] * 3
