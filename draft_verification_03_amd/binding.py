@@ -51,6 +51,17 @@ class spec_tree_args(ctypes.Structure):
     ]
 
 
+class spec_tree_draft_args(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("vocab", _I32), ("row_stride", _I32), ("depth", _I32),
+        ("step", _I32), ("tree_stride", _I32), ("expand_stride", _I32),
+        ("top_head", _P), ("top_k_spec", _P), ("draft_logits", _P), ("root_token", _P),
+        ("pos_base", _P), ("parent", _P), ("node_token", _P), ("node_row", _P),
+        ("node_logp", _P), ("position_ids", _P), ("ancestor_mask", _P), ("expand_nodes", _P),
+        ("seq_flags", _P),
+    ]
+
+
 class spec_kv_args(ctypes.Structure):
     _fields_ = [
         ("batch", _I32), ("num_layers", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
@@ -70,7 +81,7 @@ class SpecError(RuntimeError):
 _lib = None
 
 # Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def lib_path() -> str:
@@ -97,6 +108,11 @@ def lib():
         L.spec_verify_tree.restype = ctypes.c_int
         L.kv_commit_path.argtypes = [ctypes.POINTER(spec_kv_args), _P]
         L.kv_commit_path.restype = ctypes.c_int
+        L.spec_tree_draft_workspace_size.argtypes = [_I32, _I32, _I32, _P, _P]
+        L.spec_tree_draft_workspace_size.restype = ctypes.c_size_t
+        L.spec_tree_draft_step.argtypes = [ctypes.POINTER(spec_tree_draft_args), _P,
+                                           ctypes.c_size_t, _P]
+        L.spec_tree_draft_step.restype = ctypes.c_int
         if L.spec_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{_build.LIB} has ABI version {L.spec_abi_version()}, the "
                                f"binding expects {ABI_VERSION}: rebuild the library")
@@ -270,6 +286,68 @@ def kv_args(*, k_cache, v_cache, path_nodes, path_len, committed_len, num_kv_hea
 
 def kv_commit_path(args: spec_kv_args, stream=None):
     _check(lib().kv_commit_path(ctypes.byref(args), _stream(stream)))
+
+
+def _tree_config(top_head, top_k_spec):
+    th = (_I32 * len(top_head))(*[int(h) for h in top_head])
+    flat = [int(k) for s in range(len(top_head)) for k in top_k_spec[s]]
+    ks = (_I32 * max(len(flat), 1))(*flat)
+    return th, ks
+
+
+def spec_tree_draft_workspace_size(batch, vocab, top_head, top_k_spec) -> int:
+    th, ks = _tree_config(top_head, top_k_spec)
+    return int(lib().spec_tree_draft_workspace_size(int(batch), int(vocab), len(top_head),
+                                                    ctypes.cast(th, _P), ctypes.cast(ks, _P)))
+
+
+def tree_draft_args(*, top_head, top_k_spec, step, draft_logits, parent, node_token, node_row,
+                    node_logp, position_ids, ancestor_mask, expand_nodes, vocab,
+                    root_token=None, pos_base=None, seq_flags=None, row_stride=None):
+    """Fills a spec_tree_draft_args; the tree arrays are [B, tree_stride] device tensors,
+    ancestor_mask is [B, tree_stride, (tree_stride + 31) // 32] and expand_nodes is
+    [B, expand_stride]."""
+    a = spec_tree_draft_args()
+    a.batch = int(parent.shape[0])
+    a.vocab = int(vocab)
+    a.row_stride = int(row_stride if row_stride is not None else draft_logits.shape[-1])
+    a.depth = len(top_head)
+    a.step = int(step)
+    a.tree_stride = int(parent.shape[1])
+    a.expand_stride = int(expand_nodes.shape[1])
+    th, ks = _tree_config(top_head, top_k_spec)
+    a._keep_cfg = (th, ks)
+    a.top_head = ctypes.cast(th, _P)
+    a.top_k_spec = ctypes.cast(ks, _P)
+    a.draft_logits = _ptr(draft_logits)
+    a.root_token = _ptr(root_token)
+    a.pos_base = _ptr(pos_base)
+    a.parent = _ptr(parent)
+    a.node_token = _ptr(node_token)
+    a.node_row = _ptr(node_row)
+    a.node_logp = _ptr(node_logp)
+    a.position_ids = _ptr(position_ids)
+    a.ancestor_mask = _ptr(ancestor_mask)
+    a.expand_nodes = _ptr(expand_nodes)
+    a.seq_flags = _ptr(seq_flags)
+    _keep(a, draft_logits, root_token, pos_base, parent, node_token, node_row, node_logp,
+          position_ids, ancestor_mask, expand_nodes, seq_flags)
+    return a
+
+
+def spec_tree_draft_step(args: spec_tree_draft_args, workspace=None, stream=None, device=None):
+    """Enqueues one tree-drafting step (see spec_verify.h). Returns the workspace tensor."""
+    if workspace is None and args.batch > 0:
+        th, ks = args._keep_cfg
+        need = int(lib().spec_tree_draft_workspace_size(args.batch, max(args.vocab, 1),
+                                                        args.depth, ctypes.cast(th, _P),
+                                                        ctypes.cast(ks, _P)))
+        if need > 0:
+            workspace = _workspace(need, device or torch.device("cuda"))
+    ws = _ptr(workspace)
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(lib().spec_tree_draft_step(ctypes.byref(args), ws, nbytes, _stream(stream)))
+    return workspace
 
 
 # ---- HIP events for the optional row-pass timing (profile_events) -----------------------

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 
 #include "spec_verify.h"
 #include "specv_internal.h"
@@ -29,6 +30,83 @@ constexpr int32_t kMaxGamma = 64;       // first-rejection scan is one wave64 ba
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(SPEC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Checks a tree configuration (top_head, top_k_spec host arrays over `depth` steps). Returns
+// SPEC_OK and the node count (root included) in *nodes, or fails with a message.
+int check_tree_config(int32_t vocab, int32_t depth, const int32_t* top_head,
+                      const int32_t* top_k_spec, int* nodes) {
+  if (depth < 1 || depth > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "depth must be in [1, 64] (got %d)", depth);
+  if (!top_head || !top_k_spec)
+    return fail(SPEC_ERR_INVALID_ARG, "top_head and top_k_spec are required host arrays");
+  if (top_head[0] != 1)
+    return fail(SPEC_ERR_INVALID_ARG, "top_head[0] must be 1: step 0 expands the root");
+  int n = 1, layer = 1, ko = 0;
+  for (int s = 0; s < depth; ++s) {
+    const int h = top_head[s];
+    if (h < 1 || h > layer || h > specv::kTreeDraftMaxHead)
+      return fail(SPEC_ERR_INVALID_ARG,
+                  "top_head[%d] = %d must be in [1, min(%d, %d nodes made at the step before)]",
+                  s, h, specv::kTreeDraftMaxHead, layer);
+    layer = 0;
+    for (int j = 0; j < h; ++j) {
+      const int k = top_k_spec[ko + j];
+      if (k < 1 || k > specv::kTreeDraftMaxK || k > vocab)
+        return fail(SPEC_ERR_INVALID_ARG, "top_k_spec[%d][%d] = %d must be in [1, min(%d, vocab)]",
+                    s, j, k, specv::kTreeDraftMaxK);
+      layer += k;
+    }
+    ko += h;
+    n += layer;
+    if (n > specv::kTreeDraftMaxNodes)
+      return fail(SPEC_ERR_INVALID_ARG, "the tree has more than %d nodes",
+                  specv::kTreeDraftMaxNodes);
+  }
+  *nodes = n;
+  return SPEC_OK;
+}
+
+// Geometry of one step of a checked configuration.
+specv::TreeDraftPlan tree_draft_plan(int32_t batch, int32_t vocab, int32_t depth, int32_t step,
+                                     const int32_t* top_head, const int32_t* top_k_spec) {
+  specv::TreeDraftPlan p = {};
+  int first = 1, prev_first = 0, ko = 0, rows = 0;
+  for (int s = 0; s < step; ++s) {
+    int made = 0;
+    for (int j = 0; j < top_head[s]; ++j) made += top_k_spec[ko + j];
+    ko += top_head[s];
+    rows += top_head[s];
+    prev_first = first;
+    first += made;
+  }
+  p.h = top_head[step];
+  p.par_lo = step == 0 ? 0 : prev_first;
+  p.par_hi = step == 0 ? 1 : first;
+  p.first_new = first;
+  int off = 0;
+  for (int j = 0; j < p.h; ++j) {
+    p.kk[j] = top_k_spec[ko + j];
+    p.koff[j] = off;
+    off += p.kk[j];
+    p.kmax = p.kk[j] > p.kmax ? p.kk[j] : p.kmax;
+  }
+  p.n_new = off;
+  p.h_next = step + 1 < depth ? top_head[step + 1] : 0;
+  p.row_base_next = rows + p.h;
+  p.splits = specv::tree_draft_splits(batch * p.h, vocab);
+  return p;
+}
+
+size_t tree_draft_bytes(int32_t batch, int32_t vocab, int32_t depth, const int32_t* top_head,
+                        const int32_t* top_k_spec) {
+  size_t need = 256;
+  for (int s = 0; s < depth; ++s) {
+    const specv::TreeDraftPlan p = tree_draft_plan(batch, vocab, depth, s, top_head, top_k_spec);
+    const size_t b = (size_t)batch * p.h * p.splits * specv::tree_draft_record_bytes(p.kmax);
+    need = b > need ? b : need;
+  }
+  return specv::align256(need);
 }
 
 }  // namespace
@@ -155,6 +233,60 @@ int kv_commit_path(const spec_kv_args* a, void* hip_stream) {
   }
   hipError_t e = specv::launch_kv(*a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "kv_commit_path launch");
+  return SPEC_OK;
+}
+
+size_t spec_tree_draft_workspace_size(int32_t batch, int32_t vocab, int32_t depth,
+                                      const int32_t* top_head, const int32_t* top_k_spec) {
+  if (batch < 0 || vocab < 1 || vocab > kMaxVocab) return 0;
+  char saved[sizeof g_err];
+  std::memcpy(saved, g_err, sizeof g_err);
+  int nodes = 0;
+  const int rc = check_tree_config(vocab, depth, top_head, top_k_spec, &nodes);
+  std::memcpy(g_err, saved, sizeof g_err);  // a size query leaves the error string alone
+  if (rc != SPEC_OK) return 0;
+  return tree_draft_bytes(batch, vocab, depth, top_head, top_k_spec);
+}
+
+int spec_tree_draft_step(const spec_tree_draft_args* a, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+  g_err[0] = '\0';
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "spec_tree_draft_step: args is NULL");
+  if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->vocab < 1 || a->vocab > kMaxVocab)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", kMaxVocab, a->vocab);
+  if (a->row_stride < a->vocab || a->row_stride % 8 != 0)
+    return fail(SPEC_ERR_INVALID_ARG, "row_stride must be >= vocab and a multiple of 8");
+  int nodes = 0;
+  const int rc = check_tree_config(a->vocab, a->depth, a->top_head, a->top_k_spec, &nodes);
+  if (rc != SPEC_OK) return rc;
+  if (a->step < 0 || a->step >= a->depth)
+    return fail(SPEC_ERR_INVALID_ARG, "step must be in [0, depth) (got %d, depth %d)", a->step,
+                a->depth);
+  if (a->tree_stride < nodes || a->tree_stride > specv::kTreeDraftMaxNodes)
+    return fail(SPEC_ERR_INVALID_ARG, "tree_stride must be in [%d, %d] (got %d)", nodes,
+                specv::kTreeDraftMaxNodes, a->tree_stride);
+  int hmax = 0;
+  for (int s = 0; s < a->depth; ++s) hmax = a->top_head[s] > hmax ? a->top_head[s] : hmax;
+  if (a->expand_stride < hmax)
+    return fail(SPEC_ERR_INVALID_ARG, "expand_stride must be >= %d (got %d)", hmax,
+                a->expand_stride);
+  if (a->batch == 0) return SPEC_OK;
+  if (!a->draft_logits || !a->parent || !a->node_token || !a->node_row || !a->node_logp ||
+      !a->position_ids || !a->ancestor_mask || !a->expand_nodes ||
+      (a->step == 0 && !a->root_token))
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(a->draft_logits))
+    return fail(SPEC_ERR_INVALID_ARG, "draft_logits must be 16-byte aligned");
+  const specv::TreeDraftPlan p =
+      tree_draft_plan(a->batch, a->vocab, a->depth, a->step, a->top_head, a->top_k_spec);
+  if ((int64_t)a->batch * p.h * p.splits > 0x7FFFFFFFLL)
+    return fail(SPEC_ERR_INVALID_ARG, "batch * top_head[step] exceeds the grid limit");
+  const size_t need = tree_draft_bytes(a->batch, a->vocab, a->depth, a->top_head, a->top_k_spec);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  hipError_t e = specv::launch_tree_draft(*a, p, workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "spec_tree_draft_step launch");
   return SPEC_OK;
 }
 

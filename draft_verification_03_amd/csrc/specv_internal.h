@@ -42,6 +42,31 @@ hipError_t launch_tree(const spec_tree_args& a, void* ws, hipStream_t s);
 
 hipError_t launch_kv(const spec_kv_args& a, hipStream_t s);
 
+// Tree drafting: limits and the geometry of one step, derived on the host from the tree
+// configuration (top_head, top_k_spec) and the step index.
+constexpr int kTreeDraftMaxK = 64;       // children per expanded node
+constexpr int kTreeDraftMaxHead = 64;    // expanded nodes per step
+constexpr int kTreeDraftMaxNodes = 256;  // nodes per tree
+constexpr int kTreeDraftMaxSplits = 16;  // workgroups per draft row
+
+struct TreeDraftPlan {
+  int32_t h;              // nodes expanded at this step (draft rows per sequence)
+  int32_t kmax;           // largest child count of this step
+  int32_t splits;         // workgroups per draft row
+  int32_t par_lo, par_hi; // node range the expanded nodes must lie in (step 0: the root)
+  int32_t first_new;      // index of the first node this step creates
+  int32_t n_new;          // nodes this step creates
+  int32_t h_next;         // nodes the next step expands (0 after the last step)
+  int32_t row_base_next;  // target row of the next step's first expanded node
+  int32_t kk[kTreeDraftMaxHead];    // children of the j-th expanded node
+  int32_t koff[kTreeDraftMaxHead];  // its first child, relative to first_new
+};
+
+int tree_draft_splits(int32_t rows, int32_t vocab);
+size_t tree_draft_record_bytes(int32_t kmax);
+hipError_t launch_tree_draft(const spec_tree_draft_args& a, const TreeDraftPlan& p, void* ws,
+                             hipStream_t s);
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace specv

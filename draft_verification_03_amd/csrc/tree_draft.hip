@@ -1,0 +1,417 @@
+// tree_draft.hip -- one tree-drafting step on gfx950 ("投机推理：小模型搭树，大模型一次验证",
+// tree configuration and draft-step sections; "10.6 投机解码" §10.6.3, tree drafts and
+// Table 10-17).
+//
+//  1. draft_topk_kernel -- every draft row of the step is split into S chunks, one
+//     256-thread workgroup per chunk. The chunk streams from HBM once with 16-byte loads.
+//     Every lane keeps a running maximum and sum of exp(l - max) (the softmax normaliser);
+//     every wave keeps (logit, token) candidates in LDS behind a threshold, the K-th largest
+//     logit the wave holds, so that after its first trip almost nothing passes. A wave's best
+//     K come from K rounds of a wave-wide maximum over its candidates; the workgroup merges
+//     its waves' lists and writes one record (max, sum, best K) per chunk.
+//  2. tree_grow_kernel -- one workgroup per sequence merges each expanded node's S records
+//     into the row's normaliser and its K best tokens, appends the children with their path
+//     log-probabilities, positions and ancestor-mask rows, and ranks the new layer by path
+//     log-probability to choose the next step's expanded nodes and their target rows.
+//
+// Every address of the tree arrays has one writer per launch, so no write of one thread is
+// ordered against another's.
+#include "row_ops.h"
+#include "spec_device.h"
+#include "specv_internal.h"
+
+namespace specv {
+namespace {
+
+constexpr int kDraftWaves = 4;
+constexpr int kDraftThreads = kDraftWaves * kWave;
+constexpr int kCandCap = 1024;  // candidate slots per wave
+constexpr int kCandRegs = kCandCap / kWave;
+constexpr int kGrowThreads = 256;
+constexpr int kMaxHead = kTreeDraftMaxHead;
+constexpr int kMaskWordsMax = 8;  // 256 nodes
+constexpr int kTargetWgs = 1024;  // about four workgroups per CU
+constexpr int kMinChunkVec = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+
+static_assert(kTreeDraftMaxSplits * kTreeDraftMaxK <= kCandRegs * kWave,
+              "a row's merged candidates must fit the merge registers");
+
+// A candidate packs the bf16 order key above the complement of the token id: the larger
+// candidate has the larger logit, or the same logit and the lower id. 0 is no candidate (key 0
+// is a NaN pattern, and logits are never NaN).
+__device__ __forceinline__ uint64_t cand_of(uint32_t bits16, uint32_t idx) {
+  return ((uint64_t)key_of_bits(bits16) << 32) | (uint32_t)~idx;
+}
+__device__ __forceinline__ int cand_token(uint64_t c) { return (int)~(uint32_t)c; }
+__device__ __forceinline__ float cand_logit(uint64_t c) {
+  return value_of_key((uint32_t)(c >> 32));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The K (<= 64) largest of the wave's candidates e[] (0 = empty), largest first: lane r
+// receives the r-th in `mine`. Returns how many exist (< K when fewer candidates are held).
+template <int R>
+__device__ __forceinline__ int wave_top(const uint64_t (&e)[R], int K, uint64_t& mine) {
+  uint64_t prev = ~0ull;
+  int found = 0;
+  mine = 0;
+  for (int r = 0; r < K; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) best = (e[i] < prev && e[i] > best) ? e[i] : best;
+    best = wave_max_u64(best);
+    if (best == 0) break;
+    if (lane_id() == r) mine = best;
+    prev = best;
+    ++found;
+  }
+  return found;
+}
+
+// Reduces a wave's candidate buffer (n entries) to its K best, largest first, and returns
+// their number; tau becomes the K-th best's logit (-inf while fewer than K are held).
+__device__ __forceinline__ int compact(uint64_t* buf, int n, int K, float& tau, int lane) {
+  uint64_t e[kCandRegs];
+#pragma unroll
+  for (int i = 0; i < kCandRegs; ++i) {
+    const int j = i * kWave + lane;
+    e[i] = j < n ? buf[j] : 0ull;
+  }
+  uint64_t mine;
+  const int f = wave_top(e, K, mine);
+  if (lane < f) buf[lane] = mine;
+  tau = f == K ? cand_logit(readlane_u64(mine, K - 1)) : -INFINITY;
+  return f;
+}
+
+struct DraftParams {
+  const uint16_t* logits;
+  uint8_t* part;
+  int32_t V, stride, nvec, S, chunk, h, rec_bytes;
+  int32_t kk[kMaxHead];
+};
+
+struct PartHead {
+  float m;  // largest logit of the chunk (-inf if none)
+  float s;  // sum over the chunk of exp(l - m)
+  int32_t n;
+  int32_t pad;
+};
+
+__global__ __launch_bounds__(kDraftThreads) void draft_topk_kernel(DraftParams P) {
+  __shared__ uint64_t s_buf[kDraftWaves][kCandCap];
+  __shared__ float s_m[kDraftWaves], s_s[kDraftWaves];
+  __shared__ int s_n[kDraftWaves];
+  const int row = blockIdx.x / P.S;
+  const int split = blockIdx.x - row * P.S;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int K = P.kk[row % P.h];
+  const int c0 = split * P.chunk;
+  const int c1 = min(P.nvec, c0 + P.chunk);
+  const int lim = min(P.V, c1 * 8);  // token ids of this chunk lie below lim
+  uint64_t* buf = s_buf[wave];
+  float m = -INFINITY, s = 0.f, tau = -INFINITY;
+  int n = 0;
+  if (c1 > c0) {
+    const uint4* rp = reinterpret_cast<const uint4*>(P.logits + (size_t)row * P.stride) + c0;
+    stream_row_strided<2>(rp, c1 - c0, lane, wave, kDraftWaves, [&](uint4* d, int v0, bool ml) {
+      if (ml) mask_tail(d, c0 + v0, P.nvec, P.V, lane);
+      float x[kU][8];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) unpack8(d[u], x[u]);
+      float vm[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) vm[u] = max8(x[u]);
+      static_assert(kU == 4, "trip max below assumes four vectors per trip");
+      const float tm = vmax3(vmax3(vm[0], vm[1], vm[2]), vm[3], vm[3]);
+      if (tm > m) {
+        s = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - tm) * kLog2e);
+        m = tm;
+      }
+      if (m != -INFINITY) {
+        const float nref = -m * kLog2e;
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[u][e], kLog2e, nref));
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (__ballot(vm[u] >= tau) == 0) continue;  // wave-uniform: nothing passes
+        if (n + 8 * kWave > kCandCap) n = compact(buf, n, K, tau, lane);
+        const int vg = c0 + v0 + u * kWave + lane;  // vector index in the row
+        const uint32_t w[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
+        uint32_t fl = 0;
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = x[u][e] >= tau && vg * 8 + e < lim;
+          fl |= (uint32_t)ok << e;
+          c += ok;
+        }
+        const int incl = wave_incl_scan_dpp(c);
+        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        int off = n + incl - c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (fl >> e & 1u) {
+            const uint32_t b16 = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+            buf[off++] = cand_of(b16, (uint32_t)(vg * 8 + e));
+          }
+        }
+        n += total;
+      }
+    });
+  }
+  n = compact(buf, n, K, tau, lane);
+  // the wave's normaliser relative to its own maximum
+  const float mw = wave_max_dpp(m);
+  const float sw = wave_sum_dpp(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mw) * kLog2e));
+  if (lane == 0) {
+    s_m[wave] = mw;
+    s_s[wave] = sw;
+    s_n[wave] = n;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0 merges the workgroup: the waves' lists hold at most K <= 64 entries each
+  uint64_t e[kDraftWaves];
+#pragma unroll
+  for (int w = 0; w < kDraftWaves; ++w) e[w] = lane < s_n[w] ? s_buf[w][lane] : 0ull;
+  uint64_t mine;
+  const int f = wave_top(e, K, mine);
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kDraftWaves; ++w) M = fmaxf(M, s_m[w]);
+  float Z = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDraftWaves; ++w)
+    Z += s_m[w] == -INFINITY ? 0.f : s_s[w] * __builtin_amdgcn_exp2f((s_m[w] - M) * kLog2e);
+  uint8_t* rec = P.part + (size_t)blockIdx.x * P.rec_bytes;
+  if (lane == 0) {
+    PartHead hd;
+    hd.m = M;
+    hd.s = Z;
+    hd.n = f;
+    hd.pad = 0;
+    *reinterpret_cast<PartHead*>(rec) = hd;
+  }
+  if (lane < K) reinterpret_cast<uint64_t*>(rec + sizeof(PartHead))[lane] = lane < f ? mine : 0ull;
+}
+
+struct GrowParams {
+  const uint8_t* part;
+  const int32_t* root_token;
+  const int32_t* pos_base;
+  int32_t* parent;
+  int32_t* node_token;
+  int32_t* node_row;
+  float* node_logp;
+  int32_t* position_ids;
+  uint32_t* mask;
+  int32_t* expand_nodes;
+  int32_t* seq_flags;
+  int32_t step, ts, mw, es, h, S, rec_bytes;
+  int32_t par_lo, par_hi, first_new, n_new, h_next, row_base_next;
+  int32_t kk[kMaxHead];
+  int32_t koff[kMaxHead];
+};
+
+__global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
+  __shared__ int s_exp[kMaxHead];
+  __shared__ float s_plp[kMaxHead];
+  __shared__ int s_ppos[kMaxHead];
+  __shared__ uint32_t s_pmask[kMaxHead][kMaskWordsMax];
+  __shared__ float s_lp[kTreeDraftMaxNodes];
+  __shared__ int s_bad;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const size_t nb = (size_t)b * P.ts;
+  int32_t* par = P.parent + nb;
+  int32_t* tok = P.node_token + nb;
+  int32_t* nrow = P.node_row + nb;
+  float* lp = P.node_logp + nb;
+  int32_t* pos = P.position_ids + nb;
+  uint32_t* mask = P.mask + nb * P.mw;
+  int32_t* expn = P.expand_nodes + (size_t)b * P.es;
+  const int new_hi = P.first_new + P.n_new;
+  if (P.step == 0) {
+    // every entry but this step's new nodes (written below) gets its initial value
+    for (int i = tid; i < P.ts; i += kGrowThreads) {
+      if (i >= P.first_new && i < new_hi) continue;
+      const bool root = i == 0;
+      par[i] = -1;
+      tok[i] = root ? P.root_token[b] : -1;
+      nrow[i] = root ? 0 : -1;
+      lp[i] = root ? 0.f : -INFINITY;
+      pos[i] = root ? (P.pos_base ? P.pos_base[b] : 0) : -1;
+    }
+    for (int k = tid; k < P.ts * P.mw; k += kGrowThreads) {
+      const int i = k / P.mw;
+      if (i >= P.first_new && i < new_hi) continue;
+      mask[k] = (k == 0) ? 1u : 0u;
+    }
+    if (tid == 0) {
+      s_exp[0] = 0;
+      s_plp[0] = 0.f;
+      s_ppos[0] = P.pos_base ? P.pos_base[b] : 0;
+      s_bad = 0;
+    }
+    if (tid < kMaskWordsMax) s_pmask[0][tid] = tid == 0 ? 1u : 0u;
+  } else {
+    if (tid < kWave) {  // h <= 64: wave 0 reads the expanded nodes
+      int node = -1;
+      bool bad = false;
+      if (lane < P.h) {
+        node = expn[lane];
+        bad = node < P.par_lo || node >= P.par_hi;
+        if (!bad) {
+          s_exp[lane] = node;
+          s_plp[lane] = lp[node];
+          s_ppos[lane] = pos[node];
+          for (int w = 0; w < P.mw; ++w) s_pmask[lane][w] = mask[(size_t)node * P.mw + w];
+        }
+      }
+      const bool any = __ballot(bad) != 0;
+      if (lane == 0) s_bad = any;
+    }
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0 && P.seq_flags) P.seq_flags[b] |= SPEC_FLAG_BAD_TREE;
+    return;
+  }
+  // children of each expanded node, one wave per node
+  for (int j = wave; j < P.h; j += kGrowThreads / kWave) {
+    const size_t row = (size_t)b * P.h + j;
+    const uint8_t* rec0 = P.part + row * P.S * P.rec_bytes;
+    float m = -INFINITY, sm = 0.f;
+    if (lane < P.S) {
+      const PartHead hd = *reinterpret_cast<const PartHead*>(rec0 + (size_t)lane * P.rec_bytes);
+      m = hd.m;
+      sm = hd.s;
+    }
+    const float M = wave_max_dpp(m);
+    const float Z = wave_sum_dpp(m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f((m - M) * kLog2e));
+    const float lz = logf(Z);  // log of sum over the row of exp(l - M)
+    const int K = P.kk[j];
+    uint64_t e[kCandRegs];
+#pragma unroll
+    for (int t = 0; t < kCandRegs; ++t) {
+      const int i = t * kWave + lane;
+      const int li = i / K, r = i - li * K;
+      e[t] = li < P.S ? reinterpret_cast<const uint64_t*>(rec0 + (size_t)li * P.rec_bytes +
+                                                          sizeof(PartHead))[r]
+                      : 0ull;
+    }
+    uint64_t mine;
+    const int f = wave_top(e, K, mine);
+    if (lane < f) {
+      const int c = P.first_new + P.koff[j] + lane;
+      const float l = cand_logit(mine);
+      const float v = s_plp[j] + ((l - M) - lz);
+      par[c] = s_exp[j];
+      tok[c] = cand_token(mine);
+      lp[c] = v;
+      pos[c] = s_ppos[j] + 1;
+      for (int w = 0; w < P.mw; ++w)
+        mask[(size_t)c * P.mw + w] = s_pmask[j][w] | ((c >> 5) == w ? 1u << (c & 31) : 0u);
+      s_lp[c - P.first_new] = v;
+    }
+  }
+  __syncthreads();
+  // the new layer's rows: the h_next most probable nodes get the next step's target rows
+  for (int t = tid; t < P.n_new; t += kGrowThreads) {
+    const float me = s_lp[t];
+    int rank = 0;
+    for (int u = 0; u < P.n_new; ++u) {
+      const float o = s_lp[u];
+      rank += (o > me) || (o == me && u < t);
+    }
+    const bool chosen = rank < P.h_next;
+    nrow[P.first_new + t] = chosen ? P.row_base_next + rank : -1;
+    if (chosen) expn[rank] = P.first_new + t;
+  }
+}
+
+}  // namespace
+
+int tree_draft_splits(int32_t rows, int32_t vocab) {
+  const int nvec = (vocab + 7) / 8;
+  int s = (kTargetWgs + rows - 1) / max(rows, 1);
+  const int cap = max(1, min(kTreeDraftMaxSplits, nvec / kMinChunkVec));
+  return max(1, min(s, cap));
+}
+
+size_t tree_draft_record_bytes(int32_t kmax) {
+  return sizeof(PartHead) + (size_t)kmax * sizeof(uint64_t);
+}
+
+hipError_t launch_tree_draft(const spec_tree_draft_args& a, const TreeDraftPlan& p, void* ws,
+                             hipStream_t st) {
+  DraftParams D;
+  D.logits = a.draft_logits;
+  D.part = reinterpret_cast<uint8_t*>(ws);
+  D.V = a.vocab;
+  D.stride = a.row_stride;
+  D.nvec = (a.vocab + 7) / 8;
+  D.S = p.splits;
+  D.chunk = (D.nvec + p.splits - 1) / p.splits;
+  D.h = p.h;
+  D.rec_bytes = (int32_t)tree_draft_record_bytes(p.kmax);
+  for (int j = 0; j < kMaxHead; ++j) D.kk[j] = j < p.h ? p.kk[j] : 0;
+  const unsigned grid = (unsigned)(a.batch * p.h * p.splits);
+  hipLaunchKernelGGL(draft_topk_kernel, dim3(grid), dim3(kDraftThreads), 0, st, D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GrowParams G;
+  G.part = D.part;
+  G.root_token = a.root_token;
+  G.pos_base = a.pos_base;
+  G.parent = a.parent;
+  G.node_token = a.node_token;
+  G.node_row = a.node_row;
+  G.node_logp = a.node_logp;
+  G.position_ids = a.position_ids;
+  G.mask = a.ancestor_mask;
+  G.expand_nodes = a.expand_nodes;
+  G.seq_flags = a.seq_flags;
+  G.step = a.step;
+  G.ts = a.tree_stride;
+  G.mw = (a.tree_stride + 31) / 32;
+  G.es = a.expand_stride;
+  G.h = p.h;
+  G.S = p.splits;
+  G.rec_bytes = D.rec_bytes;
+  G.par_lo = p.par_lo;
+  G.par_hi = p.par_hi;
+  G.first_new = p.first_new;
+  G.n_new = p.n_new;
+  G.h_next = p.h_next;
+  G.row_base_next = p.row_base_next;
+  for (int j = 0; j < kMaxHead; ++j) {
+    G.kk[j] = j < p.h ? p.kk[j] : 0;
+    G.koff[j] = j < p.h ? p.koff[j] : 0;
+  }
+  hipLaunchKernelGGL(tree_grow_kernel, dim3((unsigned)a.batch), dim3(kGrowThreads), 0, st, G);
+  return hipGetLastError();
+}
+
+}  // namespace specv

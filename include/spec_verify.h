@@ -14,7 +14,8 @@
  *     after temperature and top-k/top-p is the one to test), §5 (bonus token), §6 (reserved
  *     slots and one committed-length pointer, the same in every layer);
  *   "投机解码" (LLM glossary), exact acceptance section (q = 0 and zero-residual cases);
- *   "投机推理：小模型搭树，大模型一次验证", validation and path-walk sections (tree).
+ *   "投机推理：小模型搭树，大模型一次验证", validation and path-walk sections (tree), tree
+ *     configuration and draft-step sections (tree drafting).
  *
  * Conventions for every call
  *  - Logits are bf16, passed as raw uint16 bit patterns, row-major with row_stride elements
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
@@ -215,6 +216,63 @@ typedef struct spec_kv_args {
   int32_t* seq_flags;        /* [B] or NULL (bits OR-ed in)                                */
 } spec_kv_args;
 
+/*
+ * One drafting step of a token tree ("投机推理：小模型搭树，大模型一次验证", sections on the
+ * tree configuration -- gamma, topKSpec, topHead -- and on the three draft steps of the dump
+ * example; "10.6 投机解码" §10.6.3, tree drafts, Table 10-17 and the depth positions).
+ *
+ * A tree is grown by `depth` calls, step = 0, 1, ..., depth-1, with the draft model's forward
+ * between them. Step s reads one draft logits row per node expanded at this step: row j of
+ * sequence b follows expand_nodes[b][j], j < top_head[s] (step 0 expands the root alone). The
+ * j-th expanded node gets as children the top_k_spec[s][j] tokens of largest draft logit,
+ * larger first, ties to the lower token id. A node's path log-probability (node_logp) is its
+ * parent's plus the natural log of its token's draft softmax probability (temperature 1, no
+ * filter); the root's is 0. Unless s is the last step, the top_head[s+1] nodes of the new
+ * layer with the largest path log-probability (compared as float; ties to the lower node
+ * index) then become expand_nodes[b][0..top_head[s+1]), most probable first, and receive
+ * the target rows sum(top_head[0..s]) + j in that order (node_row).
+ *
+ * Node numbering: root 0, then layer by layer; inside a layer by the rank of the parent and
+ * then of the child. Target rows belong to the expanded nodes in expansion order (the root
+ * has row 0): the layout spec_verify_tree reads with rows_per_seq = sum(top_head). With
+ * tree_stride = 1 + sum(top_k_spec) the arrays pass to spec_verify_tree as they are
+ * (num_nodes = tree_stride, max_depth = depth).
+ *
+ * Step 0 writes every entry of each sequence's arrays: node 0 gets token root_token[b],
+ * parent -1, row 0, log-probability 0, position pos_base[b] (0 if pos_base is NULL) and
+ * mask bit 0; every other entry parent -1, token -1, row -1, log-probability -inf, position
+ * -1 and no mask bits, until a later step creates the node. A created node's mask row holds
+ * its own bit and its ancestors' (node i sees node j iff bit j%32 of word j/32 is set), and
+ * its position is its parent's plus one.
+ *
+ * Data errors: at step s >= 1, an expand_nodes[b][j] outside the previous step's layer sets
+ * SPEC_FLAG_BAD_TREE in seq_flags[b] (when given) and that sequence's step writes nothing.
+ */
+typedef struct spec_tree_draft_args {
+  int32_t batch;          /* B >= 0                                                        */
+  int32_t vocab;          /* V >= 1                                                        */
+  int32_t row_stride;     /* elements; >= vocab, multiple of 8                             */
+  int32_t depth;          /* steps per tree (gamma); 1..64                                 */
+  int32_t step;           /* this step; 0..depth-1                                         */
+  int32_t tree_stride;    /* node entries per sequence; 1 + sum(top_k_spec) .. 256         */
+  int32_t expand_stride;  /* entries per sequence of expand_nodes; >= every top_head[s]    */
+  const int32_t* top_head;    /* HOST [depth]: top_head[0] = 1, and for s >= 1
+                                 1 <= top_head[s] <= the number of nodes made at step s-1 */
+  const int32_t* top_k_spec;  /* HOST: top_k_spec[s][0..top_head[s]) for s = 0..depth-1,
+                                 concatenated; each in 1..min(64, vocab)                   */
+  const uint16_t* draft_logits; /* [B][top_head[step]][row_stride] bf16                     */
+  const int32_t* root_token;    /* [B]; read at step 0                                      */
+  const int32_t* pos_base;      /* [B] or NULL; the root's position, read at step 0         */
+  int32_t* parent;              /* [B][tree_stride] in/out                                  */
+  int32_t* node_token;          /* [B][tree_stride] in/out                                  */
+  int32_t* node_row;            /* [B][tree_stride] in/out                                  */
+  float* node_logp;             /* [B][tree_stride] in/out                                  */
+  int32_t* position_ids;        /* [B][tree_stride] in/out                                  */
+  uint32_t* ancestor_mask;      /* [B][tree_stride][(tree_stride + 31) / 32] in/out         */
+  int32_t* expand_nodes;        /* [B][expand_stride] in/out                                */
+  int32_t* seq_flags;           /* [B] or NULL (bits OR-ed in)                              */
+} spec_tree_draft_args;
+
 /* ABI revision of this header (SPEC_ABI_VERSION). */
 int spec_abi_version(void);
 
@@ -238,6 +296,17 @@ int spec_verify_tree(const spec_tree_args* args, void* workspace, size_t workspa
 
 /* Enqueue the KV path commit and pointer update. Returns SPEC_OK or a negative status. */
 int kv_commit_path(const spec_kv_args* args, void* hip_stream);
+
+/* Workspace bytes every step of spec_tree_draft_step needs for this tree configuration
+ * (top_head and top_k_spec are HOST arrays as in spec_tree_draft_args; device memory,
+ * 256-byte aligned, contents need not be initialised). Returns 0 for an invalid
+ * configuration. */
+size_t spec_tree_draft_workspace_size(int32_t batch, int32_t vocab, int32_t depth,
+                                      const int32_t* top_head, const int32_t* top_k_spec);
+
+/* Enqueue one tree-drafting step. Returns SPEC_OK or a negative status. */
+int spec_tree_draft_step(const spec_tree_draft_args* args, void* workspace,
+                         size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

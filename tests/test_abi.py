@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["spec_abi_version", "spec_last_error", "spec_verify_chain_workspace_size",
                  "spec_verify_chain", "spec_verify_tree_workspace_size", "spec_verify_tree",
-                 "kv_commit_path"]:
+                 "kv_commit_path", "spec_tree_draft_workspace_size", "spec_tree_draft_step"]:
         assert want in names
 
 
@@ -45,6 +45,7 @@ def test_struct_layout_matches_c(tmp_path):
         "spec_chain_args": [f for f, _ in B.spec_chain_args._fields_],
         "spec_tree_args": [f for f, _ in B.spec_tree_args._fields_],
         "spec_kv_args": [f for f, _ in B.spec_kv_args._fields_],
+        "spec_tree_draft_args": [f for f, _ in B.spec_tree_draft_args._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spec_verify.h"',
              "int main(void){"]
@@ -67,7 +68,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_abi_version_and_workspace_sizes():
-    assert B.spec_abi_version() == 2
+    assert B.spec_abi_version() == B.ABI_VERSION == 3
     assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
     assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
     assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
@@ -157,6 +158,69 @@ def test_tree_validation(kw, code):
         assert B.lib().spec_verify_tree(ctypes.byref(a), None, 0, None) == B.SPEC_ERR_WORKSPACE
     else:
         assert B.lib().spec_verify_tree(ctypes.byref(a), 0x100000, 1 << 20, None) == code
+
+
+TH, KS = (1, 2, 2), ((6,), (2, 2), (1, 1))
+
+
+def test_tree_draft_workspace_size():
+    n = B.spec_tree_draft_workspace_size(128, 151936, TH, KS)
+    assert n > 0 and n % 256 == 0
+    assert B.spec_tree_draft_workspace_size(128, 151936, (2, 2), ((1, 1), (1, 1))) == 0
+    assert B.spec_tree_draft_workspace_size(128, 4, (1,), ((5,),)) == 0  # K > V
+    assert B.spec_tree_draft_workspace_size(-1, 100, TH, KS) == 0
+
+
+def _draft(th=TH, ks=KS, **kw):
+    base = dict(batch=2, vocab=100, row_stride=104, depth=len(th), step=0, tree_stride=13,
+                expand_stride=2, draft_logits=0x1000, root_token=0x2000, parent=0x3000,
+                node_token=0x4000, node_row=0x5000, node_logp=0x6000, position_ids=0x7000,
+                ancestor_mask=0x8000, expand_nodes=0x9000)
+    base.update(kw)
+    a = B.spec_tree_draft_args()
+    thc = (ctypes.c_int32 * len(th))(*th)
+    flat = [k for s in range(len(th)) for k in ks[s]]
+    ksc = (ctypes.c_int32 * max(len(flat), 1))(*flat)
+    a._cfg = (thc, ksc)
+    a.top_head = ctypes.cast(thc, ctypes.c_void_p).value
+    a.top_k_spec = ctypes.cast(ksc, ctypes.c_void_p).value
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("th,ks,kw,code", [
+    (TH, KS, dict(batch=-1), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(vocab=0), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(row_stride=100), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(depth=0), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(step=3), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(step=-1), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(tree_stride=12), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(tree_stride=257), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(expand_stride=1), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(draft_logits=None), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(root_token=None), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(ancestor_mask=None), B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(draft_logits=0x1008), B.SPEC_ERR_INVALID_ARG),
+    ((2, 1), ((1, 1), (1,)), dict(), B.SPEC_ERR_INVALID_ARG),          # root is alone
+    ((1, 3), ((2,), (1, 1, 1)), dict(expand_stride=3), B.SPEC_ERR_INVALID_ARG),
+    ((1,), ((0,),), dict(), B.SPEC_ERR_INVALID_ARG),                  # K = 0
+    ((1,), ((65,),), dict(vocab=1000, row_stride=1000), B.SPEC_ERR_INVALID_ARG),
+    ((1,), ((101,),), dict(), B.SPEC_ERR_INVALID_ARG),                # K > V
+    ((1, 2), ((2,), (128, 128)), dict(tree_stride=256, vocab=1000, row_stride=1000),
+     B.SPEC_ERR_INVALID_ARG),
+    (TH, KS, dict(step=1, root_token=None), B.SPEC_ERR_WORKSPACE),    # root read at step 0 only
+])
+def test_tree_draft_validation(th, ks, kw, code):
+    a = _draft(th, ks, **kw)
+    assert B.lib().spec_tree_draft_step(ctypes.byref(a), None, 0, None) == code
+    assert B.spec_last_error() != ""
+
+
+def test_tree_draft_empty_batch_is_a_no_op():
+    a = _draft(batch=0)
+    assert B.lib().spec_tree_draft_step(ctypes.byref(a), None, 0, None) == B.SPEC_OK
 
 
 def _kv(**kw):

@@ -1,0 +1,242 @@
+"""GPU parity of spec_tree_draft_step against the fp64 oracle through the C ABI
+("投机推理：小模型搭树，大模型一次验证": tree configuration and draft steps; "10.6 投机解码"
+§10.6.3: ancestor mask of Table 10-17 and depth positions).
+
+Tokens, parents, expansions, rows, positions and mask bits are compared exactly; path
+log-probabilities within LOGP_TOL. The choice of the next step's expanded nodes is a
+floating-point decision (path log-probabilities, decided in fp32 by the kernel): a sequence
+whose oracle margin between neighbouring ranked candidates falls below LOGP_TOL at some step
+is counted and compared only up to that step.
+
+LOGP_TOL: the kernel's log-probability is (l - M) - log(Z) per step, summed over at most
+64 steps in fp32; (l - M) is exact, Z is an fp32 sum of at most 2^19 terms of relative error
+well below 1e-6 in these rows, and each addition rounds to half an ulp of |logp| < 64
+(2^-19): a few 1e-6 per step at the depths tested here, so 5e-5 bounds it with room.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_verification_03_amd import binding as B
+from draft_verification_03_amd import workloads as W
+
+from harness import dev, say
+
+pytestmark = pytest.mark.gpu
+
+LOGP_TOL = 5e-5
+
+
+def run_gpu(x, tree_stride=None, expand_stride=None, corrupt=None):
+    """All steps of one tree round on the GPU; returns host copies of the tree arrays and the
+    expansion list after every step."""
+    th, ks, Bn = x["top_head"], x["top_k_spec"], x["batch"]
+    n = oracle.tree_nodes(th, ks)
+    ts = n if tree_stride is None else tree_stride
+    es = max(th) if expand_stride is None else expand_stride
+    mw = (ts + 31) // 32
+    i32 = dict(dtype=torch.int32, device="cuda")
+    t = dict(parent=torch.full((Bn, ts), 7, **i32), node_token=torch.full((Bn, ts), 7, **i32),
+             node_row=torch.full((Bn, ts), 7, **i32),
+             node_logp=torch.full((Bn, ts), 7.0, dtype=torch.float32, device="cuda"),
+             position_ids=torch.full((Bn, ts), 7, **i32),
+             ancestor_mask=torch.full((Bn, ts, mw), 7, **i32),
+             expand_nodes=torch.full((Bn, es), -7, **i32))
+    flags = torch.zeros(Bn, **i32)
+    root, pos = dev(x["root_token"]), dev(x["pos_base"])
+    ws = None
+    expands = []
+    for s in range(len(th)):
+        if corrupt is not None and s == corrupt[0]:
+            t["expand_nodes"][corrupt[1], 0] = corrupt[2]
+        rows = dev(x["rows"][s])
+        a = B.tree_draft_args(top_head=th, top_k_spec=ks, step=s, draft_logits=rows,
+                              root_token=root, pos_base=pos, seq_flags=flags, vocab=x["vocab"],
+                              **t)
+        ws = B.spec_tree_draft_step(a, workspace=ws)
+        torch.cuda.synchronize()
+        expands.append(t["expand_nodes"].cpu().numpy().copy())
+    out = {k: v.cpu().numpy() for k, v in t.items()}
+    out["ancestor_mask"] = out["ancestor_mask"].view(np.uint32)
+    out["seq_flags"] = flags.cpu().numpy()
+    out["expands"] = expands
+    out["num_nodes"] = n
+    return out
+
+
+def run_oracle(x, tree_stride=None):
+    return oracle.tree_draft(x["rows"], x["top_head"], x["top_k_spec"], x["root_token"],
+                             pos_base=x["pos_base"], tree_stride=tree_stride, vocab=x["vocab"],
+                             nthreads=16)
+
+
+def compare(x, o, g, label=""):
+    """Returns the number of sequences with a selection near its decision boundary."""
+    th = x["top_head"]
+    depth = len(th)
+    n = o["num_nodes"]
+    ts = o["parent"].shape[1]
+    layer = o["position_ids"] - x["pos_base"][:, None]  # depth of created nodes
+    boundary = 0
+    for b in range(x["batch"]):
+        sb = depth  # first step whose expansion is a near-boundary decision
+        for s in range(1, depth):
+            if o["select_margin"][s, b] < LOGP_TOL:
+                sb = s
+                break
+        boundary += sb < depth
+        # nodes of layers 0..sb were made before the first uncertain expansion was used
+        ok = np.zeros(ts, bool)
+        ok[:n] = layer[b, :n] <= sb
+        for k in ("parent", "node_token", "position_ids"):
+            assert np.array_equal(g[k][b][ok], o[k][b][ok]), (label, b, k)
+        # node rows of layer l nodes are decided by the expansion of step l
+        okr = np.zeros(ts, bool)
+        okr[:n] = layer[b, :n] < sb
+        assert np.array_equal(g["node_row"][b][okr], o["node_row"][b][okr]), (label, b, "row")
+        lo, lg = o["node_logp"][b][ok], g["node_logp"][b][ok].astype(np.float64)
+        fin = np.isfinite(lo)
+        assert np.array_equal(np.isfinite(lg), fin), (label, b)
+        assert np.all(lo[~fin] == lg[~fin]), (label, b)
+        if fin.any():
+            err = np.max(np.abs(lo[fin] - lg[fin]))
+            assert err <= LOGP_TOL, (label, b, err)
+        bits = np.unpackbits(g["ancestor_mask"][b].view(np.uint8), axis=1,
+                             bitorder="little")[:, :ts]
+        for i in np.nonzero(ok)[0]:
+            assert np.array_equal(bits[i], o["ancestor"][b, i]), (label, b, i)
+        # the list left after step s - 1 is what step s expands
+        for s in range(1, min(sb + 1, depth)):
+            assert np.array_equal(g["expands"][s - 1][b, :th[s]], o["expand"][s, b, :th[s]]), \
+                (label, b, s)
+        # entries past the tree keep their initial values
+        assert (g["parent"][b, n:] == -1).all() and (g["node_token"][b, n:] == -1).all()
+        assert (g["node_row"][b, n:] == -1).all() and (g["position_ids"][b, n:] == -1).all()
+        assert np.isneginf(g["node_logp"][b, n:]).all() and (bits[n:] == 0).all()
+    assert (g["seq_flags"] == 0).all()
+    return boundary
+
+
+def check(x, label, tree_stride=None, expand_stride=None):
+    say(f"[tree-draft] {label}: B={x['batch']} V={x['vocab']} top_head={x['top_head']} "
+        f"top_k_spec={x['top_k_spec']}")
+    g = run_gpu(x, tree_stride, expand_stride)
+    o = run_oracle(x, tree_stride)
+    nb = compare(x, o, g, label)
+    say(f"[tree-draft] {label}: sequences with a near-boundary expansion: {nb}")
+    assert nb <= max(1, x["batch"] // 50)
+    return o, g
+
+
+CONFIGS = [
+    ((1, 2, 2), ((6,), (2, 2), (1, 1))),
+    ((1, 3, 2), ((3,), (3, 2, 1), (2, 2))),
+    ((1,), ((5,),)),
+    ((1, 1, 1, 1), ((1,), (1,), (1,), (1,))),
+    ((1, 4), ((4,), (2, 1, 3, 1))),
+]
+
+
+@pytest.mark.parametrize("cfg", range(len(CONFIGS)))
+@pytest.mark.parametrize("V,quant", [(3000, None), (2999, 1), (40000, None), (40003, 2)])
+def test_small(cfg, V, quant):
+    th, ks = CONFIGS[cfg]
+    x = W.tree_draft_inputs(seed=80 + cfg, B=16, V=V, top_head=th, top_k_spec=ks, quant=quant)
+    check(x, f"cfg{cfg} V={V} quant={quant}")
+
+
+def test_page_shape_full_size():
+    """The page's tree ([6], [2, 2], [1, 1] with top_head [1, 2, 2]) at B=128, V=151936."""
+    x = W.tree_draft_inputs()
+    o, g = check(x, "page shape, B=128 V=151936")
+    assert g["num_nodes"] == 13
+
+
+def test_largest_children_and_heads():
+    """64 children per node (the most) and 64 expanded nodes per step (the most)."""
+    x = W.tree_draft_inputs(seed=90, B=8, V=151936, top_head=(1, 2, 3),
+                            top_k_spec=((64,), (64, 64), (20, 20, 20)))
+    check(x, "K=64")
+    x = W.tree_draft_inputs(seed=91, B=8, V=50000, top_head=(1, 64), top_k_spec=((64,), (1,) * 64))
+    check(x, "64 heads")
+
+
+def test_tiny_vocab_and_k_equal_to_v():
+    x = W.tree_draft_inputs(seed=92, B=32, V=5, top_head=(1, 2), top_k_spec=((5,), (5, 3)))
+    check(x, "V=5, K=V")
+    x = W.tree_draft_inputs(seed=93, B=32, V=13, top_head=(1, 3), top_k_spec=((4,), (13, 1, 2)),
+                            quant=1)
+    check(x, "V=13 ties")
+
+
+def test_rows_with_fewer_finite_logits_than_k():
+    """Children beyond the finite logits are -inf tokens, lowest ids first."""
+    x = W.tree_draft_inputs(seed=94, B=8, V=20000, top_head=(1, 2), top_k_spec=((6,), (4, 4)))
+    for r in x["rows"]:
+        keep = np.random.default_rng(5).integers(0, 20000, size=3)
+        bits = r.copy()
+        bits[:, :20000] = 0xFF80  # -inf
+        bits[:, keep] = r[:, keep]
+        r[:] = bits
+    o, g = check(x, "3 finite logits per row")
+    assert np.isneginf(o["node_logp"]).any()
+
+
+def test_wider_tree_stride_and_expand_stride():
+    x = W.tree_draft_inputs(seed=95, B=16, V=32000)
+    check(x, "tree_stride 64, expand_stride 9", tree_stride=64, expand_stride=9)
+
+
+def test_corrupt_expand_list_flags_the_sequence():
+    x = W.tree_draft_inputs(seed=96, B=4, V=8000)
+    g = run_gpu(x, corrupt=(2, 2, 3))  # sequence 2, step 2: node 3 is not in layer 2
+    assert g["seq_flags"][2] == B.FLAG_BAD_TREE
+    assert (g["seq_flags"][[0, 1, 3]] == 0).all()
+    assert (g["parent"][2, 11:] == -1).all()  # its step 2 wrote nothing
+    o = run_oracle(x)
+    assert np.array_equal(g["parent"][2, :11], o["parent"][2, :11])
+
+
+def test_repeatable_bits():
+    x = W.tree_draft_inputs(seed=97, B=32, V=151936)
+    g1, g2 = run_gpu(x), run_gpu(x)
+    for k in ("parent", "node_token", "node_row", "node_logp", "position_ids", "ancestor_mask"):
+        assert np.array_equal(g1[k].view(np.uint32), g2[k].view(np.uint32)), k
+
+
+def test_tree_round_draft_then_verify():
+    """The drafted tree feeds spec_verify_tree as it is: the accepted path and emitted
+    tokens equal the oracle's verification of the oracle's tree."""
+    x = W.tree_draft_inputs(seed=98, B=64, V=151936)
+    g = run_gpu(x)
+    o = run_oracle(x)
+    nb = compare(x, o, g, "round")
+    rng = np.random.default_rng(98)
+    R = sum(x["top_head"])
+    n = g["num_nodes"]
+    # target rows: the draft rows of each expanded node plus noise, so paths are accepted
+    tl = np.zeros((x["batch"], R, x["stride"]), np.uint16)
+    base = 0
+    for s, h in enumerate(x["top_head"]):
+        d = W.bf16_to_f32(x["rows"][s][:, :x["vocab"]]).reshape(x["batch"], h, -1)
+        t = d + rng.standard_normal(d.shape, dtype=np.float32) * np.float32(0.3)
+        tl[:, base:base + h, :x["vocab"]] = W.bf16_bits(t)
+        base += h
+    ov = oracle.verify_tree(tl, o["parent"], o["node_row"], o["node_token"], R, 3, n,
+                            vocab=x["vocab"])
+    pn = torch.zeros((x["batch"], 3), dtype=torch.int32, device="cuda")
+    pl = torch.zeros(x["batch"], dtype=torch.int32, device="cuda")
+    to = torch.zeros((x["batch"], 4), dtype=torch.int32, device="cuda")
+    ne = torch.zeros(x["batch"], dtype=torch.int32, device="cuda")
+    a = B.tree_args(target_logits=dev(tl), parent=dev(g["parent"]), node_row=dev(g["node_row"]),
+                    node_token=dev(g["node_token"]), path_nodes=pn, path_len=pl, out_tokens=to,
+                    num_emitted=ne, vocab=x["vocab"], rows_per_seq=R, max_depth=3,
+                    tree_stride=n)
+    B.spec_verify_tree(a)
+    torch.cuda.synchronize()
+    if nb == 0:
+        assert np.array_equal(pl.cpu().numpy(), ov["path_len"])
+        assert np.array_equal(pn.cpu().numpy(), ov["path_nodes"])
+        assert np.array_equal(ne.cpu().numpy(), ov["num_emitted"])
+    say(f"[tree-draft] round: mean accepted {ov['path_len'].mean():.2f}")
