@@ -11,6 +11,12 @@ bounded sample of the same workload as a reported baseline.
 
   python bench.py [--steps K] [--warmup W] [--warmup-seconds S] [--gpus 1] [--no-cpu-baseline]
   python bench.py --copy-calibration     # a plain copy of known size, for counter scaling
+  python bench.py --workload tree_draft  # the tree-drafting steps of one round instead
+
+With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
+大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
+with V=151936 draft rows: three spec_tree_draft_step calls reading 128, 256 and 256 draft
+rows. The line reports draft rows/s and the HBM bandwidth of the steps against 8 TB/s.
 """
 from __future__ import annotations
 
@@ -119,6 +125,100 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+def tree_draft_bench(args):
+    """One round of tree drafting per step (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import ctypes
+    from draft_verification_03_amd import binding as B
+    from draft_verification_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("generating the tree-drafting workload (B=128, V=151936, top_head [1,2,2])")
+    x = W.tree_draft_inputs()
+    th, ks, Bn, V = x["top_head"], x["top_k_spec"], x["batch"], x["vocab"]
+    n = 1 + sum(sum(k) for k in ks)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    t = dict(parent=torch.empty((Bn, n), **i32), node_token=torch.empty((Bn, n), **i32),
+             node_row=torch.empty((Bn, n), **i32),
+             node_logp=torch.empty((Bn, n), dtype=torch.float32, device="cuda"),
+             position_ids=torch.empty((Bn, n), **i32),
+             ancestor_mask=torch.empty((Bn, n, (n + 31) // 32), **i32),
+             expand_nodes=torch.empty((Bn, max(th)), **i32))
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
+        np.int16 if a.dtype == np.uint16 else a.dtype)).cuda()
+    rows = [dv(r) for r in x["rows"]]
+    root, pos = dv(x["root_token"]), dv(x["pos_base"])
+    steps = [B.tree_draft_args(top_head=th, top_k_spec=ks, step=s, draft_logits=rows[s],
+                               root_token=root, pos_base=pos, vocab=V, **t)
+             for s in range(len(th))]
+    ws = torch.empty(B.spec_tree_draft_workspace_size(Bn, V, th, ks), dtype=torch.uint8,
+                     device="cuda")
+    L = B.lib()
+    wsp, wsn = ws.data_ptr(), ws.numel()
+
+    def round_(stream):
+        for a in steps:
+            rc = L.spec_tree_draft_step(ctypes.byref(a), wsp, wsn, stream)
+            if rc != 0:
+                raise B.SpecError(rc, B.spec_last_error())
+
+    st = torch.cuda.current_stream().cuda_stream
+    t_warm = time.time()
+    done = 0
+    while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        for _ in range(10):
+            round_(st)
+        done += 10
+        torch.cuda.synchronize()
+    log(f"timing {args.steps} rounds")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        round_(st)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nrows = Bn * sum(th)
+    row_bytes = nrows * V * 2
+    gbs = row_bytes / (ms / 1e3) / 1e9
+    log(f"round {ms * 1e3:.1f} us for {nrows} draft rows ({gbs:.0f} GB/s)")
+    res = {
+        "metric": "tree drafting: draft rows/s at B=128 V=151936, top_head [1,2,2], "
+                  "top_k_spec [[6],[2,2],[1,1]]; achieved HBM GB/s vs peak",
+        "value": nrows / (ms / 1e3), "unit": "draft rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "tree drafting round, B=128, V=151936 bf16 draft rows "
+                               "N(0,2^2), top_head [1,2,2], top_k_spec [[6],[2,2],[1,1]]",
+                   "draft_rows_per_round": nrows, "round_algorithmic_bytes": row_bytes},
+        "roofline": {"bound": "hbm", "kernel": "draft_topk_kernel + tree_grow_kernel",
+                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_launch": row_bytes, "avg_launch_us": ms * 1e3,
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the oracle on whole rounds")
+        oracle.lib()
+        t0 = time.time()
+        reps = 0
+        while time.time() - t0 < 10.0 or reps == 0:
+            oracle.tree_draft(x["rows"], th, ks, x["root_token"], pos_base=x["pos_base"],
+                              vocab=V, nthreads=16)
+            reps += 1
+        el = time.time() - t0
+        res["cpu_baseline"] = {"value": reps * nrows / el, "unit": "draft rows/s", "cores": 16,
+                               "kind": "oracle",
+                               "sample": f"{reps} whole rounds ({nrows} draft rows each), "
+                                         f"{el:.1f} s wall"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +228,7 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workload", choices=["chain", "tree_draft"], default="chain")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
@@ -136,6 +237,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "tree_draft":
+        tree_draft_bench(args)
         return
 
     import numpy as np

@@ -3,12 +3,14 @@
 // Table 10-17).
 //
 //  1. draft_topk_kernel -- every draft row of the step is split into S chunks, one
-//     256-thread workgroup per chunk. The chunk streams from HBM once with 16-byte loads.
-//     Every lane keeps a running maximum and sum of exp(l - max) (the softmax normaliser);
-//     every wave keeps (logit, token) candidates in LDS behind a threshold, the K-th largest
-//     logit the wave holds, so that after its first trip almost nothing passes. A wave's best
-//     K come from K rounds of a wave-wide maximum over its candidates; the workgroup merges
-//     its waves' lists and writes one record (max, sum, best K) per chunk.
+//     256-thread workgroup per chunk. The chunk streams from HBM once with 16-byte loads,
+//     two trips of 2 KB per wave in flight. Every lane keeps a running maximum and sum of
+//     exp(l - max) (the softmax normaliser); every wave keeps (logit, token) candidates in LDS
+//     behind a threshold: first the K-th largest of its lanes' first-trip maxima (K logits lie
+//     at or above it), then the K-th largest candidate held, so that a trip whose lanes all
+//     stay below it costs one ballot. A wave's best K come from K rounds of a wave-wide
+//     maximum over its candidates; the workgroup merges its waves' lists and writes one record
+//     (max, sum, best K) per chunk.
 //  2. tree_grow_kernel -- one workgroup per sequence merges each expanded node's S records
 //     into the row's normaliser and its K best tokens, appends the children with their path
 //     log-probabilities, positions and ancestor-mask rows, and ranks the new layer by path
@@ -25,17 +27,17 @@ namespace {
 
 constexpr int kDraftWaves = 4;
 constexpr int kDraftThreads = kDraftWaves * kWave;
-constexpr int kCandCap = 1024;  // candidate slots per wave
-constexpr int kCandRegs = kCandCap / kWave;
+constexpr int kTv = 2;                  // vectors per lane per trip
+constexpr int kTripVec = kTv * kWave;   // a wave's trip: 128 vectors, 1024 logits
+constexpr int kCandCap = kTripVec * 8 + kTreeDraftMaxK;  // a compacted list plus one trip
 constexpr int kGrowThreads = 256;
+constexpr int kGrowWaves = kGrowThreads / kWave;
+constexpr int kStageCap = kTreeDraftMaxSplits * kTreeDraftMaxK;  // a row's merged candidates
 constexpr int kMaxHead = kTreeDraftMaxHead;
 constexpr int kMaskWordsMax = 8;  // 256 nodes
-constexpr int kTargetWgs = 1024;  // about four workgroups per CU
+constexpr int kTargetWgs = 1024;  // four 256-thread workgroups per CU
 constexpr int kMinChunkVec = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
-
-static_assert(kTreeDraftMaxSplits * kTreeDraftMaxK <= kCandRegs * kWave,
-              "a row's merged candidates must fit the merge registers");
 
 // A candidate packs the bf16 order key above the complement of the token id: the larger
 // candidate has the larger logit, or the same logit and the lower id. 0 is no candidate (key 0
@@ -48,15 +50,28 @@ __device__ __forceinline__ float cand_logit(uint64_t c) {
   return value_of_key((uint32_t)(c >> 32));
 }
 
+// One DPP step of a 64-bit maximum: lanes that the move does not write keep their own value.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_max_u64_step(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v,
+                                                            CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+      (int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF, false);
+  const uint64_t w = ((uint64_t)hi << 32) | lo;
+  return w > v ? w : v;
+}
+// Wave maximum of a 64-bit value through the same DPP tree as wave_max_dpp, read back from
+// lane 63.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+  v = dpp_max_u64_step<0xB1>(v);
+  v = dpp_max_u64_step<0x4E>(v);
+  v = dpp_max_u64_step<0x141>(v);
+  v = dpp_max_u64_step<0x140>(v);
+  v = dpp_max_u64_step<0x142, 0xA>(v);
+  v = dpp_max_u64_step<0x143, 0xC>(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
@@ -65,40 +80,52 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// The K (<= 64) largest of the wave's candidates e[] (0 = empty), largest first: lane r
-// receives the r-th in `mine`. Returns how many exist (< K when fewer candidates are held).
-template <int R>
-__device__ __forceinline__ int wave_top(const uint64_t (&e)[R], int K, uint64_t& mine) {
+// The K (<= 64) largest of the candidates src[0..n) in LDS (0 = empty slot), largest first:
+// lane r receives the r-th in `mine` (0 past the end). Returns how many exist. K rounds, each
+// a scan of the lane's entries and a wave maximum below the previous round's.
+__device__ __forceinline__ int wave_select(const uint64_t* src, int n, int K, int lane,
+                                           uint64_t& mine) {
   uint64_t prev = ~0ull;
   int found = 0;
   mine = 0;
   for (int r = 0; r < K; ++r) {
     uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < R; ++i) best = (e[i] < prev && e[i] > best) ? e[i] : best;
+    for (int j = lane; j < n; j += kWave) {
+      const uint64_t e = src[j];
+      best = (e < prev && e > best) ? e : best;
+    }
     best = wave_max_u64(best);
     if (best == 0) break;
-    if (lane_id() == r) mine = best;
+    if (lane == r) mine = best;
     prev = best;
     ++found;
   }
   return found;
 }
 
-// Reduces a wave's candidate buffer (n entries) to its K best, largest first, and returns
-// their number; tau becomes the K-th best's logit (-inf while fewer than K are held).
+// Reduces a wave's candidate buffer to its K best, largest first, in place; tau becomes the
+// K-th best's logit (-inf while fewer than K are held). Returns the new count.
 __device__ __forceinline__ int compact(uint64_t* buf, int n, int K, float& tau, int lane) {
-  uint64_t e[kCandRegs];
-#pragma unroll
-  for (int i = 0; i < kCandRegs; ++i) {
-    const int j = i * kWave + lane;
-    e[i] = j < n ? buf[j] : 0ull;
-  }
   uint64_t mine;
-  const int f = wave_top(e, K, mine);
-  if (lane < f) buf[lane] = mine;
+  const int f = wave_select(buf, n, K, lane, mine);
+  if (lane < f) buf[lane] = mine;  // every read of the rounds above precedes this write
   tau = f == K ? cand_logit(readlane_u64(mine, K - 1)) : -INFINITY;
   return f;
+}
+
+// The K-th largest of the 64 lanes' values v, repeats counted (-inf if fewer than K lanes
+// hold a finite value): at least K lanes hold a value at or above it.
+__device__ __forceinline__ float lane_kth_max(float v, int K) {
+  float last = -INFINITY;
+  int taken = 0;
+  while (taken < K) {
+    const float m = wave_max_dpp(v);
+    if (m == -INFINITY) return -INFINITY;
+    taken += __popcll(__ballot(v == m));
+    last = m;
+    v = (v == m) ? -INFINITY : v;
+  }
+  return last;
 }
 
 struct DraftParams {
@@ -115,88 +142,131 @@ struct PartHead {
   int32_t pad;
 };
 
+// Loads one trip (kTv vectors per lane, kWave vectors apart) of a chunk of nv vectors;
+// vectors past the chunk read as -inf.
+__device__ __forceinline__ void load_trip2(const uint4* __restrict__ base, int v0, int nv,
+                                           int lane, uint4 (&d)[kTv]) {
+  if (v0 + kTripVec <= nv) {
+#pragma unroll
+    for (int u = 0; u < kTv; ++u) d[u] = base[v0 + u * kWave + lane];
+  } else {
+#pragma unroll
+    for (int u = 0; u < kTv; ++u) {
+      const int v = v0 + u * kWave + lane;
+      d[u] = v < nv ? base[v] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kDraftThreads) void draft_topk_kernel(DraftParams P) {
   __shared__ uint64_t s_buf[kDraftWaves][kCandCap];
+  __shared__ uint64_t s_merge[kDraftWaves * kWave];
   __shared__ float s_m[kDraftWaves], s_s[kDraftWaves];
-  __shared__ int s_n[kDraftWaves];
   const int row = blockIdx.x / P.S;
   const int split = blockIdx.x - row * P.S;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int K = P.kk[row % P.h];
   const int c0 = split * P.chunk;
-  const int c1 = min(P.nvec, c0 + P.chunk);
-  const int lim = min(P.V, c1 * 8);  // token ids of this chunk lie below lim
+  const int nv = max(0, min(P.nvec, c0 + P.chunk) - c0);  // vectors of this chunk
+  const int lim = min(P.V, (c0 + nv) * 8);                 // its token ids lie below lim
   uint64_t* buf = s_buf[wave];
   float m = -INFINITY, s = 0.f, tau = -INFINITY;
   int n = 0;
-  if (c1 > c0) {
-    const uint4* rp = reinterpret_cast<const uint4*>(P.logits + (size_t)row * P.stride) + c0;
-    stream_row_strided<2>(rp, c1 - c0, lane, wave, kDraftWaves, [&](uint4* d, int v0, bool ml) {
-      if (ml) mask_tail(d, c0 + v0, P.nvec, P.V, lane);
-      float x[kU][8];
+  bool first = true;
+  const uint4* base = reinterpret_cast<const uint4*>(P.logits + (size_t)row * P.stride) + c0;
+
+  auto consume = [&](uint4 (&d)[kTv], int v0) {
+    if (c0 + v0 + kTripVec >= P.nvec) {  // the trip may hold the row's last vector
+      const int rem = P.V & 7;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) unpack8(d[u], x[u]);
-      float vm[kU];
+      for (int u = 0; u < kTv; ++u) {
+        if (rem != 0 && c0 + v0 + u * kWave + lane == P.nvec - 1) {
+          uint32_t w[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
 #pragma unroll
-      for (int u = 0; u < kU; ++u) vm[u] = max8(x[u]);
-      static_assert(kU == 4, "trip max below assumes four vectors per trip");
-      const float tm = vmax3(vmax3(vm[0], vm[1], vm[2]), vm[3], vm[3]);
-      if (tm > m) {
-        s = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - tm) * kLog2e);
-        m = tm;
-      }
-      if (m != -INFINITY) {
-        const float nref = -m * kLog2e;
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[u][e], kLog2e, nref));
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (__ballot(vm[u] >= tau) == 0) continue;  // wave-uniform: nothing passes
-        if (n + 8 * kWave > kCandCap) n = compact(buf, n, K, tau, lane);
-        const int vg = c0 + v0 + u * kWave + lane;  // vector index in the row
-        const uint32_t w[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
-        uint32_t fl = 0;
-        int c = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = x[u][e] >= tau && vg * 8 + e < lim;
-          fl |= (uint32_t)ok << e;
-          c += ok;
-        }
-        const int incl = wave_incl_scan_dpp(c);
-        const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        int off = n + incl - c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (fl >> e & 1u) {
-            const uint32_t b16 = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
-            buf[off++] = cand_of(b16, (uint32_t)(vg * 8 + e));
+          for (int e = 0; e < 8; ++e) {
+            if (e >= rem) {
+              if (e & 1) w[e >> 1] = (w[e >> 1] & 0x0000FFFFu) | 0xFF800000u;
+              else w[e >> 1] = (w[e >> 1] & 0xFFFF0000u) | 0x0000FF80u;
+            }
           }
+          d[u] = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        n += total;
       }
-    });
+    }
+    float x[kTv * 8];
+#pragma unroll
+    for (int u = 0; u < kTv; ++u) unpack8(d[u], x + 8 * u);
+    float tm = vmax3(x[0], x[1], x[2]);
+#pragma unroll
+    for (int i = 3; i + 1 < kTv * 8; i += 2) tm = vmax3(tm, x[i], x[i + 1]);
+    tm = vmax3(tm, x[kTv * 8 - 1], x[kTv * 8 - 1]);
+    if (tm > m) {
+      s = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - tm) * kLog2e);
+      m = tm;
+    }
+    if (m != -INFINITY) {
+      const float nref = -m * kLog2e;
+#pragma unroll
+      for (int i = 0; i < kTv * 8; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, nref));
+    }
+    if (first) {  // seed the threshold: K lanes hold a logit at or above this bound
+      tau = lane_kth_max(tm, K);
+      first = false;
+    }
+    if (__ballot(tm >= tau) == 0) return;  // nothing passes (wave-uniform)
+    uint32_t fl = 0;
+#pragma unroll
+    for (int i = 0; i < kTv * 8; ++i) {
+      const int idx = (c0 + v0 + (i >> 3) * kWave + lane) * 8 + (i & 7);
+      fl |= (uint32_t)(x[i] >= tau && idx < lim) << i;
+    }
+    const int cnt = __popc(fl);
+    const int incl = wave_incl_scan_dpp(cnt);
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (n + total > kCandCap) n = compact(buf, n, K, tau, lane);  // then n <= K <= 64
+    int off = n + incl - cnt;
+    while (fl) {
+      const int i = __builtin_ctz(fl);
+      fl &= fl - 1;
+      float val = x[0];
+#pragma unroll
+      for (int k = 1; k < kTv * 8; ++k) val = (i == k) ? x[k] : val;
+      const int idx = (c0 + v0 + (i >> 3) * kWave + lane) * 8 + (i & 7);
+      buf[off++] = cand_of(__float_as_uint(val) >> 16, (uint32_t)idx);
+    }
+    n += total;
+  };
+
+  // this wave's trips t = wave, wave + 4, ...: two in flight, alternating buffers
+  int t = wave;
+  uint4 da[kTv], db[kTv];
+  if (t * kTripVec < nv) load_trip2(base, t * kTripVec, nv, lane, da);
+  while (t * kTripVec < nv) {
+    const int t1 = t + kDraftWaves;
+    if (t1 * kTripVec < nv) load_trip2(base, t1 * kTripVec, nv, lane, db);
+    consume(da, t * kTripVec);
+    if (t1 * kTripVec >= nv) break;
+    const int t2 = t1 + kDraftWaves;
+    if (t2 * kTripVec < nv) load_trip2(base, t2 * kTripVec, nv, lane, da);
+    consume(db, t1 * kTripVec);
+    t = t2;
   }
-  n = compact(buf, n, K, tau, lane);
+  {
+    uint64_t mine;
+    const int f = wave_select(buf, n, K, lane, mine);
+    s_merge[wave * kWave + lane] = lane < f ? mine : 0ull;
+  }
   // the wave's normaliser relative to its own maximum
   const float mw = wave_max_dpp(m);
   const float sw = wave_sum_dpp(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mw) * kLog2e));
   if (lane == 0) {
     s_m[wave] = mw;
     s_s[wave] = sw;
-    s_n[wave] = n;
   }
   __syncthreads();
   if (wave != 0) return;
-  // wave 0 merges the workgroup: the waves' lists hold at most K <= 64 entries each
-  uint64_t e[kDraftWaves];
-#pragma unroll
-  for (int w = 0; w < kDraftWaves; ++w) e[w] = lane < s_n[w] ? s_buf[w][lane] : 0ull;
   uint64_t mine;
-  const int f = wave_top(e, K, mine);
+  const int f = wave_select(s_merge, kDraftWaves * kWave, K, lane, mine);
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kDraftWaves; ++w) M = fmaxf(M, s_m[w]);
@@ -240,6 +310,7 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
   __shared__ int s_ppos[kMaxHead];
   __shared__ uint32_t s_pmask[kMaxHead][kMaskWordsMax];
   __shared__ float s_lp[kTreeDraftMaxNodes];
+  __shared__ uint64_t s_stage[kGrowWaves][kStageCap];
   __shared__ int s_bad;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -299,7 +370,7 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
     return;
   }
   // children of each expanded node, one wave per node
-  for (int j = wave; j < P.h; j += kGrowThreads / kWave) {
+  for (int j = wave; j < P.h; j += kGrowWaves) {
     const size_t row = (size_t)b * P.h + j;
     const uint8_t* rec0 = P.part + row * P.S * P.rec_bytes;
     float m = -INFINITY, sm = 0.f;
@@ -312,17 +383,15 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
     const float Z = wave_sum_dpp(m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f((m - M) * kLog2e));
     const float lz = logf(Z);  // log of sum over the row of exp(l - M)
     const int K = P.kk[j];
-    uint64_t e[kCandRegs];
-#pragma unroll
-    for (int t = 0; t < kCandRegs; ++t) {
-      const int i = t * kWave + lane;
+    const int nc = P.S * K;  // the S chunk lists, K candidates each
+    uint64_t* stage = s_stage[wave];
+    for (int i = lane; i < nc; i += kWave) {
       const int li = i / K, r = i - li * K;
-      e[t] = li < P.S ? reinterpret_cast<const uint64_t*>(rec0 + (size_t)li * P.rec_bytes +
-                                                          sizeof(PartHead))[r]
-                      : 0ull;
+      stage[i] = reinterpret_cast<const uint64_t*>(rec0 + (size_t)li * P.rec_bytes +
+                                                   sizeof(PartHead))[r];
     }
     uint64_t mine;
-    const int f = wave_top(e, K, mine);
+    const int f = wave_select(stage, nc, K, lane, mine);
     if (lane < f) {
       const int c = P.first_new + P.koff[j] + lane;
       const float l = cand_logit(mine);
