@@ -29,7 +29,9 @@ constexpr int kDraftWaves = 4;
 constexpr int kDraftThreads = kDraftWaves * kWave;
 constexpr int kTv = 2;                  // vectors per lane per trip
 constexpr int kTripVec = kTv * kWave;   // a wave's trip: 128 vectors, 1024 logits
-constexpr int kCandCap = kTripVec * 8 + kTreeDraftMaxK;  // a compacted list plus one trip
+constexpr int kStageSlots = 2 * kWave;  // staged lane-trips per wave
+constexpr int kFlushLanes = 32;         // staged lane-trips turned into candidates at once
+constexpr int kCandCap = kFlushLanes * kTv * 8 + kTreeDraftMaxK;  // a compacted list + a group
 constexpr int kGrowThreads = 256;
 constexpr int kGrowWaves = kGrowThreads / kWave;
 constexpr int kStageCap = kTreeDraftMaxSplits * kTreeDraftMaxK;  // a row's merged candidates
@@ -103,13 +105,13 @@ __device__ __forceinline__ int wave_select(const uint64_t* src, int n, int K, in
   return found;
 }
 
-// Reduces a wave's candidate buffer to its K best, largest first, in place; tau becomes the
-// K-th best's logit (-inf while fewer than K are held). Returns the new count.
+// Reduces a wave's candidate buffer to its K best, largest first, in place, and returns the
+// new count; tau rises to the K-th best's logit when K are held.
 __device__ __forceinline__ int compact(uint64_t* buf, int n, int K, float& tau, int lane) {
   uint64_t mine;
   const int f = wave_select(buf, n, K, lane, mine);
   if (lane < f) buf[lane] = mine;  // every read of the rounds above precedes this write
-  tau = f == K ? cand_logit(readlane_u64(mine, K - 1)) : -INFINITY;
+  if (f == K) tau = fmaxf(tau, cand_logit(readlane_u64(mine, K - 1)));
   return f;
 }
 
@@ -160,8 +162,11 @@ __device__ __forceinline__ void load_trip2(const uint4* __restrict__ base, int v
 
 __global__ __launch_bounds__(kDraftThreads) void draft_topk_kernel(DraftParams P) {
   __shared__ uint64_t s_buf[kDraftWaves][kCandCap];
-  __shared__ uint64_t s_merge[kDraftWaves * kWave];
+  __shared__ uint4 s_stage[kDraftWaves][kStageSlots][kTv];
+  __shared__ int s_svec[kDraftWaves][kStageSlots];
   __shared__ float s_m[kDraftWaves], s_s[kDraftWaves];
+  __shared__ int s_n[kDraftWaves];
+  __shared__ float s_tau;  // the largest of the waves' thresholds: a bound for the whole chunk
   const int row = blockIdx.x / P.S;
   const int split = blockIdx.x - row * P.S;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -170,10 +175,61 @@ __global__ __launch_bounds__(kDraftThreads) void draft_topk_kernel(DraftParams P
   const int nv = max(0, min(P.nvec, c0 + P.chunk) - c0);  // vectors of this chunk
   const int lim = min(P.V, (c0 + nv) * 8);                 // its token ids lie below lim
   uint64_t* buf = s_buf[wave];
+  uint4 (*stage)[kTv] = s_stage[wave];
+  int* svec = s_svec[wave];
   float m = -INFINITY, s = 0.f, tau = -INFINITY;
-  int n = 0;
+  int n = 0;   // candidates in buf
+  int ns = 0;  // staged lane-trips
   bool first = true;
   const uint4* base = reinterpret_cast<const uint4*>(P.logits + (size_t)row * P.stride) + c0;
+  if (tid == 0) s_tau = -INFINITY;
+  __syncthreads();
+  // Any wave's threshold bounds the chunk's K-th largest logit from below (that wave holds K
+  // logits at or above it), so every wave filters with the largest one published.
+  auto publish = [&]() {
+    if (lane == 0)
+      __hip_atomic_fetch_max(&s_tau, tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+
+  // Turns the staged lane-trips into candidates, kFlushLanes at a time (one per lane): each
+  // lane appends the logits of its lane-trip that reach the threshold.
+  auto flush = [&]() {
+    for (int g = 0; g < ns; g += kFlushLanes) {
+      if (n + kFlushLanes * kTv * 8 > kCandCap) {  // then n <= K <= 64
+        n = compact(buf, n, K, tau, lane);
+        publish();
+      }
+      const int e = g + lane;
+      uint32_t fl = 0;
+      float x[kTv * 8] = {};
+      int vb = 0;
+      if (lane < kFlushLanes && e < ns) {
+        vb = svec[e];
+#pragma unroll
+        for (int u = 0; u < kTv; ++u) unpack8(stage[e][u], x + 8 * u);
+#pragma unroll
+        for (int i = 0; i < kTv * 8; ++i) {
+          const int idx = (vb + (i >> 3) * kWave) * 8 + (i & 7);
+          fl |= (uint32_t)(x[i] >= tau && idx < lim) << i;
+        }
+      }
+      const int cnt = __popc(fl);
+      const int incl = wave_incl_scan_dpp(cnt);
+      const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+      int off = n + incl - cnt;
+      while (fl) {
+        const int i = __builtin_ctz(fl);
+        fl &= fl - 1;
+        float val = x[0];
+#pragma unroll
+        for (int k = 1; k < kTv * 8; ++k) val = (i == k) ? x[k] : val;
+        const int idx = (vb + (i >> 3) * kWave) * 8 + (i & 7);
+        buf[off++] = cand_of(__float_as_uint(val) >> 16, (uint32_t)idx);
+      }
+      n += total;
+    }
+    ns = 0;
+  };
 
   auto consume = [&](uint4 (&d)[kTv], int v0) {
     if (c0 + v0 + kTripVec >= P.nvec) {  // the trip may hold the row's last vector
@@ -212,29 +268,22 @@ __global__ __launch_bounds__(kDraftThreads) void draft_topk_kernel(DraftParams P
     if (first) {  // seed the threshold: K lanes hold a logit at or above this bound
       tau = lane_kth_max(tm, K);
       first = false;
+      publish();
     }
-    if (__ballot(tm >= tau) == 0) return;  // nothing passes (wave-uniform)
-    uint32_t fl = 0;
+    tau = fmaxf(tau, __hip_atomic_load(&s_tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    // lanes whose trip maximum reaches the threshold stage their lane-trip
+    const bool pass = tm >= tau;
+    const uint64_t bal = __ballot(pass);
+    if (bal == 0) return;  // wave-uniform
+    if (pass) {
+      const int sl = ns + (int)__builtin_amdgcn_mbcnt_hi(
+                              (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 #pragma unroll
-    for (int i = 0; i < kTv * 8; ++i) {
-      const int idx = (c0 + v0 + (i >> 3) * kWave + lane) * 8 + (i & 7);
-      fl |= (uint32_t)(x[i] >= tau && idx < lim) << i;
+      for (int u = 0; u < kTv; ++u) stage[sl][u] = d[u];
+      svec[sl] = c0 + v0 + lane;
     }
-    const int cnt = __popc(fl);
-    const int incl = wave_incl_scan_dpp(cnt);
-    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
-    if (n + total > kCandCap) n = compact(buf, n, K, tau, lane);  // then n <= K <= 64
-    int off = n + incl - cnt;
-    while (fl) {
-      const int i = __builtin_ctz(fl);
-      fl &= fl - 1;
-      float val = x[0];
-#pragma unroll
-      for (int k = 1; k < kTv * 8; ++k) val = (i == k) ? x[k] : val;
-      const int idx = (c0 + v0 + (i >> 3) * kWave + lane) * 8 + (i & 7);
-      buf[off++] = cand_of(__float_as_uint(val) >> 16, (uint32_t)idx);
-    }
-    n += total;
+    ns += (int)__popcll(bal);
+    if (ns > kStageSlots - kWave) flush();  // a trip stages at most kWave lane-trips
   };
 
   // this wave's trips t = wave, wave + 4, ...: two in flight, alternating buffers
@@ -251,22 +300,39 @@ __global__ __launch_bounds__(kDraftThreads) void draft_topk_kernel(DraftParams P
     consume(db, t1 * kTripVec);
     t = t2;
   }
-  {
-    uint64_t mine;
-    const int f = wave_select(buf, n, K, lane, mine);
-    s_merge[wave * kWave + lane] = lane < f ? mine : 0ull;
-  }
+  if (ns > 0) flush();
   // the wave's normaliser relative to its own maximum
   const float mw = wave_max_dpp(m);
   const float sw = wave_sum_dpp(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mw) * kLog2e));
   if (lane == 0) {
     s_m[wave] = mw;
     s_s[wave] = sw;
+    s_n[wave] = n;
   }
   __syncthreads();
   if (wave != 0) return;
-  uint64_t mine;
-  const int f = wave_select(s_merge, kDraftWaves * kWave, K, lane, mine);
+  // wave 0 selects the chunk's K best from every wave's candidates
+  uint64_t mine = 0;
+  int f = 0;
+  {
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < K; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int w = 0; w < kDraftWaves; ++w) {
+        const int nw = s_n[w];
+        for (int j = lane; j < nw; j += kWave) {
+          const uint64_t e = s_buf[w][j];
+          best = (e < prev && e > best) ? e : best;
+        }
+      }
+      best = wave_max_u64(best);
+      if (best == 0) break;
+      if (lane == r) mine = best;
+      prev = best;
+      ++f;
+    }
+  }
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kDraftWaves; ++w) M = fmaxf(M, s_m[w]);
@@ -305,12 +371,12 @@ struct GrowParams {
 };
 
 __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
-  __shared__ int s_exp[kMaxHead];
-  __shared__ float s_plp[kMaxHead];
-  __shared__ int s_ppos[kMaxHead];
-  __shared__ uint32_t s_pmask[kMaxHead][kMaskWordsMax];
-  __shared__ float s_lp[kTreeDraftMaxNodes];
   __shared__ uint64_t s_stage[kGrowWaves][kStageCap];
+  __shared__ uint32_t s_pmask[kGrowWaves][kMaskWordsMax];
+  __shared__ int s_ctok[kTreeDraftMaxNodes], s_cpar[kTreeDraftMaxNodes];
+  __shared__ int s_cpos[kTreeDraftMaxNodes];
+  __shared__ float s_lp[kTreeDraftMaxNodes];
+  __shared__ uint32_t s_cmask[kTreeDraftMaxNodes][kMaskWordsMax];
   __shared__ int s_bad;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -323,8 +389,9 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
   uint32_t* mask = P.mask + nb * P.mw;
   int32_t* expn = P.expand_nodes + (size_t)b * P.es;
   const int new_hi = P.first_new + P.n_new;
+  if (tid == 0) s_bad = 0;
   if (P.step == 0) {
-    // every entry but this step's new nodes (written below) gets its initial value
+    // every entry but this step's new nodes (written at the end) gets its initial value
     for (int i = tid; i < P.ts; i += kGrowThreads) {
       if (i >= P.first_new && i < new_hi) continue;
       const bool root = i == 0;
@@ -339,49 +406,13 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
       if (i >= P.first_new && i < new_hi) continue;
       mask[k] = (k == 0) ? 1u : 0u;
     }
-    if (tid == 0) {
-      s_exp[0] = 0;
-      s_plp[0] = 0.f;
-      s_ppos[0] = P.pos_base ? P.pos_base[b] : 0;
-      s_bad = 0;
-    }
-    if (tid < kMaskWordsMax) s_pmask[0][tid] = tid == 0 ? 1u : 0u;
-  } else {
-    if (tid < kWave) {  // h <= 64: wave 0 reads the expanded nodes
-      int node = -1;
-      bool bad = false;
-      if (lane < P.h) {
-        node = expn[lane];
-        bad = node < P.par_lo || node >= P.par_hi;
-        if (!bad) {
-          s_exp[lane] = node;
-          s_plp[lane] = lp[node];
-          s_ppos[lane] = pos[node];
-          for (int w = 0; w < P.mw; ++w) s_pmask[lane][w] = mask[(size_t)node * P.mw + w];
-        }
-      }
-      const bool any = __ballot(bad) != 0;
-      if (lane == 0) s_bad = any;
-    }
   }
-  __syncthreads();
-  if (s_bad) {
-    if (tid == 0 && P.seq_flags) P.seq_flags[b] |= SPEC_FLAG_BAD_TREE;
-    return;
-  }
-  // children of each expanded node, one wave per node
+  __syncthreads();  // s_bad is set before any wave may raise it
+  // Children of each expanded node, one wave per node, kept in LDS until every expanded node
+  // has been checked. The node's chunk records are loaded together with the node itself.
   for (int j = wave; j < P.h; j += kGrowWaves) {
     const size_t row = (size_t)b * P.h + j;
     const uint8_t* rec0 = P.part + row * P.S * P.rec_bytes;
-    float m = -INFINITY, sm = 0.f;
-    if (lane < P.S) {
-      const PartHead hd = *reinterpret_cast<const PartHead*>(rec0 + (size_t)lane * P.rec_bytes);
-      m = hd.m;
-      sm = hd.s;
-    }
-    const float M = wave_max_dpp(m);
-    const float Z = wave_sum_dpp(m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f((m - M) * kLog2e));
-    const float lz = logf(Z);  // log of sum over the row of exp(l - M)
     const int K = P.kk[j];
     const int nc = P.S * K;  // the S chunk lists, K candidates each
     uint64_t* stage = s_stage[wave];
@@ -390,24 +421,56 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
       stage[i] = reinterpret_cast<const uint64_t*>(rec0 + (size_t)li * P.rec_bytes +
                                                    sizeof(PartHead))[r];
     }
+    float m = -INFINITY, sm = 0.f;
+    if (lane < P.S) {
+      const PartHead hd = *reinterpret_cast<const PartHead*>(rec0 + (size_t)lane * P.rec_bytes);
+      m = hd.m;
+      sm = hd.s;
+    }
+    const int pnode = P.step == 0 ? 0 : expn[j];
+    const bool bad = pnode < P.par_lo || pnode >= P.par_hi;
+    if (bad) {
+      if (lane == 0) s_bad = 1;
+      continue;
+    }
+    float plp = 0.f;
+    int ppos = P.pos_base ? P.pos_base[b] : 0;
+    if (P.step != 0) {
+      plp = lp[pnode];
+      ppos = pos[pnode];
+      if (lane < P.mw) s_pmask[wave][lane] = mask[(size_t)pnode * P.mw + lane];
+    } else if (lane < P.mw) {
+      s_pmask[wave][lane] = lane == 0 ? 1u : 0u;
+    }
+    const float M = wave_max_dpp(m);
+    const float Z = wave_sum_dpp(m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f((m - M) * kLog2e));
+    const float lz = logf(Z);  // log of sum over the row of exp(l - M)
     uint64_t mine;
     const int f = wave_select(stage, nc, K, lane, mine);
     if (lane < f) {
       const int c = P.first_new + P.koff[j] + lane;
-      const float l = cand_logit(mine);
-      const float v = s_plp[j] + ((l - M) - lz);
-      par[c] = s_exp[j];
-      tok[c] = cand_token(mine);
-      lp[c] = v;
-      pos[c] = s_ppos[j] + 1;
+      const int t = c - P.first_new;
+      s_ctok[t] = cand_token(mine);
+      s_cpar[t] = pnode;
+      s_cpos[t] = ppos + 1;
+      s_lp[t] = plp + ((cand_logit(mine) - M) - lz);
       for (int w = 0; w < P.mw; ++w)
-        mask[(size_t)c * P.mw + w] = s_pmask[j][w] | ((c >> 5) == w ? 1u << (c & 31) : 0u);
-      s_lp[c - P.first_new] = v;
+        s_cmask[t][w] = s_pmask[wave][w] | ((c >> 5) == w ? 1u << (c & 31) : 0u);
     }
   }
   __syncthreads();
-  // the new layer's rows: the h_next most probable nodes get the next step's target rows
+  if (s_bad) {
+    if (tid == 0 && P.seq_flags) P.seq_flags[b] |= SPEC_FLAG_BAD_TREE;
+    return;
+  }
+  // the new nodes, and the new layer's rows: its h_next most probable nodes get the next
+  // step's target rows
   for (int t = tid; t < P.n_new; t += kGrowThreads) {
+    const int c = P.first_new + t;
+    par[c] = s_cpar[t];
+    tok[c] = s_ctok[t];
+    lp[c] = s_lp[t];
+    pos[c] = s_cpos[t];
     const float me = s_lp[t];
     int rank = 0;
     for (int u = 0; u < P.n_new; ++u) {
@@ -415,8 +478,12 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
       rank += (o > me) || (o == me && u < t);
     }
     const bool chosen = rank < P.h_next;
-    nrow[P.first_new + t] = chosen ? P.row_base_next + rank : -1;
-    if (chosen) expn[rank] = P.first_new + t;
+    nrow[c] = chosen ? P.row_base_next + rank : -1;
+    if (chosen) expn[rank] = c;
+  }
+  for (int k = tid; k < P.n_new * P.mw; k += kGrowThreads) {
+    const int t = k / P.mw, w = k - t * P.mw;
+    mask[(size_t)(P.first_new + t) * P.mw + w] = s_cmask[t][w];
   }
 }
 
