@@ -75,6 +75,10 @@ def _declare(L):
     L.oracle_tree_draft.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P,
                                     _P, _P, _P, _I, _P, _I]
     L.oracle_tree_draft.restype = _I
+    L.oracle_kv_commit_paged.argtypes = [_I, _I, _I, _I, _P, _P, _I, _I, _I, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, _I, _I, _P, _P, _P,
+                                         _P, _P, _P, _P]
+    L.oracle_kv_commit_paged.restype = _I
 
 
 class _RowInfo(ctypes.Structure):
@@ -308,3 +312,28 @@ def tree_draft(rows_by_step, top_head, top_k_spec, root_token, pos_base=None, tr
         raise ValueError("invalid tree configuration")
     out["num_nodes"] = n
     return out
+
+
+def kv_commit_paged(k_layers, v_layers, block_table, path_nodes, path_len, committed_len,
+                    free_list, free_count, lead_slots, max_depth):
+    """Paged commit on host caches, in place (reading R22). k_layers/v_layers: lists of
+    uint16 arrays shaped [num_blocks, block_size, H, D] (contiguous). block_table
+    [B, max_blocks] and free_list [num_blocks] are updated in place. Returns
+    (committed_len, free_count, seq_flags)."""
+    nb, bs, H, D = k_layers[0].shape
+    nl = len(k_layers)
+    kp = (ctypes.c_void_p * nl)(*[a.ctypes.data for a in k_layers])
+    vp = (ctypes.c_void_p * nl)(*[a.ctypes.data for a in v_layers])
+    bt = block_table
+    assert bt.dtype == np.int32 and bt.flags.c_contiguous
+    assert free_list.dtype == np.int32 and free_list.flags.c_contiguous
+    B, max_blocks = bt.shape
+    pn = _c(path_nodes, np.int32)
+    pl = _c(path_len, np.int32)
+    cl = np.array(committed_len, dtype=np.int32, copy=True)
+    fc = np.array([free_count], dtype=np.int32)
+    fl = np.zeros(B, dtype=np.int32)
+    lib().oracle_kv_commit_paged(B, nl, H, D, kp, vp, bs, max_blocks, nb, bs * H * D, H * D, D,
+                                 int(lead_slots), int(max_depth), _ptr(bt), _ptr(pn), _ptr(pl),
+                                 _ptr(cl), _ptr(free_list), _ptr(fc), _ptr(fl))
+    return cl, int(fc[0]), fl

@@ -65,6 +65,15 @@
  *       i see node j iff j is i or an ancestor of i, and a node's position is the root's
  *       plus its depth ([LI] §10.6.3, Table 10-17). The selection compares path
  *       log-probabilities rounded to binary32, the precision the GPU library decides in.
+ *   R22 paged KV commit ([LI] §10.6.3: after a rejection the cache length is cut back, and a
+ *       paged cache releases the blocks it no longer needs): logical slot s of sequence b
+ *       lives in physical block block_table[b][s / block_size] at offset s % block_size.
+ *       The path copy of R12 runs through that mapping; then the committed length becomes
+ *       L' = L + lead_slots + D, and every mapped logical block at or past ceil(L' /
+ *       block_size) is released: its id is appended to the free list, sequences in order and
+ *       each sequence's blocks in logical order, and its table entry becomes -1. A sequence
+ *       with a copied slot outside the table or in an unmapped block, or whose L' needs more
+ *       blocks than the table has, is flagged SLOT_OOB and left untouched.
  */
 #include <math.h>
 #include <stdint.h>
@@ -725,6 +734,74 @@ int oracle_tree_draft(int B, int V, int row_stride, int depth, const int32_t* to
     }
     free(tok);
     free(lay);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Paged KV commit and release ([LI] §10.6.3 cache truncation and block release; [KV] §6   */
+/* committed-length pointer). Reading R22. Layer l's K cache starts at k_cache[l]; element */
+/* (physical block p, offset o, head h, e) sits at p*block_stride + o*slot_stride +        */
+/* h*head_stride + e. block_table is [B][max_blocks] (-1 = unmapped); free_list holds      */
+/* free_count[0] ids and receives the released ones after them.                            */
+/* ------------------------------------------------------------------------------------ */
+static int64_t paged_off(const int32_t* bt, int block_size, int slot, int64_t block_stride,
+                         int64_t slot_stride) {
+  return (int64_t)bt[slot / block_size] * block_stride + (int64_t)(slot % block_size) * slot_stride;
+}
+
+int oracle_kv_commit_paged(int B, int num_layers, int num_kv_heads, int head_dim,
+                           uint16_t* const* k_cache, uint16_t* const* v_cache, int block_size,
+                           int max_blocks, int num_blocks, int64_t block_stride,
+                           int64_t slot_stride, int64_t head_stride, int lead_slots,
+                           int max_depth, int32_t* block_table, const int32_t* path_nodes,
+                           const int32_t* path_len, int32_t* committed_len, int32_t* free_list,
+                           int32_t* free_count, int32_t* seq_flags) {
+  for (int b = 0; b < B; ++b) {
+    int32_t* bt = block_table + (size_t)b * max_blocks;
+    const int L = committed_len[b], D = path_len[b];
+    const int base = L + lead_slots - 1;
+    const int64_t new_len = (int64_t)L + lead_slots + D;
+    int ok = D >= 0 && D <= max_depth && base >= -1 &&
+             (new_len + block_size - 1) / block_size <= max_blocks;
+    /* every slot a copy touches must be mapped */
+    for (int j = 1; ok && j <= D; ++j) {
+      const int node = path_nodes[(size_t)b * max_depth + j - 1];
+      if (node < 1) { ok = 0; break; }
+      const int src = base + node, dst = base + j;
+      if (src == dst) continue;
+      const int slots[2] = {src, dst};
+      for (int q = 0; q < 2; ++q) {
+        const int sl = slots[q];
+        if (sl < 0 || sl >= max_blocks * block_size) { ok = 0; break; }
+        const int pb = bt[sl / block_size];
+        if (pb < 0 || pb >= num_blocks) { ok = 0; break; }
+      }
+    }
+    if (!ok) {
+      if (seq_flags) seq_flags[b] |= OF_SLOT_OOB;
+      continue;
+    }
+    for (int j = 1; j <= D; ++j) {
+      const int src = base + path_nodes[(size_t)b * max_depth + j - 1], dst = base + j;
+      if (src == dst) continue;
+      const int64_t so = paged_off(bt, block_size, src, block_stride, slot_stride);
+      const int64_t d_o = paged_off(bt, block_size, dst, block_stride, slot_stride);
+      for (int l = 0; l < num_layers; ++l)
+        for (int kv = 0; kv < 2; ++kv) {
+          uint16_t* c = kv ? v_cache[l] : k_cache[l];
+          for (int h = 0; h < num_kv_heads; ++h)
+            memmove(c + d_o + h * head_stride, c + so + h * head_stride,
+                    sizeof(uint16_t) * (size_t)head_dim);
+        }
+    }
+    committed_len[b] = (int32_t)new_len;
+    const int need = (int)((new_len + block_size - 1) / block_size);
+    for (int lb = need; lb < max_blocks; ++lb) {
+      if (bt[lb] < 0) continue;
+      free_list[free_count[0]++] = bt[lb];
+      bt[lb] = -1;
+    }
   }
   return 0;
 }
