@@ -62,6 +62,18 @@ class spec_tree_draft_args(ctypes.Structure):
     ]
 
 
+class spec_paged_kv_args(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("num_layers", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
+        ("block_size", _I32), ("max_blocks", _I32), ("num_blocks", _I32),
+        ("free_capacity", _I32), ("lead_slots", _I32), ("max_depth", _I32),
+        ("block_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64), ("k_cache", _P), ("v_cache", _P),
+        ("block_table", _P), ("path_nodes", _P), ("path_len", _P), ("committed_len", _P),
+        ("free_list", _P), ("free_count", _P), ("seq_flags", _P),
+    ]
+
+
 class spec_kv_args(ctypes.Structure):
     _fields_ = [
         ("batch", _I32), ("num_layers", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
@@ -81,7 +93,7 @@ class SpecError(RuntimeError):
 _lib = None
 
 # Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def lib_path() -> str:
@@ -113,6 +125,8 @@ def lib():
         L.spec_tree_draft_step.argtypes = [ctypes.POINTER(spec_tree_draft_args), _P,
                                            ctypes.c_size_t, _P]
         L.spec_tree_draft_step.restype = ctypes.c_int
+        L.kv_commit_paged.argtypes = [ctypes.POINTER(spec_paged_kv_args), _P]
+        L.kv_commit_paged.restype = ctypes.c_int
         if L.spec_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{_build.LIB} has ABI version {L.spec_abi_version()}, the "
                                f"binding expects {ABI_VERSION}: rebuild the library")
@@ -286,6 +300,47 @@ def kv_args(*, k_cache, v_cache, path_nodes, path_len, committed_len, num_kv_hea
 
 def kv_commit_path(args: spec_kv_args, stream=None):
     _check(lib().kv_commit_path(ctypes.byref(args), _stream(stream)))
+
+
+def kv_paged_args(*, k_cache, v_cache, block_table, path_nodes, path_len, committed_len,
+                  free_list, free_count, num_kv_heads, head_dim, block_size, num_blocks,
+                  block_stride, slot_stride, head_stride, lead_slots, max_depth,
+                  seq_flags=None):
+    """k_cache / v_cache: lists of device tensors (one per layer) or raw pointers; the block
+    table is [B, max_blocks] and the free list [free_capacity] (device int32)."""
+    nl = len(k_cache)
+    a = spec_paged_kv_args()
+    a.batch = int(block_table.shape[0])
+    a.num_layers = nl
+    a.num_kv_heads = int(num_kv_heads)
+    a.head_dim = int(head_dim)
+    a.block_size = int(block_size)
+    a.max_blocks = int(block_table.shape[1])
+    a.num_blocks = int(num_blocks)
+    a.free_capacity = int(free_list.shape[0])
+    a.lead_slots = int(lead_slots)
+    a.max_depth = int(max_depth)
+    a.block_stride, a.slot_stride = int(block_stride), int(slot_stride)
+    a.head_stride = int(head_stride)
+    arr_k = (ctypes.c_void_p * nl)(*[_ptr(t) for t in k_cache])
+    arr_v = (ctypes.c_void_p * nl)(*[_ptr(t) for t in v_cache])
+    a._keep = (arr_k, arr_v)  # the host arrays must live until the call returns
+    a.k_cache = ctypes.cast(arr_k, _P)
+    a.v_cache = ctypes.cast(arr_v, _P)
+    a.block_table = _ptr(block_table)
+    a.path_nodes = _ptr(path_nodes)
+    a.path_len = _ptr(path_len)
+    a.committed_len = _ptr(committed_len)
+    a.free_list = _ptr(free_list)
+    a.free_count = _ptr(free_count)
+    a.seq_flags = _ptr(seq_flags)
+    _keep(a, block_table, path_nodes, path_len, committed_len, free_list, free_count,
+          seq_flags, *k_cache, *v_cache)
+    return a
+
+
+def kv_commit_paged(args: spec_paged_kv_args, stream=None):
+    _check(lib().kv_commit_paged(ctypes.byref(args), _stream(stream)))
 
 
 def _tree_config(top_head, top_k_spec):

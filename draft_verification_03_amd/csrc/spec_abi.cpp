@@ -290,4 +290,44 @@ int spec_tree_draft_step(const spec_tree_draft_args* a, void* workspace, size_t 
   return SPEC_OK;
 }
 
+int kv_commit_paged(const spec_paged_kv_args* a, void* hip_stream) {
+  g_err[0] = '\0';
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "kv_commit_paged: args is NULL");
+  if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->num_layers < 1 || a->num_layers > 128)
+    return fail(SPEC_ERR_INVALID_ARG, "num_layers must be in [1, 128] (got %d)", a->num_layers);
+  if (a->num_kv_heads < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", a->num_kv_heads);
+  if (a->head_dim < 8 || a->head_dim % 8 != 0)
+    return fail(SPEC_ERR_INVALID_ARG,
+                "head_dim must be a positive multiple of 8 (16-byte rows; got %d)", a->head_dim);
+  if (a->block_size < 1 || a->max_blocks < 1 || a->num_blocks < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "block_size, max_blocks and num_blocks must be >= 1");
+  if ((int64_t)a->max_blocks * a->block_size > 0x7FFFFFFFLL)
+    return fail(SPEC_ERR_INVALID_ARG, "max_blocks * block_size exceeds the slot index range");
+  if (a->free_capacity < a->num_blocks)
+    return fail(SPEC_ERR_INVALID_ARG, "free_capacity must be >= num_blocks (got %d < %d)",
+                a->free_capacity, a->num_blocks);
+  if (a->block_stride < 0 || a->slot_stride < 0 || a->head_stride < 0 ||
+      a->block_stride % 8 || a->slot_stride % 8 || a->head_stride % 8)
+    return fail(SPEC_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
+  if (a->lead_slots != 0 && a->lead_slots != 1)
+    return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
+  if (a->max_depth < 1 || a->max_depth > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "max_depth must be in [1, 64] (got %d)", a->max_depth);
+  if (a->batch == 0) return SPEC_OK;
+  if (!a->k_cache || !a->v_cache || !a->block_table || !a->path_nodes || !a->path_len ||
+      !a->committed_len || !a->free_list || !a->free_count)
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  for (int l = 0; l < a->num_layers; ++l) {
+    if (!a->k_cache[l] || !a->v_cache[l])
+      return fail(SPEC_ERR_INVALID_ARG, "k_cache[%d] / v_cache[%d] is NULL", l, l);
+    if (!aligned16(a->k_cache[l]) || !aligned16(a->v_cache[l]))
+      return fail(SPEC_ERR_INVALID_ARG, "cache pointers of layer %d must be 16-byte aligned", l);
+  }
+  hipError_t e = specv::launch_kv_paged(*a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_commit_paged launch");
+  return SPEC_OK;
+}
+
 }  // extern "C"

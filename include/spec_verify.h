@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
@@ -273,6 +273,57 @@ typedef struct spec_tree_draft_args {
   int32_t* seq_flags;           /* [B] or NULL (bits OR-ed in)                              */
 } spec_tree_draft_args;
 
+/*
+ * Paged KV commit and release ("10.6 投机解码" §10.6.3: after a rejection the cache length is
+ * cut back, and a paged cache releases the blocks it no longer needs; "KV Cache 优化（四）"
+ * §6: one committed-length pointer, the same in every layer).
+ *
+ * Sequence b's logical slot s lives in physical block block_table[b][s / block_size] at
+ * offset s % block_size; element (block p, offset o, head h, e) of layer l's K cache is
+ * k_cache[l][p*block_stride + o*slot_stride + h*head_stride + e], e < head_dim (bf16,
+ * copied bit for bit). With L = committed_len[b], D = path_len[b] and base = L + lead_slots
+ * - 1, for j = 1..D (in increasing j) every layer's K and V rows of every KV head move from
+ * logical slot base + path_nodes[b][j-1] to logical slot base + j (skipped when equal), as
+ * kv_commit_path does in a contiguous cache. Then committed_len[b] becomes L' = L +
+ * lead_slots + D, and every mapped logical block at or past ceil(L' / block_size) is
+ * released: its id is appended to free_list after the free_count[0] ids already there --
+ * sequences in order, each sequence's blocks in logical order -- and its table entry becomes
+ * -1. A chain round's identity path (path_nodes[b][j-1] = j) moves no byte: the call is then
+ * the rollback itself, length cut back and surplus blocks released; a draft model's cache is
+ * rolled back the same way.
+ *
+ * A sequence with a copied slot outside its table or in an unmapped block (or a block id
+ * outside [0, num_blocks)), a path node < 1, or an L' needing more than max_blocks blocks
+ * gets SPEC_FLAG_SLOT_OOB and is left untouched. Table entries are -1 or block ids; each
+ * block id appears at most once in the tables and the free list together (no shared
+ * blocks). free_list has free_capacity entries (>= num_blocks); ids that would land at or
+ * past it are not written (that happens only if the pool breaks the rule above).
+ */
+typedef struct spec_paged_kv_args {
+  int32_t batch;          /* B >= 0                                                        */
+  int32_t num_layers;     /* 1..128                                                        */
+  int32_t num_kv_heads;   /* >= 1                                                          */
+  int32_t head_dim;       /* elements; a positive multiple of 8 (16-byte rows)             */
+  int32_t block_size;     /* slots per block; >= 1                                         */
+  int32_t max_blocks;     /* entries per sequence in block_table; >= 1                     */
+  int32_t num_blocks;     /* physical blocks of every layer's pool; >= 1                   */
+  int32_t free_capacity;  /* entries of free_list; >= num_blocks                           */
+  int32_t lead_slots;     /* 0 or 1                                                        */
+  int32_t max_depth;      /* row length of path_nodes; 1..64                               */
+  int64_t block_stride;   /* elements between blocks; multiples of 8                       */
+  int64_t slot_stride;    /* elements between a block's slots                              */
+  int64_t head_stride;    /* elements between a slot's heads                               */
+  uint16_t* const* k_cache; /* HOST array [num_layers] of device pointers (16-B aligned)    */
+  uint16_t* const* v_cache; /* HOST array [num_layers] of device pointers (16-B aligned)    */
+  int32_t* block_table;      /* [B][max_blocks] in/out                                      */
+  const int32_t* path_nodes; /* [B][max_depth], node indices >= 1 in depth order            */
+  const int32_t* path_len;   /* [B], 0..max_depth                                           */
+  int32_t* committed_len;    /* [B] in/out                                                  */
+  int32_t* free_list;        /* [free_capacity] in/out                                      */
+  int32_t* free_count;       /* [1] in/out                                                  */
+  int32_t* seq_flags;        /* [B] or NULL (bits OR-ed in)                                 */
+} spec_paged_kv_args;
+
 /* ABI revision of this header (SPEC_ABI_VERSION). */
 int spec_abi_version(void);
 
@@ -307,6 +358,10 @@ size_t spec_tree_draft_workspace_size(int32_t batch, int32_t vocab, int32_t dept
 /* Enqueue one tree-drafting step. Returns SPEC_OK or a negative status. */
 int spec_tree_draft_step(const spec_tree_draft_args* args, void* workspace,
                          size_t workspace_bytes, void* hip_stream);
+
+/* Enqueue the paged KV commit, pointer update and block release (no workspace). Returns
+ * SPEC_OK or a negative status. */
+int kv_commit_paged(const spec_paged_kv_args* args, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["spec_abi_version", "spec_last_error", "spec_verify_chain_workspace_size",
                  "spec_verify_chain", "spec_verify_tree_workspace_size", "spec_verify_tree",
-                 "kv_commit_path", "spec_tree_draft_workspace_size", "spec_tree_draft_step"]:
+                 "kv_commit_path", "spec_tree_draft_workspace_size", "spec_tree_draft_step",
+                 "kv_commit_paged"]:
         assert want in names
 
 
@@ -46,6 +47,7 @@ def test_struct_layout_matches_c(tmp_path):
         "spec_tree_args": [f for f, _ in B.spec_tree_args._fields_],
         "spec_kv_args": [f for f, _ in B.spec_kv_args._fields_],
         "spec_tree_draft_args": [f for f, _ in B.spec_tree_draft_args._fields_],
+        "spec_paged_kv_args": [f for f, _ in B.spec_paged_kv_args._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spec_verify.h"',
              "int main(void){"]
@@ -68,7 +70,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_abi_version_and_workspace_sizes():
-    assert B.spec_abi_version() == B.ABI_VERSION == 3
+    assert B.spec_abi_version() == B.ABI_VERSION == 4
     assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
     assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
     assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
@@ -264,3 +266,41 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "spec_oracle" not in text, f
+
+
+def _paged(**kw):
+    a = B.spec_paged_kv_args()
+    ptrs = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    base = dict(batch=2, num_layers=2, num_kv_heads=8, head_dim=128, block_size=16,
+                max_blocks=64, num_blocks=256, free_capacity=256, lead_slots=1, max_depth=3,
+                block_stride=16 * 8 * 128, slot_stride=8 * 128, head_stride=128,
+                k_cache=ctypes.cast(ptrs, ctypes.c_void_p).value,
+                v_cache=ctypes.cast(ptrs, ctypes.c_void_p).value, block_table=0x3000,
+                path_nodes=0x5000, path_len=0x6000, committed_len=0x7000, free_list=0x8000,
+                free_count=0x9000)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    a._keep = ptrs
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=-1), dict(num_layers=0), dict(num_layers=129), dict(num_kv_heads=0),
+    dict(head_dim=12), dict(block_size=0), dict(max_blocks=0), dict(num_blocks=0),
+    dict(free_capacity=255), dict(slot_stride=1020), dict(lead_slots=2), dict(max_depth=0),
+    dict(max_depth=65), dict(block_table=None), dict(free_list=None), dict(free_count=None),
+    dict(k_cache=None), dict(max_blocks=1 << 20, block_size=1 << 12),
+])
+def test_kv_paged_validation(kw):
+    a = _paged(**kw)
+    assert B.lib().kv_commit_paged(ctypes.byref(a), None) == B.SPEC_ERR_INVALID_ARG
+    assert B.spec_last_error() != ""
+
+
+def test_kv_paged_misaligned_layer_pointer_and_empty_batch():
+    ptrs = (ctypes.c_void_p * 2)(0x10000, 0x20004)
+    a = _paged(v_cache=ctypes.cast(ptrs, ctypes.c_void_p).value)
+    a._keep2 = ptrs
+    assert B.lib().kv_commit_paged(ctypes.byref(a), None) == B.SPEC_ERR_INVALID_ARG
+    assert B.lib().kv_commit_paged(ctypes.byref(_paged(batch=0)), None) == B.SPEC_OK
