@@ -12,11 +12,18 @@ bounded sample of the same workload as a reported baseline.
   python bench.py [--steps K] [--warmup W] [--warmup-seconds S] [--gpus 1] [--no-cpu-baseline]
   python bench.py --copy-calibration     # a plain copy of known size, for counter scaling
   python bench.py --workload tree_draft  # the tree-drafting steps of one round instead
+  python bench.py --workload paged_kv    # the paged KV commit of the tree workload instead
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
 大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
 with V=151936 draft rows: three spec_tree_draft_step calls reading 128, 256 and 256 draft
 rows. The line reports draft rows/s and the HBM bandwidth of the steps against 8 TB/s.
+
+With --workload paged_kv a step is one kv_commit_paged call committing the tree workload's
+accepted paths (B=128, depth <= 3) into a cache of 32 layers x K,V x 8 heads x 128 bf16 paged
+in 16-slot blocks (64 shuffled blocks per sequence, 17.2 GB), releasing the surplus blocks.
+The block table, lengths and free count are restored before each call, outside the events
+that time it.
 """
 from __future__ import annotations
 
@@ -219,6 +226,94 @@ def tree_draft_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def paged_kv_bench(args):
+    """The paged KV commit of the tree workload (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from draft_verification_03_amd import binding as B
+    from draft_verification_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("generating the tree workload's accepted paths")
+    x = W.tree_inputs()
+    o = oracle.verify_tree(x["logits"], x["parent"], x["node_row"], x["node_token"],
+                           x["rows_per_seq"], x["max_depth"], x["num_nodes"], vocab=x["vocab"])
+    NL, H, Dh, S = (W.KV_SHAPE[k] for k in ("num_layers", "num_kv_heads", "head_dim", "slots"))
+    Bn, bs = 128, 16
+    mb = S // bs
+    nb = Bn * mb
+    rng = np.random.default_rng(404)
+    bt0 = rng.permutation(nb).astype(np.int32).reshape(Bn, mb)
+    L0, paths, plen = x["committed_len"], o["path_nodes"], o["path_len"]
+    log(f"allocating the paged cache ({2 * NL * nb * bs * H * Dh * 2 / 1e9:.1f} GB)")
+    caches = [[torch.empty((nb, bs, H, Dh), dtype=torch.int16, device="cuda").random_(-32768, 32767)
+               for _ in range(2)] for _ in range(NL)]
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    bt_init, L_init = dv(bt0), dv(L0)
+    btt, Lt = bt_init.clone(), L_init.clone()
+    ft = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    fct = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = B.kv_paged_args(k_cache=[c[0] for c in caches], v_cache=[c[1] for c in caches],
+                        block_table=btt, path_nodes=dv(paths), path_len=dv(plen),
+                        committed_len=Lt, free_list=ft, free_count=fct, num_kv_heads=H,
+                        head_dim=Dh, block_size=bs, num_blocks=nb, block_stride=bs * H * Dh,
+                        slot_stride=H * Dh, head_stride=Dh, lead_slots=1,
+                        max_depth=x["max_depth"])
+
+    def restore():
+        btt.copy_(bt_init)
+        Lt.copy_(L_init)
+        fct.zero_()
+
+    t_warm = time.time()
+    done = 0
+    while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        restore()
+        B.kv_commit_paged(a)
+        done += 1
+        if done % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} calls")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        restore()
+        e0.record()
+        B.kv_commit_paged(a)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    moved = sum(int((paths[b, :plen[b]] != np.arange(1, plen[b] + 1)).sum()) for b in range(Bn))
+    row_bytes = NL * 2 * H * Dh * 2  # one slot's K and V rows in every layer
+    nbytes = 2 * moved * row_bytes + Bn * mb * 4  # moved rows read + written, tables read
+    released = int(fct.cpu()[0])
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"commit {ms * 1e3:.1f} us: {moved} rows moved ({2 * moved * row_bytes / 1e6:.1f} MB "
+        f"read + written), {released} blocks released, {gbs:.0f} GB/s")
+    res = {
+        "metric": "paged KV commit: sequences/s at B=128, 32 layers x 8 KV heads x 128, "
+                  "16-slot blocks; achieved HBM GB/s vs peak",
+        "value": Bn / (ms / 1e3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u16", "data": "synthetic",
+        "config": {"workload": "paged KV commit of the tree workload's accepted paths, B=128, "
+                               "32 layers x K,V x 8 heads x 128 bf16, 16-slot blocks, 64 "
+                               "shuffled blocks per sequence",
+                   "rows_moved": moved, "blocks_released": released,
+                   "call_algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "kernel": "paged_copy_kernel + paged_release_kernel",
+                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": nbytes,
+                     "avg_launch_us": ms * 1e3, "kernel_source_hash": kernel_source_hash()},
+    }
+    print(json.dumps(res), flush=True)
+    del caches
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,7 +323,7 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=["chain", "tree_draft"], default="chain")
+    ap.add_argument("--workload", choices=["chain", "tree_draft", "paged_kv"], default="chain")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
@@ -240,6 +335,9 @@ def main():
         return
     if args.workload == "tree_draft":
         tree_draft_bench(args)
+        return
+    if args.workload == "paged_kv":
+        paged_kv_bench(args)
         return
 
     import numpy as np

@@ -8,11 +8,13 @@
 //     slot base + path[j-1] to logical slot base + j, each slot found through the sequence's
 //     block table. A thread handles its own chunk in j order, which reproduces in-order
 //     copying (a tree path has path[j-1] >= j, so no source is overwritten first).
-//  2. paged_release_kernel -- one 1024-thread workgroup: per sequence the same validity check,
-//     the new committed length and the count of mapped blocks past it; an exclusive scan of
-//     the counts over the sequences (in tiles of 1024 with a running carry) gives each
-//     sequence its place in the free list, so the released ids land in (sequence, logical
-//     block) order whatever the launch timing. It runs after every copy has read the tables.
+//  2. paged_release_kernel -- one 1024-thread workgroup over tiles of whole table rows: one
+//     thread per sequence checks it (the same predicate), writes its new committed length and
+//     notes its first block past that length; then the tile's table entries, taken in
+//     row-major order (8 consecutive per thread), are flagged and scanned, and a released
+//     entry's place in the free list is the number of released entries before it -- so the
+//     ids land in (sequence, logical block) order whatever the launch timing. It runs after
+//     every copy has read the tables.
 #include "spec_device.h"
 #include "specv_internal.h"
 
@@ -23,6 +25,9 @@ constexpr int kMaxLayers = 128;
 constexpr int kThreads = 256;
 constexpr int kRelThreads = 1024;
 constexpr int kRelWaves = kRelThreads / kWave;
+constexpr int kRun = 8;           // table entries per thread per chunk
+constexpr int kRelEntries = kRelThreads * kRun;  // table entries per tile (whole rows)
+constexpr int kRelRows = kRelEntries;            // rows per tile at most
 
 struct PagedParams {
   uint16_t* k[kMaxLayers];
@@ -99,50 +104,67 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P, int
 }
 
 __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams P) {
+  __shared__ int s_need[kRelRows];  // first released logical block of each row (-1: invalid)
   __shared__ int s_wave[kRelWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int fc0 = min(max(*P.free_count, 0), P.free_cap);
-  int carry = 0;  // blocks released by the tiles before this one (uniform)
-  for (int b0 = 0; b0 < P.B; b0 += kRelThreads) {
-    const int b = b0 + tid;
-    int L = 0, D = 0, need = 0, cnt = 0;
-    bool ok = false;
-    const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
-    if (b < P.B) {
-      ok = seq_valid(P, b, L, D);
+  const int mb = P.max_blocks;
+  const int rows = max(1, min(kRelRows, kRelEntries / mb));  // whole rows per tile
+  int carry = 0;  // blocks released before this chunk (uniform)
+  for (int b0 = 0; b0 < P.B; b0 += rows) {
+    const int nr = min(rows, P.B - b0);
+    // one thread per sequence: validity, new length and the first block past it
+    for (int i = tid; i < nr; i += kRelThreads) {
+      const int b = b0 + i;
+      int L, D;
+      const bool ok = seq_valid(P, b, L, D);
+      s_need[i] = ok ? (int)(((int64_t)L + P.lead + D + P.bs - 1) / P.bs) : -1;
       if (ok) {
-        need = (int)(((int64_t)L + P.lead + D + P.bs - 1) / P.bs);
-        for (int lb = need; lb < P.max_blocks; ++lb) cnt += bt[lb] >= 0;
-      }
-    }
-    // exclusive scan of cnt over the tile: waves, then their totals
-    const int incl = wave_incl_scan_dpp(cnt);
-    if (lane == kWave - 1) s_wave[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < kRelWaves; ++w) {
-      const int tw = s_wave[w];
-      before += w < wave ? tw : 0;
-      total += tw;
-    }
-    if (b < P.B) {
-      if (ok) {
-        int off = fc0 + carry + before + incl - cnt;
-        int32_t* btw = P.bt + (size_t)b * P.max_blocks;
-        for (int lb = need; lb < P.max_blocks; ++lb) {
-          const int pb = btw[lb];
-          if (pb < 0) continue;
-          if (off < P.free_cap) P.free_list[off] = pb;
-          ++off;
-          btw[lb] = -1;
-        }
-        P.committed[b] = L + P.lead + D;
+        P.committed[b] = L + P.lead + D;  // every read of committed[b] is above
       } else if (P.flags) {
         P.flags[b] |= SPEC_FLAG_SLOT_OOB;
       }
     }
-    carry += total;
-    __syncthreads();  // s_wave is read by every thread before the next tile writes it
+    __syncthreads();
+    // the tile's table entries in row-major order, kRun consecutive per thread: the free
+    // list position of a released entry is the count of released entries before it
+    const int64_t e0 = (int64_t)b0 * mb, ne = (int64_t)nr * mb;
+    for (int64_t c0 = 0; c0 < ne; c0 += (int64_t)kRelThreads * kRun) {
+      int pb[kRun];
+      int cnt = 0;
+#pragma unroll
+      for (int r = 0; r < kRun; ++r) {
+        const int64_t e = c0 + (int64_t)tid * kRun + r;  // entry of the tile
+        pb[r] = -1;
+        if (e < ne) {
+          const int i = (int)(e / mb), lb = (int)(e - (int64_t)i * mb);
+          const int need = s_need[i];
+          const int v = P.bt[e0 + e];
+          if (need >= 0 && lb >= need && v >= 0) pb[r] = v;
+        }
+        cnt += pb[r] >= 0;
+      }
+      const int incl = wave_incl_scan_dpp(cnt);
+      if (lane == kWave - 1) s_wave[wave] = incl;
+      __syncthreads();
+      int before = 0, total = 0;
+      for (int w = 0; w < kRelWaves; ++w) {
+        const int tw = s_wave[w];
+        before += w < wave ? tw : 0;
+        total += tw;
+      }
+      int at = fc0 + carry + before + incl - cnt;
+#pragma unroll
+      for (int r = 0; r < kRun; ++r) {
+        if (pb[r] >= 0) {
+          if (at < P.free_cap) P.free_list[at] = pb[r];
+          ++at;
+          P.bt[e0 + c0 + (int64_t)tid * kRun + r] = -1;
+        }
+      }
+      carry += total;
+      __syncthreads();  // s_wave is read by every thread before the next chunk writes it
+    }
   }
   if (tid == 0) *P.free_count = min(fc0 + carry, P.free_cap);
 }
