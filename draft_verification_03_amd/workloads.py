@@ -24,6 +24,10 @@ draft tree of "投机推理：小模型搭树，大模型一次验证"):
   [2, 2], [1, 1]] ("投机推理" tree configuration section), B=128, V=151936; step s has
   B * top_head[s] draft rows of N(0, 2^2) logits; root tokens uniform, root positions
   L_b ~ U{0..1010}.
+* ``ngram``   -- B=256 token histories (prompt + generated text) of U{1024..8192} tokens over
+  V=128256, built from segments: with probability 1/2 a fresh span of U{4..32} uniform tokens,
+  else a copy of an earlier span of the history, so that trailing n-grams recur (the pages'
+  setting for model-free drafts: output that overlaps its input).
 
 Every chain workload has committed lengths L_b ~ U{0..4095} and seq_id = b.
 """
@@ -67,7 +71,8 @@ CHAIN_CONFIGS = {
                noise=(0.3, 1.5), T=(0.5, 1.2), top_p=None),
 }
 
-SEEDS = {"markov": 101, "c2": 202, "c3": 303, "tree": 404, "c5": 505, "tree_draft": 606}
+SEEDS = {"markov": 101, "c2": 202, "c3": 303, "tree": 404, "c5": 505, "tree_draft": 606,
+         "ngram": 707}
 
 
 def _pool_map(fn, n):
@@ -281,6 +286,28 @@ def tree_draft_inputs(seed: int | None = None, B: int = 128, V: int = 151936,
                 root_token=rng.integers(0, V, size=B).astype(np.int32),
                 pos_base=rng.integers(0, max_len + 1, size=B).astype(np.int32), vocab=V,
                 stride=st, batch=B)
+
+
+def ngram_inputs(seed: int | None = None, B: int = 256, min_len: int = 1024,
+                 max_len: int = 8192, V: int = 128256, copy_prob: float = 0.5,
+                 span=(4, 32), stride: int | None = None) -> dict:
+    """Token histories for the n-gram lookup: segments that are either fresh uniform tokens or
+    copies of an earlier span of the same history."""
+    rng = np.random.default_rng(SEEDS["ngram"] if seed is None else seed)
+    st = round_up(max_len, 8) if stride is None else stride
+    tok = np.zeros((B, st), np.int32)
+    lens = rng.integers(min_len, max_len + 1, size=B).astype(np.int32)
+    for b in range(B):
+        h = []
+        while len(h) < lens[b]:
+            n = int(rng.integers(span[0], span[1] + 1))
+            if len(h) > n and rng.random() < copy_prob:
+                i = int(rng.integers(0, len(h) - n))
+                h.extend(h[i:i + n])
+            else:
+                h.extend(rng.integers(0, V, size=n).tolist())
+        tok[b, :lens[b]] = h[:lens[b]]
+    return dict(tokens=tok, hist_len=lens, vocab=V, stride=st, batch=B)
 
 
 # --------------------------------------------------------------------------------------

@@ -79,6 +79,8 @@ def _declare(L):
                                          ctypes.c_int64, ctypes.c_int64, _I, _I, _P, _P, _P,
                                          _P, _P, _P, _P]
     L.oracle_kv_commit_paged.restype = _I
+    L.oracle_ngram_draft.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+    L.oracle_ngram_draft.restype = _I
 
 
 class _RowInfo(ctypes.Structure):
@@ -337,3 +339,18 @@ def kv_commit_paged(k_layers, v_layers, block_table, path_nodes, path_len, commi
                                  int(lead_slots), int(max_depth), _ptr(bt), _ptr(pn), _ptr(pl),
                                  _ptr(cl), _ptr(free_list), _ptr(fc), _ptr(fl))
     return cl, int(fc[0]), fl
+
+
+def ngram_draft(tokens, hist_len, nmin, nmax, gamma, draft_stride=None):
+    """n-gram prompt lookup over token histories [B, stride] (reading R23). Returns drafts
+    [B, draft_stride] (-1 padded), num_drafts, match_len and match_pos."""
+    t = _c(tokens, np.int32)
+    hl = _c(hist_len, np.int32)
+    B, stride = t.shape
+    ds = int(gamma if draft_stride is None else draft_stride)
+    out = {"drafts": np.full((B, ds), -1, np.int32), "num_drafts": np.zeros(B, np.int32),
+           "match_len": np.zeros(B, np.int32), "match_pos": np.zeros(B, np.int32)}
+    lib().oracle_ngram_draft(B, stride, _ptr(t), _ptr(hl), int(nmin), int(nmax), int(gamma), ds,
+                             _ptr(out["drafts"]), _ptr(out["num_drafts"]),
+                             _ptr(out["match_len"]), _ptr(out["match_pos"]))
+    return out

@@ -74,6 +74,12 @@
  *       each sequence's blocks in logical order, and its table entry becomes -1. A sequence
  *       with a copied slot outside the table or in an unmapped block, or whose L' needs more
  *       blocks than the table has, is flagged SLOT_OOB and left untouched.
+ *   R23 n-gram prompt lookup ([KV] variants, n-gram and prefix matching; [LI] §10.6.3,
+ *       model-free drafts and the ngram method's prompt_lookup_min / prompt_lookup_max):
+ *       the suffix of length n of the history h[0..len) is looked up among the earlier
+ *       occurrences h[i..i+n), i < len - n; the longest n in [min, max] with an occurrence
+ *       wins, and for it the latest occurrence (largest i). The drafts are the tokens that
+ *       follow it, h[i+n .. min(i+n+gamma, len)); no occurrence for any n gives no draft.
  */
 #include <math.h>
 #include <stdint.h>
@@ -802,6 +808,40 @@ int oracle_kv_commit_paged(int B, int num_layers, int num_kv_heads, int head_dim
       free_list[free_count[0]++] = bt[lb];
       bt[lb] = -1;
     }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* n-gram prompt lookup ([KV] variants section on n-gram / prefix matching; [LI] §10.6.3   */
+/* model-free drafts, prompt_lookup_min / prompt_lookup_max). Reading R23. tokens is       */
+/* [B][stride]; drafts is [B][draft_stride] (tokens, then -1); num_drafts, match_len and    */
+/* match_pos are [B].                                                                      */
+/* ------------------------------------------------------------------------------------ */
+int oracle_ngram_draft(int B, int stride, const int32_t* tokens, const int32_t* hist_len,
+                       int nmin, int nmax, int gamma, int draft_stride, int32_t* drafts,
+                       int32_t* num_drafts, int32_t* match_len, int32_t* match_pos) {
+  for (int b = 0; b < B; ++b) {
+    const int32_t* h = tokens + (size_t)b * stride;
+    const int len = hist_len[b];
+    int best_n = 0, best_i = -1;
+    for (int n = nmax; n >= nmin && best_i < 0; --n) {
+      if (n > len - 1) continue; /* an earlier occurrence needs i >= 0 and i < len - n */
+      for (int i = len - n - 1; i >= 0; --i) {
+        int same = 1;
+        for (int k = 0; k < n; ++k)
+          if (h[i + k] != h[len - n + k]) { same = 0; break; }
+        if (same) { best_n = n; best_i = i; break; }
+      }
+    }
+    int32_t* d = drafts + (size_t)b * draft_stride;
+    for (int j = 0; j < draft_stride; ++j) d[j] = -1;
+    int nd = 0;
+    if (best_i >= 0)
+      for (int j = 0; j < gamma && best_i + best_n + j < len; ++j) d[nd++] = h[best_i + best_n + j];
+    num_drafts[b] = nd;
+    match_len[b] = best_n;
+    match_pos[b] = best_i;
   }
   return 0;
 }
