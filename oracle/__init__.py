@@ -79,7 +79,7 @@ def _declare(L):
                                          ctypes.c_int64, ctypes.c_int64, _I, _I, _P, _P, _P,
                                          _P, _P, _P, _P]
     L.oracle_kv_commit_paged.restype = _I
-    L.oracle_ngram_draft.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+    L.oracle_ngram_draft.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
     L.oracle_ngram_draft.restype = _I
 
 
@@ -349,8 +349,10 @@ def ngram_draft(tokens, hist_len, nmin, nmax, gamma, draft_stride=None):
     B, stride = t.shape
     ds = int(gamma if draft_stride is None else draft_stride)
     out = {"drafts": np.full((B, ds), -1, np.int32), "num_drafts": np.zeros(B, np.int32),
-           "match_len": np.zeros(B, np.int32), "match_pos": np.zeros(B, np.int32)}
+           "match_len": np.zeros(B, np.int32), "match_pos": np.zeros(B, np.int32),
+           "seq_flags": np.zeros(B, np.int32)}
     lib().oracle_ngram_draft(B, stride, _ptr(t), _ptr(hl), int(nmin), int(nmax), int(gamma), ds,
                              _ptr(out["drafts"]), _ptr(out["num_drafts"]),
-                             _ptr(out["match_len"]), _ptr(out["match_pos"]))
+                             _ptr(out["match_len"]), _ptr(out["match_pos"]),
+                             _ptr(out["seq_flags"]))
     return out

@@ -816,14 +816,19 @@ int oracle_kv_commit_paged(int B, int num_layers, int num_kv_heads, int head_dim
 /* n-gram prompt lookup ([KV] variants section on n-gram / prefix matching; [LI] §10.6.3   */
 /* model-free drafts, prompt_lookup_min / prompt_lookup_max). Reading R23. tokens is       */
 /* [B][stride]; drafts is [B][draft_stride] (tokens, then -1); num_drafts, match_len and    */
-/* match_pos are [B].                                                                      */
+/* match_pos are [B]. A history length outside [0, stride] is flagged BAD_PARAM (no draft). */
 /* ------------------------------------------------------------------------------------ */
 int oracle_ngram_draft(int B, int stride, const int32_t* tokens, const int32_t* hist_len,
                        int nmin, int nmax, int gamma, int draft_stride, int32_t* drafts,
-                       int32_t* num_drafts, int32_t* match_len, int32_t* match_pos) {
+                       int32_t* num_drafts, int32_t* match_len, int32_t* match_pos,
+                       int32_t* seq_flags) {
   for (int b = 0; b < B; ++b) {
     const int32_t* h = tokens + (size_t)b * stride;
-    const int len = hist_len[b];
+    int len = hist_len[b];
+    if (len < 0 || len > stride) {
+      if (seq_flags) seq_flags[b] |= OF_BAD_PARAM;
+      len = 0;
+    }
     int best_n = 0, best_i = -1;
     for (int n = nmax; n >= nmin && best_i < 0; --n) {
       if (n > len - 1) continue; /* an earlier occurrence needs i >= 0 and i < len - n */

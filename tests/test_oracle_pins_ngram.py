@@ -83,3 +83,10 @@ def test_workload_histories_recur(orc):
     x = W.ngram_inputs(B=32, min_len=256, max_len=1024)
     o = orc.ngram_draft(x["tokens"], x["hist_len"], 1, 4, 8)
     assert (o["num_drafts"] > 0).mean() > 0.3
+
+
+def test_length_outside_the_row_is_flagged(orc):
+    tok = np.arange(32, dtype=np.int32).reshape(2, 16) % 3
+    o = orc.ngram_draft(tok, np.array([17, -1], np.int32), 1, 3, 4)
+    assert list(o["seq_flags"]) == [orc.F_BAD_PARAM] * 2
+    assert (o["num_drafts"] == 0).all() and (o["drafts"] == -1).all()
