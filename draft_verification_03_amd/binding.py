@@ -74,6 +74,15 @@ class spec_paged_kv_args(ctypes.Structure):
     ]
 
 
+class spec_ngram_args(ctypes.Structure):
+    _fields_ = [
+        ("batch", _I32), ("hist_stride", _I32), ("ngram_min", _I32), ("ngram_max", _I32),
+        ("num_draft", _I32), ("draft_stride", _I32), ("tokens", _P), ("hist_len", _P),
+        ("draft_tokens", _P), ("num_drafts", _P), ("match_len", _P), ("match_pos", _P),
+        ("seq_flags", _P),
+    ]
+
+
 class spec_kv_args(ctypes.Structure):
     _fields_ = [
         ("batch", _I32), ("num_layers", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
@@ -93,7 +102,7 @@ class SpecError(RuntimeError):
 _lib = None
 
 # Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def lib_path() -> str:
@@ -127,6 +136,8 @@ def lib():
         L.spec_tree_draft_step.restype = ctypes.c_int
         L.kv_commit_paged.argtypes = [ctypes.POINTER(spec_paged_kv_args), _P]
         L.kv_commit_paged.restype = ctypes.c_int
+        L.spec_ngram_draft.argtypes = [ctypes.POINTER(spec_ngram_args), _P]
+        L.spec_ngram_draft.restype = ctypes.c_int
         if L.spec_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{_build.LIB} has ABI version {L.spec_abi_version()}, the "
                                f"binding expects {ABI_VERSION}: rebuild the library")
@@ -341,6 +352,30 @@ def kv_paged_args(*, k_cache, v_cache, block_table, path_nodes, path_len, commit
 
 def kv_commit_paged(args: spec_paged_kv_args, stream=None):
     _check(lib().kv_commit_paged(ctypes.byref(args), _stream(stream)))
+
+
+def ngram_args(*, tokens, hist_len, draft_tokens, num_drafts, ngram_min, ngram_max,
+               num_draft, match_len=None, match_pos=None, seq_flags=None):
+    """tokens [B, hist_stride] and draft_tokens [B, draft_stride] are device int32 tensors."""
+    a = spec_ngram_args()
+    a.batch = int(tokens.shape[0])
+    a.hist_stride = int(tokens.shape[1])
+    a.ngram_min, a.ngram_max = int(ngram_min), int(ngram_max)
+    a.num_draft = int(num_draft)
+    a.draft_stride = int(draft_tokens.shape[1])
+    a.tokens = _ptr(tokens)
+    a.hist_len = _ptr(hist_len)
+    a.draft_tokens = _ptr(draft_tokens)
+    a.num_drafts = _ptr(num_drafts)
+    a.match_len = _ptr(match_len)
+    a.match_pos = _ptr(match_pos)
+    a.seq_flags = _ptr(seq_flags)
+    _keep(a, tokens, hist_len, draft_tokens, num_drafts, match_len, match_pos, seq_flags)
+    return a
+
+
+def spec_ngram_draft(args: spec_ngram_args, stream=None):
+    _check(lib().spec_ngram_draft(ctypes.byref(args), _stream(stream)))
 
 
 def _tree_config(top_head, top_k_spec):

@@ -330,4 +330,28 @@ int kv_commit_paged(const spec_paged_kv_args* a, void* hip_stream) {
   return SPEC_OK;
 }
 
+int spec_ngram_draft(const spec_ngram_args* a, void* hip_stream) {
+  g_err[0] = '\0';
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "spec_ngram_draft: args is NULL");
+  if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
+  if (a->hist_stride < 4 || a->hist_stride % 4 != 0)
+    return fail(SPEC_ERR_INVALID_ARG, "hist_stride must be a positive multiple of 4 (got %d)",
+                a->hist_stride);
+  if (a->ngram_min < 1 || a->ngram_max < a->ngram_min || a->ngram_max > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "need 1 <= ngram_min <= ngram_max <= 64 (got %d, %d)",
+                a->ngram_min, a->ngram_max);
+  if (a->num_draft < 1 || a->num_draft > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "num_draft must be in [1, 64] (got %d)", a->num_draft);
+  if (a->draft_stride < a->num_draft)
+    return fail(SPEC_ERR_INVALID_ARG, "draft_stride must be >= num_draft");
+  if (a->batch == 0) return SPEC_OK;
+  if (!a->tokens || !a->hist_len || !a->draft_tokens || !a->num_drafts)
+    return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned16(a->tokens))
+    return fail(SPEC_ERR_INVALID_ARG, "tokens must be 16-byte aligned");
+  hipError_t e = specv::launch_ngram(*a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "spec_ngram_draft launch");
+  return SPEC_OK;
+}
+
 }  // extern "C"

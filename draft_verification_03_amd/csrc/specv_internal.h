@@ -42,6 +42,7 @@ hipError_t launch_tree(const spec_tree_args& a, void* ws, hipStream_t s);
 
 hipError_t launch_kv(const spec_kv_args& a, hipStream_t s);
 hipError_t launch_kv_paged(const spec_paged_kv_args& a, hipStream_t s);
+hipError_t launch_ngram(const spec_ngram_args& a, hipStream_t s);
 
 // Tree drafting: limits and the geometry of one step, derived on the host from the tree
 // configuration (top_head, top_k_spec) and the step index.

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 4
+#define SPEC_ABI_VERSION 5
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
@@ -324,6 +324,37 @@ typedef struct spec_paged_kv_args {
   int32_t* seq_flags;        /* [B] or NULL (bits OR-ed in)                                 */
 } spec_paged_kv_args;
 
+/*
+ * n-gram prompt lookup, a drafter without weights ("KV Cache 优化（四）", variants section on
+ * n-gram / prefix matching; "10.6 投机解码" §10.6.3: model-free drafts look for the history's
+ * trailing n-gram earlier in the prompt or the generated text and propose what followed it;
+ * the ngram method's prompt_lookup_min / prompt_lookup_max bound the match window).
+ *
+ * For sequence b with history h = tokens[b][0..len), len = hist_len[b]: the trailing n-gram
+ * h[len-n..len) is looked up among the earlier occurrences h[i..i+n), i < len - n. The longest
+ * n in [ngram_min, ngram_max] with an occurrence wins, and for that n the latest occurrence
+ * (largest i). The drafts are h[i+n .. min(i+n+num_draft, len)): draft_tokens[b][0..nd) with
+ * nd = num_drafts[b], then -1 up to draft_stride; no occurrence gives nd = 0. match_len[b] = n
+ * (0 if none) and match_pos[b] = i (-1 if none), when given. A history length outside
+ * [0, hist_stride] sets SPEC_FLAG_BAD_PARAM and gives no draft. The drafts of a batch feed
+ * spec_verify_chain with gamma_b = num_drafts[b] (cu_gamma its exclusive prefix sum).
+ */
+typedef struct spec_ngram_args {
+  int32_t batch;         /* B >= 0                                                         */
+  int32_t hist_stride;   /* elements per history row; a positive multiple of 4             */
+  int32_t ngram_min;     /* prompt_lookup_min; 1..ngram_max                                */
+  int32_t ngram_max;     /* prompt_lookup_max; ngram_min..64                               */
+  int32_t num_draft;     /* drafts per sequence at most (gamma); 1..64                     */
+  int32_t draft_stride;  /* elements per row of draft_tokens; >= num_draft                 */
+  const int32_t* tokens;   /* [B][hist_stride] token ids (16-byte aligned)                  */
+  const int32_t* hist_len; /* [B]                                                          */
+  int32_t* draft_tokens;   /* [B][draft_stride]                                            */
+  int32_t* num_drafts;     /* [B]                                                          */
+  int32_t* match_len;      /* [B] or NULL                                                  */
+  int32_t* match_pos;      /* [B] or NULL                                                  */
+  int32_t* seq_flags;      /* [B] or NULL (bits OR-ed in)                                  */
+} spec_ngram_args;
+
 /* ABI revision of this header (SPEC_ABI_VERSION). */
 int spec_abi_version(void);
 
@@ -362,6 +393,9 @@ int spec_tree_draft_step(const spec_tree_draft_args* args, void* workspace,
 /* Enqueue the paged KV commit, pointer update and block release (no workspace). Returns
  * SPEC_OK or a negative status. */
 int kv_commit_paged(const spec_paged_kv_args* args, void* hip_stream);
+
+/* Enqueue the n-gram prompt lookup (no workspace). Returns SPEC_OK or a negative status. */
+int spec_ngram_draft(const spec_ngram_args* args, void* hip_stream);
 
 #ifdef __cplusplus
 }

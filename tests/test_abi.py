@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     for want in ["spec_abi_version", "spec_last_error", "spec_verify_chain_workspace_size",
                  "spec_verify_chain", "spec_verify_tree_workspace_size", "spec_verify_tree",
                  "kv_commit_path", "spec_tree_draft_workspace_size", "spec_tree_draft_step",
-                 "kv_commit_paged"]:
+                 "kv_commit_paged", "spec_ngram_draft"]:
         assert want in names
 
 
@@ -48,6 +48,7 @@ def test_struct_layout_matches_c(tmp_path):
         "spec_kv_args": [f for f, _ in B.spec_kv_args._fields_],
         "spec_tree_draft_args": [f for f, _ in B.spec_tree_draft_args._fields_],
         "spec_paged_kv_args": [f for f, _ in B.spec_paged_kv_args._fields_],
+        "spec_ngram_args": [f for f, _ in B.spec_ngram_args._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "spec_verify.h"',
              "int main(void){"]
@@ -70,7 +71,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_abi_version_and_workspace_sizes():
-    assert B.spec_abi_version() == B.ABI_VERSION == 4
+    assert B.spec_abi_version() == B.ABI_VERSION == 5
     assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
     assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
     assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
@@ -304,3 +305,27 @@ def test_kv_paged_misaligned_layer_pointer_and_empty_batch():
     a._keep2 = ptrs
     assert B.lib().kv_commit_paged(ctypes.byref(a), None) == B.SPEC_ERR_INVALID_ARG
     assert B.lib().kv_commit_paged(ctypes.byref(_paged(batch=0)), None) == B.SPEC_OK
+
+
+def _ngram(**kw):
+    a = B.spec_ngram_args()
+    base = dict(batch=2, hist_stride=64, ngram_min=1, ngram_max=4, num_draft=8, draft_stride=8,
+                tokens=0x1000, hist_len=0x2000, draft_tokens=0x3000, num_drafts=0x4000)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=-1), dict(hist_stride=0), dict(hist_stride=66), dict(ngram_min=0),
+    dict(ngram_min=5), dict(ngram_max=65), dict(num_draft=0), dict(num_draft=65),
+    dict(draft_stride=7), dict(tokens=None), dict(num_drafts=None), dict(tokens=0x1008),
+])
+def test_ngram_validation(kw):
+    assert B.lib().spec_ngram_draft(ctypes.byref(_ngram(**kw)), None) == B.SPEC_ERR_INVALID_ARG
+    assert B.spec_last_error() != ""
+
+
+def test_ngram_empty_batch_is_a_no_op():
+    assert B.lib().spec_ngram_draft(ctypes.byref(_ngram(batch=0)), None) == B.SPEC_OK
