@@ -13,6 +13,7 @@ bounded sample of the same workload as a reported baseline.
   python bench.py --copy-calibration     # a plain copy of known size, for counter scaling
   python bench.py --workload tree_draft  # the tree-drafting steps of one round instead
   python bench.py --workload paged_kv    # the paged KV commit of the tree workload instead
+  python bench.py --workload ngram       # the n-gram prompt lookup instead
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
 大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
@@ -24,6 +25,10 @@ accepted paths (B=128, depth <= 3) into a cache of 32 layers x K,V x 8 heads x 1
 in 16-slot blocks (64 shuffled blocks per sequence, 17.2 GB), releasing the surplus blocks.
 The block table, lengths and free count are restored before each call, outside the events
 that time it.
+
+With --workload ngram a step is one spec_ngram_draft call over B=256 token histories of
+U{1024..8192} tokens (prompt_lookup_min 1, max 4, 8 drafts); the bytes are the histories'
+tokens, read once.
 """
 from __future__ import annotations
 
@@ -314,6 +319,74 @@ def paged_kv_bench(args):
     torch.cuda.empty_cache()
 
 
+def ngram_bench(args):
+    """The n-gram prompt lookup (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    from draft_verification_03_amd import binding as B
+    from draft_verification_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("generating the n-gram workload (B=256, 1024..8192 tokens)")
+    x = W.ngram_inputs()
+    Bn, g = x["batch"], 8
+    tok = torch.from_numpy(x["tokens"]).cuda()
+    lens = torch.from_numpy(x["hist_len"]).cuda()
+    d = torch.empty((Bn, g), dtype=torch.int32, device="cuda")
+    nd = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    a = B.ngram_args(tokens=tok, hist_len=lens, draft_tokens=d, num_drafts=nd, ngram_min=1,
+                     ngram_max=4, num_draft=g)
+    t_warm = time.time()
+    done = 0
+    while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        for _ in range(10):
+            B.spec_ngram_draft(a)
+        done += 10
+        torch.cuda.synchronize()
+    log(f"timing {args.steps} calls")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        B.spec_ngram_draft(a)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = int(x["hist_len"].sum()) * 4 + Bn * (g + 1) * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    drafted = int((nd > 0).sum())
+    log(f"lookup {ms * 1e3:.1f} us for {Bn} histories ({gbs:.0f} GB/s), {drafted} drafted")
+    res = {
+        "metric": "n-gram prompt lookup: sequences/s at B=256, 1024..8192-token histories; "
+                  "achieved HBM GB/s vs peak",
+        "value": Bn / (ms / 1e3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "n-gram prompt lookup, B=256 histories of U{1024..8192} tokens "
+                               "(half fresh spans, half copies of earlier spans), n in [1, 4], "
+                               "8 drafts",
+                   "call_algorithmic_bytes": nbytes, "sequences_drafted": drafted},
+        "roofline": {"bound": "hbm", "kernel": "ngram_draft_kernel", "achieved": gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_launch": nbytes, "avg_launch_us": ms * 1e3,
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the oracle on the whole batch")
+        t0 = time.time()
+        reps = 0
+        while time.time() - t0 < 10.0 or reps == 0:
+            oracle.ngram_draft(x["tokens"], x["hist_len"], 1, 4, g)
+            reps += 1
+        el = time.time() - t0
+        res["cpu_baseline"] = {"value": reps * Bn / el, "unit": "sequences/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} whole batches of {Bn} histories, "
+                                         f"{el:.1f} s wall, one thread"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,7 +396,7 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=["chain", "tree_draft", "paged_kv"], default="chain")
+    ap.add_argument("--workload", choices=["chain", "tree_draft", "paged_kv", "ngram"], default="chain")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
@@ -338,6 +411,9 @@ def main():
         return
     if args.workload == "paged_kv":
         paged_kv_bench(args)
+        return
+    if args.workload == "ngram":
+        ngram_bench(args)
         return
 
     import numpy as np
