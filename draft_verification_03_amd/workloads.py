@@ -17,9 +17,10 @@ draft tree of "投机推理：小模型搭树，大模型一次验证"):
   per row boosted by +8, draft = target + N(0, 1^2), T=0.7, top-p 0.9 on both laws.
 * ``c5``      -- B=1024, gamma_b ~ U{1..8}, V=128256: target N(0, 2^2), T_b ~ U[0.5, 1.2],
   draft = target + N(0, sigma_b^2) with sigma_b ~ U[0.3, 1.5], no top-p.
-* ``tree``    -- B=128, V=151936, 13-node tree (root + [6], [2,2], [1,1]), 5 target rows per
-  sequence, target N(0, 2^2), draft rows = target + N(0, 0.5^2); KV cache 32 layers x 8 KV
-  heads x head_dim 128, 1024 slots.
+* ``tree``    -- B=128, V=151936, 13-node tree (root + [6], [2,2], [1,1]) with random
+  distinct sibling tokens, 5 target rows per sequence of N(0, 2^2) logits, each boosting one
+  child's token by +14 with probability 0.7; KV cache 32 layers x 8 KV heads x head_dim 128,
+  1024 slots.
 * ``tree_draft`` -- the drafting side of the same tree: top_head [1, 2, 2], top_k_spec [[6],
   [2, 2], [1, 1]] ("投机推理" tree configuration section), B=128, V=151936; step s has
   B * top_head[s] draft rows of N(0, 2^2) logits; root tokens uniform, root positions
@@ -191,24 +192,18 @@ def log_rows_bf16(table: np.ndarray, stride: int = 8) -> np.ndarray:
 TREE_SPEC = dict(top_k=[[6], [2, 2], [1, 1]], top_head=[1, 2, 2])
 
 
-def _top(row: np.ndarray, k: int) -> np.ndarray:
-    """Indices of the k largest entries, larger first, ties to the lower index."""
-    order = np.lexsort((np.arange(row.shape[0]), -row.astype(np.float64)))
-    return order[:k]
+def tree_inputs(seed: int | None = None, B: int = 128, V: int = 151936, sigma: float = 2.0,
+                hit: float = 0.7, boost: float = 14.0, max_len: int = 1010) -> dict:
+    """Synthetic draft trees of the [6], [2,2], [1,1] shape and their target rows.
 
-
-def tree_inputs(seed: int | None = None, B: int = 128, V: int = 151936,
-                noise: float = 0.5, sigma: float = 2.0, max_len: int = 1010) -> dict:
-    """Synthetic draft trees with the [6], [2,2], [1,1] shape and their target rows.
-
-    Per sequence the drafter sees draft rows = target rows + N(0, noise^2) (bf16-rounded
-    values compared). Root: top-6 draft tokens become nodes 1..6 (larger first). Depth 2:
-    nodes 1 and 2 (the two best depth-1 nodes) each get their top-2 tokens, nodes 7..10.
-    Depth 3: of nodes 7..10 the two with the highest path score -- the sum along the path of
-    (draft logit of the child - largest draft logit of its parent's row) -- each get their
-    top-1 token, nodes 11 and 12. Target rows exist for the five expanded nodes:
-    [root, node 1, node 2, first expanded depth-2 node, second]. Node 0 is the root token
-    (already emitted; never verified).
+    Topology per sequence: root 0; nodes 1..6 are its children; nodes 7, 8 are children of
+    node 1 and 9, 10 of node 2; two of nodes 7..10, drawn at random, get one child each
+    (nodes 11 and 12, in index order). Sibling tokens are distinct uniform ids. Target rows
+    exist for the five expanded nodes [root, 1, 2, the two expanded depth-2 nodes]: N(0,
+    sigma^2) logits in which, with probability ``hit``, the token of one of the node's
+    children gets +``boost`` (drawn uniformly among the children that have rows of their own,
+    if any), so that the tree walk can go on through it; otherwise the row's argmax has nothing
+    to do with the children. Node 0 is the root token (already emitted; never verified).
     """
     rng = np.random.default_rng(SEEDS["tree"] if seed is None else seed)
     N = 13
@@ -220,41 +215,25 @@ def tree_inputs(seed: int | None = None, B: int = 128, V: int = 151936,
     node_token = np.zeros((B, N), dtype=np.int32)
     for b in range(B):
         t = rng.standard_normal((R, V), dtype=np.float32) * np.float32(sigma)
-        d = bf16_to_f32(bf16_bits(t + rng.standard_normal((R, V), dtype=np.float32) *
-                                  np.float32(noise)))
-        logits[b, :, :V] = bf16_bits(t)
-        par = [-1] * N
+        deep = sorted(int(i) for i in rng.choice(np.arange(7, 11), size=2, replace=False))
+        par = [-1, 0, 0, 0, 0, 0, 0, 1, 1, 2, 2, deep[0], deep[1]]
         tok = [0] * N
         tok[0] = int(rng.integers(0, V))
-        score = [0.0] * N
-        # depth 1
-        top6 = _top(d[0], 6)
-        for i, v in enumerate(top6):
-            par[1 + i] = 0
-            tok[1 + i] = int(v)
-            score[1 + i] = float(d[0][v] - d[0].max())
-        # depth 2: children of nodes 1 and 2, target/draft rows 1 and 2
-        nid = 7
-        for parent_node, row in ((1, 1), (2, 2)):
-            for v in _top(d[row], 2):
-                par[nid] = parent_node
-                tok[nid] = int(v)
-                score[nid] = score[parent_node] + float(d[row][v] - d[row].max())
-                nid += 1
-        # depth 3: expand the two best depth-2 nodes (ties to the lower node index)
-        cand = sorted(range(7, 11), key=lambda i: (-score[i], i))[:2]
-        rows = {0: 0, 1: 1, 2: 2}
-        for j, node in enumerate(cand):
-            row = 3 + j
-            rows[node] = row
-            v = _top(d[row], 1)[0]
-            par[nid] = node
-            tok[nid] = int(v)
-            nid += 1
+        for node in range(N):  # distinct tokens among each node's children
+            kids = [c for c in range(1, N) if par[c] == node]
+            for c, v in zip(kids, rng.choice(V, size=len(kids), replace=False)):
+                tok[c] = int(v)
+        rows = {0: 0, 1: 1, 2: 2, deep[0]: 3, deep[1]: 4}
+        for node, r in rows.items():
+            kids = [c for c in range(1, N) if par[c] == node]
+            inner = [c for c in kids if c in rows] or kids
+            if rng.random() < hit:
+                t[r, tok[inner[int(rng.integers(0, len(inner)))]]] += np.float32(boost)
+        logits[b, :, :V] = bf16_bits(t)
         parent[b] = par
         node_token[b] = tok
-        for node, row in rows.items():
-            node_row[b, node] = row
+        for node, r in rows.items():
+            node_row[b, node] = r
     L = rng.integers(0, max_len, size=B).astype(np.int32)
     return dict(logits=logits, parent=parent, node_row=node_row, node_token=node_token,
                 rows_per_seq=R, num_nodes=N, max_depth=3, vocab=V, stride=st,
