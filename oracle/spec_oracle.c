@@ -80,6 +80,10 @@
  *       occurrences h[i..i+n), i < len - n; the longest n in [min, max] with an occurrence
  *       wins, and for it the latest occurrence (largest i). The drafts are the tokens that
  *       follow it, h[i+n .. min(i+n+gamma, len)); no occurrence for any n gives no draft.
+ *   R24 a drafter without a law (the n-gram lookup above) proposes each draft with certainty:
+ *       with no draft rows and T > 0 the draft law q_k is the point mass at d_k, so
+ *       a = min(1, p_k(d_k)) and the residual max(0, p_k - q_k) is p_k with d_k removed
+ *       ([KV] §4 eq. a(x) and eq. p'(x) with that q). Filters leave a point mass as it is.
  */
 #include <math.h>
 #include <stdint.h>
@@ -373,7 +377,7 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         if (d < 0 || d >= V) bad = 1;
       }
       if (bad) flags |= OF_BAD_TOKEN;
-      if (!(T >= 0.0) || !(P > 0.0 && P <= 1.0) || (T > 0.0 && g > 0 && !draft)) {
+      if (!(T >= 0.0) || !(P > 0.0 && P <= 1.0)) {
         flags |= OF_BAD_PARAM;
         bad = 1;
       }
@@ -411,11 +415,16 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
           stopped = 1;
           break;
         }
-        const uint16_t* drow = draft + (size_t)(drow0 + k - 1) * row_stride;
         oracle_dist(trow, V, T, P, K, p, scratch, &ip);
-        oracle_dist(drow, V, T, P, K, q, scratch, &iq);
         if (ip.topp_margin < margin) margin = ip.topp_margin;
-        if (iq.topp_margin < margin) margin = iq.topp_margin;
+        if (draft) {
+          const uint16_t* drow = draft + (size_t)(drow0 + k - 1) * row_stride;
+          oracle_dist(drow, V, T, P, K, q, scratch, &iq);
+          if (iq.topp_margin < margin) margin = iq.topp_margin;
+        } else { /* reading R24: the point mass at the draft token */
+          for (int v = 0; v < V; ++v) q[v] = 0.0;
+          q[d] = 1.0;
+        }
         double u_acc = uniform_override ? (double)uniform_override[ovr]
                                         : oracle_uniform(seed, id, (uint32_t)(L + k), PURPOSE_ACCEPT);
         double u_res = uniform_override ? (double)uniform_override[ovr + 1]
