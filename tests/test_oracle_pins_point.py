@@ -74,7 +74,11 @@ def test_chain_with_point_mass_drafts(orc, T, P):
                 assert r["probe_rows"][cu[b], 1] == 1.0
                 res = p.copy()
                 res[toks[cu[b]]] = 0.0
-                want = int(np.searchsorted(np.cumsum(res) / res.sum(), u[t0], side="right"))
+                if res.sum() > 0:
+                    want = int(np.searchsorted(np.cumsum(res) / res.sum(), u[t0], side="right"))
+                else:  # p(d) = 1 (a nucleus of one token): no residual mass, the draw is from p
+                    want = int(np.searchsorted(np.cumsum(p), u[t0], side="right"))
+                    assert r["seq_flags"][b] & orc.F_RESID_FALLBACK
                 assert r["out_tokens"][t0] == want
             else:
                 assert r["num_accepted"][b] == g
