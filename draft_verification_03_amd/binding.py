@@ -102,7 +102,7 @@ class SpecError(RuntimeError):
 _lib = None
 
 # Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 def lib_path() -> str:

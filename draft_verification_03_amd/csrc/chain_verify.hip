@@ -144,8 +144,7 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
   s.eos = P.eos ? P.eos[b] : -1;
   s.cap = P.cap ? P.cap[b] : 0;
   s.bad_param = !(s.g >= 0 && s.g <= P.max_gamma && c0 >= 0 && c1 <= P.n_draft) ||
-                !temperature_ok(s.T) || !top_p_ok(s.P) ||
-                (s.T != 0.0f && s.g > 0 && P.draft == nullptr);
+                !temperature_ok(s.T) || !top_p_ok(s.P);
   if (s.T == 0.0f) s.T = 0.0f;  // -0 is greedy too
   s.filter = s.T != 0.0f && (s.P < 1.0f || (s.K >= 1 && s.K < P.V));
   return s;
@@ -695,9 +694,6 @@ void row_stats_kernel(ChainParams P) {
   if (!bonus && k > s.g) return;
   if (r == 1 && s.T == 0.0f) return;  // greedy: q is not read
   const int drow = s.d0 + k - 1;       // draft row (draft positions only)
-  const uint16_t* base = r == 0 ? P.target + (size_t)(s.t0 + k - 1) * P.stride
-                                : P.draft + (size_t)drow * P.stride;
-  const uint4* rp = reinterpret_cast<const uint4*>(base);
   const size_t slot = bonus ? 2 * (size_t)P.n_draft + (size_t)b : (size_t)drow * 2 + r;
   RowStat* st = P.stat + slot;
   NucEntry* list = P.nuc + slot * kNucMax;
@@ -708,7 +704,17 @@ void row_stats_kernel(ChainParams P) {
       if (tid == 0) *st = RowStat{0.0f, 1.0f, -INFINITY, 0.0f, 0, -1, 0, 1};
       return;
     }
+    if (r == 1 && P.draft == nullptr) {  // no draft rows: q is the point mass at d
+      if (tid == 0) {
+        list[0] = NucEntry{d, 1.0f};
+        *st = RowStat{0.0f, 1.0f, -INFINITY, 1.0f, d, 1, 0, 1};
+      }
+      return;
+    }
   }
+  const uint16_t* base = r == 0 ? P.target + (size_t)(s.t0 + k - 1) * P.stride
+                                : P.draft + (size_t)drow * P.stride;
+  const uint4* rp = reinterpret_cast<const uint4*>(base);
 
   const bool filt = TOPP && s.filter;
   if (tid == 0) {
@@ -917,6 +923,7 @@ __device__ __forceinline__ Draw draw_from_lists(const NucEntry* pl, int np, floa
 struct RowLaw {
   const uint4* row;
   float c, nref, t, iz;
+  int point = -1;  // >= 0: the law is the point mass at this token (row is not read)
 };
 
 __device__ __forceinline__ void law_weights(const RowLaw& L, const uint4& d, float w[8]) {
@@ -939,7 +946,12 @@ __device__ __forceinline__ void data_weights(const RowLaw& Lp, const RowLaw& Lq,
   law_weights(Lp, dp, w);
   if (residual) {
     float wq[8];
-    law_weights(Lq, dq, wq);
+    if (Lq.point >= 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wq[e] = (v * 8 + e == Lq.point) ? 1.0f : 0.0f;
+    } else {
+      law_weights(Lq, dq, wq);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = fmaxf(0.0f, w[e] - wq[e]);
   }
@@ -951,7 +963,7 @@ __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, 
                                             int v, int nvec, int V, float w[8]) {
   const uint4 z{0u, 0u, 0u, 0u};
   const uint4 dp = v < nvec ? Lp.row[v] : z;
-  const uint4 dq = (residual && v < nvec) ? Lq.row[v] : z;
+  const uint4 dq = (residual && Lq.point < 0 && v < nvec) ? Lq.row[v] : z;
   data_weights(Lp, Lq, residual, v, nvec, V, dp, dq, w);
 }
 
@@ -1101,7 +1113,7 @@ __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq,
     for (int t = 0; t < kTilesPerIter; ++t) {
       const int v = (g0 + t) * kWave + lane;
       dp[t] = v < nvec ? Lp.row[v] : z;
-      dq[t] = (residual && v < nvec) ? Lq.row[v] : z;
+      dq[t] = (residual && Lq.point < 0 && v < nvec) ? Lq.row[v] : z;
     }
 #pragma unroll
     for (int t = 0; t < kTilesPerIter; ++t) {
@@ -1321,9 +1333,12 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
                           : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
                                       SPEC_PURPOSE_RESIDUAL);
     const RowLaw Lp{prow, c, -sp.m * c, sp.t, 1.0f / sp.z};
-    const RowLaw Lq{reinterpret_cast<const uint4*>(P.draft +
-                                                   (size_t)(s.d0 + kstar - 1) * P.stride),
-                    c, -sq.m * c, sq.t, 1.0f / sq.z};
+    // no draft rows: the draft law is the point mass at the draft token
+    const RowLaw Lq = P.draft ? RowLaw{reinterpret_cast<const uint4*>(
+                                           P.draft + (size_t)(s.d0 + kstar - 1) * P.stride),
+                                       c, -sq.m * c, sq.t, 1.0f / sq.z}
+                              : RowLaw{nullptr, c, 0.0f, -INFINITY, 1.0f,
+                                       P.tokens[s.d0 + kstar - 1]};
     Draw d;
     const bool lists_p = sp.nuc >= 0, lists_pq = lists_p && sq.nuc >= 0;
     const NucEntry* lp = s_lp;

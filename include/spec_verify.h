@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 5
+#define SPEC_ABI_VERSION 6
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
@@ -63,7 +63,7 @@ extern "C" {
 #define SPEC_FLAG_TOPP_SLOW 64      /* a top-k/top-p threshold needed another read of a row
                                        (a second capture, or the exact multi-pass search)   */
 #define SPEC_FLAG_BAD_PARAM 128     /* T < 0, top_p outside (0,1], gamma_b out of range, or
-                                       T > 0 with draft_logits NULL: no progress            */
+                                       a history length outside its row: no progress       */
 #define SPEC_FLAG_EOS 256           /* the round's last emitted token is the EOS id         */
 #define SPEC_FLAG_LEN_CAP 512       /* the emission cap cut the round short                 */
 
@@ -87,7 +87,9 @@ extern "C" {
  *    kept); K <= 0 or K >= V keeps all. Top-p then keeps every token whose logit is >= t*,
  *    t* the largest logit value at which the mass of all kept tokens at or above it reaches
  *    P of the top-k set's mass. T = 0 is greedy: p_k is one-hot at the target argmax (lowest
- *    id on ties) and q is not read.
+ *    id on ties) and q is not read. With draft_logits NULL and T > 0, q_k is the point mass
+ *    at d_k -- a drafter without a law, such as spec_ngram_draft, proposes d_k with
+ *    certainty -- so a_k = p_k(d_k) and the residual is p_k without d_k.
  *  - test: a_k = min(1, p_k(d_k)/q_k(d_k)) (eq. a(x)); where q_k(d_k) = 0, a_k = [p_k(d_k) > 0]
  *    and SPEC_FLAG_Q_ZERO is set; accept iff u_acc < a_k, u_acc = U(L+k, ACCEPT). Greedy:
  *    accept iff d_k equals the target argmax.
@@ -118,7 +120,8 @@ typedef struct spec_chain_args {
   int32_t lead_slots;       /* 0 or 1 (1: the round also wrote x's slot at L)                */
   uint64_t seed;            /* Philox key                                                    */
   const uint16_t* target_logits; /* [total_draft_rows + B][row_stride] bf16                 */
-  const uint16_t* draft_logits;  /* [total_draft_rows][row_stride] bf16; NULL iff all T = 0  */
+  const uint16_t* draft_logits;  /* [total_draft_rows][row_stride] bf16, or NULL: point-mass
+                                    draft laws (no draft row is read)                      */
   const int32_t* cu_gamma;       /* [B+1], cu_gamma[0] = 0, non-decreasing                    */
   const int32_t* draft_tokens;   /* [total_draft_rows]; may be NULL if total_draft_rows = 0  */
   const float* temperature;      /* [B], >= 0                                                */

@@ -73,7 +73,8 @@ def run_gpu_chain(x, tokens, seed, override=None, lead=1, probes=True, no_draft=
     n_t = n_d + Bn
     t = dict(
         target=dev(x["target"]),
-        draft=None if (no_draft or x["draft"].shape[0] == 0) else dev(x["draft"]),
+        draft=None if (no_draft or x["draft"] is None or x["draft"].shape[0] == 0)
+        else dev(x["draft"]),
         cu=dev(cu), tok=dev(tokens if n_d else np.zeros(1, np.int32)),
         temp=dev(x["temperature"]),
         topp=None if x["top_p"] is None else dev(x["top_p"]),
