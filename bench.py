@@ -14,6 +14,7 @@ bounded sample of the same workload as a reported baseline.
   python bench.py --workload tree_draft  # the tree-drafting steps of one round instead
   python bench.py --workload paged_kv    # the paged KV commit of the tree workload instead
   python bench.py --workload ngram       # the n-gram prompt lookup instead
+  python bench.py --workload tree        # greedy tree verify + KV commit instead
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
 大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
@@ -25,6 +26,14 @@ accepted paths (B=128, depth <= 3) into a cache of 32 layers x K,V x 8 heads x 1
 in 16-slot blocks (64 shuffled blocks per sequence, 17.2 GB), releasing the surplus blocks.
 The block table, lengths and free count are restored before each call, outside the events
 that time it.
+
+With --workload tree a step is one spec_verify_tree call over the tree workload (B=128,
+V=151936, 5 target rows and 12 nodes per sequence, tree [6], [2, 2], [1, 1]) followed by one
+kv_commit_path of the accepted paths into a contiguous cache of 32 layers x K,V x 8 heads x
+128 bf16 (1024 slots per sequence, 17.2 GB). The committed lengths are restored before each
+step, outside the events. The line reports verify rows/s and the verify call's HBM bandwidth
+(the argmax kernel's rows, plus its small walk launch) against 8 TB/s; the commit's time and
+bytes ride along under "kv_commit".
 
 With --workload ngram a step is one spec_ngram_draft call over B=256 token histories of
 U{1024..8192} tokens (prompt_lookup_min 1, max 4, 8 drafts); the bytes are the histories'
@@ -319,6 +328,110 @@ def paged_kv_bench(args):
     torch.cuda.empty_cache()
 
 
+def tree_bench(args):
+    """Greedy tree verify and the contiguous KV commit of the tree workload (see the module
+    docstring)."""
+    import numpy as np
+    import torch
+
+    from draft_verification_03_amd import binding as B
+    from draft_verification_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("generating the tree workload (B=128, V=151936, 5 rows and 12 nodes per sequence)")
+    x = W.tree_inputs()
+    Bn = x["node_token"].shape[0]
+    R, md, V = x["rows_per_seq"], x["max_depth"], x["vocab"]
+    lg = x["logits"]
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
+        {np.dtype(np.uint16): np.int16}.get(a.dtype, a.dtype))).cuda()
+    logits = dv(lg.reshape(-1, lg.shape[-1]))
+    pn = torch.full((Bn, md), -1, dtype=torch.int32, device="cuda")
+    pl = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    out = torch.full((Bn, md + 1), -1, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    tfl = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    ta = B.tree_args(target_logits=logits, parent=dv(x["parent"]), node_row=dv(x["node_row"]),
+                     node_token=dv(x["node_token"]), path_nodes=pn, path_len=pl,
+                     out_tokens=out, num_emitted=ne, seq_flags=tfl, vocab=V, rows_per_seq=R,
+                     max_depth=md, tree_stride=x["num_nodes"], row_stride=lg.shape[-1])
+    ws = torch.empty(max(B.spec_verify_tree_workspace_size(Bn, R), 1), dtype=torch.uint8,
+                     device="cuda")
+    NL, H, Dh, S = (W.KV_SHAPE[k] for k in ("num_layers", "num_kv_heads", "head_dim", "slots"))
+    log(f"allocating the cache ({2 * NL * Bn * S * H * Dh * 2 / 1e9:.1f} GB)")
+    caches = [[torch.empty((Bn, S, H, Dh), dtype=torch.int16, device="cuda").random_(-32768, 32767)
+               for _ in range(2)] for _ in range(NL)]
+    L_init = dv(x["committed_len"])
+    Lt = L_init.clone()
+    kfl = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    ka = B.kv_args(k_cache=[c[0] for c in caches], v_cache=[c[1] for c in caches],
+                   path_nodes=pn, path_len=pl, committed_len=Lt, seq_flags=kfl,
+                   num_kv_heads=H, head_dim=Dh, seq_stride=S * H * Dh, slot_stride=H * Dh,
+                   head_stride=Dh, slot_capacity=S, lead_slots=1, max_depth=md)
+
+    def step():
+        B.spec_verify_tree(ta, workspace=ws)
+        B.kv_commit_path(ka)
+
+    t_warm = time.time()
+    done = 0
+    while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        Lt.copy_(L_init)
+        step()
+        done += 1
+        if done % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+           for _ in range(args.steps)]
+    for e0, e1, e2 in evs:
+        Lt.copy_(L_init)
+        e0.record()
+        B.spec_verify_tree(ta, workspace=ws)
+        e1.record()
+        B.kv_commit_path(ka)
+        e2.record()
+    torch.cuda.synchronize()
+    ms_tree = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in evs]))
+    ms_kv = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in evs]))
+    paths, plen = pn.cpu().numpy(), pl.cpu().numpy()
+    assert not kfl.cpu().numpy().any(), "KV commit flagged a sequence"
+    assert not (tfl.cpu().numpy() & B.FLAG_BAD_TREE).any(), "tree flagged as malformed"
+    moved = sum(int((paths[b, :plen[b]] != np.arange(1, plen[b] + 1)).sum()) for b in range(Bn))
+    rows = Bn * R
+    tree_bytes = rows * V * 2
+    kv_bytes = 2 * moved * NL * 2 * H * Dh * 2  # moved K and V rows, read and written
+    gbs = tree_bytes / (ms_tree / 1e3) / 1e9
+    kv_gbs = kv_bytes / (ms_kv / 1e3) / 1e9
+    ms = ms_tree + ms_kv
+    log(f"verify {ms_tree * 1e3:.1f} us ({gbs:.0f} GB/s), commit {ms_kv * 1e3:.1f} us "
+        f"({moved} rows moved, {kv_bytes / 1e6:.1f} MB read + written, {kv_gbs:.0f} GB/s), "
+        f"path lengths {np.bincount(plen, minlength=md + 1).tolist()}")
+    res = {
+        "metric": "tree verify rows/sec at B=128 V=151936, 5 rows per sequence, with the KV "
+                  "commit of the accepted paths; achieved HBM GB/s vs peak",
+        "value": rows / (ms / 1e3), "unit": "verify rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": "greedy tree verify, B=128, V=151936, tree [6], [2, 2], [1, 1] "
+                               "(12 nodes, 5 rows), then KV commit of the accepted paths, 32 "
+                               "layers x K,V x 8 heads x 128 bf16, 1024 slots",
+                   "rows": rows, "rows_moved": moved},
+        "roofline": {"bound": "hbm", "kernel": "tree_argmax_kernel + tree_walk_kernel",
+                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_launch": tree_bytes, "avg_launch_us": ms_tree * 1e3,
+                     "kernel_source_hash": kernel_source_hash()},
+        "kv_commit": {"kernel": "kv_copy_kernel + kv_pointer_kernel", "us": ms_kv * 1e3,
+                      "bytes": kv_bytes, "achieved": kv_gbs, "frac": kv_gbs / PEAK_HBM_GBS},
+    }
+    print(json.dumps(res), flush=True)
+    del caches
+    torch.cuda.empty_cache()
+
+
 def ngram_bench(args):
     """The n-gram prompt lookup (see the module docstring)."""
     import numpy as np
@@ -396,7 +509,7 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=["chain", "tree_draft", "paged_kv", "ngram"], default="chain")
+    ap.add_argument("--workload", choices=["chain", "tree", "tree_draft", "paged_kv", "ngram"], default="chain")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
@@ -414,6 +527,9 @@ def main():
         return
     if args.workload == "ngram":
         ngram_bench(args)
+        return
+    if args.workload == "tree":
+        tree_bench(args)
         return
 
     import numpy as np

@@ -3,11 +3,16 @@
 // blocks it no longer needs; "KV Cache 优化（四）：Speculative Decoding 投机解码" §6: one
 // committed-length pointer, the same boundary in every layer).
 //
-//  1. paged_copy_kernel    -- one thread per 16-byte chunk of one head's K or V row in one
-//     layer of one sequence; for j = 1..D in increasing order it moves the chunk of logical
-//     slot base + path[j-1] to logical slot base + j, each slot found through the sequence's
-//     block table. A thread handles its own chunk in j order, which reproduces in-order
-//     copying (a tree path has path[j-1] >= j, so no source is overwritten first).
+//  1. paged_copy_kernel    -- S 256-thread workgroups per sequence (workgroup b * S + s), each
+//     over a share of the sequence's 16-byte chunks (8 elements of one head's K or V row in
+//     one layer). A workgroup reads the sequence's length, path length and path once; thread
+//     j-1 checks step j and translates its source and destination slots through the block
+//     table into physical offsets in LDS. For its chunk a thread then moves slot base +
+//     path[j-1] to slot base + j for j = 1..D in increasing order -- in-order copying for
+//     any path -- kGroup steps at a time: when no source of a group is the destination of an
+//     earlier step of the group (always so for a tree path, path[j-1] >= j), the group's
+//     loads, for kBatch chunks at once, are issued before its stores; otherwise one
+//     load-store pair at a time.
 //  2. paged_release_kernel -- one 1024-thread workgroup over tiles of whole table rows: one
 //     thread per sequence checks it (the same predicate), writes its new committed length and
 //     notes its first block past that length; then the tile's table entries, taken in
@@ -23,6 +28,12 @@ namespace {
 
 constexpr int kMaxLayers = 128;
 constexpr int kThreads = 256;
+constexpr int kMaxDepth = 64;
+constexpr int kGroup = 4;  // path steps whose loads are in flight together
+constexpr int kBatch = 4;  // chunks per thread whose loads are in flight together
+constexpr int kChunksPerWg = kThreads * kBatch;
+// 16-byte chunk as a native vector: an array of them stays in registers
+typedef uint32_t chunk16 __attribute__((ext_vector_type(4)));
 constexpr int kRelThreads = 1024;
 constexpr int kRelWaves = kRelThreads / kWave;
 constexpr int kRun = 8;           // table entries per thread per chunk
@@ -41,6 +52,7 @@ struct PagedParams {
   int32_t* flags;
   int64_t block_stride, slot_stride, head_stride;
   int32_t B, NL, H, chunks, bs, max_blocks, num_blocks, free_cap, lead, max_depth;
+  int32_t split;  // copy workgroups per sequence
 };
 
 // A slot's physical block, or -1 when the slot lies outside the table or its block is not a
@@ -73,33 +85,108 @@ __device__ __forceinline__ bool seq_valid(const PagedParams& P, int b, int& L, i
   return true;
 }
 
-__global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P, int64_t total) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (t >= total) return;
-  int64_t r = t;
-  const int ch = (int)(r % P.chunks);
-  r /= P.chunks;
-  const int h = (int)(r % P.H);
-  r /= P.H;
-  const int kv = (int)(r % 2);
-  r /= 2;
-  const int l = (int)(r % P.NL);
-  const int b = (int)(r / P.NL);
-  int L, D;
-  if (!seq_valid(P, b, L, D) || D == 0) return;
-  const int base = L + P.lead - 1;
-  const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
-  const int32_t* path = P.path + (size_t)b * P.max_depth;
-  uint16_t* head = (kv ? P.v[l] : P.k[l]) + (int64_t)h * P.head_stride + ch * 8;
-  auto at = [&](int slot) {
-    return head + (int64_t)block_of(P, bt, slot) * P.block_stride +
-           (int64_t)(slot % P.bs) * P.slot_stride;
-  };
-  for (int j = 1; j <= D; ++j) {
-    const int src = base + path[j - 1], dst = base + j;
-    if (src == dst) continue;
-    const uint4 val = *reinterpret_cast<const uint4*>(at(src));
-    *reinterpret_cast<uint4*>(at(dst)) = val;
+__global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
+  __shared__ int64_t s_so[kMaxDepth], s_do[kMaxDepth];  // physical element offsets per step
+  __shared__ int32_t s_path[kMaxDepth];
+  __shared__ uint8_t s_mv[kMaxDepth];
+  __shared__ int s_L, s_D, s_bad;
+  const int b = blockIdx.x / P.split, part = blockIdx.x % P.split, tid = threadIdx.x;
+  const int nch = P.NL * 2 * P.H * P.chunks;
+  const int c0 = part * kChunksPerWg + tid;
+  // chunk addresses within a slot, computed before the barrier so that the layer pointers
+  // load while the sequence is read: a slot past the sequence's chunks repeats chunk c0 and
+  // stores nothing, and a thread past them all (c0 >= nch) never uses its addresses
+  uint16_t* head[kBatch];
+  bool has[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    int c = c0 + u * kThreads;
+    has[u] = c < nch;
+    if (!has[u]) c = min(c0, nch - 1);
+    const int ch = c % P.chunks;
+    c /= P.chunks;
+    const int h = c % P.H;
+    c /= P.H;
+    uint16_t* cache = (c & 1) ? P.v[c >> 1] : P.k[c >> 1];
+    head[u] = cache + (int64_t)h * P.head_stride + ch * 8;
+  }
+  if (tid == 0) {
+    s_L = P.committed[b];
+    s_D = P.plen[b];
+    s_bad = 0;
+  }
+  __syncthreads();
+  const int L = s_L, D = s_D;
+  // the checks of seq_valid, step j by thread j - 1
+  const int64_t base = (int64_t)L + P.lead - 1;
+  const int64_t slots = (int64_t)P.max_blocks * P.bs;
+  const bool head_ok = D >= 0 && D <= P.max_depth && base >= -1 &&
+                       ((int64_t)L + P.lead + D + P.bs - 1) / P.bs <= P.max_blocks;
+  if (head_ok && tid < D) {
+    const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
+    const int node = P.path[(size_t)b * P.max_depth + tid];
+    const int64_t src = base + node, dst = base + tid + 1;
+    bool ok = node >= 1;
+    bool mv = false;
+    if (ok && src != dst) {
+      const int pbs = src < slots ? bt[src / P.bs] : -1;
+      const int pbd = dst < slots ? bt[dst / P.bs] : -1;
+      ok = pbs >= 0 && pbs < P.num_blocks && pbd >= 0 && pbd < P.num_blocks;
+      mv = ok;
+      s_so[tid] = (int64_t)pbs * P.block_stride + (src % P.bs) * P.slot_stride;
+      s_do[tid] = (int64_t)pbd * P.block_stride + (dst % P.bs) * P.slot_stride;
+    }
+    s_path[tid] = node;
+    s_mv[tid] = mv;
+    if (!ok) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (!head_ok || s_bad || D == 0 || c0 >= nch) return;
+  for (int j0 = 1; j0 <= D; j0 += kGroup) {
+    const int n = min(kGroup, D - j0 + 1);
+    int64_t so[kGroup], dof[kGroup];
+    bool mv[kGroup];
+    int first = -1;  // the group's first step that moves a slot
+    bool together = true;  // no source of the group is an earlier step's destination
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      mv[g] = g < n && s_mv[j0 + g - 1];
+      if (mv[g] && first < 0) first = g;
+      so[g] = g < n ? s_so[j0 + g - 1] : 0;
+      dof[g] = g < n ? s_do[j0 + g - 1] : 0;
+#pragma unroll
+      for (int e = 0; e < g; ++e) together &= g >= n || s_path[j0 + g - 1] != j0 + e;
+    }
+    if (first < 0) continue;  // nothing moves in this group
+    if (together) {
+      // every load is issued (a step that moves nothing re-reads the first moving step's
+      // source), then the stores of the moving steps
+      int64_t ld[kGroup];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) ld[g] = mv[g] ? so[g] : so[first];
+      chunk16 val[kBatch][kGroup];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g)
+          val[u][g] = *reinterpret_cast<const chunk16*>(head[u] + ld[g]);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g)
+          if (has[u] && mv[g]) *reinterpret_cast<chunk16*>(head[u] + dof[g]) = val[u][g];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (!has[u]) continue;
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {  // mv[g] is false past the group's n steps
+          if (!mv[g]) continue;
+          const chunk16 val = *reinterpret_cast<const chunk16*>(head[u] + so[g]);
+          *reinterpret_cast<chunk16*>(head[u] + dof[g]) = val;
+        }
+      }
+    }
   }
 }
 
@@ -197,11 +284,11 @@ hipError_t launch_kv_paged(const spec_paged_kv_args& a, hipStream_t st) {
   P.free_cap = a.free_capacity;
   P.lead = a.lead_slots;
   P.max_depth = a.max_depth;
-  const int64_t total = (int64_t)a.batch * a.num_layers * 2 * a.num_kv_heads * P.chunks;
-  if (total > 0) {
-    const int64_t blocks = (total + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(paged_copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, P,
-                       total);
+  if (a.batch > 0) {
+    const int nch = a.num_layers * 2 * a.num_kv_heads * P.chunks;  // bounded by the host check
+    P.split = (nch + kChunksPerWg - 1) / kChunksPerWg;
+    hipLaunchKernelGGL(paged_copy_kernel, dim3((unsigned)((int64_t)a.batch * P.split)),
+                       dim3(kThreads), 0, st, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

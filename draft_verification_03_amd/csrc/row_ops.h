@@ -35,107 +35,6 @@ __device__ __forceinline__ void load_full(const uint4* __restrict__ row, int v0,
   for (int u = 0; u < kU; ++u) d[u] = base[u * kWave + lane];
 }
 
-// Streams vectors [0, nvec) of a row through consume(d, v0, maybe_last), one trip of kU
-// vectors per lane at a time, with DEPTH trips of loads in flight. The steady-state loop
-// loads full trips only, unpredicated, so that the compiler can keep the younger trips'
-// loads outstanding while it consumes the oldest; the last few full trips and the partial
-// trip follow it. maybe_last is true only where the trip may hold vector nvec - 1.
-template <int DEPTH, typename F>
-__device__ __forceinline__ void stream_row(const uint4* __restrict__ row, int nvec, int lane,
-                                           F&& consume) {
-  constexpr int kStep = kU * kWave;
-  const int nfull = nvec / kStep;
-  int t = 0;
-  if (nfull >= DEPTH) {
-    uint4 buf[DEPTH][kU];
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load_full(row, s * kStep, lane, buf[s]);
-    // Issue priority falls with progress (quarters of the row): of the waves sharing a SIMD,
-    // the one furthest behind is served first, which narrows the spread of finish times.
-    __builtin_amdgcn_s_setprio(3);
-    for (; t + 2 * DEPTH <= nfull; t += DEPTH) {  // trips t .. t+DEPTH-1; none is the last
-      const int lvl = (4 * t) / nfull;
-      if (lvl == 1) __builtin_amdgcn_s_setprio(2);
-      else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
-      else if (lvl == 3) __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        consume(buf[s], (t + s) * kStep, false);
-        load_full(row, (t + s + DEPTH) * kStep, lane, buf[s]);
-      }
-    }
-    // DEPTH .. 2*DEPTH-1 full trips remain; the first DEPTH of them are loaded
-#pragma unroll
-    for (int s = 0; s < 2 * DEPTH - 1; ++s) {
-      if (t + s < nfull) {
-        consume(buf[s % DEPTH], (t + s) * kStep, true);
-        if (t + s + DEPTH < nfull) load_full(row, (t + s + DEPTH) * kStep, lane, buf[s % DEPTH]);
-      }
-    }
-    t = nfull;
-    __builtin_amdgcn_s_setprio(0);
-  }
-  for (; t * kStep < nvec; ++t) {  // short rows, and the partial trip
-    uint4 d[kU];
-    load_trip(row, t * kStep, nvec, lane, d);
-    consume(d, t * kStep, true);
-  }
-}
-
-// Streams the trips first, first + step, first + 2*step, ... of a row (a trip is kU vectors
-// per lane at kU * kWave vectors apart from the next trip) through consume(d, v0,
-// maybe_last), with DEPTH of this wave's trips of loads in flight: the waves of a workgroup
-// pass first = 0 .. step-1 and together cover the row once, each wave's stream a regular
-// stride of full trips (unpredicated loads) plus, for one of them, the row's partial trip.
-// Issue priority falls with the wave's progress, as in stream_row.
-template <int DEPTH, typename F>
-__device__ __forceinline__ void stream_row_strided(const uint4* __restrict__ row, int nvec,
-                                                   int lane, int first, int step, F&& consume) {
-  constexpr int kStep = kU * kWave;
-  const int nfull = nvec / kStep;
-  const int nf = first < nfull ? (nfull - 1 - first) / step + 1 : 0;  // this wave's full trips
-  auto v0_of = [&](int i) { return (first + i * step) * kStep; };
-  int i = 0;
-  if (nf >= DEPTH) {
-    uint4 buf[DEPTH][kU];
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load_full(row, v0_of(s), lane, buf[s]);
-    const int q1 = nf / 4, q2 = nf / 2, q3 = (3 * nf) / 4;
-    __builtin_amdgcn_s_setprio(3);
-    for (; i + 2 * DEPTH <= nf; i += DEPTH) {  // trips i .. i+DEPTH-1; none is the row's last
-      if (i >= q3) __builtin_amdgcn_s_setprio(0);
-      else if (i >= q2) __builtin_amdgcn_s_setprio(1);
-      else if (i >= q1) __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int s = 0; s < DEPTH; ++s) {
-        consume(buf[s], v0_of(i + s), false);
-        load_full(row, v0_of(i + s + DEPTH), lane, buf[s]);
-        __builtin_amdgcn_sched_barrier(0);  // the reload issues before the next trip's waits
-      }
-    }
-    // DEPTH .. 2*DEPTH-1 full trips remain; the first DEPTH of them are loaded
-#pragma unroll
-    for (int s = 0; s < 2 * DEPTH - 1; ++s) {
-      if (i + s < nf) {
-        consume(buf[s % DEPTH], v0_of(i + s), true);
-        if (i + s + DEPTH < nf) load_full(row, v0_of(i + s + DEPTH), lane, buf[s % DEPTH]);
-      }
-    }
-    i = nf;
-    __builtin_amdgcn_s_setprio(0);
-  }
-  for (; i < nf; ++i) {  // fewer than DEPTH full trips
-    uint4 d[kU];
-    load_full(row, v0_of(i), lane, d);
-    consume(d, v0_of(i), true);
-  }
-  if (nfull * kStep < nvec && nfull >= first && (nfull - first) % step == 0) {  // partial trip
-    uint4 d[kU];
-    load_trip(row, nfull * kStep, nvec, lane, d);
-    consume(d, nfull * kStep, true);
-  }
-}
-
 // Spare load target: a claim past a row's full trips loads these 4 KB instead (data never
 // used), so that the row streams' loads are all issued unconditionally.
 static __device__ uint4 g_spare_trip[kU * kWave];
@@ -144,7 +43,8 @@ static __device__ uint4 g_spare_trip[kU * kWave];
 // workgroup's waves (one LDS atomic per trip, issued before the consume so that its latency
 // hides behind it), DEPTH trips of loads in flight: a wave that runs faster takes more trips,
 // so the waves of a row finish together. The wave that claims index nfull also streams the
-// row's partial trip, if there is one. consume(d, v0, maybe_last) as in stream_row.
+// row's partial trip, if there is one. consume(d, v0, maybe_last) takes a trip of
+// kU vectors per lane starting at vector v0; maybe_last is true where it may hold vector nvec - 1.
 template <int DEPTH, typename F>
 __device__ __forceinline__ void stream_row_claimed(const uint4* __restrict__ row, int nvec,
                                                    int lane, int* ctr, F&& consume) {
@@ -244,17 +144,6 @@ __device__ __forceinline__ void argmax_trip(uint4 d[kU], int v0, int nvec, int V
     bv = tm;
     bi = found;
   }
-}
-
-__device__ __forceinline__ int row_argmax(const uint4* __restrict__ row, int nvec, int V,
-                                          int lane) {
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  stream_row<2>(row, nvec, lane, [&](uint4* d, int v0, bool) {
-    argmax_trip(d, v0, nvec, V, lane, bv, bi);
-  });
-  wave_argmax(bv, bi);
-  return bi == 0x7FFFFFFF ? 0 : bi;
 }
 
 }  // namespace specv

@@ -222,6 +222,14 @@ int kv_commit_path(const spec_kv_args* a, void* hip_stream) {
     return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
   if (a->max_depth < 1 || a->max_depth > 64)
     return fail(SPEC_ERR_INVALID_ARG, "max_depth must be in [1, 64] (got %d)", a->max_depth);
+  {
+    // 16-byte chunks of one slot over every layer, K and V, and head; the copy grid
+    const int64_t chunks = (int64_t)a->num_layers * 2 * a->num_kv_heads * (a->head_dim / 8);
+    if (chunks > (1 << 30) || (int64_t)a->batch * ((chunks + 1023) / 1024) > 0x7FFFFFFF)
+      return fail(SPEC_ERR_INVALID_ARG,
+                  "num_layers * 2 * num_kv_heads * head_dim / 8 (or that times batch / 1024) "
+                  "exceeds the grid limit");
+  }
   if (a->batch == 0) return SPEC_OK;
   if (!a->k_cache || !a->v_cache || !a->path_nodes || !a->path_len || !a->committed_len)
     return fail(SPEC_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -315,6 +323,14 @@ int kv_commit_paged(const spec_paged_kv_args* a, void* hip_stream) {
     return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
   if (a->max_depth < 1 || a->max_depth > 64)
     return fail(SPEC_ERR_INVALID_ARG, "max_depth must be in [1, 64] (got %d)", a->max_depth);
+  {
+    // 16-byte chunks of one slot over every layer, K and V, and head; the copy grid
+    const int64_t chunks = (int64_t)a->num_layers * 2 * a->num_kv_heads * (a->head_dim / 8);
+    if (chunks > (1 << 30) || (int64_t)a->batch * ((chunks + 1023) / 1024) > 0x7FFFFFFF)
+      return fail(SPEC_ERR_INVALID_ARG,
+                  "num_layers * 2 * num_kv_heads * head_dim / 8 (or that times batch / 1024) "
+                  "exceeds the grid limit");
+  }
   if (a->batch == 0) return SPEC_OK;
   if (!a->k_cache || !a->v_cache || !a->block_table || !a->path_nodes || !a->path_len ||
       !a->committed_len || !a->free_list || !a->free_count)

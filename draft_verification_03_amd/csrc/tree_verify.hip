@@ -2,8 +2,10 @@
 // ("投机推理：小模型搭树，大模型一次验证", validation and path-walk sections; the tree rows
 // come from one target forward with a tree attention mask, "10.6 投机解码" §10.6.3).
 //
-//  1. tree_argmax_kernel -- one wave per provided target row: argmax (lowest id on ties)
-//     streamed from HBM with 16-byte loads, into the workspace.
+//  1. tree_argmax_kernel -- one 8-wave workgroup per provided target row: the waves claim the
+//     row's 4 KB trips from an LDS counter (two in flight per wave) and keep per-lane maxima
+//     with the earliest index; wave, then workgroup reductions give the argmax (lowest id on
+//     ties), written to the workspace.
 //  2. tree_walk_kernel   -- one wave per sequence: checks the topology, then walks from the
 //     root along the child whose token equals the target argmax of the current node (the
 //     lowest node index among matching siblings), never combining matches of different
@@ -18,6 +20,7 @@ namespace {
 
 constexpr int kMaxNodes = 256;
 constexpr int kMaxRows = 256;
+constexpr int kArgWaves = 8;
 
 struct TreeParams {
   const uint16_t* logits;
@@ -33,11 +36,36 @@ struct TreeParams {
   int32_t B, V, stride, nvec, N, R, max_depth, tree_stride;
 };
 
-__global__ __launch_bounds__(kWave) void tree_argmax_kernel(TreeParams P) {
+__global__ __launch_bounds__(kArgWaves * kWave) void tree_argmax_kernel(TreeParams P) {
+  __shared__ int s_trip;
+  __shared__ float s_bv[kArgWaves];
+  __shared__ int s_bi[kArgWaves];
   const int row = blockIdx.x;  // b * R + r
+  const int lane = lane_id(), wid = threadIdx.x / kWave;
+  if (threadIdx.x == 0) s_trip = 0;
+  __syncthreads();
   const uint4* rp = reinterpret_cast<const uint4*>(P.logits + (size_t)row * P.stride);
-  const int am = row_argmax(rp, P.nvec, P.V, lane_id());
-  if (lane_id() == 0) P.argmax[row] = am;
+  // a wave's claims increase, so each lane meets its trips in token order and keeps the
+  // earliest index of its maximum
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  stream_row_claimed<2>(rp, P.nvec, lane, &s_trip, [&](uint4* d, int v0, bool) {
+    argmax_trip(d, v0, P.nvec, P.V, lane, bv, bi);
+  });
+  wave_argmax(bv, bi);
+  if (lane == 0) {
+    s_bv[wid] = bv;
+    s_bi[wid] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kArgWaves; ++w)
+      if (s_bv[w] > bv || (s_bv[w] == bv && s_bi[w] < bi)) {
+        bv = s_bv[w];
+        bi = s_bi[w];
+      }
+    P.argmax[row] = bi == 0x7FFFFFFF ? 0 : bi;
+  }
 }
 
 __global__ __launch_bounds__(kWave) void tree_walk_kernel(TreeParams P) {
@@ -137,7 +165,7 @@ hipError_t launch_tree(const spec_tree_args& a, void* ws, hipStream_t st) {
   P.max_depth = a.max_depth;
   P.tree_stride = a.tree_stride;
   hipLaunchKernelGGL(tree_argmax_kernel, dim3((unsigned)(a.batch * a.rows_per_seq)),
-                     dim3(kWave), 0, st, P);
+                     dim3(kArgWaves * kWave), 0, st, P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tree_walk_kernel, dim3((unsigned)a.batch), dim3(kWave), 0, st, P);

@@ -199,6 +199,8 @@ typedef struct spec_tree_args {
  *
  * Element (b, slot, head, e) of layer l's K cache is k_cache[l][b*seq_stride +
  * slot*slot_stride + head*head_stride + e], e < head_dim, bf16 (copied bit for bit).
+ * num_layers * 2 * num_kv_heads * head_dim / 8 must not exceed 2^30, nor that count / 1024
+ * times batch 2^31 - 1 (SPEC_ERR_INVALID_ARG).
  */
 typedef struct spec_kv_args {
   int32_t batch;          /* B >= 0                                                       */
@@ -301,6 +303,8 @@ typedef struct spec_tree_draft_args {
  * block id appears at most once in the tables and the free list together (no shared
  * blocks). free_list has free_capacity entries (>= num_blocks); ids that would land at or
  * past it are not written (that happens only if the pool breaks the rule above).
+ * num_layers * 2 * num_kv_heads * head_dim / 8 must not exceed 2^30, nor that count / 1024
+ * times batch 2^31 - 1 (SPEC_ERR_INVALID_ARG).
  */
 typedef struct spec_paged_kv_args {
   int32_t batch;          /* B >= 0                                                        */

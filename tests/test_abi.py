@@ -245,6 +245,8 @@ def _kv(**kw):
     dict(batch=-1), dict(num_layers=0), dict(num_layers=129), dict(num_kv_heads=0),
     dict(head_dim=12), dict(slot_stride=1020), dict(slot_capacity=0), dict(lead_slots=3),
     dict(max_depth=0), dict(path_nodes=None), dict(k_cache=None),
+    dict(num_kv_heads=1 << 25),  # 2^31 chunks per slot: past the copy grid's limit
+    dict(batch=1 << 30, num_kv_heads=64),  # 2^14 chunks, 16 workgroups x 2^30 sequences
 ])
 def test_kv_validation(kw):
     a = _kv(**kw)
@@ -292,6 +294,7 @@ def _paged(**kw):
     dict(free_capacity=255), dict(slot_stride=1020), dict(lead_slots=2), dict(max_depth=0),
     dict(max_depth=65), dict(block_table=None), dict(free_list=None), dict(free_count=None),
     dict(k_cache=None), dict(max_blocks=1 << 20, block_size=1 << 12),
+    dict(num_kv_heads=1 << 25),  # 2^31 chunks per slot: past the copy grid's limit
 ])
 def test_kv_paged_validation(kw):
     a = _paged(**kw)

@@ -59,6 +59,28 @@ def test_paged_small_vs_oracle(seed, lead, tree):
     check(x, f"small seed={seed} lead={lead} tree={tree}")
 
 
+def test_paged_overlapping_paths():
+    """Paths that are not tree paths (a step's source is an earlier step's destination: [2, 1],
+    [3, 1, 2], ...), inside one group of in-flight steps and across groups (depth 9): the
+    commit must equal in-order copying through the block tables, byte for byte."""
+    rng = np.random.default_rng(25)
+    depth = 9
+    x = _paged_case(rng, B=16, max_blocks=12, nb=240, H=2, D=16, nl=2, depth=depth, lead=1,
+                    tree=False)
+    fixed = [[2, 1], [3, 1, 2], [2, 1, 4, 3, 6, 5, 8, 7, 9], [1, 1, 1, 1, 1, 1],
+             [5, 4, 3, 2, 1], [9, 8, 7, 6, 5, 4, 3, 2, 1], [2, 3, 4, 5, 6, 7, 8, 9, 1]]
+    paths = np.full((16, depth), -1, np.int32)
+    plen = np.zeros(16, np.int32)
+    for b in range(16):  # every node <= depth: its slot lies in the blocks the case mapped
+        c = fixed[b] if b < len(fixed) else \
+            list(rng.integers(1, depth + 1, size=int(rng.integers(1, depth + 1))))
+        paths[b, :len(c)] = c
+        plen[b] = len(c)
+    x.update(paths=paths, plen=plen)
+    g = check(x, "overlapping paths")
+    assert not g["flags"].any()
+
+
 def test_paged_rejected_inputs():
     """Unmapped source block, a length past the table and a path node 0 are flagged and left
     untouched; the valid sequence commits and releases."""

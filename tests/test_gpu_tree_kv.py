@@ -173,6 +173,35 @@ def test_kv_commit_small_vs_oracle(lead):
         assert np.array_equal(kg[l], ko[l]) and np.array_equal(vg[l], vo[l])
 
 
+def test_kv_commit_overlapping_paths_vs_oracle():
+    """Paths that are not tree paths: a step's source can be an earlier step's destination
+    ([2, 1], [3, 1, 2], ...), inside one group of in-flight steps and across groups (depth 9).
+    The commit must equal in-order copying, byte for byte."""
+    rng = np.random.default_rng(47)
+    Bn, S, H, Dh, nl, depth = 24, 40, 2, 16, 2, 9
+    k = [rng.integers(0, 65536, size=(Bn, S, H, Dh)).astype(np.uint16) for _ in range(nl)]
+    v = [rng.integers(0, 65536, size=(Bn, S, H, Dh)).astype(np.uint16) for _ in range(nl)]
+    paths = np.full((Bn, depth), -1, np.int32)
+    plen = np.zeros(Bn, np.int32)
+    fixed = [[2, 1], [3, 1, 2], [2, 1, 4, 3, 6, 5, 8, 7, 9], [1, 1, 1, 1, 1, 1],
+             [5, 4, 3, 2, 1], [1, 2, 3, 4, 5, 6, 7, 8, 9], [9, 8, 7, 6, 5, 4, 3, 2, 1],
+             [2, 3, 4, 5, 6, 7, 8, 9, 1]]
+    for b in range(Bn):
+        c = fixed[b] if b < len(fixed) else \
+            list(rng.integers(1, depth + 3, size=int(rng.integers(1, depth + 1))))
+        paths[b, :len(c)] = c
+        plen[b] = len(c)
+    L = rng.integers(0, S - depth - 4, size=Bn).astype(np.int32)
+    say("[kv] overlapping paths")
+    ko, vo = [a.copy() for a in k], [a.copy() for a in v]
+    cl_o, fl_o = oracle.kv_commit(ko, vo, paths, plen, L, 1, depth)
+    kg, vg, cl_g, fl_g = _run_gpu_kv(k, v, paths, plen, L, 1, depth)
+    assert np.array_equal(cl_g, cl_o) and np.array_equal(fl_g, fl_o)
+    assert not fl_o.any()
+    for l in range(nl):
+        assert np.array_equal(kg[l], ko[l]) and np.array_equal(vg[l], vo[l])
+
+
 def test_kv_commit_c4_full_size():
     """32 layers x K,V x [128 seq][1024 slots][8 heads][128] bf16 (17.2 GB), every element a
     hash of its coordinates. After committing the oracle's tree paths: each committed slot
