@@ -49,8 +49,14 @@ constexpr int kDepth = 2;          // trips of loads in flight per wave in the r
 constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per workgroup)
 constexpr int kRowThreads = kRowWgWaves * kWave;
 constexpr int kHist = 512;         // key offsets below the row max resolved by the window search
-constexpr int kResolveThreads = 1024;
-constexpr int kTilesPerIter = 4;  // row-pair tiles in flight per wave in the resolve pass
+// Resolve workgroup shapes (threads, row-pair tiles in flight per wave in the resolve pass):
+// one 1024-thread workgroup per CU while the batch fits the CUs, two 512-thread workgroups
+// per CU beyond (both within 128 VGPRs), so that one sequence's latency-bound decision and
+// scan overlap another's row traffic.
+constexpr int kResolveWide = 1024, kTilesWide = 4;
+constexpr int kResolveNarrow = 512, kTilesNarrow = 5;
+constexpr int kResolveMaxWaves = kResolveWide / kWave;
+constexpr int kNumCus = 256;  // compute units of the chip: one wide workgroup each
 constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass (V <= 2^19)
 constexpr int kPreRows = 8;      // draft positions whose list heads the resolve prefetches
 constexpr int kPre = 64;         // list entries prefetched per row
@@ -970,11 +976,12 @@ __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, 
 // Phase 2 of a row draw, once tile_sum holds every tile's sum and each lane knows the last
 // positive-weight token it saw: wave 0 scans the tile sums, then re-reads the chosen tile
 // and scans it.
+template <int NT>
 __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool residual,
                                           int nvec, int V, float u, int last, float* tile_sum,
                                           int* sh_i, float* sh_f) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int nw = kResolveThreads / kWave;
+  const int nw = NT / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
   last = wave_max_i(last);
   if (lane == 0) sh_i[wid] = last;
@@ -1098,25 +1105,26 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
 
 // All threads of the workgroup: inverse-CDF draw over a whole row (pair) in token order.
 // Pass 1 stores per-tile sums (a tile = 64 vectors = 512 logits, one coalesced wave load;
-// each wave keeps kTilesPerIter tiles of p and of q in flight); draw_scan finishes.
+// each wave keeps TI tiles of p and of q in flight); draw_scan finishes.
+template <int NT, int TI>
 __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq, bool residual,
                                                int nvec, int V, float u, float* tile_sum,
                                                int* sh_i, float* sh_f) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int nw = kResolveThreads / kWave;
+  const int nw = NT / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
   int last = -1;  // last token with positive weight seen by this lane
   const uint4 z{0u, 0u, 0u, 0u};
-  for (int g0 = wid * kTilesPerIter; g0 < ntiles; g0 += nw * kTilesPerIter) {
-    uint4 dp[kTilesPerIter], dq[kTilesPerIter];
+  for (int g0 = wid * TI; g0 < ntiles; g0 += nw * TI) {
+    uint4 dp[TI], dq[TI];
 #pragma unroll
-    for (int t = 0; t < kTilesPerIter; ++t) {
+    for (int t = 0; t < TI; ++t) {
       const int v = (g0 + t) * kWave + lane;
       dp[t] = v < nvec ? Lp.row[v] : z;
       dq[t] = (residual && Lq.point < 0 && v < nvec) ? Lq.row[v] : z;
     }
 #pragma unroll
-    for (int t = 0; t < kTilesPerIter; ++t) {
+    for (int t = 0; t < TI; ++t) {
       const int v = (g0 + t) * kWave + lane;
       float w[8];
       data_weights(Lp, Lq, residual, v, nvec, V, dp[t], dq[t], w);
@@ -1130,10 +1138,9 @@ __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq,
       if (lane == 0 && g0 + t < ntiles) tile_sum[g0 + t] = ts;
     }
   }
-  return draw_scan(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
+  return draw_scan<NT>(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
 }
 
-constexpr int kWgWaves = kResolveThreads / kWave;
 
 // Per-sequence decision state the resolve step shares through LDS.
 struct SeqDecision {
@@ -1168,9 +1175,11 @@ __device__ __forceinline__ size_t bonus_slot(const ChainParams& P, int b) {
   return 2 * (size_t)P.n_draft + (size_t)b;
 }
 
-__global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainParams P) {
+template <int NT, int TI>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
+void chain_resolve_kernel(ChainParams P) {
   __shared__ float tile_sum[kMaxTiles];  // inverse-CDF draw over a row (pair)
-  __shared__ int sh_i[kWgWaves];
+  __shared__ int sh_i[kResolveMaxWaves];
   __shared__ float sh_f[2];
   __shared__ NucEntry s_lp[kNucMax], s_lq[kNucMax];
   __shared__ NucEntry s_pre[kPreRows][2][kPre];
@@ -1187,9 +1196,10 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
   // The heads of the candidate rows' nucleus lists, fetched together with the statistics:
   // where the first rejection falls is not known yet, and the draw usually needs no more.
   if (cu_ok && stochastic && (P.topp || P.topk)) {
-    const int kk = tid / (2 * kPre), rr = (tid / kPre) & 1, j = tid % kPre;
-    if (kk < kPreRows && kk < s.g)
-      s_pre[kk][rr][j] = P.nuc[((size_t)(s.d0 + kk) * 2 + rr) * kNucMax + j];
+    for (int i = tid; i < kPreRows * 2 * kPre; i += NT) {
+      const int kk = i / (2 * kPre), rr = (i / kPre) & 1, j = i % kPre;
+      if (kk < s.g) s_pre[kk][rr][j] = P.nuc[((size_t)(s.d0 + kk) * 2 + rr) * kNucMax + j];
+    }
     if (tid < kPre) s_preb[tid] = P.nuc[bonus_slot(P, b) * kNucMax + tid];
   }
   RowStat sbon{};
@@ -1312,14 +1322,14 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
         const NucEntry* lb = s_preb;
         if (sbon.nuc > kPre) {
           const NucEntry* gl = P.nuc + bonus_slot(P, b) * kNucMax;
-          for (int j = tid; j < sbon.nuc; j += kResolveThreads) s_lp[j] = gl[j];
+          for (int j = tid; j < sbon.nuc; j += NT) s_lp[j] = gl[j];
           __syncthreads();
           lb = s_lp;
         }
         d = wg_list_draw(lb, sbon.nuc, sbon.z, nullptr, 0, 1.0f, false, u, sh_i, sh_f);
       } else {
         const RowLaw Lp{prow, c, -sbon.m * c, sbon.t, 1.0f / sbon.z};
-        d = draw_from_rows(Lp, Lp, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
+        d = draw_from_rows<NT, TI>(Lp, Lp, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
       }
       y = d.token;
       py = d.wtok;
@@ -1349,14 +1359,14 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
         lq = s_pre[kstar - 1][1];
       } else {
         const NucEntry* gl = P.nuc + (size_t)(s.d0 + kstar - 1) * 2 * kNucMax;
-        for (int j = tid; j < sp.nuc; j += kResolveThreads) s_lp[j] = gl[j];
+        for (int j = tid; j < sp.nuc; j += NT) s_lp[j] = gl[j];
         if (lists_pq)
-          for (int j = tid; j < sq.nuc; j += kResolveThreads) s_lq[j] = gl[kNucMax + j];
+          for (int j = tid; j < sq.nuc; j += NT) s_lq[j] = gl[kNucMax + j];
         __syncthreads();
       }
     }
     if (lists_pq) d = wg_list_draw(lp, sp.nuc, sp.z, lq, sq.nuc, sq.z, true, u, sh_i, sh_f);
-    else d = draw_from_rows(Lp, Lq, true, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
+    else d = draw_from_rows<NT, TI>(Lp, Lq, true, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
     R = d.total;
     if (d.total > 0.0f) {
       y = d.token;
@@ -1364,7 +1374,7 @@ __global__ __launch_bounds__(kResolveThreads) void chain_resolve_kernel(ChainPar
     } else {  // R = 0 means p = q: the draw from p has the same law
       flags |= SPEC_FLAG_RESID_FALLBACK;
       if (lists_p) d = wg_list_draw(lp, sp.nuc, sp.z, nullptr, 0, 1.0f, false, u, sh_i, sh_f);
-      else d = draw_from_rows(Lp, Lq, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
+      else d = draw_from_rows<NT, TI>(Lp, Lq, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
       y = d.token;
       py = d.wtok;
     }
@@ -1444,8 +1454,12 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(row_stats_kernel<false>, dim3(nrows), dim3(kRowThreads), 0, st, P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(chain_resolve_kernel, dim3((unsigned)a.batch), dim3(kResolveThreads), 0,
-                     st, P);
+  if (a.batch > kNumCus)
+    hipLaunchKernelGGL((chain_resolve_kernel<kResolveNarrow, kTilesNarrow>),
+                       dim3((unsigned)a.batch), dim3(kResolveNarrow), 0, st, P);
+  else
+    hipLaunchKernelGGL((chain_resolve_kernel<kResolveWide, kTilesWide>), dim3((unsigned)a.batch),
+                       dim3(kResolveWide), 0, st, P);
   return hipGetLastError();
 }
 

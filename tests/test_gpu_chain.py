@@ -36,6 +36,16 @@ def test_c3_full():
     say(f"[chain] c3: sequences with a multi-pass top-p row: {slow}")
 
 
+@pytest.mark.parametrize("P,K", [(0.9, None), (0.8, 40), (None, None)])
+def test_batch_beyond_the_cus(P, K):
+    """B=300 > 256 compute units: the resolve runs two 512-thread workgroups per CU. Top-p
+    (list draws from the prefetched list heads), top-k, and no filter (row draws)."""
+    x = W.chain_inputs("c3", B=300, V=20000, top_p=P)
+    if K is not None:
+        x["top_k"] = np.where(np.arange(300) % 2 == 0, K, 0).astype(np.int32)
+    check_chain(x, seed=16, label=f"B=300 V=20000 top-p {P} top-k {K}")
+
+
 def test_c5_full():
     check_chain(W.chain_inputs("c5"), seed=15, label="c5 ragged B=1024 V=128256")
 
