@@ -13,9 +13,10 @@
 //     earlier step of the group (always so for a tree path, path[j-1] >= j), the group's
 //     loads, for kBatch chunks at once, are issued before its stores; otherwise one
 //     load-store pair at a time.
-//  2. paged_release_kernel -- one 1024-thread workgroup over tiles of whole table rows: one
-//     thread per sequence checks it (the same predicate), writes its new committed length and
-//     notes its first block past that length; then the tile's table entries, taken in
+//  2. paged_release_kernel -- one 1024-thread workgroup over tiles of whole table rows: the
+//     same predicate, checked by one thread per sequence (lengths) and one per path step
+//     (slots mapped), then one thread per sequence writes its new committed length and its
+//     first block past that length is noted; then the tile's table entries, taken in
 //     row-major order (8 consecutive per thread), are flagged and scanned, and a released
 //     entry's place in the free list is the number of released entries before it -- so the
 //     ids land in (sequence, logical block) order whatever the launch timing. It runs after
@@ -55,35 +56,12 @@ struct PagedParams {
   int32_t split;  // copy workgroups per sequence
 };
 
-// A slot's physical block, or -1 when the slot lies outside the table or its block is not a
-// valid block id.
-__device__ __forceinline__ int block_of(const PagedParams& P, const int32_t* bt, int slot) {
-  if (slot < 0 || slot >= P.max_blocks * P.bs) return -1;
-  const int pb = bt[slot / P.bs];
-  return (pb >= 0 && pb < P.num_blocks) ? pb : -1;
-}
-
-// Same predicate in both kernels: every slot a copy touches is mapped, every path node is a
-// node, and the new committed length fits the table.
-__device__ __forceinline__ bool seq_valid(const PagedParams& P, int b, int& L, int& D) {
-  L = P.committed[b];
-  D = P.plen[b];
-  if (D < 0 || D > P.max_depth) return false;
-  const int base = L + P.lead - 1;
-  if (base < -1) return false;
-  const int64_t new_len = (int64_t)L + P.lead + D;
-  if ((new_len + P.bs - 1) / P.bs > P.max_blocks) return false;
-  const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
-  const int32_t* path = P.path + (size_t)b * P.max_depth;
-  for (int j = 1; j <= D; ++j) {
-    const int node = path[j - 1];
-    if (node < 1) return false;
-    const int src = base + node, dst = base + j;
-    if (src == dst) continue;
-    if (block_of(P, bt, src) < 0 || block_of(P, bt, dst) < 0) return false;
-  }
-  return true;
-}
+// The commit predicate, checked in both kernels: with L = committed_len, D = path_len and
+// base = L + lead - 1, a sequence is committed when 0 <= D <= max_depth, base >= -1, the new
+// length L + lead + D fits max_blocks blocks, every path node is >= 1, and for every step
+// j = 1..D that moves a slot (base + path[j-1] != base + j) both slots lie inside the table
+// in blocks with valid ids (0 <= id < num_blocks). Otherwise it is flagged SLOT_OOB and left
+// untouched.
 
 __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
   __shared__ int64_t s_so[kMaxDepth], s_do[kMaxDepth];  // physical element offsets per step
@@ -117,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
   }
   __syncthreads();
   const int L = s_L, D = s_D;
-  // the checks of seq_valid, step j by thread j - 1
+  // the commit predicate, step j by thread j - 1
   const int64_t base = (int64_t)L + P.lead - 1;
   const int64_t slots = (int64_t)P.max_blocks * P.bs;
   const bool head_ok = D >= 0 && D <= P.max_depth && base >= -1 &&
@@ -200,19 +178,46 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
   int carry = 0;  // blocks released before this chunk (uniform)
   for (int b0 = 0; b0 < P.B; b0 += rows) {
     const int nr = min(rows, P.B - b0);
-    // one thread per sequence: validity, new length and the first block past it
+    // the commit predicate spread over threads: one per sequence checks the lengths and
+    // notes the first block past the new length (-1: invalid), then one per (sequence, path
+    // step) checks that step and marks its sequence invalid on a failure
     for (int i = tid; i < nr; i += kRelThreads) {
       const int b = b0 + i;
-      int L, D;
-      const bool ok = seq_valid(P, b, L, D);
-      s_need[i] = ok ? (int)(((int64_t)L + P.lead + D + P.bs - 1) / P.bs) : -1;
-      if (ok) {
-        P.committed[b] = L + P.lead + D;  // every read of committed[b] is above
+      const int L = P.committed[b], D = P.plen[b];
+      const int64_t base = (int64_t)L + P.lead - 1;
+      const int64_t need = ((int64_t)L + P.lead + D + P.bs - 1) / P.bs;
+      const bool ok = D >= 0 && D <= P.max_depth && base >= -1 && need <= P.max_blocks;
+      s_need[i] = ok ? (int)need : -1;
+    }
+    __syncthreads();
+    for (int64_t q = tid; q < (int64_t)nr * P.max_depth; q += kRelThreads) {
+      const int i = (int)(q / P.max_depth), j = (int)(q - (int64_t)i * P.max_depth);
+      const int b = b0 + i;
+      const int L = P.committed[b], D = P.plen[b];
+      if (D < 0 || D > P.max_depth || j >= D) continue;  // no such step
+      const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
+      const int node = P.path[(size_t)b * P.max_depth + j];
+      const int64_t base = (int64_t)L + P.lead - 1;
+      const int64_t src = base + node, dst = base + j + 1;
+      const int64_t slots = (int64_t)P.max_blocks * P.bs;
+      bool ok = node >= 1;
+      if (ok && src != dst) {
+        const int pbs = (src >= 0 && src < slots) ? bt[src / P.bs] : -1;
+        const int pbd = (dst >= 0 && dst < slots) ? bt[dst / P.bs] : -1;
+        ok = pbs >= 0 && pbs < P.num_blocks && pbd >= 0 && pbd < P.num_blocks;
+      }
+      if (!ok) atomicMin(&s_need[i], -1);
+    }
+    __syncthreads();
+    // the new lengths: every read of committed_len above came first
+    for (int i = tid; i < nr; i += kRelThreads) {
+      const int b = b0 + i;
+      if (s_need[i] >= 0) {
+        P.committed[b] = P.committed[b] + P.lead + P.plen[b];
       } else if (P.flags) {
         P.flags[b] |= SPEC_FLAG_SLOT_OOB;
       }
     }
-    __syncthreads();
     // the tile's table entries in row-major order, kRun consecutive per thread: the free
     // list position of a released entry is the count of released entries before it
     const int64_t e0 = (int64_t)b0 * mb, ne = (int64_t)nr * mb;
