@@ -64,12 +64,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# The row pass's sources: its kernel file and the library headers it includes.
+CHAIN_SOURCES = ("chain_verify.hip", "row_ops.h", "spec_device.h", "specv_internal.h")
+
+
+def kernel_source_hash(files=None) -> str:
+    """First 16 hex digits of the sha256 of the given csrc files (in this order), or of every
+    csrc source in name order."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_verification_03_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    if files is None:
+        files = [f for f in sorted(os.listdir(csrc)) if f.endswith((".hip", ".h", ".cpp"))]
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -613,7 +620,7 @@ def main():
     value = rows / (ms_step / 1e3)
     row_avg_ms = float(np.mean(row_ms))
     achieved = ab["row_pass"] / (row_avg_ms / 1e3) / 1e9
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(CHAIN_SOURCES)
     traffic = read_traffic(src_hash)
     fl = flags.cpu().numpy()
     log(f"step {ms_step * 1e3:.1f} us, row pass {row_avg_ms * 1e3:.1f} us "
