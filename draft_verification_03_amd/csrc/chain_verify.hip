@@ -463,17 +463,29 @@ __device__ int collect_wg(Src src, int n, int V, float t, float c, float nref, R
 // which the running count (by_count) or fixed-point mass of the tokens at or above it
 // reaches thr. *mass_at receives the running mass there (the row's whole mass if thr is not
 // reached; the return value is then -1). Every thread returns the same values.
+// The whole-row search does not use the captured vectors, so their LDS holds kRadixCopies
+// copies of each radix histogram, bin-major (bin * kRadixCopies + copy: the copies of a bin
+// sit in different banks). A lane adds into copy lane % kRadixCopies: on flat rows most
+// logits share a few bins, and the copies divide the conflicts of one atomic by that much.
+constexpr int kRadixCopies = 4;
+static_assert(256 * kRadixCopies * (sizeof(unsigned long long) + sizeof(uint32_t)) <=
+                  sizeof(uint4) * kCapN,
+              "radix histogram copies fit the capture buffer");
+
 __device__ int radix_cut(const uint4* __restrict__ row, int nvec, int V, float c, float nref,
                          uint32_t kM, bool by_count, uint64_t thr, uint64_t* mass_at,
                          RowLds* L, int tid) {
   const int lane = tid % kWave;
   constexpr int PER = 256 / kWave;
+  unsigned long long* hist = reinterpret_cast<unsigned long long*>(L->data);
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(hist + 256 * kRadixCopies);
+  const int copy = lane % kRadixCopies;
   int hi = -1;
   uint64_t base_c = 0, base_m = 0;
   for (int pass = 0; pass < 2; ++pass) {
-    for (int j = tid; j < 256; j += kRowThreads) {
-      L->hist[j] = 0ull;
-      L->hcnt[j] = 0u;
+    for (int j = tid; j < 256 * kRadixCopies; j += kRowThreads) {
+      hist[j] = 0ull;
+      hcnt[j] = 0u;
     }
     __syncthreads();
     for (int v = tid; v < nvec; v += kRowThreads) {
@@ -485,17 +497,23 @@ __device__ int radix_cut(const uint4* __restrict__ row, int nvec, int V, float c
         const uint32_t o = kM - key_of(x[e]);
         if (pass == 1 && (int)(o >> 8) != hi) continue;
         const uint32_t bin = pass == 0 ? (o >> 8) : (o & 255u);
-        atomicAdd(&L->hcnt[bin], 1u);
+        atomicAdd(&hcnt[bin * kRadixCopies + copy], 1u);
         const uint64_t fw = fixw(weight(x[e], c, nref));
-        if (fw) atomicAdd(&L->hist[bin], (unsigned long long)fw);
+        if (fw) atomicAdd(&hist[bin * kRadixCopies + copy], (unsigned long long)fw);
       }
     }
     __syncthreads();
     uint64_t cnt[PER], ms[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      cnt[j] = L->hcnt[lane * PER + j];
-      ms[j] = L->hist[lane * PER + j];
+      const int b = lane * PER + j;
+      cnt[j] = 0;
+      ms[j] = 0;
+#pragma unroll
+      for (int k = 0; k < kRadixCopies; ++k) {
+        cnt[j] += hcnt[b * kRadixCopies + k];
+        ms[j] += hist[b * kRadixCopies + k];
+      }
     }
     __syncthreads();  // the bins are cleared again only after every wave has read them
     uint64_t cum = 0;
