@@ -59,6 +59,14 @@ def test_paged_small_vs_oracle(seed, lead, tree):
     check(x, f"small seed={seed} lead={lead} tree={tree}")
 
 
+def test_paged_ragged_workgroup_split():
+    """3 layers x K,V x 11 heads x 128: 1056 chunks per slot, so a sequence's copy spans two
+    workgroups, the second holding 32 chunks."""
+    x = _paged_case(np.random.default_rng(26), B=6, max_blocks=8, nb=64, H=11, D=128, nl=3,
+                    depth=3, lead=1, tree=True)
+    check(x, "ragged workgroup split")
+
+
 def test_paged_overlapping_paths():
     """Paths that are not tree paths (a step's source is an earlier step's destination: [2, 1],
     [3, 1, 2], ...), inside one group of in-flight steps and across groups (depth 9): the

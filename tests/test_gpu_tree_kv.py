@@ -173,6 +173,25 @@ def test_kv_commit_small_vs_oracle(lead):
         assert np.array_equal(kg[l], ko[l]) and np.array_equal(vg[l], vo[l])
 
 
+def test_kv_commit_ragged_workgroup_split():
+    """3 layers x K,V x 11 heads x 128: 1056 chunks per slot, so a sequence's copy spans two
+    workgroups, the second holding 32 chunks; tree paths and a chain rollback."""
+    rng = np.random.default_rng(48)
+    Bn, S, H, Dh, nl, depth = 5, 24, 11, 128, 3, 3
+    k = [rng.integers(0, 65536, size=(Bn, S, H, Dh)).astype(np.uint16) for _ in range(nl)]
+    v = [rng.integers(0, 65536, size=(Bn, S, H, Dh)).astype(np.uint16) for _ in range(nl)]
+    paths = np.array([[2, 5, 9], [1, 2, 3], [3, 4, -1], [6, -1, -1], [-1, -1, -1]], np.int32)
+    plen = np.array([3, 3, 2, 1, 0], np.int32)
+    L = np.array([4, 10, 0, 7, 3], np.int32)
+    say("[kv] ragged workgroup split")
+    ko, vo = [a.copy() for a in k], [a.copy() for a in v]
+    cl_o, fl_o = oracle.kv_commit(ko, vo, paths, plen, L, 1, depth)
+    kg, vg, cl_g, fl_g = _run_gpu_kv(k, v, paths, plen, L, 1, depth)
+    assert np.array_equal(cl_g, cl_o) and np.array_equal(fl_g, fl_o) and not fl_o.any()
+    for l in range(nl):
+        assert np.array_equal(kg[l], ko[l]) and np.array_equal(vg[l], vo[l])
+
+
 def test_kv_commit_overlapping_paths_vs_oracle():
     """Paths that are not tree paths: a step's source can be an earlier step's destination
     ([2, 1], [3, 1, 2], ...), inside one group of in-flight steps and across groups (depth 9).
