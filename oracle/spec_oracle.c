@@ -63,8 +63,8 @@
  *       within a layer by the rank of the parent and then of the child. Target rows belong
  *       to the expanded nodes in expansion order (root row 0). The ancestor mask lets node
  *       i see node j iff j is i or an ancestor of i, and a node's position is the root's
- *       plus its depth ([LI] §10.6.3, Table 10-17). The selection compares path
- *       log-probabilities rounded to binary32, the precision the GPU library decides in.
+ *       plus its depth ([LI] §10.6.3, Table 10-17). The selection compares the fp64 path
+ *       log-probabilities themselves; equal values go to the lower node index.
  *   R22 paged KV commit ([LI] §10.6.3: after a rejection the cache length is cut back, and a
  *       paged cache releases the blocks it no longer needs): logical slot s of sequence b
  *       lives in physical block block_table[b][s / block_size] at offset s % block_size.
@@ -618,14 +618,13 @@ static int cmp_tok(const void* a, const void* b) {
 
 typedef struct {
   double lp;
-  float lp32;
   int node;
 } onode_t;
 
 static int cmp_node(const void* a, const void* b) {
   const onode_t* x = (const onode_t*)a;
   const onode_t* y = (const onode_t*)b;
-  if (x->lp32 != y->lp32) return x->lp32 > y->lp32 ? -1 : 1;
+  if (x->lp != y->lp) return x->lp > y->lp ? -1 : 1;
   return (x->node > y->node) - (x->node < y->node);
 }
 
@@ -727,7 +726,6 @@ int oracle_tree_draft(int B, int V, int row_stride, int depth, const int32_t* to
           const int cnt = n - first, hn = top_head[s + 1];
           for (int i = 0; i < cnt; ++i) {
             lay[i].lp = lp[first + i];
-            lay[i].lp32 = (float)lp[first + i];
             lay[i].node = first + i;
           }
           qsort(lay, (size_t)cnt, sizeof(onode_t), cmp_node);

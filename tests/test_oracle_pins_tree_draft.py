@@ -10,6 +10,8 @@ Pinned against:
     boolean transitive closure) on random and tie-heavy rows;
   * invariants (path probability = product of softmax probabilities along the path,
     expanded nodes at least as probable as the rest of their layer);
+  * a case whose two candidates tie once rounded to binary32 but not in fp64
+    (golden/tree_rank_fp64.json): the expansion follows the fp64 path probability;
   * invalid configurations.
 """
 import json
@@ -125,7 +127,7 @@ def _brute_tree(rows_by_step, top_head, top_k_spec, root_token, pos_base, V):
             rows_before += h
             if s + 1 < len(top_head):
                 layer = list(range(first, nxt))
-                ranked = sorted(layer, key=lambda i: (-np.float32(lp[b, i]), i))
+                ranked = sorted(layer, key=lambda i: (-lp[b, i], i))
                 cur = ranked[:top_head[s + 1]]
                 for j, node in enumerate(cur):
                     nrow[b, node] = rows_before + j
@@ -242,3 +244,33 @@ def test_tree_stride_too_small_is_rejected(orc):
         orc.tree_draft(x["rows"], (1,), ((5,),), x["root_token"], tree_stride=5, vocab=64)
     o = orc.tree_draft(x["rows"], (1,), ((5,),), x["root_token"], tree_stride=9, vocab=64)
     assert list(o["parent"][0, 6:]) == [-1, -1, -1] and list(o["node_row"][0, 6:]) == [-1] * 3
+
+
+def test_expansion_ranks_fp64_path_probabilities(orc):
+    """The expansion decision is taken on the path probabilities themselves: two depth-2
+    candidates whose fp64 path log-probabilities round to the same binary32 value are ranked
+    by their fp64 values, so the more probable one is expanded although its node index is
+    higher (a binary32 ranking would tie them and take the lower index)."""
+    g = _load("tree_rank_fp64.json")
+    V = g["vocab"]
+    th = tuple(g["top_head"])
+    ks = tuple(tuple(k) for k in g["top_k_spec"])
+    root = np.array([g["root_row_bf16"]], np.uint16)
+    kids = np.array(g["child_rows_bf16"], np.uint16)
+    rows = [root, kids, root.copy()]
+    # expected, from the definition with library routines: the root's two most probable
+    # children (nodes 1, 2) take rows A and B; node 3 is A's top child, node 4 is B's
+    R = W.bf16_to_f32(root[0]).astype(np.float64)
+    ls_r = log_softmax(R)
+    top2 = np.lexsort((np.arange(V), -R))[:2]
+    lp = []
+    for j in range(2):
+        l = W.bf16_to_f32(kids[j]).astype(np.float64)
+        lp.append(ls_r[top2[j]] + log_softmax(l)[np.lexsort((np.arange(V), -l))[0]])
+    assert np.float32(lp[0]) == np.float32(lp[1]) and lp[1] > lp[0]  # the fixture's premise
+    o = orc.tree_draft(rows, th, ks, np.array([0], np.int32), vocab=V)
+    assert list(o["node_token"][0, 1:3]) == list(top2)
+    assert abs(o["node_logp"][0, 3] - lp[0]) < 1e-12 and abs(o["node_logp"][0, 4] - lp[1]) < 1e-12
+    assert o["expand"][2, 0, 0] == 4
+    assert o["node_row"][0, 4] == 3 and o["node_row"][0, 3] == -1
+    assert 0 < o["select_margin"][2, 0] < 1e-6  # a near-boundary decision for GPU parity
