@@ -15,6 +15,8 @@ bounded sample of the same workload as a reported baseline.
   python bench.py --workload paged_kv    # the paged KV commit of the tree workload instead
   python bench.py --workload ngram       # the n-gram prompt lookup instead
   python bench.py --workload tree        # greedy tree verify + KV commit instead
+  python bench.py --workload c2|c5       # the other chain workloads (c3 is the default)
+  python bench.py --workload markov      # the vocab-4 Markov rounds (launch-bound)
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
 大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
@@ -516,7 +518,9 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--workload", choices=["chain", "tree", "tree_draft", "paged_kv", "ngram"], default="chain")
+    ap.add_argument("--workload", default="chain",
+                    choices=["chain", "c2", "c3", "c5", "markov", "tree", "tree_draft",
+                             "paged_kv", "ngram"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
@@ -538,7 +542,30 @@ def main():
     if args.workload == "tree":
         tree_bench(args)
         return
+    if args.workload == "markov":
+        markov_bench(args)
+        return
+    chain_bench(args, "c3" if args.workload == "chain" else args.workload)
 
+
+# Chain workloads: what each line reports and how its inputs are held in HBM.
+CHAIN_LEGS = {
+    "c2": dict(sets=16, workload="chain verify B=64 gamma=4 V=32000 bf16 logits, target "
+                                 "N(0,2^2), draft = target + N(0,0.5^2), T=1, no top-k/top-p; "
+                                 "16 input sets (590 MB) rotated call by call, so that the "
+                                 "working set exceeds twice the 256 MB last-level cache"),
+    "c3": dict(sets=1, workload="chain verify B=256 gamma=8 V=128256 bf16 logits, target "
+                                "N(0,3^2) with 1% of ids +8, draft = target + N(0,1^2), T=0.7, "
+                                "top-p 0.9 on p and q"),
+    "c5": dict(sets=1, workload="ragged chain verify B=1024 gamma_b~U{1..8} V=128256 bf16 "
+                                "logits, target N(0,2^2), draft noise sigma_b~U[0.3,1.5], "
+                                "T_b~U[0.5,1.2], no top-k/top-p, bonus on full accept, pointer "
+                                "rollback"),
+}
+
+
+def chain_bench(args, name):
+    """One spec_verify_chain call per step over chain workload ``name`` (c2, c3, c5)."""
     import numpy as np
     import torch
 
@@ -546,88 +573,100 @@ def main():
     from draft_verification_03_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    log("generating the c3 workload (B=256, gamma=8, V=128256, T=0.7, top-p 0.9)")
-    x = W.chain_inputs("c3")
-    cu = x["cu_gamma"]
-    Bn, nd, V = len(cu) - 1, int(cu[-1]), x["vocab"]
+    leg = CHAIN_LEGS[name]
+    nsets = leg["sets"]
+    log(f"generating the {name} workload ({nsets} input set(s))")
+    xs = [W.chain_inputs(name) if i == 0 else W.chain_inputs(name, seed=W.SEEDS[name] * 1000 + i)
+          for i in range(nsets)]
+    x = xs[0]
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
         {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}.get(a.dtype, a.dtype))).cuda()
-    tgt, drf = dv(x["target"]), dv(x["draft"])
-    temp, topp, sid, cu_d = dv(x["temperature"]), dv(x["top_p"]), dv(x["seq_id"]), dv(cu)
-    L0 = dv(x["committed_len"])
-
-    # The drafter's tokens: one gamma = 0 round per draft row through the same library.
-    log("drawing draft tokens (gamma = 0 rounds over the draft rows)")
-    b_of = np.repeat(np.arange(Bn), np.diff(cu))
-    k_of = np.arange(nd) - cu[b_of]
-    d_out = torch.empty(nd, dtype=torch.int32, device="cuda")
-    da = B.chain_args(target_logits=drf, cu_gamma=dv(np.zeros(nd + 1, np.int32)),
-                      temperature=dv(x["temperature"][b_of]), top_p=dv(x["top_p"][b_of]),
-                      seq_id=dv(x["seq_id"][b_of]),
-                      committed_len=dv((x["committed_len"][b_of] + k_of).astype(np.int32)),
-                      out_tokens=d_out, num_accepted=torch.empty(nd, dtype=torch.int32,
-                                                                 device="cuda"),
-                      seed=SEED_DRAFT, vocab=V, max_gamma=0, total_draft_rows=0,
-                      row_stride=x["stride"])
-    B.spec_verify_chain(da)
-    torch.cuda.synchronize()
-    toks = d_out
-
-    L = L0.clone()
-    out = torch.empty(nd + Bn, dtype=torch.int32, device="cuda")
-    nacc = torch.empty(Bn, dtype=torch.int32, device="cuda")
-    flags = torch.empty(Bn, dtype=torch.int32, device="cuda")
-    a = B.chain_args(target_logits=tgt, draft_logits=drf, cu_gamma=cu_d, draft_tokens=toks,
-                     temperature=temp, top_p=topp, seq_id=sid, committed_len=L,
-                     out_tokens=out, num_accepted=nacc, seq_flags=flags, seed=SEED, vocab=V,
-                     max_gamma=int(np.diff(cu).max()), total_draft_rows=nd,
-                     row_stride=x["stride"])
-    ws = torch.empty(B.spec_verify_chain_workspace_size(Bn, nd, V), dtype=torch.uint8,
-                     device="cuda")
+    calls = []
+    for xi in xs:
+        cu = xi["cu_gamma"]
+        Bn, nd, V = len(cu) - 1, int(cu[-1]), xi["vocab"]
+        tgt, drf = dv(xi["target"]), dv(xi["draft"])
+        topp = None if xi["top_p"] is None else dv(xi["top_p"])
+        # The drafter's tokens: one gamma = 0 round per draft row through the same library.
+        b_of = np.repeat(np.arange(Bn), np.diff(cu))
+        k_of = np.arange(nd) - cu[b_of]
+        d_out = torch.empty(nd, dtype=torch.int32, device="cuda")
+        da = B.chain_args(target_logits=drf, cu_gamma=dv(np.zeros(nd + 1, np.int32)),
+                          temperature=dv(xi["temperature"][b_of]),
+                          top_p=None if xi["top_p"] is None else dv(xi["top_p"][b_of]),
+                          seq_id=dv(xi["seq_id"][b_of]),
+                          committed_len=dv((xi["committed_len"][b_of] + k_of).astype(np.int32)),
+                          out_tokens=d_out,
+                          num_accepted=torch.empty(nd, dtype=torch.int32, device="cuda"),
+                          seed=SEED_DRAFT, vocab=V, max_gamma=0, total_draft_rows=0,
+                          row_stride=xi["stride"])
+        B.spec_verify_chain(da)
+        torch.cuda.synchronize()
+        L = dv(xi["committed_len"])
+        out = torch.empty(nd + Bn, dtype=torch.int32, device="cuda")
+        nacc = torch.empty(Bn, dtype=torch.int32, device="cuda")
+        flags = torch.empty(Bn, dtype=torch.int32, device="cuda")
+        a = B.chain_args(target_logits=tgt, draft_logits=drf, cu_gamma=dv(cu), draft_tokens=d_out,
+                         temperature=dv(xi["temperature"]), top_p=topp, seq_id=dv(xi["seq_id"]),
+                         committed_len=L, out_tokens=out, num_accepted=nacc, seq_flags=flags,
+                         seed=SEED, vocab=V, max_gamma=int(np.diff(cu).max()),
+                         total_draft_rows=nd, row_stride=xi["stride"])
+        ws = torch.empty(B.spec_verify_chain_workspace_size(Bn, nd, V), dtype=torch.uint8,
+                         device="cuda")
+        calls.append(dict(a=a, ws=ws, L=L, nacc=nacc, flags=flags))
     # Warm-up: the W steps, continued until --warmup-seconds have passed, so that the timed
     # steps run at the GPU's settled clocks (the first few hundred milliseconds of a burst
-    # of work run measurably slower).
+    # of work run measurably slower). The committed lengths advance call after call; the
+    # uniforms are keyed by position, so every call is a fresh round of the same shape.
     t_warm = time.time()
     done = 0
     while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
         for _ in range(10):
-            B.spec_verify_chain(a, workspace=ws)
-        done += 10
+            c = calls[done % nsets]
+            B.spec_verify_chain(c["a"], workspace=c["ws"])
+            done += 1
         torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    # Headline: the steps back to back with nothing between them (an event recorded between
-    # the row pass and the resolve step delays the resolve by a few microseconds).
+    # Headline: the steps back to back with nothing between them.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
-        B.spec_verify_chain(a, workspace=ws)
+    for i in range(args.steps):
+        c = calls[i % nsets]
+        B.spec_verify_chain(c["a"], workspace=c["ws"])
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     # Row-pass durations: the same steps again, each with one event pair that the library
     # records on the launch stream around the row kernel.
     evs = [B.EventPair() for _ in range(args.steps)]
-    for e in evs:
-        a.profile_events = e.ptr
-        B.spec_verify_chain(a, workspace=ws)
+    for i, e in enumerate(evs):
+        c = calls[i % nsets]
+        c["a"].profile_events = e.ptr
+        B.spec_verify_chain(c["a"], workspace=c["ws"])
+        c["a"].profile_events = None
     torch.cuda.synchronize()
     row_ms = [e.elapsed_ms() for e in evs]
-    a.profile_events = None
     ms_step = total_ms / args.steps
-    ab = algorithmic_bytes(x)
-    rows = ab["rows"]
+    abs_ = [algorithmic_bytes(xi) for xi in xs]
+    # per step, averaged over the rotated sets (equal shares of the steps)
+    rows = float(np.mean([ab["rows"] for ab in abs_]))
+    row_pass = float(np.mean([ab["row_pass"] for ab in abs_]))
+    call_bytes = float(np.mean([ab["call"] for ab in abs_]))
     value = rows / (ms_step / 1e3)
     row_avg_ms = float(np.mean(row_ms))
-    achieved = ab["row_pass"] / (row_avg_ms / 1e3) / 1e9
+    achieved = row_pass / (row_avg_ms / 1e3) / 1e9
     src_hash = kernel_source_hash(CHAIN_SOURCES)
-    traffic = read_traffic(src_hash)
-    fl = flags.cpu().numpy()
+    traffic = read_traffic(src_hash) if name == "c3" else None
+    fl = calls[0]["flags"].cpu().numpy()
     log(f"step {ms_step * 1e3:.1f} us, row pass {row_avg_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s), accepted/seq {nacc.float().mean().item():.3f}, "
+        f"({achieved:.0f} GB/s), call {call_bytes / (ms_step / 1e3) / 1e9:.0f} GB/s, "
+        f"accepted/seq {calls[0]['nacc'].float().mean().item():.3f}, "
         f"top-p multi-pass sequences {int(((fl & B.FLAG_TOPP_SLOW) != 0).sum())}")
+    cu = x["cu_gamma"]
     res = {
-        "metric": METRIC,
+        "metric": METRIC if name == "c3" else
+        f"verify rows/sec, {name} chain workload; achieved HBM GB/s vs peak",
         "value": value,
         "unit": "verify rows/s",
         "n_gpus": 1,
@@ -639,20 +678,127 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "chain verify B=256 gamma=8 V=128256 bf16 logits, target "
-                               "N(0,3^2) with 1% of ids +8, draft = target + N(0,1^2), T=0.7, "
-                               "top-p 0.9 on p and q",
-                   "batch": Bn, "gamma": int(np.diff(cu).max()), "vocab": V,
-                   "verify_rows_per_call": rows, "call_algorithmic_bytes": ab["call"],
-                   "call_hbm_gbs": ab["call"] / (ms_step / 1e3) / 1e9},
+        "config": {"workload": leg["workload"],
+                   "batch": len(cu) - 1, "max_gamma": int(np.diff(cu).max()),
+                   "vocab": x["vocab"], "input_sets": nsets,
+                   "verify_rows_per_call": rows, "call_algorithmic_bytes": call_bytes,
+                   "call_hbm_gbs": call_bytes / (ms_step / 1e3) / 1e9},
         "roofline": {"bound": "hbm", "kernel": ROW_KERNEL, "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "bytes_per_launch": ab["row_pass"],
+                     "traffic": traffic, "bytes_per_launch": row_pass,
                      "avg_launch_us": row_avg_ms * 1e3, "kernel_source_hash": src_hash},
     }
     if not args.no_cpu_baseline:
-        log(f"timing the oracle on the first {args.cpu_sample_seqs} sequences")
-        res["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
+        n = min(args.cpu_sample_seqs, len(cu) - 1)
+        log(f"timing the oracle on the first {n} sequences")
+        res["cpu_baseline"] = cpu_baseline(x, n)
+    print(json.dumps(res), flush=True)
+
+
+def markov_bench(args):
+    """The vocab-4 Markov workload: one spec_verify_chain call per round (B=1, gamma=4,
+    V=4), on rounds whose inputs are all resident in HBM, one call after another. A round of
+    a real stream depends on the previous one's output; here the rounds' contexts and drafts
+    are drawn beforehand (last token uniform, drafts a chain of the draft table), so the line
+    measures the call itself: it is bound by launch latency, not by its 72 bytes."""
+    import numpy as np
+    import torch
+
+    from draft_verification_03_amd import binding as B
+    from draft_verification_03_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    T, D = W.markov_tables()
+    tl, dl = W.log_rows_bf16(T), W.log_rows_bf16(D)
+    g, nr = 4, 2048
+    rng = np.random.default_rng(W.SEEDS["markov"] + 1)
+    last = rng.integers(0, 4, size=nr)
+    drafts = np.zeros((nr, g), np.int32)
+    cdf = np.cumsum(D, axis=1)
+    for r in range(nr):
+        prev = last[r]
+        for j in range(g):
+            prev = int(np.searchsorted(cdf[prev], rng.random(), side="right").clip(0, 3))
+            drafts[r, j] = prev
+    ctx = np.concatenate([last[:, None], drafts], axis=1)
+    tgt = tl[ctx.reshape(-1)].reshape(nr, g + 1, 8)
+    drf = dl[ctx[:, :g].reshape(-1)].reshape(nr, g, 8)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    d_tgt = torch.from_numpy(tgt.view(np.int16)).cuda()
+    d_drf = torch.from_numpy(drf.view(np.int16)).cuda()
+    d_tok = torch.from_numpy(drafts).cuda()
+    pos = (np.arange(nr) * 3).astype(np.int32)  # distinct positions: fresh uniforms per round
+    d_L = torch.from_numpy(pos.copy()).cuda()
+    d_out = torch.zeros((nr, g + 1), **i32)
+    d_n = torch.zeros(nr, **i32)
+    cu = torch.tensor([0, g], **i32)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.spec_verify_chain_workspace_size(1, g, 4), dtype=torch.uint8,
+                     device="cuda")
+    args_r = [B.chain_args(target_logits=d_tgt[r], draft_logits=d_drf[r], cu_gamma=cu,
+                           draft_tokens=d_tok[r], temperature=one, committed_len=d_L[r:r + 1],
+                           out_tokens=d_out[r], num_accepted=d_n[r:r + 1], seed=SEED, vocab=4,
+                           max_gamma=g, total_draft_rows=g, row_stride=8) for r in range(nr)]
+    t_warm = time.time()
+    done = 0
+    while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
+        for _ in range(10):
+            B.spec_verify_chain(args_r[done % nr], workspace=ws)
+            done += 1
+        torch.cuda.synchronize()
+    steps = args.steps
+    log(f"timing {steps} rounds")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        B.spec_verify_chain(args_r[i % nr], workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    evs = [B.EventPair() for _ in range(steps)]
+    for i, e in enumerate(evs):
+        a = args_r[i % nr]
+        a.profile_events = e.ptr
+        B.spec_verify_chain(a, workspace=ws)
+        a.profile_events = None
+    torch.cuda.synchronize()
+    row_ms = float(np.mean([e.elapsed_ms() for e in evs]))
+    nbytes = (2 * g + 1) * 4 * 2 + g * 4  # the rows' 4 logits each, and the draft tokens
+    gbs = nbytes / (row_ms / 1e3) / 1e9
+    log(f"round {ms * 1e3:.1f} us ({1e3 / ms:.0f} rounds/s), row kernel {row_ms * 1e3:.1f} us")
+    res = {
+        "metric": "Markov workload: verification rounds/s at B=1 gamma=4 V=4 (launch-bound)",
+        "value": 1e3 / ms, "unit": "rounds/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "vocab-4 Markov rounds, Dirichlet(2) target table, draft = "
+                               "target + U(-0.05,0.05) renormalised, B=1, gamma=4, T=1; 2048 "
+                               "pre-drawn rounds resident in HBM, one call per round",
+                   "call_algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "kernel": ROW_KERNEL, "achieved": gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_launch": nbytes, "avg_launch_us": row_ms * 1e3,
+                     "kernel_source_hash": kernel_source_hash(CHAIN_SOURCES),
+                     "note": "launch-latency bound: 72 bytes per round"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the oracle, one call per round")
+        t0 = time.time()
+        reps = 0
+        onef = np.ones(1, np.float32)
+        while time.time() - t0 < 10.0 or reps == 0:
+            r = reps % nr
+            oracle.verify_chain_v(tgt[r], drf[r], np.array([0, g], np.int32), drafts[r], onef,
+                                  None, np.zeros(1, np.uint32), pos[r:r + 1], seed=SEED,
+                                  vocab=4, nthreads=1)
+            reps += 1
+        el = time.time() - t0
+        res["cpu_baseline"] = {"value": reps / el, "unit": "rounds/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} rounds, one oracle call each (ctypes), "
+                                         f"{el:.1f} s wall, one thread"}
     print(json.dumps(res), flush=True)
 
 

@@ -26,7 +26,7 @@ SPEC_ERR_WORKSPACE = -4
 
 FLAG_BAD_TOKEN, FLAG_Q_ZERO, FLAG_RESID_FALLBACK, FLAG_NO_ROW = 1, 2, 4, 8
 FLAG_SLOT_OOB, FLAG_BAD_TREE, FLAG_TOPP_SLOW, FLAG_BAD_PARAM = 16, 32, 64, 128
-FLAG_EOS, FLAG_LEN_CAP = 256, 512
+FLAG_EOS, FLAG_LEN_CAP, FLAG_FREE_FULL = 256, 512, 1024
 
 
 class spec_chain_args(ctypes.Structure):

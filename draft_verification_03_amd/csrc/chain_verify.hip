@@ -109,11 +109,12 @@ __device__ __forceinline__ uint64_t fixw(float w) {
 
 __device__ __forceinline__ int wave_incl_scan_i(int v, int) { return wave_incl_scan_dpp(v); }
 
-// Parameters checked on their bit patterns (NaN fails every test). T: >= 0 (or -0), not NaN;
-// +inf is allowed (a flat law).
+// Parameters checked on their bit patterns (NaN fails every test). T: +0 or -0 (greedy), or
+// 2^-126 <= T <= 2^126, so that the scale log2(e)/T is a finite normal value (a scale of 0
+// would turn the -inf padding of a row's last vector into NaN).
 __device__ __forceinline__ bool temperature_ok(float T) {
   const uint32_t b = __float_as_uint(T);
-  return (b & 0x80000000u) ? (b == 0x80000000u) : (b <= 0x7F800000u);
+  return (b & 0x7FFFFFFFu) == 0u || (b >= 0x00800000u && b <= 0x7E800000u);
 }
 // top_p: 0 < P <= 1.
 __device__ __forceinline__ bool top_p_ok(float P) {

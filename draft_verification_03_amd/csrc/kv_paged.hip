@@ -7,20 +7,23 @@
 //     over a share of the sequence's 16-byte chunks (8 elements of one head's K or V row in
 //     one layer). A workgroup reads the sequence's length, path length and path once; thread
 //     j-1 checks step j and translates its source and destination slots through the block
-//     table into physical offsets in LDS. For its chunk a thread then moves slot base +
+//     table into physical offsets in LDS, and the threads check the table entries the
+//     release would free. For its chunk a thread then moves slot base +
 //     path[j-1] to slot base + j for j = 1..D in increasing order -- in-order copying for
 //     any path -- kGroup steps at a time: when no source of a group is the destination of an
 //     earlier step of the group (always so for a tree path, path[j-1] >= j), the group's
 //     loads, for kBatch chunks at once, are issued before its stores; otherwise one
 //     load-store pair at a time.
-//  2. paged_release_kernel -- one 1024-thread workgroup over tiles of whole table rows: the
-//     same predicate, checked by one thread per sequence (lengths) and one per path step
-//     (slots mapped), then one thread per sequence writes its new committed length and its
-//     first block past that length is noted; then the tile's table entries, taken in
-//     row-major order (8 consecutive per thread), are flagged and scanned, and a released
+//  2. paged_release_kernel -- one 1024-thread workgroup over tiles of whole table rows. Each
+//     tile first issues all of its global reads together -- the rows' lengths, their path
+//     rows and their table entries, kept in LDS -- and then decides from LDS alone: the
+//     commit predicate (one thread per path step, one per table entry for the ids of the
+//     blocks that would be freed), the new committed lengths, then the tile's entries taken
+//     in row-major order (8 consecutive per thread) are flagged and scanned, and a released
 //     entry's place in the free list is the number of released entries before it -- so the
-//     ids land in (sequence, logical block) order whatever the launch timing. It runs after
-//     every copy has read the tables.
+//     ids land in (sequence, logical block) order whatever the launch timing. An entry whose
+//     place falls at or past the free list's capacity stays in its table (FREE_FULL). It runs
+//     after every copy has read the tables.
 #include "spec_device.h"
 #include "specv_internal.h"
 
@@ -39,7 +42,8 @@ constexpr int kRelThreads = 1024;
 constexpr int kRelWaves = kRelThreads / kWave;
 constexpr int kRun = 8;           // table entries per thread per chunk
 constexpr int kRelEntries = kRelThreads * kRun;  // table entries per tile (whole rows)
-constexpr int kRelRows = kRelEntries;            // rows per tile at most
+constexpr int kRelRows = 1024;                   // rows per tile at most
+constexpr int kRelPath = 4096;                   // path entries per tile at most
 
 struct PagedParams {
   uint16_t* k[kMaxLayers];
@@ -58,10 +62,11 @@ struct PagedParams {
 
 // The commit predicate, checked in both kernels: with L = committed_len, D = path_len and
 // base = L + lead - 1, a sequence is committed when 0 <= D <= max_depth, base >= -1, the new
-// length L + lead + D fits max_blocks blocks, every path node is >= 1, and for every step
+// length L + lead + D fits max_blocks blocks, every path node is >= 1, for every step
 // j = 1..D that moves a slot (base + path[j-1] != base + j) both slots lie inside the table
-// in blocks with valid ids (0 <= id < num_blocks). Otherwise it is flagged SLOT_OOB and left
-// untouched.
+// in blocks with valid ids (0 <= id < num_blocks), and no table entry at or past the first
+// block beyond the new length (the blocks the release frees) is >= num_blocks. Otherwise it
+// is flagged SLOT_OOB and left untouched.
 
 __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
   __shared__ int64_t s_so[kMaxDepth], s_do[kMaxDepth];  // physical element offsets per step
@@ -118,6 +123,12 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
     s_mv[tid] = mv;
     if (!ok) atomicOr(&s_bad, 1);
   }
+  if (head_ok) {  // the blocks the release would free must hold block ids
+    const int need = (int)(((int64_t)L + P.lead + D + P.bs - 1) / P.bs);
+    const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
+    for (int lb = need + tid; lb < P.max_blocks; lb += kThreads)
+      if (bt[lb] >= P.num_blocks) atomicOr(&s_bad, 1);
+  }
   __syncthreads();
   if (!head_ok || s_bad || D == 0 || c0 >= nch) return;
   for (int j0 = 1; j0 <= D; j0 += kGroup) {
@@ -169,69 +180,94 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
 }
 
 __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams P) {
-  __shared__ int s_need[kRelRows];  // first released logical block of each row (-1: invalid)
+  __shared__ int32_t s_bt[kRelEntries];   // the tile's table entries, row-major
+  __shared__ int32_t s_path[kRelPath];    // the tile's path rows
+  __shared__ int s_need[kRelRows];        // first released logical block of a row (-1: invalid)
+  __shared__ int s_L[kRelRows], s_D[kRelRows];
   __shared__ int s_wave[kRelWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int fc0 = min(max(*P.free_count, 0), P.free_cap);
-  const int mb = P.max_blocks;
-  const int rows = max(1, min(kRelRows, kRelEntries / mb));  // whole rows per tile
-  int carry = 0;  // blocks released before this chunk (uniform)
+  const int mb = P.max_blocks, md = P.max_depth;
+  const bool in_lds = mb <= kRelEntries;  // a whole table row fits the tile's LDS
+  const int rows = max(1, min(min(kRelRows, kRelEntries / mb), kRelPath / md));
+  int carry = 0;  // blocks released before this tile (uniform)
   for (int b0 = 0; b0 < P.B; b0 += rows) {
     const int nr = min(rows, P.B - b0);
-    // the commit predicate spread over threads: one per sequence checks the lengths and
-    // notes the first block past the new length (-1: invalid), then one per (sequence, path
-    // step) checks that step and marks its sequence invalid on a failure
+    const int64_t e0 = (int64_t)b0 * mb, ne = (int64_t)nr * mb;
+    // 1. every global read of the tile at once: lengths, path rows, table entries (in LDS,
+    //    and kRun consecutive entries per thread in registers for the scan)
     for (int i = tid; i < nr; i += kRelThreads) {
-      const int b = b0 + i;
-      const int L = P.committed[b], D = P.plen[b];
+      const int L = P.committed[b0 + i], D = P.plen[b0 + i];
+      s_L[i] = L;
+      s_D[i] = D;
       const int64_t base = (int64_t)L + P.lead - 1;
       const int64_t need = ((int64_t)L + P.lead + D + P.bs - 1) / P.bs;
-      const bool ok = D >= 0 && D <= P.max_depth && base >= -1 && need <= P.max_blocks;
+      const bool ok = D >= 0 && D <= md && base >= -1 && need <= mb;
       s_need[i] = ok ? (int)need : -1;
     }
+    for (int q = tid; q < nr * md; q += kRelThreads) s_path[q] = P.path[(size_t)b0 * md + q];
+    int v_reg[kRun];
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) {
+      const int64_t e = (int64_t)tid * kRun + r;  // first chunk of the tile
+      v_reg[r] = e < ne ? P.bt[e0 + e] : -1;
+      if (in_lds && e < ne) s_bt[e] = v_reg[r];
+    }
     __syncthreads();
-    for (int64_t q = tid; q < (int64_t)nr * P.max_depth; q += kRelThreads) {
-      const int i = (int)(q / P.max_depth), j = (int)(q - (int64_t)i * P.max_depth);
-      const int b = b0 + i;
-      const int L = P.committed[b], D = P.plen[b];
-      if (D < 0 || D > P.max_depth || j >= D) continue;  // no such step
-      const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
-      const int node = P.path[(size_t)b * P.max_depth + j];
-      const int64_t base = (int64_t)L + P.lead - 1;
+    // 2. the commit predicate from LDS: path steps (slots mapped to valid blocks), and the
+    //    entries the release would free (valid ids)
+    for (int q = tid; q < nr * md; q += kRelThreads) {
+      const int i = q / md, j = q - i * md;
+      const int D = s_D[i];
+      if (s_need[i] < 0 || j >= D) continue;
+      const int node = s_path[q];
+      const int64_t base = (int64_t)s_L[i] + P.lead - 1;
       const int64_t src = base + node, dst = base + j + 1;
-      const int64_t slots = (int64_t)P.max_blocks * P.bs;
+      const int64_t slots = (int64_t)mb * P.bs;
       bool ok = node >= 1;
       if (ok && src != dst) {
-        const int pbs = (src >= 0 && src < slots) ? bt[src / P.bs] : -1;
-        const int pbd = (dst >= 0 && dst < slots) ? bt[dst / P.bs] : -1;
+        const int64_t row = (int64_t)(b0 + i) * mb;
+        int pbs = -1, pbd = -1;
+        if (src >= 0 && src < slots) pbs = in_lds ? s_bt[i * mb + src / P.bs] : P.bt[row + src / P.bs];
+        if (dst >= 0 && dst < slots) pbd = in_lds ? s_bt[i * mb + dst / P.bs] : P.bt[row + dst / P.bs];
         ok = pbs >= 0 && pbs < P.num_blocks && pbd >= 0 && pbd < P.num_blocks;
       }
       if (!ok) atomicMin(&s_need[i], -1);
     }
-    __syncthreads();
-    // the new lengths: every read of committed_len above came first
-    for (int i = tid; i < nr; i += kRelThreads) {
-      const int b = b0 + i;
-      if (s_need[i] >= 0) {
-        P.committed[b] = P.committed[b] + P.lead + P.plen[b];
-      } else if (P.flags) {
-        P.flags[b] |= SPEC_FLAG_SLOT_OOB;
+    for (int64_t c0 = 0; c0 < ne; c0 += (int64_t)kRelThreads * kRun) {
+#pragma unroll
+      for (int r = 0; r < kRun; ++r) {
+        const int64_t e = c0 + (int64_t)tid * kRun + r;
+        if (e >= ne) continue;
+        const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
+        const int i = (int)(e / mb), lb = (int)(e - (int64_t)i * mb);
+        const int need = s_need[i];
+        if (need >= 0 && lb >= need && v >= P.num_blocks) atomicMin(&s_need[i], -1);
       }
     }
-    // the tile's table entries in row-major order, kRun consecutive per thread: the free
-    // list position of a released entry is the count of released entries before it
-    const int64_t e0 = (int64_t)b0 * mb, ne = (int64_t)nr * mb;
+    __syncthreads();
+    // 3. the new lengths and SLOT_OOB flags
+    for (int i = tid; i < nr; i += kRelThreads) {
+      if (s_need[i] >= 0) {
+        P.committed[b0 + i] = s_L[i] + P.lead + s_D[i];
+      } else if (P.flags) {
+        P.flags[b0 + i] |= SPEC_FLAG_SLOT_OOB;
+      }
+    }
+    // 4. the tile's entries in row-major order, kRun consecutive per thread: a released
+    //    entry's free-list position is the count of released entries before it; one that
+    //    lands at or past the capacity stays in the table and flags its sequence FREE_FULL
     for (int64_t c0 = 0; c0 < ne; c0 += (int64_t)kRelThreads * kRun) {
       int pb[kRun];
       int cnt = 0;
 #pragma unroll
       for (int r = 0; r < kRun; ++r) {
-        const int64_t e = c0 + (int64_t)tid * kRun + r;  // entry of the tile
+        const int64_t e = c0 + (int64_t)tid * kRun + r;
         pb[r] = -1;
         if (e < ne) {
           const int i = (int)(e / mb), lb = (int)(e - (int64_t)i * mb);
           const int need = s_need[i];
-          const int v = P.bt[e0 + e];
+          const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
           if (need >= 0 && lb >= need && v >= 0) pb[r] = v;
         }
         cnt += pb[r] >= 0;
@@ -249,9 +285,14 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
 #pragma unroll
       for (int r = 0; r < kRun; ++r) {
         if (pb[r] >= 0) {
-          if (at < P.free_cap) P.free_list[at] = pb[r];
+          const int64_t e = c0 + (int64_t)tid * kRun + r;
+          if (at < P.free_cap) {
+            P.free_list[at] = pb[r];
+            P.bt[e0 + e] = -1;
+          } else if (P.flags) {
+            atomicOr(&P.flags[b0 + (int)(e / mb)], SPEC_FLAG_FREE_FULL);
+          }
           ++at;
-          P.bt[e0 + c0 + (int64_t)tid * kRun + r] = -1;
         }
       }
       carry += total;

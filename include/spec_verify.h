@@ -62,8 +62,12 @@ extern "C" {
 #define SPEC_FLAG_BAD_TREE 32       /* parent/node_row malformed: no progress               */
 #define SPEC_FLAG_TOPP_SLOW 64      /* a top-k/top-p threshold needed another read of a row
                                        (a second capture, or the exact multi-pass search)   */
-#define SPEC_FLAG_BAD_PARAM 128     /* T < 0, top_p outside (0,1], gamma_b out of range, or
-                                       a history length outside its row: no progress       */
+#define SPEC_FLAG_BAD_PARAM 128     /* T neither 0 nor in [2^-126, 2^126] (negative, NaN,
+                                       inf, subnormal, huge), top_p outside (0,1], gamma_b
+                                       out of range, or a history length outside its row:
+                                       no progress                                          */
+#define SPEC_FLAG_FREE_FULL 1024    /* paged release: the free list was full; the blocks
+                                       that did not fit stay in the block table            */
 #define SPEC_FLAG_EOS 256           /* the round's last emitted token is the EOS id         */
 #define SPEC_FLAG_LEN_CAP 512       /* the emission cap cut the round short                 */
 
@@ -124,7 +128,7 @@ typedef struct spec_chain_args {
                                     draft laws (no draft row is read)                      */
   const int32_t* cu_gamma;       /* [B+1], cu_gamma[0] = 0, non-decreasing                    */
   const int32_t* draft_tokens;   /* [total_draft_rows]; may be NULL if total_draft_rows = 0  */
-  const float* temperature;      /* [B], >= 0                                                */
+  const float* temperature;      /* [B], 0 (greedy) or in [2^-126, 2^126] (else BAD_PARAM)   */
   const float* top_p;            /* [B] in (0, 1], or NULL = no top-p                        */
   const int32_t* top_k;          /* [B] or NULL = no top-k; K <= 0 or K >= vocab: off        */
   const uint32_t* seq_id;        /* [B] Philox stream ids, or NULL = b                       */
@@ -301,8 +305,11 @@ typedef struct spec_tree_draft_args {
  * outside [0, num_blocks)), a path node < 1, or an L' needing more than max_blocks blocks
  * gets SPEC_FLAG_SLOT_OOB and is left untouched. Table entries are -1 or block ids; each
  * block id appears at most once in the tables and the free list together (no shared
- * blocks). free_list has free_capacity entries (>= num_blocks); ids that would land at or
- * past it are not written (that happens only if the pool breaks the rule above).
+ * blocks). A table entry among the blocks the release would free that is >= num_blocks
+ * (not a block id) also gives SLOT_OOB, sequence untouched; negative entries are unmapped.
+ * free_list has free_capacity entries (>= num_blocks); a released block that finds it full
+ * stays in its table entry and the sequence gets SPEC_FLAG_FREE_FULL (copy and length done;
+ * only a pool that breaks the rule above gets there).
  * num_layers * 2 * num_kv_heads * head_dim / 8 must not exceed 2^30, nor that count / 1024
  * times batch 2^31 - 1 (SPEC_ERR_INVALID_ARG).
  */
@@ -327,7 +334,7 @@ typedef struct spec_paged_kv_args {
   const int32_t* path_len;   /* [B], 0..max_depth                                           */
   int32_t* committed_len;    /* [B] in/out                                                  */
   int32_t* free_list;        /* [free_capacity] in/out                                      */
-  int32_t* free_count;       /* [1] in/out                                                  */
+  int32_t* free_count;       /* [1] in/out; taken within [0, free_capacity]                */
   int32_t* seq_flags;        /* [B] or NULL (bits OR-ed in)                                 */
 } spec_paged_kv_args;
 

@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "libspec_oracle.so")
 PURPOSE_ACCEPT, PURPOSE_RESIDUAL, PURPOSE_BONUS = 0, 1, 2
 F_BAD_TOKEN, F_Q_ZERO, F_RESID_FALLBACK, F_NO_ROW = 1, 2, 4, 8
 F_SLOT_OOB, F_BAD_TREE, F_BAD_PARAM, F_EOS, F_LEN_CAP = 16, 32, 128, 256, 512
+F_FREE_FULL = 1024
 
 
 def build(force: bool = True) -> str:
@@ -64,7 +65,7 @@ def _declare(L):
     L.oracle_position_step.restype = _I
     L.oracle_verify_chain.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _I, ctypes.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                      _I]
+                                      _P, _P, _I]
     L.oracle_verify_chain.restype = _I
     L.oracle_verify_tree.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, _I]
@@ -77,7 +78,7 @@ def _declare(L):
     L.oracle_tree_draft.restype = _I
     L.oracle_kv_commit_paged.argtypes = [_I, _I, _I, _I, _P, _P, _I, _I, _I, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, _I, _I, _P, _P, _P,
-                                         _P, _P, _P, _P]
+                                         _P, _P, _I, _P, _P]
     L.oracle_kv_commit_paged.restype = _I
     L.oracle_ngram_draft.argtypes = [_I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
     L.oracle_ngram_draft.restype = _I
@@ -195,17 +196,25 @@ def verify_chain_v(target, draft, cu_gamma, draft_tokens, temperature, top_p=Non
         # [B][2]: distance to the nearest decision boundary among (0) the acceptance tests
         # and the top-p cuts of their rows, (1) those and the final draw (and its row's cut)
         "margin": np.full((B, 2), np.inf, dtype=np.float64),
+        # [n_draft][2] per tested draft position: |u_acc - a_k|, and the nearer of the top-p
+        # cut margins of p_k and q_k (inf where the position was not tested)
+        "row_margin": np.full((max(n_draft, 1), 2), np.inf, dtype=np.float64),
+        # [B][2] the final draw: the top-p cut margin of the bonus row (inf for a residual
+        # draw or none), and the draw's own margin (0 when R < 1e-5; inf without a draw)
+        "draw_margin": np.full((B, 2), np.inf, dtype=np.float64),
     }
     rc = lib().oracle_verify_chain(
         B, V, stride, _ptr(target), _ptr(draft), _ptr(cu), _ptr(toks), _ptr(temp), _ptr(tp),
         _ptr(tk), _ptr(eos), _ptr(cap), _ptr(sid), _ptr(L), int(lead_slots), int(seed),
         _ptr(ovr), _ptr(out["out_tokens"]), _ptr(out["num_accepted"]), _ptr(out["num_emitted"]),
         _ptr(out["committed_len"]), _ptr(out["seq_flags"]),
-        _ptr(out["probe_rows"]), _ptr(out["probe_seq"]), _ptr(out["margin"]), int(nthreads))
+        _ptr(out["probe_rows"]), _ptr(out["probe_seq"]), _ptr(out["margin"]),
+        _ptr(out["row_margin"]), _ptr(out["draw_margin"]), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_verify_chain failed")
     out["out_tokens"] = out["out_tokens"][:n_target]
     out["probe_rows"] = out["probe_rows"][:n_draft]
+    out["row_margin"] = out["row_margin"][:n_draft]
     return out
 
 
@@ -320,7 +329,8 @@ def kv_commit_paged(k_layers, v_layers, block_table, path_nodes, path_len, commi
                     free_list, free_count, lead_slots, max_depth):
     """Paged commit on host caches, in place (reading R22). k_layers/v_layers: lists of
     uint16 arrays shaped [num_blocks, block_size, H, D] (contiguous). block_table
-    [B, max_blocks] and free_list [num_blocks] are updated in place. Returns
+    [B, max_blocks] and free_list (its length is the free list's capacity) are updated in
+    place. Returns
     (committed_len, free_count, seq_flags)."""
     nb, bs, H, D = k_layers[0].shape
     nl = len(k_layers)
@@ -337,7 +347,8 @@ def kv_commit_paged(k_layers, v_layers, block_table, path_nodes, path_len, commi
     fl = np.zeros(B, dtype=np.int32)
     lib().oracle_kv_commit_paged(B, nl, H, D, kp, vp, bs, max_blocks, nb, bs * H * D, H * D, D,
                                  int(lead_slots), int(max_depth), _ptr(bt), _ptr(pn), _ptr(pl),
-                                 _ptr(cl), _ptr(free_list), _ptr(fc), _ptr(fl))
+                                 _ptr(cl), _ptr(free_list), int(free_list.size), _ptr(fc),
+                                 _ptr(fl))
     return cl, int(fc[0]), fl
 
 

@@ -20,7 +20,9 @@
  *          walking the accepted path.
  *
  * Readings where the pages leave a step open (each is a plain reading, stated once here):
- *   R1  temperature is applied as softmax(l/T); T = 0 means greedy (one-hot argmax).
+ *   R1  temperature is applied as softmax(l/T); T = 0 means greedy (one-hot argmax). Other
+ *       than 0, T must lie in [2^-126, 2^126], where 1/T is a normal binary32; a negative,
+ *       NaN, infinite, subnormal or larger T is invalid (flag BAD_PARAM).
  *   R2  temperature first, then top-p on the tempered law; the same T and top-p for p and q.
  *   R3  top-p is a value threshold over the logits: t* is the largest logit value whose
  *       cumulative mass (all tokens with logit >= t*) reaches P; every token with logit
@@ -73,7 +75,10 @@
  *       block_size) is released: its id is appended to the free list, sequences in order and
  *       each sequence's blocks in logical order, and its table entry becomes -1. A sequence
  *       with a copied slot outside the table or in an unmapped block, or whose L' needs more
- *       blocks than the table has, is flagged SLOT_OOB and left untouched.
+ *       blocks than the table has, or whose table holds a block id >= num_blocks among the
+ *       blocks the release would free, is flagged SLOT_OOB and left untouched. A released
+ *       block that finds the free list full (free_capacity ids) stays in the table and the
+ *       sequence is flagged FREE_FULL (a pool that keeps every id once never gets there).
  *   R23 n-gram prompt lookup ([KV] variants, n-gram and prefix matching; [LI] §10.6.3,
  *       model-free drafts and the ngram method's prompt_lookup_min / prompt_lookup_max):
  *       the suffix of length n of the history h[0..len) is looked up among the earlier
@@ -87,6 +92,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <float.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -105,6 +111,7 @@
 #define OF_BAD_PARAM 128
 #define OF_EOS 256
 #define OF_LEN_CAP 512
+#define OF_FREE_FULL 1024
 
 #define PURPOSE_ACCEPT 0u
 #define PURPOSE_RESIDUAL 1u
@@ -334,7 +341,8 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
                         const float* uniform_override, int32_t* out_tokens,
                         int32_t* num_accepted, int32_t* num_emitted, int32_t* committed_len_out,
                         int32_t* seq_flags, double* probe_rows, double* probe_seq,
-                        double* margin_out, int nthreads) {
+                        double* margin_out, double* row_margin, double* draw_margin,
+                        int nthreads) {
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -370,14 +378,18 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
       for (int k = 0; k < g; ++k) {
         double* pr = probe_rows ? probe_rows + 3 * (size_t)(drow0 + k) : NULL;
         if (pr) pr[0] = pr[1] = pr[2] = NAN;
+        if (row_margin) row_margin[2 * (size_t)(drow0 + k)] = row_margin[2 * (size_t)(drow0 + k) + 1] = INFINITY;
       }
+      if (draw_margin) draw_margin[2 * b] = draw_margin[2 * b + 1] = INFINITY;
       int bad = 0;
       for (int k = 0; k < g; ++k) {
         int d = draft_tokens[drow0 + k];
         if (d < 0 || d >= V) bad = 1;
       }
       if (bad) flags |= OF_BAD_TOKEN;
-      if (!(T >= 0.0) || !(P > 0.0 && P <= 1.0)) {
+      /* T: 0 (greedy) or 2^-126 <= T <= 2^126, where 1/T is a normal binary32 */
+      if (!(T == 0.0 || (T >= (double)FLT_MIN && T <= ldexp(1.0, 126))) ||
+          !(P > 0.0 && P <= 1.0)) {
         flags |= OF_BAD_PARAM;
         bad = 1;
       }
@@ -417,10 +429,12 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         }
         oracle_dist(trow, V, T, P, K, p, scratch, &ip);
         if (ip.topp_margin < margin) margin = ip.topp_margin;
+        double cut_margin = ip.topp_margin; /* the top-p cuts of this position's rows */
         if (draft) {
           const uint16_t* drow = draft + (size_t)(drow0 + k - 1) * row_stride;
           oracle_dist(drow, V, T, P, K, q, scratch, &iq);
           if (iq.topp_margin < margin) margin = iq.topp_margin;
+          if (iq.topp_margin < cut_margin) cut_margin = iq.topp_margin;
         } else { /* reading R24: the point mass at the draft token */
           for (int v = 0; v < V; ++v) q[v] = 0.0;
           q[d] = 1.0;
@@ -435,6 +449,10 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
         if (pr) { pr[0] = p[d]; pr[1] = q[d]; pr[2] = info[0]; }
         double am = fabs(u_acc - info[0]);
         if (am < margin) margin = am;
+        if (row_margin) {
+          row_margin[2 * (size_t)(drow0 + k - 1)] = am;
+          row_margin[2 * (size_t)(drow0 + k - 1) + 1] = cut_margin;
+        }
         if (acc) {
           n_acc = k;
           if (d == eos) { flags |= OF_EOS; stopped = 1; drawn = 0; break; }
@@ -442,6 +460,7 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
           continue;
         }
         dmargin = info[3];
+        if (draw_margin) draw_margin[2 * b + 1] = info[3];
         y = tok;
         R_out = info[1];
         py_out = info[2];
@@ -464,6 +483,10 @@ int oracle_verify_chain(int B, int V, int row_stride, const uint16_t* target,
           double sm;
           y = oracle_sample(p, V, u, &sm);
           if (sm < dmargin) dmargin = sm;
+          if (draw_margin) {
+            draw_margin[2 * b] = ip.topp_margin;
+            draw_margin[2 * b + 1] = sm;
+          }
           py_out = p[y];
         }
         n_acc = g;
@@ -769,7 +792,10 @@ int oracle_kv_commit_paged(int B, int num_layers, int num_kv_heads, int head_dim
                            int64_t slot_stride, int64_t head_stride, int lead_slots,
                            int max_depth, int32_t* block_table, const int32_t* path_nodes,
                            const int32_t* path_len, int32_t* committed_len, int32_t* free_list,
-                           int32_t* free_count, int32_t* seq_flags) {
+                           int free_capacity, int32_t* free_count, int32_t* seq_flags) {
+  /* the count of ids already listed, taken within [0, free_capacity] */
+  if (free_count[0] < 0) free_count[0] = 0;
+  if (free_count[0] > free_capacity) free_count[0] = free_capacity;
   for (int b = 0; b < B; ++b) {
     int32_t* bt = block_table + (size_t)b * max_blocks;
     const int L = committed_len[b], D = path_len[b];
@@ -791,6 +817,10 @@ int oracle_kv_commit_paged(int B, int num_layers, int num_kv_heads, int head_dim
         if (pb < 0 || pb >= num_blocks) { ok = 0; break; }
       }
     }
+    /* every block the release would free must be a valid id */
+    const int need = ok ? (int)((new_len + block_size - 1) / block_size) : max_blocks;
+    for (int lb = need; ok && lb < max_blocks; ++lb)
+      if (bt[lb] >= num_blocks) ok = 0;
     if (!ok) {
       if (seq_flags) seq_flags[b] |= OF_SLOT_OOB;
       continue;
@@ -809,9 +839,12 @@ int oracle_kv_commit_paged(int B, int num_layers, int num_kv_heads, int head_dim
         }
     }
     committed_len[b] = (int32_t)new_len;
-    const int need = (int)((new_len + block_size - 1) / block_size);
     for (int lb = need; lb < max_blocks; ++lb) {
       if (bt[lb] < 0) continue;
+      if (free_count[0] >= free_capacity) { /* no room: the block stays in the table */
+        if (seq_flags) seq_flags[b] |= OF_FREE_FULL;
+        continue;
+      }
       free_list[free_count[0]++] = bt[lb];
       bt[lb] = -1;
     }

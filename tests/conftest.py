@@ -17,3 +17,21 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Writes the parity report (near-boundary counts per comparison) when SPECV_PARITY_REPORT
+    names a file."""
+    path = os.environ.get("SPECV_PARITY_REPORT")
+    if not path:
+        return
+    try:
+        import harness
+    except ImportError:
+        return
+    if not harness.REPORT:
+        return
+    import json
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(dict(exitstatus=int(exitstatus), entries=harness.REPORT), f, indent=1)

@@ -3,9 +3,11 @@ copies of host inputs, run the oracle on the same host inputs, compare.
 
 Parity rule (from the benchmark spec of the verification step): greedy and tree results are
 bit-exact; stochastic results match in tokens, accepted lengths and committed lengths, with
-probabilities within 1e-5 absolute, except in a sequence where some decision on its path
-has its uniform (or, for top-p, the kept mass) within 1e-5 of the decision boundary (the
-oracle reports that distance); such sequences are counted and returned, not compared.
+probabilities within 1e-5 absolute, except where a decision's uniform (or, for top-p, the
+kept mass) lies within 1e-5 of its boundary (the oracle reports that distance per decision).
+Such a sequence is compared up to that decision and not after it; it is counted by the kind
+of its first near-boundary decision (acceptance test, top-p cut of a tested row, the final
+draw, the top-p cut of the bonus row), and the counts go to the session's parity report.
 """
 from __future__ import annotations
 
@@ -112,31 +114,77 @@ def _close(a, b, tol):
     return bool(np.all(both_nan | (np.abs(a - b) <= tol)))
 
 
+class Boundary:
+    """Near-boundary sequences of one comparison, by the kind of their first such decision:
+    ``acceptance`` (|u - a| < 1e-5 at a tested position), ``topp`` (the top-p cut of a tested
+    position's p or q row), ``draw`` (the final residual/bonus draw's CDF step, or R < 1e-5),
+    ``draw_topp`` (the bonus row's top-p cut)."""
+
+    KINDS = ("acceptance", "topp", "draw", "draw_topp")
+
+    def __init__(self):
+        for k in self.KINDS:
+            setattr(self, k, [])
+
+    @property
+    def before_draw(self):
+        """Sequences whose first near-boundary decision precedes the final draw."""
+        return self.acceptance + self.topp
+
+    @property
+    def at_draw(self):
+        return self.draw + self.draw_topp
+
+    def counts(self):
+        return {k: len(getattr(self, k)) for k in self.KINDS}
+
+    def __iter__(self):  # (before the draw, at the draw), as two lists
+        return iter((self.before_draw, self.at_draw))
+
+
 def compare_chain(x, o, g, exact=False, probes=True):
-    """Asserts parity sequence by sequence. A sequence whose acceptance tests (or the top-p
-    cuts they use) lie within 1e-5 of a boundary is not compared; one whose final draw does
-    is compared up to the draw (accepted count, committed length, accepted tokens, per-row
-    probabilities). Returns (acceptance-boundary sequences, draw-boundary sequences)."""
+    """Asserts parity sequence by sequence and returns the near-boundary sequences
+    (:class:`Boundary`).
+
+    A sequence whose first near-boundary decision is the acceptance test or a top-p cut at
+    draft position kb is compared up to it: the kb - 1 accepted drafts (both sides accept
+    them; nothing before kb is uncertain), their tokens and per-row probabilities, and at kb
+    itself the probabilities when only the acceptance test is uncertain (the law is not).
+    One whose first near-boundary decision is the final draw is compared up to the draw:
+    accepted count, committed length, accepted tokens, per-row probabilities."""
     cu = x["cu_gamma"]
     Bn = len(cu) - 1
-    acc_bnd, draw_bnd = [], []
+    bnd = Boundary()
+    tol = 0.0 if exact else PROB_TOL
     for b in range(Bn):
         m_acc, m_all = (np.inf, np.inf) if exact else o["margin"][b]
+        n = int(o["num_accepted"][b])
+        t0, d0 = int(cu[b]) + b, int(cu[b])
+        gb = int(cu[b + 1] - cu[b])
+        ctx = f"seq {b}: oracle n={n} flags={o['seq_flags'][b]} gpu n={g['num_accepted'][b]}"
         if m_acc < MARGIN:
-            acc_bnd.append(b)
+            rm = o["row_margin"][d0:d0 + gb]
+            near = np.flatnonzero(rm.min(axis=1) < MARGIN)
+            assert near.size, ctx  # the sequence margin comes from one of its positions
+            kb = int(near[0])  # 0-based: positions 0..kb-1 are certain accepts
+            law_ok = rm[kb, 1] >= MARGIN
+            (bnd.acceptance if law_ok else bnd.topp).append(b)
+            assert g["num_accepted"][b] >= kb, ctx
+            assert np.array_equal(g["out_tokens"][t0:t0 + kb], o["out_tokens"][t0:t0 + kb]), ctx
+            if probes and g["probe_rows"] is not None:
+                m = kb + 1 if law_ok else kb
+                assert _close(g["probe_rows"][d0:d0 + m], o["probe_rows"][d0:d0 + m], tol), ctx
             continue
         full = m_all >= MARGIN
         if not full:
-            draw_bnd.append(b)
-        n = int(o["num_accepted"][b])
-        ctx = f"seq {b}: oracle n={n} flags={o['seq_flags'][b]} gpu n={g['num_accepted'][b]}"
+            dm = o["draw_margin"][b]
+            (bnd.draw_topp if dm[0] < MARGIN else bnd.draw).append(b)
         assert g["num_accepted"][b] == n, ctx
         assert g["committed_len"][b] == o["committed_len"][b], ctx
         ign = B.FLAG_TOPP_SLOW | (0 if full else B.FLAG_RESID_FALLBACK)
         assert (g["seq_flags"][b] & ~ign) == (o["seq_flags"][b] & ~ign), ctx
         if o["seq_flags"][b] & (B.FLAG_BAD_TOKEN | B.FLAG_BAD_PARAM):
             continue
-        t0 = int(cu[b]) + b
         ne = int(o["num_emitted"][b])
         drawn = ne == n + 1  # no early stop inside the accepted drafts
         if full:
@@ -144,15 +192,25 @@ def compare_chain(x, o, g, exact=False, probes=True):
         m = ne if full else n
         assert np.array_equal(g["out_tokens"][t0:t0 + m], o["out_tokens"][t0:t0 + m]), ctx
         if probes and g["probe_rows"] is not None:
-            gb = int(cu[b + 1] - cu[b])
             tested = min(n + 1, gb) if drawn else n
-            d0 = int(cu[b])
-            tol = 0.0 if exact else PROB_TOL
             assert _close(g["probe_rows"][d0:d0 + tested], o["probe_rows"][d0:d0 + tested],
                           tol), ctx
             if full:
                 assert _close(g["probe_seq"][b], o["probe_seq"][b], tol), ctx
-    return acc_bnd, draw_bnd
+    return bnd
+
+
+# Parity report of the session: one entry per comparison, written by conftest at the end of
+# the session to the file named by SPECV_PARITY_REPORT (if set).
+REPORT = []
+
+
+def record(label, sequences, kind, counts, **extra):
+    entry = dict(label=label, sequences=int(sequences), kind=kind,
+                 boundary={k: int(v) for k, v in counts.items()})
+    entry.update(extra)
+    REPORT.append(entry)
+    say(f"[parity] {label}: {sequences} sequences, near-boundary {entry['boundary']}")
 
 
 def expected_boundary(o, frac_slack=5.0):
@@ -174,12 +232,12 @@ def check_chain(x, seed=1234, override=None, lead=1, tokens=None, exact=False, l
     o = run_oracle_chain(x, tokens, seed, override, lead)
     say(f"[chain] {label}: oracle done; launching GPU")
     g = run_gpu_chain(x, tokens, seed, override, lead)
-    acc_bnd, draw_bnd = compare_chain(x, o, g, exact=exact)
+    bnd = compare_chain(x, o, g, exact=exact)
     Bn = len(x["cu_gamma"]) - 1
-    say(f"[chain] {label}: parity ok; boundary sequences: acceptance {len(acc_bnd)}, "
-        f"final draw {len(draw_bnd)} of {Bn}")
+    record(label, Bn, "chain greedy" if exact else "chain", bnd.counts(),
+           draft_rows=int(x["cu_gamma"][-1]), vocab=int(x["vocab"]))
     # acceptance tests sit within 1e-5 of their boundary with probability ~2e-5 per test
-    assert len(acc_bnd) <= max(2, max_acc_boundary_frac * Bn)
+    assert len(bnd.before_draw) <= max(2, max_acc_boundary_frac * Bn)
     if override is None and not exact:
-        assert len(draw_bnd) <= expected_boundary(o)
-    return o, g, (acc_bnd, draw_bnd)
+        assert len(bnd.at_draw) <= expected_boundary(o)
+    return o, g, bnd

@@ -10,7 +10,7 @@ import oracle
 from draft_verification_03_amd import binding as B
 from draft_verification_03_amd import workloads as W
 
-from harness import dev, say
+from harness import dev, record, say
 from test_oracle_pins_paged import _paged_case
 
 pytestmark = pytest.mark.gpu
@@ -139,8 +139,9 @@ def test_paged_c4_full_size():
     """The tree workload's cache paged in 16-slot blocks: 32 layers x K,V x 8192 blocks x 16
     x 8 heads x 128 bf16 (17.2 GB), 64 shuffled blocks per sequence, every element a hash of
     (layer, K/V, block, offset, head, dim). The oracle's accepted tree paths are committed:
-    every moved row holds its source's hash, a sample of other rows is unchanged, and the
-    tables, free list and lengths equal the oracle's (run on a one-element-wide cache)."""
+    every element of every pool equals the hash of its source (a moved row's source row, else
+    its own), bit for bit, and the tables, free list and lengths equal the oracle's (run on a
+    one-element-wide cache)."""
     x = W.tree_inputs()
     o = oracle.verify_tree(x["logits"], x["parent"], x["node_row"], x["node_token"],
                            x["rows_per_seq"], x["max_depth"], x["num_nodes"], vocab=x["vocab"])
@@ -184,26 +185,79 @@ def test_paged_c4_full_size():
     assert np.array_equal(Lt.cpu().numpy(), cl_o) and np.array_equal(fl.cpu().numpy(), fl_o)
     assert int(fct.cpu()[0]) == fc_o and np.array_equal(ft.cpu().numpy()[:fc_o], free_o[:fc_o])
     assert np.array_equal(btt.cpu().numpy(), bt_o)
-    # expected source (physical block, offset) of every committed logical slot
-    src = np.tile(np.arange(S), (Bn, 1))
+    # expected source (physical block, offset) of every physical row: a moved row's source
+    # through the table (the copy reads before the release), every other row itself
+    spb = np.tile(np.arange(nb)[:, None], (1, bs))
+    soff = np.tile(np.arange(bs)[None, :], (nb, 1))
+    moved = 0
     for b in range(Bn):
         for j in range(1, plen[b] + 1):
-            src[b, L[b] + j] = L[b] + paths[b, j - 1]
-    moved = src != np.arange(S)[None]
-    sample = moved | (rng.random((Bn, S)) < 0.02)
-    sample &= np.arange(S)[None] < cl_o[:, None]  # committed slots (their blocks stay mapped)
-    bi, si = np.nonzero(sample)
-    dst_pb = torch.from_numpy(bt[bi, si // bs]).cuda()
-    dst_off = torch.from_numpy(si % bs).cuda()
-    s2 = src[bi, si]
-    src_pb = torch.from_numpy(bt[bi, s2 // bs]).cuda().view(-1, 1, 1)
-    src_off = torch.from_numpy(s2 % bs).cuda().view(-1, 1, 1)
-    hh2, dd2 = hh.view(1, H, 1), dd.view(1, 1, Dh)
-    say(f"[paged] c4 full size: checking {len(bi)} rows, {int(moved.sum())} moved")
+            d, sr = L[b] + j, L[b] + paths[b, j - 1]
+            if d != sr:
+                spb[bt[b, d // bs], d % bs] = bt[b, sr // bs]
+                soff[bt[b, d // bs], d % bs] = sr % bs
+                moved += 1
+    spt = torch.from_numpy(spb).cuda().view(nb, bs, 1, 1)
+    sot = torch.from_numpy(soff).cuda().view(nb, bs, 1, 1)
+    say(f"[paged] c4 full size: checking all {nb * bs} rows of the {2 * NL} pools, {moved} moved")
     for l in range(NL):
         for kv in range(2):
-            got = caches[l][kv][dst_pb, dst_off].to(torch.int64) & 0xFFFF
-            want = W.kv_hash(l, kv, src_pb, src_off, hh2, dd2)
+            got = caches[l][kv].to(torch.int64) & 0xFFFF
+            want = W.kv_hash(l, kv, spt, sot, hh, dd)
             assert torch.equal(got, want), (l, kv)
+            del got, want
+    record("paged KV commit, 32 layers x K,V x 8192 blocks x 16 x 8 x 128 bf16", Bn,
+           "paged kv bit-exact", {}, rows_checked=nb * bs * 2 * NL, rows_moved=moved * 2 * NL,
+           blocks_released=int(fc_o))
     del caches
     torch.cuda.empty_cache()
+
+
+def test_paged_invalid_released_id_is_flagged():
+    """A table entry >= num_blocks among the blocks the release would free flags the
+    sequence SLOT_OOB (nothing moves, table and length stay); negative entries there are
+    unmapped."""
+    nb, bs, H, D = 8, 4, 1, 8
+    rng = np.random.default_rng(11)
+    x = dict(k=[rng.integers(0, 65536, size=(nb, bs, H, D)).astype(np.uint16)],
+             v=[rng.integers(0, 65536, size=(nb, bs, H, D)).astype(np.uint16)],
+             bt=np.array([[0, 1, 99, -1], [2, 3, -1, -5]], np.int32),
+             L=np.array([1, 1], np.int32), paths=np.array([[2, 3, 4], [3, 2, 1]], np.int32),
+             plen=np.array([3, 3], np.int32), lead=1, depth=3, bs=bs)
+    free = np.full(nb, -1, np.int32)
+    free[:4] = [4, 5, 6, 7]
+    x.update(free=free, free_count=4)
+    g = check(x, "invalid released id")
+    assert list(g["flags"]) == [B.FLAG_SLOT_OOB, 0]
+
+
+def test_paged_full_free_list_keeps_blocks():
+    """A free list with one slot left (a pool that lists ids twice): the first released
+    block fits, the others stay in their tables and flag FREE_FULL; lengths still move."""
+    nb, bs, H, D = 6, 2, 1, 8
+    k = [np.arange(nb * bs * H * D, dtype=np.uint16).reshape(nb, bs, H, D)]
+    x = dict(k=k, v=[k[0].copy()], bt=np.array([[0, 1, 2], [3, 4, 5]], np.int32),
+             L=np.array([0, 0], np.int32), paths=np.array([[1], [1]], np.int32),
+             plen=np.array([1, 1], np.int32), lead=1, depth=1, bs=bs)
+    free = np.array([9, 9, 9, 9, 9, -1], np.int32)
+    x.update(free=free, free_count=5)
+    g = check(x, "full free list")
+    assert list(g["flags"]) == [B.FLAG_FREE_FULL, B.FLAG_FREE_FULL] and g["fc"] == 6
+
+
+def test_paged_table_rows_beyond_the_lds_tile():
+    """max_blocks = 9000 one-slot blocks per sequence (a table row larger than the release
+    tile's LDS): path checks read the table from memory and each row's release spans two
+    scan chunks."""
+    mb, bs, H, D, Bn = 9000, 1, 1, 8, 3
+    nb = Bn * mb
+    rng = np.random.default_rng(31)
+    bt = rng.permutation(nb).astype(np.int32).reshape(Bn, mb)
+    bt[1, 8000:] = -1  # partly mapped
+    k = [rng.integers(0, 65536, size=(nb, bs, H, D)).astype(np.uint16)]
+    x = dict(k=k, v=[k[0][::-1].copy()], bt=bt, L=np.array([40, 8990 - 9, 7], np.int32),
+             paths=np.array([[3, 5, 6], [1, 2, 3], [2, 4, 3]], np.int32),
+             plen=np.array([3, 3, 2], np.int32), lead=1, depth=3, bs=bs)
+    x.update(free=np.full(nb, -1, np.int32), free_count=0)
+    g = check(x, "table rows of 9000 blocks")
+    assert not g["flags"].any() and g["fc"] > 9000

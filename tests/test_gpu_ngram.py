@@ -9,7 +9,7 @@ import oracle
 from draft_verification_03_amd import binding as B
 from draft_verification_03_amd import workloads as W
 
-from harness import dev, say
+from harness import dev, record, say
 from test_oracle_pins_ngram import CASES
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +68,8 @@ def test_workload_full_size():
     x = W.ngram_inputs()
     gpu, o = check(x["tokens"], x["hist_len"], 1, 4, 8, "workload B=256, 1024..8192 tokens")
     say(f"[ngram] drafted for {(o['num_drafts'] > 0).sum()} of {len(o['num_drafts'])}")
+    record("n-gram lookup B=256, 1024..8192 tokens, n in [1,4], gamma=8", 256, "ngram bit-exact",
+           {}, drafted=int((o["num_drafts"] > 0).sum()))
     assert (o["num_drafts"] > 0).sum() > 50
 
 

@@ -4,9 +4,9 @@
 
 Tokens, parents, expansions, rows, positions and mask bits are compared exactly; path
 log-probabilities within LOGP_TOL. The choice of the next step's expanded nodes is a
-floating-point decision (path log-probabilities, decided in fp32 by the kernel): a sequence
-whose oracle margin between neighbouring ranked candidates falls below LOGP_TOL at some step
-is counted and compared only up to that step.
+floating-point decision (the oracle ranks fp64 path log-probabilities, the kernel fp32 ones):
+a sequence whose oracle margin between neighbouring ranked candidates falls below LOGP_TOL at
+some step is counted, reported, and compared only up to that step.
 
 LOGP_TOL: the kernel's log-probability is (l - M) - log(Z) per step, summed over at most
 64 steps in fp32; (l - M) is exact, Z is an fp32 sum of at most 2^19 terms of relative error
@@ -21,7 +21,7 @@ import oracle
 from draft_verification_03_amd import binding as B
 from draft_verification_03_amd import workloads as W
 
-from harness import dev, say
+from harness import dev, record, say
 
 pytestmark = pytest.mark.gpu
 
@@ -124,7 +124,8 @@ def check(x, label, tree_stride=None, expand_stride=None):
     g = run_gpu(x, tree_stride, expand_stride)
     o = run_oracle(x, tree_stride)
     nb = compare(x, o, g, label)
-    say(f"[tree-draft] {label}: sequences with a near-boundary expansion: {nb}")
+    record(f"tree drafting {label}", x["batch"], "tree drafting", {"expansion": nb},
+           vocab=int(x["vocab"]))
     assert nb <= max(1, x["batch"] // 50)
     return o, g
 

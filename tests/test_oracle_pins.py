@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from draft_verification_03_amd import workloads as W
+from markov_stream import oracle_proposer, round_rows, run_stream, transition_freq
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
 TREE = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
@@ -299,46 +300,21 @@ def test_greedy_equals_argmax_decoding(orc):
 
 
 def _markov_stream(orc, T, D, k, n_tokens, seed, seed_draft):
-    """Speculative stream over Markov tables fed to the oracle as bf16(ln p) rows: the
-    drafter draws d_1..d_k one by one from the draft rows (gamma = 0 oracle calls), the
-    oracle verifies the round, the stream continues from its last emitted token."""
+    """The oracle's speculative stream over Markov tables given as bf16(ln p) rows
+    (tests/markov_stream.py drives the rounds)."""
     tl = W.log_rows_bf16(np.asarray(T))
     dl = W.log_rows_bf16(np.asarray(D))
-    out = []
-    calls = acc_total = 0
-    cur = 0
     one = np.ones(1, np.float32)
-    while len(out) < n_tokens:
-        pos = len(out)
-        drafts = []
-        prev = cur
-        for j in range(k):
-            t = orc.draw_tokens(dl[prev:prev + 1], one, None, seed_draft,
-                                np.zeros(1, np.uint32), np.array([pos + j], np.int32), vocab=4)
-            drafts.append(int(t[0]))
-            prev = drafts[-1]
-        ctx = [cur] + drafts
-        tgt = np.stack([tl[c] for c in ctx])
-        drf = np.stack([dl[c] for c in ctx[:k]])
-        r = orc.verify_chain_v(tgt, drf, np.array([0, k], np.int32),
-                               np.array(drafts, np.int32), one, None, np.zeros(1, np.uint32),
-                               np.array([pos], np.int32), seed=seed, vocab=4)
-        n = int(r["num_accepted"][0])
-        em = list(r["out_tokens"][:n + 1])
-        calls += 1
-        acc_total += n
-        out.extend(em[:n_tokens - len(out)])
-        cur = out[-1]
-    return np.array(out), calls, acc_total
 
+    def verify(last, drafts, pos):
+        tgt, drf = round_rows(tl, dl, last, drafts)
+        r = orc.verify_chain_v(tgt, drf, np.array([0, k], np.int32), np.array(drafts, np.int32),
+                               one, None, np.zeros(1, np.uint32), np.array([pos], np.int32),
+                               seed=seed, vocab=4)
+        return r["out_tokens"][:int(r["num_emitted"][0])]
 
-def _freq(tokens, V=4):
-    c = np.zeros((V, V))
-    prev = 0
-    for t in tokens:
-        c[prev, t] += 1
-        prev = t
-    return c / c.sum(axis=1, keepdims=True)
+    toks, st = run_stream(oracle_proposer(orc, dl, k, seed_draft), verify, n_tokens)
+    return toks, st.rounds, st.accepted
 
 
 def test_markov_experiment(orc):
@@ -351,7 +327,7 @@ def test_markov_experiment(orc):
     g = GOLD["markov_experiment"]
     T, D = np.array(g["target"]), np.array(g["draft"])
     toks, calls, acc = _markov_stream(orc, T, D, g["k"], g["tokens"], seed=303, seed_draft=909)
-    f = _freq(toks)
+    f = transition_freq(toks)
     assert np.abs(f - T).max() < g["max_error"]
     tq = [list(orc.dist(W.log_rows_bf16(T)[i][:4], 1.0)[0]) for i in range(4)]
     dq = [list(orc.dist(W.log_rows_bf16(D)[i][:4], 1.0)[0]) for i in range(4)]
@@ -367,7 +343,7 @@ def test_markov_dirichlet_tables(orc):
     """The Dirichlet(2) Markov workload: frequencies within 0.02 of its own target table."""
     T, D = W.markov_tables()
     toks, calls, acc = _markov_stream(orc, T, D, 4, 100000, seed=11, seed_draft=12)
-    assert np.abs(_freq(toks) - T).max() < 0.02
+    assert np.abs(transition_freq(toks) - T).max() < 0.02
 
 
 # ----------------------------------------------------------------------------------------
@@ -551,3 +527,30 @@ def test_chain_edge_cases(orc):
     assert r["num_accepted"][2] == 1  # p(d) > 0 and q(d) = 0: accepted with a = 1
     assert r["seq_flags"][3] & orc.F_Q_ZERO and r["seq_flags"][3] & orc.F_RESID_FALLBACK
     assert r["num_accepted"][3] == 0 and r["probe_seq"][3, 0] == 0.0
+
+
+def test_temperature_outside_binary32_reciprocal_range_is_rejected(orc):
+    """T must be 0 (greedy) or lie in [2^-126, 2^126], where 1/T is a normal binary32:
+    +inf, NaN, a subnormal T, a T above 2^126 and a negative T flag BAD_PARAM and make no
+    progress; both ends of the range are valid laws (reading R1)."""
+    V = 16
+    rng = np.random.default_rng(3)
+    row = W.bf16_bits(rng.standard_normal((4, V)).astype(np.float32))
+    x = dict(target=np.concatenate([row[:2], row[2:]]), draft=row[:2])
+    cu = np.array([0, 1, 2], np.int32)
+    tok = np.array([3, 5], np.int32)
+    fmin = np.float32(np.finfo(np.float32).tiny)
+    for T, bad in ((np.inf, True), (np.nan, True), (np.float32(1e-40), True), (-1.0, True),
+                   (np.float32(3.0e38), True), (fmin, False), (0.0, False),
+                   (np.float32(2.0 ** 126), False)):
+        temp = np.array([T, 1.0], np.float32)
+        r = orc.verify_chain_v(x["target"][:4], x["draft"], cu, tok, temp, None,
+                               np.arange(2, dtype=np.uint32), np.array([7, 9], np.int32),
+                               seed=5, vocab=V)
+        assert bool(r["seq_flags"][0] & orc.F_BAD_PARAM) == bad, T
+        assert not r["seq_flags"][1] & orc.F_BAD_PARAM
+        if bad:
+            assert r["num_accepted"][0] == 0 and r["num_emitted"][0] == 0
+            assert r["committed_len"][0] == 7
+        else:
+            assert r["num_emitted"][0] >= 1 and r["committed_len"][0] >= 8

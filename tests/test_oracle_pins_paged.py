@@ -171,3 +171,50 @@ def test_rejected_inputs_leave_the_sequence_untouched(orc):
     # seq 0, 2, 3's blocks keep their bytes
     for p in [0, 1, 6, 7, 8, 9, 10, 11]:
         assert np.array_equal(k[0][p], k0[p]) and np.array_equal(v[0][p], v0[p])
+
+
+def test_released_block_ids_must_be_valid(orc):
+    """A table entry among the blocks the release would free that is not a valid block id
+    (>= num_blocks) makes the sequence SLOT_OOB: nothing moves, its table and length stay;
+    a negative entry there is an unmapped block (nothing to release)."""
+    nb, bs, H, D = 8, 4, 1, 8
+    rng = np.random.default_rng(11)
+    k = [rng.integers(0, 65536, size=(nb, bs, H, D)).astype(np.uint16)]
+    v = [rng.integers(0, 65536, size=(nb, bs, H, D)).astype(np.uint16)]
+    bt = np.array([[0, 1, 99, -1],   # L' = 5: block 2 (id 99) would be released: flagged
+                   [2, 3, -1, -5]],  # L' = 5: entries 2, 3 unmapped: nothing released
+                  np.int32)
+    L = np.array([1, 1], np.int32)
+    paths = np.array([[2, 3, 4], [3, 2, 1]], np.int32)
+    plen = np.array([3, 3], np.int32)
+    free = np.full(nb, -1, np.int32)
+    free[:4] = [4, 5, 6, 7]
+    bt0, k0 = bt.copy(), k[0].copy()
+    cl, fc, fl = orc.kv_commit_paged(k, v, bt, paths, plen, L, free, 4, 1, 3)
+    assert list(fl) == [orc.F_SLOT_OOB, 0] and list(cl) == [1, 5] and fc == 4
+    assert np.array_equal(bt, bt0)
+    for p in (0, 1):  # sequence 0's blocks keep their bytes
+        assert np.array_equal(k[0][p], k0[p])
+    # sequence 1 (base 1): slot 4 -> slot 2, slot 3 stays, then slot 2 -> slot 4, in order;
+    # block id 2 holds slots 0..3 and block id 3 slots 4..7
+    assert np.array_equal(k[0][2][2], k0[3][0]) and np.array_equal(k[0][3][0], k0[3][0])
+
+
+def test_full_free_list_keeps_the_block_in_the_table(orc):
+    """A released block that finds the free list at its capacity stays in the table and the
+    sequence is flagged FREE_FULL; the length and the copy are done, and blocks that fit are
+    released as usual (sequences in order, blocks in logical order)."""
+    nb, bs, H, D = 6, 2, 1, 8
+    k = [np.arange(nb * bs * H * D, dtype=np.uint16).reshape(nb, bs, H, D)]
+    v = [k[0].copy()]
+    bt = np.array([[0, 1, 2], [3, 4, 5]], np.int32)
+    L = np.array([0, 0], np.int32)
+    paths = np.array([[1], [1]], np.int32)
+    plen = np.array([1, 1], np.int32)
+    free = np.full(3, -1, np.int32)  # capacity 3, one id already listed
+    free[0] = 9
+    cl, fc, fl = orc.kv_commit_paged(k, v, bt, paths, plen, L, free, 1, 1, 1)
+    # L' = 2: each sequence keeps block 0 and would release blocks 1, 2
+    assert list(cl) == [2, 2] and fc == 3 and list(free) == [9, 1, 2]
+    assert list(fl) == [0, orc.F_FREE_FULL]
+    assert list(bt[0]) == [0, -1, -1] and list(bt[1]) == [3, 4, 5]
