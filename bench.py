@@ -16,6 +16,7 @@ bounded sample of the same workload as a reported baseline.
   python bench.py --workload ngram       # the n-gram prompt lookup instead
   python bench.py --workload tree        # greedy tree verify + KV commit instead
   python bench.py --workload c2|c5       # the other chain workloads (c3 is the default)
+  python bench.py --workload c3_no_top_p|c3_greedy|c3_top_k_50   # c3 variants
   python bench.py --workload markov      # the vocab-4 Markov rounds (launch-bound)
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
@@ -86,14 +87,17 @@ def algorithmic_bytes(x) -> dict:
     """Bytes the verification must move at least once, per call.
 
     The row kernel reads every logits row once: per draft position its p row and its q row
-    (2 * V * 2 B) plus the draft token (4 B), and per sequence the bonus row p_{gamma+1}
-    (V * 2 B). The call adds the outputs (tokens, accepted counts, committed lengths)."""
+    (2 * V * 2 B; a greedy sequence's q rows are not read) plus the draft token (4 B), and per
+    sequence the bonus row p_{gamma+1} (V * 2 B). The call adds the outputs (tokens,
+    accepted counts, committed lengths)."""
     import numpy as np
     cu = x["cu_gamma"]
     B = len(cu) - 1
     nd = int(cu[-1])
     V = x["vocab"]
-    row_pass = (2 * nd + B) * V * 2 + nd * 4
+    b_of = np.repeat(np.arange(B), np.diff(cu))
+    nq = int((x["temperature"][b_of] != 0).sum())  # greedy positions read no q row
+    row_pass = (nd + nq + B) * V * 2 + nd * 4
     outputs = (nd + B) * 4 + B * 4 * 2
     return dict(row_pass=row_pass, call=row_pass + outputs, rows=int(np.sum(np.diff(cu) + 1)))
 
@@ -122,19 +126,21 @@ def cpu_baseline(x, n_seq, min_seconds=10.0):
     sub.update(target=x["target"][:nd + n_seq], draft=x["draft"][:nd], cu_gamma=cu,
                temperature=x["temperature"][:n_seq],
                top_p=None if x["top_p"] is None else x["top_p"][:n_seq],
-               seq_id=x["seq_id"][:n_seq], committed_len=x["committed_len"][:n_seq])
+               seq_id=x["seq_id"][:n_seq], committed_len=x["committed_len"][:n_seq],
+               top_k=None if x.get("top_k") is None else x["top_k"][:n_seq])
     b_of = np.repeat(np.arange(n_seq), np.diff(cu))
     tok = oracle.draw_tokens(sub["draft"], sub["temperature"][b_of],
                              None if sub["top_p"] is None else sub["top_p"][b_of], SEED_DRAFT,
                              sub["seq_id"][b_of], sub["committed_len"][b_of] + np.arange(nd) - cu[b_of],
-                             vocab=x["vocab"])
+                             vocab=x["vocab"],
+                             top_k=None if sub["top_k"] is None else sub["top_k"][b_of])
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     reps, dt = 0, 0.0
     while dt < min_seconds:
         t0 = time.perf_counter()
         oracle.verify_chain_v(sub["target"], sub["draft"], cu, tok, sub["temperature"],
                               sub["top_p"], sub["seq_id"], sub["committed_len"], seed=SEED,
-                              vocab=x["vocab"], nthreads=threads)
+                              vocab=x["vocab"], nthreads=threads, top_k=sub["top_k"])
         dt += time.perf_counter() - t0
         reps += 1
     rows = nd + n_seq
@@ -519,8 +525,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--workload", default="chain",
-                    choices=["chain", "c2", "c3", "c5", "markov", "tree", "tree_draft",
-                             "paged_kv", "ngram"])
+                    choices=["chain", "c2", "c3", "c5", "c3_no_top_p", "c3_greedy",
+                             "c3_top_k_50", "markov", "tree", "tree_draft", "paged_kv",
+                             "ngram"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
@@ -548,7 +555,8 @@ def main():
     chain_bench(args, "c3" if args.workload == "chain" else args.workload)
 
 
-# Chain workloads: what each line reports and how its inputs are held in HBM.
+# Chain workloads: what each line reports and how its inputs are held in HBM. "base" names
+# the configuration the inputs come from and "mod" how a variant changes it.
 CHAIN_LEGS = {
     "c2": dict(sets=16, workload="chain verify B=64 gamma=4 V=32000 bf16 logits, target "
                                  "N(0,2^2), draft = target + N(0,0.5^2), T=1, no top-k/top-p; "
@@ -561,6 +569,14 @@ CHAIN_LEGS = {
                                 "logits, target N(0,2^2), draft noise sigma_b~U[0.3,1.5], "
                                 "T_b~U[0.5,1.2], no top-k/top-p, bonus on full accept, pointer "
                                 "rollback"),
+    "c3_no_top_p": dict(sets=1, base="c3", mod=dict(top_p=None),
+                        workload="the c3 chain workload without top-p (every draw reads its "
+                                 "rows)"),
+    "c3_greedy": dict(sets=1, base="c3", mod=dict(temperature=0.0),
+                      workload="the c3 chain workload at T=0 (greedy: argmax rows, q rows "
+                               "not read)"),
+    "c3_top_k_50": dict(sets=1, base="c3", top_k=50,
+                        workload="the c3 chain workload with top-k 50 ahead of top-p 0.9"),
 }
 
 
@@ -576,8 +592,13 @@ def chain_bench(args, name):
     leg = CHAIN_LEGS[name]
     nsets = leg["sets"]
     log(f"generating the {name} workload ({nsets} input set(s))")
-    xs = [W.chain_inputs(name) if i == 0 else W.chain_inputs(name, seed=W.SEEDS[name] * 1000 + i)
+    base = leg.get("base", name)
+    xs = [W.chain_inputs(base, **leg.get("mod", {})) if i == 0 else
+          W.chain_inputs(base, seed=W.SEEDS[base] * 1000 + i, **leg.get("mod", {}))
           for i in range(nsets)]
+    if "top_k" in leg:
+        for xi in xs:
+            xi["top_k"] = np.full(len(xi["cu_gamma"]) - 1, leg["top_k"], np.int32)
     x = xs[0]
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
         {np.dtype(np.uint16): np.int16, np.dtype(np.uint32): np.int32}.get(a.dtype, a.dtype))).cuda()
@@ -591,9 +612,11 @@ def chain_bench(args, name):
         b_of = np.repeat(np.arange(Bn), np.diff(cu))
         k_of = np.arange(nd) - cu[b_of]
         d_out = torch.empty(nd, dtype=torch.int32, device="cuda")
+        tk = xi.get("top_k")
         da = B.chain_args(target_logits=drf, cu_gamma=dv(np.zeros(nd + 1, np.int32)),
                           temperature=dv(xi["temperature"][b_of]),
                           top_p=None if xi["top_p"] is None else dv(xi["top_p"][b_of]),
+                          top_k=None if tk is None else dv(tk[b_of]),
                           seq_id=dv(xi["seq_id"][b_of]),
                           committed_len=dv((xi["committed_len"][b_of] + k_of).astype(np.int32)),
                           out_tokens=d_out,
@@ -608,6 +631,7 @@ def chain_bench(args, name):
         flags = torch.empty(Bn, dtype=torch.int32, device="cuda")
         a = B.chain_args(target_logits=tgt, draft_logits=drf, cu_gamma=dv(cu), draft_tokens=d_out,
                          temperature=dv(xi["temperature"]), top_p=topp, seq_id=dv(xi["seq_id"]),
+                         top_k=None if tk is None else dv(tk),
                          committed_len=L, out_tokens=out, num_accepted=nacc, seq_flags=flags,
                          seed=SEED, vocab=V, max_gamma=int(np.diff(cu).max()),
                          total_draft_rows=nd, row_stride=xi["stride"])

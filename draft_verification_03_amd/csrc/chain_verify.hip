@@ -50,11 +50,11 @@ constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per
 constexpr int kRowThreads = kRowWgWaves * kWave;
 constexpr int kHist = 512;         // key offsets below the row max resolved by the window search
 // Resolve workgroup shapes (threads, row-pair tiles in flight per wave in the resolve pass):
-// one 1024-thread workgroup per CU while the batch fits the CUs, two 512-thread workgroups
-// per CU beyond (both within 128 VGPRs), so that one sequence's latency-bound decision and
-// scan overlap another's row traffic.
+// one 1024-thread workgroup per CU while the batch fits the CUs, 256-thread workgroups
+// beyond (four per CU at 128 VGPRs), so that the latency-bound decisions and scans of some
+// sequences overlap the row traffic of others.
 constexpr int kResolveWide = 1024, kTilesWide = 4;
-constexpr int kResolveNarrow = 512, kTilesNarrow = 5;
+constexpr int kResolveNarrow = 256, kTilesNarrow = 5;
 constexpr int kResolveMaxWaves = kResolveWide / kWave;
 constexpr int kNumCus = 256;  // compute units of the chip: one wide workgroup each
 constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass (V <= 2^19)
@@ -986,9 +986,11 @@ __device__ __forceinline__ void data_weights(const RowLaw& Lp, const RowLaw& Lq,
 }
 __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, bool residual,
                                             int v, int nvec, int V, float w[8]) {
-  const uint4 z{0u, 0u, 0u, 0u};
-  const uint4 dp = v < nvec ? Lp.row[v] : z;
-  const uint4 dq = (residual && Lq.point < 0 && v < nvec) ? Lq.row[v] : z;
+  // clamped, unconditional 16-byte loads; data_weights gives 0 past the row
+  const int vc = min(v, nvec - 1);
+  const uint4 dp = Lp.row[vc];
+  uint4 dq{0u, 0u, 0u, 0u};
+  if (residual && Lq.point < 0) dq = Lq.row[vc];
   data_weights(Lp, Lq, residual, v, nvec, V, dp, dq, w);
 }
 
@@ -1125,26 +1127,34 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
 // All threads of the workgroup: inverse-CDF draw over a whole row (pair) in token order.
 // Pass 1 stores per-tile sums (a tile = 64 vectors = 512 logits, one coalesced wave load;
 // each wave keeps TI tiles of p and of q in flight); draw_scan finishes.
+// Per-tile sums of a row (pair): each wave takes TI tiles at a time (a tile = 64 vectors =
+// 512 logits, one coalesced wave load per row); tile g -> tile_sum[g]. Returns the last token
+// with positive weight this lane saw (-1: none). A vector past the row loads the row's last
+// vector instead (its weight is zero), so that every load is one unconditional 16-byte load:
+// a load under a per-lane condition compiles to four predicated 4-byte loads.
 template <int NT, int TI>
-__device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq, bool residual,
-                                               int nvec, int V, float u, float* tile_sum,
-                                               int* sh_i, float* sh_f) {
+__device__ __forceinline__ int tile_sums(const RowLaw& Lp, const RowLaw& Lq, bool residual,
+                                         int nvec, int V, float* tile_sum) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int nw = NT / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
+  const bool with_q = residual && Lq.point < 0;
   int last = -1;  // last token with positive weight seen by this lane
-  const uint4 z{0u, 0u, 0u, 0u};
   for (int g0 = wid * TI; g0 < ntiles; g0 += nw * TI) {
     uint4 dp[TI], dq[TI];
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
-      const int v = (g0 + t) * kWave + lane;
-      dp[t] = v < nvec ? Lp.row[v] : z;
-      dq[t] = (residual && Lq.point < 0 && v < nvec) ? Lq.row[v] : z;
+      dp[t] = Lp.row[min((g0 + t) * kWave + lane, nvec - 1)];
+      dq[t] = uint4{0u, 0u, 0u, 0u};
+    }
+    if (with_q) {
+#pragma unroll
+      for (int t = 0; t < TI; ++t) dq[t] = Lq.row[min((g0 + t) * kWave + lane, nvec - 1)];
     }
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
-      const int v = (g0 + t) * kWave + lane;
+      const int v0 = (g0 + t) * kWave + lane;
+      const int v = v0 < nvec ? v0 : nvec;  // data_weights gives 0 past the row
       float w[8];
       data_weights(Lp, Lq, residual, v, nvec, V, dp[t], dq[t], w);
       float ls = 0.0f;
@@ -1157,9 +1167,16 @@ __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq,
       if (lane == 0 && g0 + t < ntiles) tile_sum[g0 + t] = ts;
     }
   }
-  return draw_scan<NT>(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
+  return last;
 }
 
+template <int NT, int TI>
+__device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq, bool residual,
+                                               int nvec, int V, float u, float* tile_sum,
+                                               int* sh_i, float* sh_f) {
+  const int last = tile_sums<NT, TI>(Lp, Lq, residual, nvec, V, tile_sum);
+  return draw_scan<NT>(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
+}
 
 // Per-sequence decision state the resolve step shares through LDS.
 struct SeqDecision {
@@ -1194,6 +1211,77 @@ __device__ __forceinline__ size_t bonus_slot(const ChainParams& P, int b) {
   return 2 * (size_t)P.n_draft + (size_t)b;
 }
 
+// The round's decision for sequence b, by one wave (lane = its lane id): the acceptance tests
+// from the row statistics, the first rejection, the early stop, the flags; the statistics of
+// the rows at the first rejection. Written to sd, and the probes if the call asks for them.
+__device__ __forceinline__ void decide_wave(const ChainParams& P, const SeqInfo& s, bool cu_ok,
+                                            bool stochastic, SeqDecision& sd, int lane) {
+  const bool in_g = cu_ok && lane < s.g;
+  int tok = 0;
+  RowStat sp{}, sq{};
+  if (in_g) {
+    tok = P.tokens[s.d0 + lane];
+    sp = P.stat[(size_t)(s.d0 + lane) * 2];
+    if (stochastic) sq = P.stat[(size_t)(s.d0 + lane) * 2 + 1];
+  }
+  const bool bad_tok = __ballot(in_g && (tok < 0 || tok >= P.V)) != 0;
+  int acc = 1, rflags = 0;
+  if (in_g && !s.bad_param && !bad_tok) {
+    float pd, qd, a;
+    if (s.T == 0.0f) {  // greedy: accept iff the draft is the target argmax
+      acc = tok == sp.argmax ? 1 : 0;
+      pd = (float)acc;
+      qd = NAN;
+      a = (float)acc;
+    } else {
+      pd = sp.wd / sp.z;
+      qd = sq.wd / sq.z;
+      if (qd > 0.0f) {
+        a = fminf(1.0f, pd / qd);
+      } else {
+        a = pd > 0.0f ? 1.0f : 0.0f;
+        rflags |= SPEC_FLAG_Q_ZERO;
+      }
+      const float u = P.ovr ? P.ovr[(size_t)(s.t0 + lane) * 2]
+                            : uniform24(P.seed_lo, P.seed_hi, s.id,
+                                        (uint32_t)(s.L + lane + 1), SPEC_PURPOSE_ACCEPT);
+      acc = (u < a) ? 1 : 0;
+      rflags |= (sp.flags | sq.flags) & SPEC_FLAG_TOPP_SLOW;
+    }
+    if (P.probe_rows) {
+      P.probe_rows[(size_t)(s.d0 + lane) * 3 + 0] = pd;
+      P.probe_rows[(size_t)(s.d0 + lane) * 3 + 1] = qd;
+      P.probe_rows[(size_t)(s.d0 + lane) * 3 + 2] = a;
+    }
+  }
+  const uint64_t rej = __ballot(in_g && acc == 0);
+  int n_acc = rej ? __ffsll((long long)rej) - 1 : s.g;
+  // Early stop ("KV Cache 优化（四）" §5): emission ends after an accepted draft equal to
+  // the EOS id, or once the cap's worth of accepted drafts is out; the round then ends
+  // there, with no later test and no residual or bonus draw.
+  const uint64_t eos_at = __ballot(in_g && s.eos >= 0 && tok == s.eos && lane < n_acc);
+  int stop = eos_at ? __ffsll((long long)eos_at) : 0x7FFFFFFF;  // 1-based position
+  int stop_flag = SPEC_FLAG_EOS;
+  if (s.cap > 0 && s.cap < stop) {
+    stop = s.cap;
+    stop_flag = SPEC_FLAG_LEN_CAP;
+  }
+  const bool early = stop <= n_acc;
+  if (early) n_acc = stop;
+  int f = (lane < (early ? n_acc : min(n_acc + 1, s.g))) ? rflags : 0;  // tested positions
+  for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
+  if (lane == 0) {
+    sd.n_acc = n_acc;
+    sd.drawn = early ? 0 : 1;
+    sd.flags = f | (early ? stop_flag : 0);
+    sd.bad = (bad_tok ? SPEC_FLAG_BAD_TOKEN : 0) | (s.bad_param ? SPEC_FLAG_BAD_PARAM : 0);
+  }
+  if (in_g && lane == n_acc) {  // the first rejected position
+    sd.sp = sp;
+    sd.sq = sq;
+  }
+}
+
 template <int NT, int TI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
 void chain_resolve_kernel(ChainParams P) {
@@ -1223,72 +1311,7 @@ void chain_resolve_kernel(ChainParams P) {
   }
   RowStat sbon{};
   if (!s.bad_param) sbon = P.stat[bonus_slot(P, b)];
-  if (wid == 0) {
-    const bool in_g = cu_ok && lane < s.g;
-    int tok = 0;
-    RowStat sp{}, sq{};
-    if (in_g) {
-      tok = P.tokens[s.d0 + lane];
-      sp = P.stat[(size_t)(s.d0 + lane) * 2];
-      if (stochastic) sq = P.stat[(size_t)(s.d0 + lane) * 2 + 1];
-    }
-    const bool bad_tok = __ballot(in_g && (tok < 0 || tok >= P.V)) != 0;
-    int acc = 1, rflags = 0;
-    if (in_g && !s.bad_param && !bad_tok) {
-      float pd, qd, a;
-      if (s.T == 0.0f) {  // greedy: accept iff the draft is the target argmax
-        acc = tok == sp.argmax ? 1 : 0;
-        pd = (float)acc;
-        qd = NAN;
-        a = (float)acc;
-      } else {
-        pd = sp.wd / sp.z;
-        qd = sq.wd / sq.z;
-        if (qd > 0.0f) {
-          a = fminf(1.0f, pd / qd);
-        } else {
-          a = pd > 0.0f ? 1.0f : 0.0f;
-          rflags |= SPEC_FLAG_Q_ZERO;
-        }
-        const float u = P.ovr ? P.ovr[(size_t)(s.t0 + lane) * 2]
-                              : uniform24(P.seed_lo, P.seed_hi, s.id,
-                                          (uint32_t)(s.L + lane + 1), SPEC_PURPOSE_ACCEPT);
-        acc = (u < a) ? 1 : 0;
-        rflags |= (sp.flags | sq.flags) & SPEC_FLAG_TOPP_SLOW;
-      }
-      if (P.probe_rows) {
-        P.probe_rows[(size_t)(s.d0 + lane) * 3 + 0] = pd;
-        P.probe_rows[(size_t)(s.d0 + lane) * 3 + 1] = qd;
-        P.probe_rows[(size_t)(s.d0 + lane) * 3 + 2] = a;
-      }
-    }
-    const uint64_t rej = __ballot(in_g && acc == 0);
-    int n_acc = rej ? __ffsll((long long)rej) - 1 : s.g;
-    // Early stop ("KV Cache 优化（四）" §5): emission ends after an accepted draft equal to
-    // the EOS id, or once the cap's worth of accepted drafts is out; the round then ends
-    // there, with no later test and no residual or bonus draw.
-    const uint64_t eos_at = __ballot(in_g && s.eos >= 0 && tok == s.eos && lane < n_acc);
-    int stop = eos_at ? __ffsll((long long)eos_at) : 0x7FFFFFFF;  // 1-based position
-    int stop_flag = SPEC_FLAG_EOS;
-    if (s.cap > 0 && s.cap < stop) {
-      stop = s.cap;
-      stop_flag = SPEC_FLAG_LEN_CAP;
-    }
-    const bool early = stop <= n_acc;
-    if (early) n_acc = stop;
-    int f = (lane < (early ? n_acc : min(n_acc + 1, s.g))) ? rflags : 0;  // tested positions
-    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
-    if (lane == 0) {
-      sd.n_acc = n_acc;
-      sd.drawn = early ? 0 : 1;
-      sd.flags = f | (early ? stop_flag : 0);
-      sd.bad = (bad_tok ? SPEC_FLAG_BAD_TOKEN : 0) | (s.bad_param ? SPEC_FLAG_BAD_PARAM : 0);
-    }
-    if (in_g && lane == n_acc) {  // the first rejected position
-      sd.sp = sp;
-      sd.sq = sq;
-    }
-  }
+  if (wid == 0) decide_wave(P, s, cu_ok, stochastic, sd, lane);
   __syncthreads();
   const int n_acc = sd.n_acc;
   int flags = sd.flags;
