@@ -12,7 +12,9 @@
 //     p_{gamma_b+1}. The waves take the row's trips in turn (16-byte loads, two trips in
 //     flight per wave), so the row streams from HBM once as one wide sequential read, and
 //     the hardware hands rows to CUs as they free up:
-//       - per-lane online max / sum of exp2((l - m) * log2(e)/T) (lazy rescaling);
+//       - per trip (4 KB of the row): its max and its sum of exp2((l - max) * log2(e)/T),
+//         each reduced over the wave in a fixed order and kept by trip index, so that the
+//         row's (m, Z), combined in trip order, does not depend on which wave took a trip;
 //       - with top-p: every 8-logit vector whose max is within kCaptureK*T of the best known
 //         lower bound of the row max (the waves share theirs through LDS) is copied to LDS
 //         (a superset of the final window m - kCaptureK*T; past kCapN vectors only their
@@ -61,9 +63,8 @@ constexpr int kMaxTiles = 1024;  // 64-vector tiles per row in the resolve pass 
 constexpr int kPreRows = 8;      // draft positions whose list heads the resolve prefetches
 constexpr int kPre = 64;         // list entries prefetched per row
 constexpr double kFix = 17592186044416.0;  // 2^44: fixed-point scale of masses
-// A trip whose weights, taken against the lane's previous maximum, may exceed 2^100 is
-// recomputed against its own maximum (first trip of a row, or a large jump at small T).
-constexpr float kTripBig = 1.2676506e30f;  // 2^100
+// Trips of a row at most (V <= 2^19 logits, kU vectors of 8 logits per lane per trip).
+constexpr int kMaxTrips = (1 << 19) / (8 * kU * kWave);
 
 struct ChainParams {
   const uint16_t* target;
@@ -162,8 +163,7 @@ __device__ __forceinline__ SeqInfo seq_info(const ChainParams& P, int b) {
 // ----------------------------------------------------------------------------------------
 
 struct LaneAcc {
-  float m = -INFINITY;   // running max of this lane's logits
-  float s = 0.0f;        // sum of exp2((l - m) * c) over this lane's logits
+  float m = -INFINITY;   // max of the logits this lane has consumed
   float wm = -INFINITY;  // capture reference: a lower bound of the row max known to the wave
 };
 
@@ -176,6 +176,8 @@ __device__ __forceinline__ float weight(float l, float c, float nref) {
 // LDS of one row's workgroup.
 struct RowLds {
   uint4 data[kCapN];               // captured vectors, in claim order
+  float tmax[kMaxTrips];           // each trip's max
+  float tsum[kMaxTrips];           // each trip's sum of weights against its max
   unsigned long long hist[kHist];  // fixed-point masses by key offset below the row max
   uint32_t hcnt[kHist];            // logits by key offset below the row max (top-k)
   NucEntry kept[kNucMax];          // nucleus entries before they are put in token order
@@ -183,7 +185,6 @@ struct RowLds {
   float wmax[kRowWgWaves];         // each wave's max so far, published for the others
   float lmax[kRowThreads];         // every lane's max at the end of the stream
   float pm[kRowWgWaves];           // per-wave max (value of the argmax for greedy rows)
-  float pz[kRowWgWaves];           // per-wave sum of weights relative to the wave max
   int pa[kRowWgWaves];             // per-wave argmax (greedy rows)
   int trip;                        // trips of the row claimed by the waves
   int ncap;                        // capture slots claimed: LDS slots, then spill slots
@@ -224,12 +225,12 @@ __device__ __forceinline__ void capture_trip(RowLds* L, uint16_t* spill, const u
   }
 }
 
-// One trip (kU vectors of the row) into the lane's running (m, s). The weights are taken
-// against the lane's previous maximum; only when the trip raises it (rare after the first
-// trips) is the trip's partial sum re-referenced, or recomputed when it may have overflowed.
-// With CAPTURE, the vectors whose max is within capw of the best lower bound of the row max
-// the wave knows (its own max so far, and the maxima the other waves published in LDS) are
-// captured: a superset of the final window.
+// One trip (kU vectors of the row): its max M_t and its sum of weights against M_t, each
+// reduced over the wave in a fixed order, kept in LDS by trip index. The row's (M, Z) is
+// combined from these records in trip order, so it does not depend on which wave claimed
+// which trip: repeated calls give identical bits. With CAPTURE, the vectors whose max is
+// within capw of the best lower bound of the row max the wave knows (its own max so far, and
+// the maxima the other waves published in LDS) are captured: a superset of the final window.
 template <bool CAPTURE>
 __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane, float c,
                                              float capw, LaneAcc& a, RowLds* L,
@@ -241,40 +242,34 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
     for (int i = 0; i < kRowWgWaves; ++i)
       wg = fmaxf(wg, __hip_atomic_load(&L->wmax[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
   }
-  const float ref = (a.m == -INFINITY) ? 0.0f : a.m;
-  const float nref = -ref * c;
   float vm[kU];
-  float st = 0.0f;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     float x[8];
     unpack8(d[u], x);
     vm[u] = max8(x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st += weight(x[e], c, nref);
   }
   static_assert(kU == 4, "trip max below assumes four vectors per trip");
   const float tm = vmax3(vmax3(vm[0], vm[1], vm[2]), vm[3], vm[3]);
-  if (tm > a.m) {
-    if (st < kTripBig) {
-      st *= __builtin_amdgcn_exp2f((ref - tm) * c);
-    } else {
-      st = 0.0f;
-      const float nt = -tm * c;
+  const float mt = wave_max_dpp(tm);
+  const float nref = mt == -INFINITY ? 0.0f : -mt * c;  // a trip of -inf logits weighs 0
+  float st = 0.0f;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        float x[8];
-        unpack8(d[u], x);
+  for (int u = 0; u < kU; ++u) {
+    float x[8];
+    unpack8(d[u], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st += weight(x[e], c, nt);
-      }
-    }
-    a.s *= __builtin_amdgcn_exp2f((a.m - tm) * c);  // 0 while a.m = -inf (a.s = 0 then)
-    a.m = tm;
+    for (int e = 0; e < 8; ++e) st += weight(x[e], c, nref);
   }
-  a.s += st;
+  const float zt = wave_sum_dpp(st);
+  if (lane == 0) {
+    const int t = v0 / (kU * kWave);
+    L->tmax[t] = mt;
+    L->tsum[t] = zt;
+  }
+  a.m = vmax3(a.m, tm, tm);
   if (CAPTURE) {
-    a.wm = vmax3(a.wm, wave_max_dpp(a.m), wg);
+    a.wm = vmax3(a.wm, mt, wg);
     // kept finite, so a vector of -inf logits (past the row end included) is never captured
     const float thr = vmax3(a.wm - capw, -3.4028235e38f, -3.4028235e38f);
     capture_trip(L, spill, d, vm, thr, v0, lane);
@@ -283,24 +278,20 @@ __device__ __forceinline__ void consume_trip(const uint4 d[kU], int v0, int lane
   }
 }
 
-// Wave-wide (m, Z) of the lanes' running (m, s).
-__device__ __forceinline__ void finish_mz(const LaneAcc& a, float c, float& M, float& Z) {
-  M = wave_max_dpp(a.m);
-  const float ref = (M == -INFINITY) ? 0.0f : M;
-  const float s = (a.m == -INFINITY) ? 0.0f : a.s * __builtin_amdgcn_exp2f((a.m - ref) * c);
-  Z = wave_sum_dpp(s);
-}
-
-// (m, Z) of the row from the waves' partials (every thread computes the same values, in the
-// same order).
-__device__ __forceinline__ void row_mz(const RowLds* L, float c, float& M, float& Z) {
-  M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kRowWgWaves; ++i) M = fmaxf(M, L->pm[i]);
-  Z = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kRowWgWaves; ++i)
-    if (L->pm[i] != -INFINITY) Z += L->pz[i] * __builtin_amdgcn_exp2f((L->pm[i] - M) * c);
+// (M, Z) of the row from its ntrips trip records: lane l takes trips l, l + 64, ... in order,
+// then fixed-order wave reductions. Every wave computes the same values the same way.
+__device__ __forceinline__ void row_mz(const RowLds* L, int ntrips, float c, int lane, float& M,
+                                       float& Z) {
+  float m = -INFINITY;
+  for (int t = lane; t < ntrips; t += kWave) m = vmax3(m, L->tmax[t], L->tmax[t]);
+  M = wave_max_dpp(m);
+  const float nref = M == -INFINITY ? 0.0f : -M * c;
+  float z = 0.0f;
+  for (int t = lane; t < ntrips; t += kWave) {
+    const float mt = L->tmax[t];
+    if (mt != -INFINITY) z += L->tsum[t] * weight(mt, c, nref);
+  }
+  Z = wave_sum_dpp(z);
 }
 
 struct TopP {
@@ -793,20 +784,12 @@ void row_stats_kernel(ChainParams P) {
   else
     stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
-      consume_trip<false>(dd, v0, lane, c, capw, acc, nullptr, nullptr);
+      consume_trip<false>(dd, v0, lane, c, capw, acc, &L, nullptr);
     });
-  {
-    float Mw, Zw;
-    finish_mz(acc, c, Mw, Zw);
-    if (lane == 0) {
-      L.pm[w] = Mw;
-      L.pz[w] = Zw;
-    }
-    if (filt) L.lmax[tid] = acc.m;
-  }
+  if (filt) L.lmax[tid] = acc.m;
   __syncthreads();
   float M, Z;
-  row_mz(&L, c, M, Z);
+  row_mz(&L, (P.nvec + kU * kWave - 1) / (kU * kWave), c, lane, M, Z);
   TopP tp{-INFINITY, Z, -1, false};
   if (filt)
     tp = topp_select(rp, P.nvec, P.V, c, use_k, s.K, s.P < 1.0f, s.P, capw, M, Z, &L, spill,
