@@ -102,7 +102,7 @@ class SpecError(RuntimeError):
 _lib = None
 
 # Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 def lib_path() -> str:
@@ -122,6 +122,8 @@ def lib():
         L.spec_verify_chain_workspace_size.argtypes = [_I32, _I32, _I32]
         L.spec_verify_chain_workspace_size.restype = ctypes.c_size_t
         L.spec_verify_chain.argtypes = [ctypes.POINTER(spec_chain_args), _P, ctypes.c_size_t, _P]
+        L.spec_verify_chain_noalloc.argtypes = [ctypes.POINTER(spec_chain_args), _P]
+        L.spec_verify_chain_noalloc.restype = _I32
         L.spec_verify_chain.restype = ctypes.c_int
         L.spec_verify_tree_workspace_size.argtypes = [_I32, _I32]
         L.spec_verify_tree_workspace_size.restype = ctypes.c_size_t
@@ -245,6 +247,16 @@ def spec_verify_chain(args: spec_chain_args, workspace=None, stream=None, device
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().spec_verify_chain(ctypes.byref(args), ws, nbytes, _stream(stream)))
     return workspace
+
+
+def spec_verify_chain_noalloc(args: spec_chain_args, stream=None):
+    """Enqueues chain verification on the library's own scratch memory (see spec_verify.h):
+    nothing is allocated."""
+    _check(lib().spec_verify_chain_noalloc(ctypes.byref(args), _stream(stream)))
+
+
+# Bytes of the library's scratch array per GPU (SPEC_CHAIN_SCRATCH_BYTES).
+CHAIN_SCRATCH_BYTES = 80 << 20
 
 
 def tree_args(*, target_logits, parent, node_row, node_token, path_nodes, path_len,

@@ -122,10 +122,13 @@ size_t spec_verify_chain_workspace_size(int32_t batch, int32_t total_draft_rows,
   return specv::chain_workspace_bytes(batch, total_draft_rows, vocab);
 }
 
-int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspace_bytes,
-                      void* hip_stream) {
-  g_err[0] = '\0';
-  if (!a) return fail(SPEC_ERR_INVALID_ARG, "spec_verify_chain: args is NULL");
+namespace {
+
+// Host-visible checks of a chain call (who names the entry point). SPEC_OK with *empty set
+// when the batch is empty and there is nothing to launch.
+int check_chain(const spec_chain_args* a, const char* who, bool* empty) {
+  *empty = false;
+  if (!a) return fail(SPEC_ERR_INVALID_ARG, "%s: args is NULL", who);
   if (a->batch < 0) return fail(SPEC_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", a->batch);
   if (a->vocab < 1 || a->vocab > kMaxVocab)
     return fail(SPEC_ERR_INVALID_ARG, "vocab must be in [1, %d] (got %d)", kMaxVocab, a->vocab);
@@ -142,7 +145,10 @@ int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspac
                 a->total_draft_rows);
   if (a->lead_slots != 0 && a->lead_slots != 1)
     return fail(SPEC_ERR_INVALID_ARG, "lead_slots must be 0 or 1 (got %d)", a->lead_slots);
-  if (a->batch == 0) return SPEC_OK;
+  if (a->batch == 0) {
+    *empty = true;
+    return SPEC_OK;
+  }
   if (!a->target_logits || !a->cu_gamma || !a->temperature || !a->committed_len ||
       !a->out_tokens || !a->num_accepted)
     return fail(SPEC_ERR_INVALID_ARG,
@@ -154,12 +160,43 @@ int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspac
     return fail(SPEC_ERR_INVALID_ARG, "logits base pointers must be 16-byte aligned");
   if ((int64_t)a->batch * (2 * a->max_gamma + 1) > 0x7FFFFFFFLL)
     return fail(SPEC_ERR_INVALID_ARG, "batch * (2 * max_gamma + 1) exceeds the grid limit");
+  return SPEC_OK;
+}
+
+}  // namespace
+
+int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  g_err[0] = '\0';
+  bool empty = false;
+  const int rc = check_chain(a, "spec_verify_chain", &empty);
+  if (rc != SPEC_OK || empty) return rc;
   const size_t need =
       specv::chain_workspace_bytes(a->batch, a->total_draft_rows, a->vocab);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(SPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
   hipError_t e = specv::launch_chain(*a, workspace, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "spec_verify_chain launch");
+  return SPEC_OK;
+}
+
+int spec_verify_chain_noalloc(const spec_chain_args* a, void* hip_stream) {
+  g_err[0] = '\0';
+  bool empty = false;
+  const int rc = check_chain(a, "spec_verify_chain_noalloc", &empty);
+  if (rc != SPEC_OK || empty) return rc;
+  const size_t need =
+      specv::chain_workspace_bytes(a->batch, a->total_draft_rows, a->vocab);
+  if (need > specv::kChainScratchBytes)
+    return fail(SPEC_ERR_WORKSPACE,
+                "spec_verify_chain_noalloc: this call needs %zu bytes of scratch, more than the "
+                "%zu the library holds per GPU; use spec_verify_chain with a workspace",
+                need, specv::kChainScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = specv::chain_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_chain_noalloc: scratch address");
+  e = specv::launch_chain(*a, ws, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_chain_noalloc launch");
   return SPEC_OK;
 }
 

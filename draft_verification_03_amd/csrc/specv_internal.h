@@ -37,6 +37,11 @@ struct NucEntry {
 size_t chain_workspace_bytes(int32_t batch, int32_t total_draft_rows, int32_t vocab);
 hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t s);
 
+// spec_verify_chain_noalloc's scratch: the library's own device array of this many bytes per
+// GPU (chain_noalloc.hip); chain_scratch() returns the current device's address of it.
+constexpr size_t kChainScratchBytes = SPEC_CHAIN_SCRATCH_BYTES;
+hipError_t chain_scratch(void** ptr);
+
 size_t tree_workspace_bytes(int32_t batch, int32_t rows_per_seq);
 hipError_t launch_tree(const spec_tree_args& a, void* ws, hipStream_t s);
 

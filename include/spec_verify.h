@@ -23,7 +23,9 @@
  *    must hold at least one finite logit; NaN and +inf logits are not supported.
  *  - All array arguments are DEVICE pointers owned by the caller, except where a field says
  *    "host". The library allocates nothing, keeps no pointer after returning, and holds no
- *    global state except a thread-local error string. Calls are thread-safe.
+ *    global state except a thread-local error string and the scratch array of
+ *    spec_verify_chain_noalloc (below). Calls are thread-safe, except that calls of
+ *    spec_verify_chain_noalloc that overlap on one GPU race on that GPU's array.
  *  - Work is enqueued on hip_stream (a hipStream_t; NULL = the default stream). Outputs are
  *    valid after the stream is synchronised; inputs must stay alive until then.
  *  - Host validation reads only host-visible fields and makes no HIP call before it passes.
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 6
+#define SPEC_ABI_VERSION 7
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
@@ -382,6 +384,22 @@ size_t spec_verify_chain_workspace_size(int32_t batch, int32_t total_draft_rows,
 /* Enqueue chain verification. Returns SPEC_OK or a negative status. */
 int spec_verify_chain(const spec_chain_args* args, void* workspace, size_t workspace_bytes,
                       void* hip_stream);
+
+/*
+ * spec_verify_chain without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, checks, kernels and results as spec_verify_chain; the
+ * workspace is the library's own scratch array of SPEC_CHAIN_SCRATCH_BYTES per GPU, held by
+ * every GPU the library runs on until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine). A call whose workspace would exceed
+ * the array (spec_verify_chain_workspace_size > SPEC_CHAIN_SCRATCH_BYTES) fails with
+ * SPEC_ERR_WORKSPACE before any HIP call; use spec_verify_chain for it. Every call on one
+ * GPU uses that GPU's array: calls that may overlap on one GPU (other streams, other host
+ * threads) race on it and must be serialized by the caller. Nothing in the array needs to
+ * hold anything between calls.
+ */
+#define SPEC_CHAIN_SCRATCH_BYTES ((size_t)80 << 20)
+int spec_verify_chain_noalloc(const spec_chain_args* args, void* hip_stream);
 
 /* Workspace bytes spec_verify_tree needs (device memory, 256-byte aligned). */
 size_t spec_verify_tree_workspace_size(int32_t batch, int32_t rows_per_seq);

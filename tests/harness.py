@@ -68,7 +68,7 @@ def run_oracle_chain(x, tokens, seed, override=None, lead=1, nthreads=0):
 
 
 def run_gpu_chain(x, tokens, seed, override=None, lead=1, probes=True, no_draft=False,
-                  workspace=None):
+                  workspace=None, noalloc=False):
     cu = x["cu_gamma"]
     Bn = len(cu) - 1
     n_d = int(cu[-1])
@@ -100,7 +100,10 @@ def run_gpu_chain(x, tokens, seed, override=None, lead=1, probes=True, no_draft=
                      vocab=x["vocab"], max_gamma=max(int(np.diff(cu).max()) if Bn else 0, 0),
                      total_draft_rows=n_d, row_stride=x["stride"], top_k=t["topk"],
                      eos_token=t["eos"], max_emit=t["cap"], num_emitted=t["nemit"])
-    B.spec_verify_chain(a, workspace=workspace)
+    if noalloc:
+        B.spec_verify_chain_noalloc(a)
+    else:
+        B.spec_verify_chain(a, workspace=workspace)
     torch.cuda.synchronize()
     return dict(out_tokens=t["out"].cpu().numpy()[:n_t], num_accepted=t["nacc"].cpu().numpy(),
                 num_emitted=t["nemit"].cpu().numpy(),

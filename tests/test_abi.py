@@ -71,7 +71,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_abi_version_and_workspace_sizes():
-    assert B.spec_abi_version() == B.ABI_VERSION == 6
+    assert B.spec_abi_version() == B.ABI_VERSION == 7
     assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
     assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
     assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
@@ -117,6 +117,37 @@ def _call_chain(a, ws=0x100000, nbytes=1 << 30):
 def test_chain_validation(kw, code):
     assert _call_chain(_chain(**kw)) == code
     assert B.spec_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), B.SPEC_ERR_INVALID_ARG),
+    (dict(vocab=0), B.SPEC_ERR_INVALID_ARG),
+    (dict(row_stride=101), B.SPEC_ERR_INVALID_ARG),
+    (dict(max_gamma=65), B.SPEC_ERR_INVALID_ARG),
+    (dict(total_draft_rows=9), B.SPEC_ERR_INVALID_ARG),
+    (dict(target_logits=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(draft_tokens=None), B.SPEC_ERR_INVALID_ARG),
+    (dict(target_logits=0x1002), B.SPEC_ERR_INVALID_ARG),
+    (dict(batch=0, total_draft_rows=0), B.SPEC_OK),
+])
+def test_chain_noalloc_validation(kw, code):
+    """The allocation-free entry point checks its arguments as spec_verify_chain does."""
+    assert B.lib().spec_verify_chain_noalloc(ctypes.byref(_chain(**kw)), None) == code
+
+
+def test_chain_noalloc_rejects_shapes_beyond_its_scratch():
+    """A call whose workspace would exceed the library's scratch array fails with
+    SPEC_ERR_WORKSPACE before any HIP call; the array's size is the header's."""
+    hdr = open(os.path.join(ROOT, "include", "spec_verify.h")).read()
+    m = re.search(r"#define SPEC_CHAIN_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.CHAIN_SCRATCH_BYTES
+    V, Bn, g = 128256, 4096, 8
+    assert B.spec_verify_chain_workspace_size(Bn, Bn * g, V) > B.CHAIN_SCRATCH_BYTES
+    a = _chain(batch=Bn, max_gamma=g, total_draft_rows=Bn * g, vocab=V, row_stride=V)
+    assert B.lib().spec_verify_chain_noalloc(ctypes.byref(a), None) == B.SPEC_ERR_WORKSPACE
+    assert "scratch" in B.spec_last_error()
+    # every batch of up to 1024 sequences with gamma_b <= 8 fits (any vocabulary)
+    assert B.spec_verify_chain_workspace_size(1024, 1024 * 8, V) <= B.CHAIN_SCRATCH_BYTES
 
 
 def test_chain_workspace_validation():
