@@ -661,14 +661,12 @@ def chain_bench(args, name):
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    # Row-pass durations: the same steps again, each with one event pair that the library
-    # records on the launch stream around the row kernel.
+    # Row-pass durations: the same steps again through spec_verify_chain_timed, which records
+    # one event pair on the launch stream around the row kernel.
     evs = [B.EventPair() for _ in range(args.steps)]
     for i, e in enumerate(evs):
         c = calls[i % nsets]
-        c["a"].profile_events = e.ptr
-        B.spec_verify_chain(c["a"], workspace=c["ws"])
-        c["a"].profile_events = None
+        B.spec_verify_chain_timed(c["a"], e, c["ws"])
     torch.cuda.synchronize()
     row_ms = [e.elapsed_ms() for e in evs]
     ms_step = total_ms / args.steps
@@ -782,10 +780,7 @@ def markov_bench(args):
     ms = start.elapsed_time(stop) / steps
     evs = [B.EventPair() for _ in range(steps)]
     for i, e in enumerate(evs):
-        a = args_r[i % nr]
-        a.profile_events = e.ptr
-        B.spec_verify_chain(a, workspace=ws)
-        a.profile_events = None
+        B.spec_verify_chain_timed(args_r[i % nr], e, ws)
     torch.cuda.synchronize()
     row_ms = float(np.mean([e.elapsed_ms() for e in evs]))
     nbytes = (2 * g + 1) * 4 * 2 + g * 4  # the rows' 4 logits each, and the draft tokens

@@ -37,7 +37,7 @@ class spec_chain_args(ctypes.Structure):
         ("temperature", _P), ("top_p", _P), ("top_k", _P), ("seq_id", _P),
         ("committed_len", _P), ("out_tokens", _P), ("num_accepted", _P), ("seq_flags", _P),
         ("probe_rows", _P), ("probe_seq", _P), ("uniform_override", _P),
-        ("profile_events", _P), ("eos_token", _P), ("max_emit", _P), ("num_emitted", _P),
+        ("eos_token", _P), ("max_emit", _P), ("num_emitted", _P),
     ]
 
 
@@ -102,7 +102,7 @@ class SpecError(RuntimeError):
 _lib = None
 
 # Layout revision of the argument structs above; must equal the library's SPEC_ABI_VERSION.
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 def lib_path() -> str:
@@ -123,6 +123,9 @@ def lib():
         L.spec_verify_chain_workspace_size.restype = ctypes.c_size_t
         L.spec_verify_chain.argtypes = [ctypes.POINTER(spec_chain_args), _P, ctypes.c_size_t, _P]
         L.spec_verify_chain_noalloc.argtypes = [ctypes.POINTER(spec_chain_args), _P]
+        L.spec_verify_chain_timed.argtypes = [ctypes.POINTER(spec_chain_args), _P,
+                                              ctypes.c_size_t, _P, _P]
+        L.spec_verify_chain_timed.restype = _I32
         L.spec_verify_chain_noalloc.restype = _I32
         L.spec_verify_chain.restype = ctypes.c_int
         L.spec_verify_tree_workspace_size.argtypes = [_I32, _I32]
@@ -199,7 +202,7 @@ def chain_args(*, target_logits, cu_gamma, temperature, committed_len, out_token
                num_accepted, vocab, max_gamma, total_draft_rows, draft_logits=None,
                draft_tokens=None, top_p=None, seq_id=None, seq_flags=None, probe_rows=None,
                probe_seq=None, uniform_override=None, seed=0, lead_slots=1, row_stride=None,
-               profile_events=None, top_k=None, eos_token=None, max_emit=None,
+               top_k=None, eos_token=None, max_emit=None,
                num_emitted=None):
     """Fills a spec_chain_args from tensors (device) or raw pointers."""
     B = int(cu_gamma.shape[0]) - 1 if hasattr(cu_gamma, "shape") else None
@@ -226,7 +229,6 @@ def chain_args(*, target_logits, cu_gamma, temperature, committed_len, out_token
     a.probe_rows = _ptr(probe_rows)
     a.probe_seq = _ptr(probe_seq)
     a.uniform_override = _ptr(uniform_override)
-    a.profile_events = profile_events
     a.eos_token = _ptr(eos_token)
     a.max_emit = _ptr(max_emit)
     a.num_emitted = _ptr(num_emitted)
@@ -247,6 +249,12 @@ def spec_verify_chain(args: spec_chain_args, workspace=None, stream=None, device
     nbytes = 0 if workspace is None else workspace.numel()
     _check(lib().spec_verify_chain(ctypes.byref(args), ws, nbytes, _stream(stream)))
     return workspace
+
+
+def spec_verify_chain_timed(args: spec_chain_args, events, workspace, stream=None):
+    """spec_verify_chain with an EventPair recorded around its row-statistics kernel."""
+    _check(lib().spec_verify_chain_timed(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                                         _stream(stream), events.ptr))
 
 
 def spec_verify_chain_noalloc(args: spec_chain_args, stream=None):
@@ -452,7 +460,7 @@ def spec_tree_draft_step(args: spec_tree_draft_args, workspace=None, stream=None
     return workspace
 
 
-# ---- HIP events for the optional row-pass timing (profile_events) -----------------------
+# ---- HIP events for the row-pass timing (spec_verify_chain_timed) -----------------------
 
 _hip = None
 
@@ -469,7 +477,7 @@ def _hiprt():
 
 
 class EventPair:
-    """Two hipEvent_t for spec_chain_args.profile_events (row-pass start / end)."""
+    """Two hipEvent_t for spec_verify_chain_timed (row-pass start / end)."""
 
     def __init__(self):
         h = _hiprt()

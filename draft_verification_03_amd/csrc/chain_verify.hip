@@ -1163,6 +1163,7 @@ __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq,
 
 // Per-sequence decision state the resolve step shares through LDS.
 struct SeqDecision {
+  int tok[kWave];  // the draft tokens d_1..d_gamma, as the decision loaded them
   int n_acc;
   int drawn;  // the round ends with a residual or bonus token (no early stop)
   int flags;
@@ -1207,6 +1208,7 @@ __device__ __forceinline__ void decide_wave(const ChainParams& P, const SeqInfo&
     sp = P.stat[(size_t)(s.d0 + lane) * 2];
     if (stochastic) sq = P.stat[(size_t)(s.d0 + lane) * 2 + 1];
   }
+  sd.tok[lane] = tok;
   const bool bad_tok = __ballot(in_g && (tok < 0 || tok >= P.V)) != 0;
   int acc = 1, rflags = 0;
   if (in_g && !s.bad_param && !bad_tok) {
@@ -1285,16 +1287,34 @@ void chain_resolve_kernel(ChainParams P) {
   const bool stochastic = !s.bad_param && s.T != 0.0f;
   // The heads of the candidate rows' nucleus lists, fetched together with the statistics:
   // where the first rejection falls is not known yet, and the draw usually needs no more.
-  if (cu_ok && stochastic && (P.topp || P.topk)) {
-    for (int i = tid; i < kPreRows * 2 * kPre; i += NT) {
+  // Every load of this phase is issued before any result is used (the list entries into
+  // registers, from in-range slots only -- rows past gamma_b read the bonus list -- then the
+  // decision's loads in wave 0), so that the phase costs one memory round trip.
+  constexpr int kPreEach = (kPreRows * 2 * kPre + NT - 1) / NT;
+  const bool prefetch = cu_ok && stochastic && (P.topp || P.topk);
+  NucEntry pre[kPreEach], preb{};
+  if (prefetch) {
+#pragma unroll
+    for (int r = 0; r < kPreEach; ++r) {
+      const int i = tid + r * NT;
       const int kk = i / (2 * kPre), rr = (i / kPre) & 1, j = i % kPre;
-      if (kk < s.g) s_pre[kk][rr][j] = P.nuc[((size_t)(s.d0 + kk) * 2 + rr) * kNucMax + j];
+      const size_t slot = kk < s.g ? (size_t)(s.d0 + kk) * 2 + rr : bonus_slot(P, b);
+      pre[r] = P.nuc[slot * kNucMax + j];
     }
-    if (tid < kPre) s_preb[tid] = P.nuc[bonus_slot(P, b) * kNucMax + tid];
+    preb = P.nuc[bonus_slot(P, b) * kNucMax + (tid & (kPre - 1))];
   }
   RowStat sbon{};
   if (!s.bad_param) sbon = P.stat[bonus_slot(P, b)];
   if (wid == 0) decide_wave(P, s, cu_ok, stochastic, sd, lane);
+  if (prefetch) {
+#pragma unroll
+    for (int r = 0; r < kPreEach; ++r) {
+      const int i = tid + r * NT;
+      const int kk = i / (2 * kPre), rr = (i / kPre) & 1, j = i % kPre;
+      if (i < kPreRows * 2 * kPre && kk < s.g) s_pre[kk][rr][j] = pre[r];
+    }
+    if (tid < kPre) s_preb[tid] = preb;
+  }
   __syncthreads();
   const int n_acc = sd.n_acc;
   int flags = sd.flags;
@@ -1312,7 +1332,7 @@ void chain_resolve_kernel(ChainParams P) {
   }
   if (!sd.drawn) {  // stopped inside the accepted drafts: they are the round's output
     if (wid == 0) {
-      if (lane < n_acc) P.out_tokens[s.t0 + lane] = P.tokens[s.d0 + lane];
+      if (lane < n_acc) P.out_tokens[s.t0 + lane] = sd.tok[lane];
       if (lane == 0) {
         P.num_acc[b] = n_acc;
         if (P.num_emit) P.num_emit[b] = n_acc;
@@ -1373,7 +1393,7 @@ void chain_resolve_kernel(ChainParams P) {
                                            P.draft + (size_t)(s.d0 + kstar - 1) * P.stride),
                                        c, -sq.m * c, sq.t, 1.0f / sq.z}
                               : RowLaw{nullptr, c, 0.0f, -INFINITY, 1.0f,
-                                       P.tokens[s.d0 + kstar - 1]};
+                                       sd.tok[kstar - 1]};
     Draw d;
     const bool lists_p = sp.nuc >= 0, lists_pq = lists_p && sq.nuc >= 0;
     const NucEntry* lp = s_lp;
@@ -1405,7 +1425,7 @@ void chain_resolve_kernel(ChainParams P) {
     }
   }
   if (wid == 0) {
-    if (lane < n_acc) P.out_tokens[s.t0 + lane] = P.tokens[s.d0 + lane];
+    if (lane < n_acc) P.out_tokens[s.t0 + lane] = sd.tok[lane];
     if (lane == 0) {
       if (s.eos >= 0 && y == s.eos) flags |= SPEC_FLAG_EOS;
       P.out_tokens[s.t0 + n_acc] = y;
@@ -1433,7 +1453,7 @@ size_t chain_workspace_bytes(int32_t batch, int32_t total_draft_rows, int32_t vo
   return n > 256 ? n : 256;
 }
 
-hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
+hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st, void* const* events) {
   ChainParams P;
   P.target = a.target_logits;
   P.draft = a.draft_logits;
@@ -1467,7 +1487,7 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st) {
   P.lead = a.lead_slots;
   P.seed_lo = (uint32_t)(a.seed & 0xFFFFFFFFu);
   P.seed_hi = (uint32_t)(a.seed >> 32);
-  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(a.profile_events);
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
   hipError_t e = hipSuccess;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   // per sequence: two rows (target, draft) per draft position slot k <= max_gamma, then the

@@ -42,8 +42,8 @@ constexpr int kRelThreads = 1024;
 constexpr int kRelWaves = kRelThreads / kWave;
 constexpr int kRun = 8;           // table entries per thread per chunk
 constexpr int kRelEntries = kRelThreads * kRun;  // table entries per tile (whole rows)
-constexpr int kRelRows = 1024;                   // rows per tile at most
-constexpr int kRelPath = 4096;                   // path entries per tile at most
+constexpr int kRelRows = kRelThreads;            // rows per tile at most (one per thread)
+constexpr int kRelPath = 4 * kRelThreads;        // path entries per tile at most
 
 struct PagedParams {
   uint16_t* k[kMaxLayers];
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
   __shared__ int64_t s_so[kMaxDepth], s_do[kMaxDepth];  // physical element offsets per step
   __shared__ int32_t s_path[kMaxDepth];
   __shared__ uint8_t s_mv[kMaxDepth];
-  __shared__ int s_L, s_D, s_bad;
+  __shared__ int s_bad;
   const int b = blockIdx.x / P.split, part = blockIdx.x % P.split, tid = threadIdx.x;
   const int nch = P.NL * 2 * P.H * P.chunks;
   const int c0 = part * kChunksPerWg + tid;
@@ -93,13 +93,12 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
     uint16_t* cache = (c & 1) ? P.v[c >> 1] : P.k[c >> 1];
     head[u] = cache + (int64_t)h * P.head_stride + ch * 8;
   }
-  if (tid == 0) {
-    s_L = P.committed[b];
-    s_D = P.plen[b];
-    s_bad = 0;
-  }
+  // the sequence's length, path length and path step tid + 1 load together (the step from
+  // a clamped index, used only below D), before the barrier that clears s_bad
+  const int L = P.committed[b], D = P.plen[b];
+  const int node = P.path[(size_t)b * P.max_depth + min(tid, P.max_depth - 1)];
+  if (tid == 0) s_bad = 0;
   __syncthreads();
-  const int L = s_L, D = s_D;
   // the commit predicate, step j by thread j - 1
   const int64_t base = (int64_t)L + P.lead - 1;
   const int64_t slots = (int64_t)P.max_blocks * P.bs;
@@ -107,7 +106,6 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
                        ((int64_t)L + P.lead + D + P.bs - 1) / P.bs <= P.max_blocks;
   if (head_ok && tid < D) {
     const int32_t* bt = P.bt + (size_t)b * P.max_blocks;
-    const int node = P.path[(size_t)b * P.max_depth + tid];
     const int64_t src = base + node, dst = base + tid + 1;
     bool ok = node >= 1;
     bool mv = false;
@@ -194,23 +192,36 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
   for (int b0 = 0; b0 < P.B; b0 += rows) {
     const int nr = min(rows, P.B - b0);
     const int64_t e0 = (int64_t)b0 * mb, ne = (int64_t)nr * mb;
-    // 1. every global read of the tile at once: lengths, path rows, table entries (in LDS,
-    //    and kRun consecutive entries per thread in registers for the scan)
-    for (int i = tid; i < nr; i += kRelThreads) {
-      const int L = P.committed[b0 + i], D = P.plen[b0 + i];
-      s_L[i] = L;
-      s_D[i] = D;
-      const int64_t base = (int64_t)L + P.lead - 1;
-      const int64_t need = ((int64_t)L + P.lead + D + P.bs - 1) / P.bs;
-      const bool ok = D >= 0 && D <= md && base >= -1 && need <= mb;
-      s_need[i] = ok ? (int)need : -1;
-    }
-    for (int q = tid; q < nr * md; q += kRelThreads) s_path[q] = P.path[(size_t)b0 * md + q];
+    // 1. every global read of the tile at once -- lengths, path rows, table entries -- as
+    //    unconditional loads from clamped indexes (a value past the tile is dropped), all
+    //    issued before the first one is used, so that the phase costs one memory round trip;
+    //    then the values go to LDS (and kRun consecutive entries per thread stay in registers
+    //    for the scan)
+    const int li = min(tid, nr - 1);
+    const int L0 = P.committed[b0 + li], D0 = P.plen[b0 + li];
+    int p_reg[kRelPath / kRelThreads];
+#pragma unroll
+    for (int k = 0; k < kRelPath / kRelThreads; ++k)
+      p_reg[k] = P.path[(size_t)b0 * md + min(tid + k * kRelThreads, nr * md - 1)];
     int v_reg[kRun];
 #pragma unroll
+    for (int r = 0; r < kRun; ++r)
+      v_reg[r] = P.bt[e0 + min((int64_t)tid * kRun + r, ne - 1)];  // first chunk of the tile
+    if (tid < nr) {
+      s_L[tid] = L0;
+      s_D[tid] = D0;
+      const int64_t base = (int64_t)L0 + P.lead - 1;
+      const int64_t need = ((int64_t)L0 + P.lead + D0 + P.bs - 1) / P.bs;
+      const bool ok = D0 >= 0 && D0 <= md && base >= -1 && need <= mb;
+      s_need[tid] = ok ? (int)need : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kRelPath / kRelThreads; ++k)
+      if (tid + k * kRelThreads < nr * md) s_path[tid + k * kRelThreads] = p_reg[k];
+#pragma unroll
     for (int r = 0; r < kRun; ++r) {
-      const int64_t e = (int64_t)tid * kRun + r;  // first chunk of the tile
-      v_reg[r] = e < ne ? P.bt[e0 + e] : -1;
+      const int64_t e = (int64_t)tid * kRun + r;
+      if (e >= ne) v_reg[r] = -1;
       if (in_lds && e < ne) s_bt[e] = v_reg[r];
     }
     __syncthreads();
@@ -234,15 +245,24 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
       }
       if (!ok) atomicMin(&s_need[i], -1);
     }
-    for (int64_t c0 = 0; c0 < ne; c0 += (int64_t)kRelThreads * kRun) {
+    // (a tile holds at most max(kRelEntries, max_blocks) entries: indexes within it fit an
+    // int; a thread's row and block follow its first entry's, one division per chunk)
+    const int ne32 = (int)ne;
+    for (int c0 = 0; c0 < ne32; c0 += kRelThreads * kRun) {
+      const int ef = c0 + tid * kRun;
+      int i = ef / mb, lb = ef - i * mb;
 #pragma unroll
       for (int r = 0; r < kRun; ++r) {
-        const int64_t e = c0 + (int64_t)tid * kRun + r;
-        if (e >= ne) continue;
-        const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
-        const int i = (int)(e / mb), lb = (int)(e - (int64_t)i * mb);
-        const int need = s_need[i];
-        if (need >= 0 && lb >= need && v >= P.num_blocks) atomicMin(&s_need[i], -1);
+        const int e = ef + r;
+        if (e < ne32) {
+          const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
+          const int need = s_need[i];
+          if (need >= 0 && lb >= need && v >= P.num_blocks) atomicMin(&s_need[i], -1);
+        }
+        if (++lb == mb) {
+          lb = 0;
+          ++i;
+        }
       }
     }
     __syncthreads();
@@ -257,20 +277,29 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
     // 4. the tile's entries in row-major order, kRun consecutive per thread: a released
     //    entry's free-list position is the count of released entries before it; one that
     //    lands at or past the capacity stays in the table and flags its sequence FREE_FULL
-    for (int64_t c0 = 0; c0 < ne; c0 += (int64_t)kRelThreads * kRun) {
-      int pb[kRun];
+    for (int c0 = 0; c0 < ne32; c0 += kRelThreads * kRun) {
+      const int ef = c0 + tid * kRun;
+      const int i0 = ef / mb;
+      int pb[kRun], pi[kRun];
       int cnt = 0;
+      {
+        int i = i0, lb = ef - i0 * mb;
 #pragma unroll
-      for (int r = 0; r < kRun; ++r) {
-        const int64_t e = c0 + (int64_t)tid * kRun + r;
-        pb[r] = -1;
-        if (e < ne) {
-          const int i = (int)(e / mb), lb = (int)(e - (int64_t)i * mb);
-          const int need = s_need[i];
-          const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
-          if (need >= 0 && lb >= need && v >= 0) pb[r] = v;
+        for (int r = 0; r < kRun; ++r) {
+          const int e = ef + r;
+          pb[r] = -1;
+          pi[r] = i;
+          if (e < ne32) {
+            const int need = s_need[i];
+            const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
+            if (need >= 0 && lb >= need && v >= 0) pb[r] = v;
+          }
+          cnt += pb[r] >= 0;
+          if (++lb == mb) {
+            lb = 0;
+            ++i;
+          }
         }
-        cnt += pb[r] >= 0;
       }
       const int incl = wave_incl_scan_dpp(cnt);
       if (lane == kWave - 1) s_wave[wave] = incl;
@@ -285,12 +314,11 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
 #pragma unroll
       for (int r = 0; r < kRun; ++r) {
         if (pb[r] >= 0) {
-          const int64_t e = c0 + (int64_t)tid * kRun + r;
           if (at < P.free_cap) {
             P.free_list[at] = pb[r];
-            P.bt[e0 + e] = -1;
+            P.bt[e0 + ef + r] = -1;
           } else if (P.flags) {
-            atomicOr(&P.flags[b0 + (int)(e / mb)], SPEC_FLAG_FREE_FULL);
+            atomicOr(&P.flags[b0 + pi[r]], SPEC_FLAG_FREE_FULL);
           }
           ++at;
         }

@@ -180,6 +180,22 @@ int spec_verify_chain(const spec_chain_args* a, void* workspace, size_t workspac
   return SPEC_OK;
 }
 
+int spec_verify_chain_timed(const spec_chain_args* a, void* workspace, size_t workspace_bytes,
+                            void* hip_stream, void* const* events) {
+  g_err[0] = '\0';
+  if (!events) return fail(SPEC_ERR_INVALID_ARG, "spec_verify_chain_timed: events is NULL");
+  bool empty = false;
+  const int rc = check_chain(a, "spec_verify_chain_timed", &empty);
+  if (rc != SPEC_OK || empty) return rc;
+  const size_t need =
+      specv::chain_workspace_bytes(a->batch, a->total_draft_rows, a->vocab);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(SPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  hipError_t e = specv::launch_chain(*a, workspace, (hipStream_t)hip_stream, events);
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_chain_timed launch");
+  return SPEC_OK;
+}
+
 int spec_verify_chain_noalloc(const spec_chain_args* a, void* hip_stream) {
   g_err[0] = '\0';
   bool empty = false;
@@ -350,6 +366,8 @@ int kv_commit_paged(const spec_paged_kv_args* a, void* hip_stream) {
     return fail(SPEC_ERR_INVALID_ARG, "block_size, max_blocks and num_blocks must be >= 1");
   if ((int64_t)a->max_blocks * a->block_size > 0x7FFFFFFFLL)
     return fail(SPEC_ERR_INVALID_ARG, "max_blocks * block_size exceeds the slot index range");
+  if (a->max_blocks > (1 << 24))
+    return fail(SPEC_ERR_INVALID_ARG, "max_blocks must be <= 2^24 (got %d)", a->max_blocks);
   if (a->free_capacity < a->num_blocks)
     return fail(SPEC_ERR_INVALID_ARG, "free_capacity must be >= num_blocks (got %d < %d)",
                 a->free_capacity, a->num_blocks);

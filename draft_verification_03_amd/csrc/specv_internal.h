@@ -35,7 +35,10 @@ struct NucEntry {
 };
 
 size_t chain_workspace_bytes(int32_t batch, int32_t total_draft_rows, int32_t vocab);
-hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t s);
+// events: NULL, or two hipEvent_t recorded just before and just after the row-statistics
+// kernel (spec_verify_chain_timed).
+hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t s,
+                        void* const* events = nullptr);
 
 // spec_verify_chain_noalloc's scratch: the library's own device array of this many bytes per
 // GPU (chain_noalloc.hip); chain_scratch() returns the current device's address of it.

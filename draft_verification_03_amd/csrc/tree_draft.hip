@@ -370,6 +370,10 @@ struct GrowParams {
   int32_t koff[kMaxHead];
 };
 
+// candidates per lane staged through registers in one round of loads (the rest, past
+// kStageRegs * 64, one at a time)
+constexpr int kStageRegs = 4;
+
 __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
   __shared__ uint64_t s_stage[kGrowWaves][kStageCap];
   __shared__ uint32_t s_pmask[kGrowWaves][kMaskWordsMax];
@@ -416,32 +420,45 @@ __global__ __launch_bounds__(kGrowThreads) void tree_grow_kernel(GrowParams P) {
     const int K = P.kk[j];
     const int nc = P.S * K;  // the S chunk lists, K candidates each
     uint64_t* stage = s_stage[wave];
-    for (int i = lane; i < nc; i += kWave) {
+    auto cand = [&](int i) {
       const int li = i / K, r = i - li * K;
-      stage[i] = reinterpret_cast<const uint64_t*>(rec0 + (size_t)li * P.rec_bytes +
-                                                   sizeof(PartHead))[r];
-    }
-    float m = -INFINITY, sm = 0.f;
-    if (lane < P.S) {
-      const PartHead hd = *reinterpret_cast<const PartHead*>(rec0 + (size_t)lane * P.rec_bytes);
-      m = hd.m;
-      sm = hd.s;
-    }
+      return reinterpret_cast<const uint64_t*>(rec0 + (size_t)li * P.rec_bytes +
+                                               sizeof(PartHead))[r];
+    };
     const int pnode = P.step == 0 ? 0 : expn[j];
     const bool bad = pnode < P.par_lo || pnode >= P.par_hi;
     if (bad) {
       if (lane == 0) s_bad = 1;
       continue;
     }
+    // the parent's path log-probability, position and mask row, the chunk heads and the
+    // candidates all load together (the candidates into registers from clamped indexes),
+    // one memory round trip after the parent's index
     float plp = 0.f;
     int ppos = P.pos_base ? P.pos_base[b] : 0;
+    uint32_t pm = lane == 0 ? 1u : 0u;
     if (P.step != 0) {
       plp = lp[pnode];
       ppos = pos[pnode];
-      if (lane < P.mw) s_pmask[wave][lane] = mask[(size_t)pnode * P.mw + lane];
-    } else if (lane < P.mw) {
-      s_pmask[wave][lane] = lane == 0 ? 1u : 0u;
+      pm = mask[(size_t)pnode * P.mw + min(lane, P.mw - 1)];
     }
+    float m = -INFINITY, sm = 0.f;
+    {
+      const PartHead hd =
+          *reinterpret_cast<const PartHead*>(rec0 + (size_t)min(lane, P.S - 1) * P.rec_bytes);
+      if (lane < P.S) {
+        m = hd.m;
+        sm = hd.s;
+      }
+    }
+    uint64_t cv[kStageRegs];
+#pragma unroll
+    for (int u = 0; u < kStageRegs; ++u) cv[u] = cand(min(lane + u * kWave, nc - 1));
+#pragma unroll
+    for (int u = 0; u < kStageRegs; ++u)
+      if (lane + u * kWave < nc) stage[lane + u * kWave] = cv[u];
+    for (int i = lane + kStageRegs * kWave; i < nc; i += kWave) stage[i] = cand(i);
+    if (lane < P.mw) s_pmask[wave][lane] = pm;
     const float M = wave_max_dpp(m);
     const float Z = wave_sum_dpp(m == -INFINITY ? 0.f : sm * __builtin_amdgcn_exp2f((m - M) * kLog2e));
     const float lz = logf(Z);  // log of sum over the row of exp(l - M)

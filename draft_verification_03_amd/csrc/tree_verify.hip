@@ -76,20 +76,37 @@ __global__ __launch_bounds__(kWave) void tree_walk_kernel(TreeParams P) {
   const int32_t* par = P.parent + (size_t)b * P.tree_stride;
   const int32_t* nrow = P.node_row + (size_t)b * P.tree_stride;
   const int32_t* tok = P.node_token + (size_t)b * P.N;
+  // every load first (clamped indexes; entries past N or R are dropped), so that the
+  // tree and the row argmaxes arrive in one memory round trip
+  constexpr int kNodesPerLane = kMaxNodes / kWave, kRowsPerLane = kMaxRows / kWave;
+  int pv[kNodesPerLane], rv[kNodesPerLane], tv[kNodesPerLane], av[kRowsPerLane];
+#pragma unroll
+  for (int k = 0; k < kNodesPerLane; ++k) {
+    const int i = min(lane + k * kWave, P.N - 1);
+    pv[k] = par[i];
+    rv[k] = nrow[i];
+    tv[k] = tok[i];
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerLane; ++k)
+    av[k] = P.argmax[(size_t)b * P.R + min(lane + k * kWave, P.R - 1)];
   bool bad = false;
-  for (int i = lane; i < kMaxNodes; i += kWave) {
+#pragma unroll
+  for (int k = 0; k < kNodesPerLane; ++k) {
+    const int i = lane + k * kWave;
     if (i < P.N) {
-      const int p = par[i], r = nrow[i];
-      s_par[i] = p;
-      s_row[i] = r;
-      s_tok[i] = tok[i];
-      bad |= (i == 0) ? (p != -1) : (p < 0 || p >= i);
-      bad |= (r < -1 || r >= P.R);
+      s_par[i] = pv[k];
+      s_row[i] = rv[k];
+      s_tok[i] = tv[k];
+      bad |= (i == 0) ? (pv[k] != -1) : (pv[k] < 0 || pv[k] >= i);
+      bad |= (rv[k] < -1 || rv[k] >= P.R);
     } else {
       s_par[i] = -2;  // never a parent
     }
   }
-  for (int r = lane; r < P.R; r += kWave) s_am[r] = P.argmax[(size_t)b * P.R + r];
+#pragma unroll
+  for (int k = 0; k < kRowsPerLane; ++k)
+    if (lane + k * kWave < P.R) s_am[lane + k * kWave] = av[k];
   bad = __ballot(bad) != 0;
   __syncthreads();
   int32_t* path = P.path_nodes + (size_t)b * P.max_depth;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 7
+#define SPEC_ABI_VERSION 8
 
 /* ---- status codes ---------------------------------------------------------------------- */
 #define SPEC_OK 0
@@ -146,8 +146,6 @@ typedef struct spec_chain_args {
   const float* uniform_override; /* [total_draft_rows + B][2] or NULL (test hook): row (b,k)
                                     supplies {u_acc for k, u for the residual/bonus draw at k}
                                     in place of the Philox uniforms                          */
-  void* profile_events;          /* NULL, or a host array of 2 hipEvent_t recorded on the
-                                    stream just before and just after the row pass kernel   */
   const int32_t* eos_token;      /* [B] or NULL: a sequence's EOS id (< 0: none)              */
   const int32_t* max_emit;       /* [B] or NULL: most tokens the round may emit (<= 0: no cap) */
   int32_t* num_emitted;          /* [B] or NULL: tokens emitted this round                   */
@@ -321,7 +319,7 @@ typedef struct spec_paged_kv_args {
   int32_t num_kv_heads;   /* >= 1                                                          */
   int32_t head_dim;       /* elements; a positive multiple of 8 (16-byte rows)             */
   int32_t block_size;     /* slots per block; >= 1                                         */
-  int32_t max_blocks;     /* entries per sequence in block_table; >= 1                     */
+  int32_t max_blocks;     /* entries per sequence in block_table; 1..2^24                  */
   int32_t num_blocks;     /* physical blocks of every layer's pool; >= 1                   */
   int32_t free_capacity;  /* entries of free_list; >= num_blocks                           */
   int32_t lead_slots;     /* 0 or 1                                                        */
@@ -400,6 +398,15 @@ int spec_verify_chain(const spec_chain_args* args, void* workspace, size_t works
  */
 #define SPEC_CHAIN_SCRATCH_BYTES ((size_t)80 << 20)
 int spec_verify_chain_noalloc(const spec_chain_args* args, void* hip_stream);
+
+/*
+ * Measurement variant of spec_verify_chain: the same call, with two caller-created
+ * hipEvent_t (events[0], events[1], a host array) recorded on hip_stream just before and just
+ * after the row-statistics kernel, so that a benchmark can time that kernel on the stream it
+ * runs on. events must not be NULL; otherwise as spec_verify_chain.
+ */
+int spec_verify_chain_timed(const spec_chain_args* args, void* workspace, size_t workspace_bytes,
+                            void* hip_stream, void* const* events);
 
 /* Workspace bytes spec_verify_tree needs (device memory, 256-byte aligned). */
 size_t spec_verify_tree_workspace_size(int32_t batch, int32_t rows_per_seq);

@@ -61,7 +61,8 @@ def oracle_proposer(oracle, draft_rows, gamma, seed_draft, vocab=4):
         for j in range(gamma):
             prev = chain[-1] if chain else last
             t = oracle.draw_tokens(draft_rows[prev:prev + 1], one, None, seed_draft, sid,
-                                   np.array([pos + j], np.int32), vocab=vocab)
+                                   np.array([pos + j], np.int32), vocab=vocab,
+                                   nthreads=1)
             chain.append(int(t[0]))
         return chain
 

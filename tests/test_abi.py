@@ -71,7 +71,7 @@ def test_struct_layout_matches_c(tmp_path):
 
 
 def test_abi_version_and_workspace_sizes():
-    assert B.spec_abi_version() == B.ABI_VERSION == 7
+    assert B.spec_abi_version() == B.ABI_VERSION == 8
     assert B.spec_verify_chain_workspace_size(256, 2048, 128256) > 0
     assert B.spec_verify_chain_workspace_size(-1, 0, 10) == 0
     assert B.spec_verify_chain_workspace_size(1, 0, 0) == 0
@@ -133,6 +133,20 @@ def test_chain_validation(kw, code):
 def test_chain_noalloc_validation(kw, code):
     """The allocation-free entry point checks its arguments as spec_verify_chain does."""
     assert B.lib().spec_verify_chain_noalloc(ctypes.byref(_chain(**kw)), None) == code
+
+
+def test_chain_timed_needs_events():
+    """The measurement variant checks its arguments as spec_verify_chain does, and needs the
+    event pair."""
+    L = B.lib()
+    assert L.spec_verify_chain_timed(ctypes.byref(_chain()), 0x100000, 1 << 30, None,
+                                     None) == B.SPEC_ERR_INVALID_ARG
+    assert "events" in B.spec_last_error()
+    ev = (ctypes.c_void_p * 2)(0x10, 0x20)
+    assert L.spec_verify_chain_timed(ctypes.byref(_chain(vocab=0)), 0x100000, 1 << 30, None,
+                                     ev) == B.SPEC_ERR_INVALID_ARG
+    assert L.spec_verify_chain_timed(ctypes.byref(_chain(batch=0, total_draft_rows=0)), None, 0,
+                                     None, ev) == B.SPEC_OK
 
 
 def test_chain_noalloc_rejects_shapes_beyond_its_scratch():
@@ -325,6 +339,7 @@ def _paged(**kw):
     dict(free_capacity=255), dict(slot_stride=1020), dict(lead_slots=2), dict(max_depth=0),
     dict(max_depth=65), dict(block_table=None), dict(free_list=None), dict(free_count=None),
     dict(k_cache=None), dict(max_blocks=1 << 20, block_size=1 << 12),
+    dict(max_blocks=(1 << 24) + 1, block_size=1),
     dict(num_kv_heads=1 << 25),  # 2^31 chunks per slot: past the copy grid's limit
 ])
 def test_kv_paged_validation(kw):

@@ -62,7 +62,7 @@ class GpuRound:
         o = oracle.verify_chain_v(tgt, drf, np.array([0, self.gamma], np.int32),
                                   np.array(drafts, np.int32), np.ones(1, np.float32), None,
                                   np.zeros(1, np.uint32), np.array([pos], np.int32),
-                                  seed=self.seed, vocab=4)
+                                  seed=self.seed, vocab=4, nthreads=1)
         n = int(o["num_accepted"][0])
         m_acc, m_all = o["margin"][0]
         if m_all < MARGIN:

@@ -310,7 +310,7 @@ def _markov_stream(orc, T, D, k, n_tokens, seed, seed_draft):
         tgt, drf = round_rows(tl, dl, last, drafts)
         r = orc.verify_chain_v(tgt, drf, np.array([0, k], np.int32), np.array(drafts, np.int32),
                                one, None, np.zeros(1, np.uint32), np.array([pos], np.int32),
-                               seed=seed, vocab=4)
+                               seed=seed, vocab=4, nthreads=1)
         return r["out_tokens"][:int(r["num_emitted"][0])]
 
     toks, st = run_stream(oracle_proposer(orc, dl, k, seed_draft), verify, n_tokens)
