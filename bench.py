@@ -18,6 +18,8 @@ bounded sample of the same workload as a reported baseline.
   python bench.py --workload c2|c5       # the other chain workloads (c3 is the default)
   python bench.py --workload c3_no_top_p|c3_greedy|c3_top_k_50   # c3 variants
   python bench.py --workload markov      # the vocab-4 Markov rounds (launch-bound)
+  python bench.py --summarize-trace DIR [--remove-csv]     # tables of a rocprofv3 trace
+  python bench.py --summarize-counters DIR [--remove-csv]  # tables of a rocprofv3 --pmc run
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
 大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
@@ -113,6 +115,82 @@ def read_traffic(src_hash):
     if not m or not t or m.group(1) != src_hash:
         return None
     return float(t.group(1))
+
+
+def _short_kernel_name(name):
+    name = name.replace("specv::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", name)
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _grid(r):
+    g = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+    w = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 1)
+    return g // max(w, 1), w
+
+
+def summarize_trace(d, last=100):
+    """Per (kernel, workgroups, workgroup size) of a rocprofv3 --kernel-trace csv run: the
+    dispatch count and the mean, median, min and max duration in us, over every dispatch and
+    over the last `last` ones, then the median gap between consecutive dispatches of the last
+    3 * `last`. Written to DIR/summary.txt and printed."""
+    import statistics as st
+    rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                   _short_kernel_name(r["Kernel_Name"])) + _grid(r)
+                  for r in _csv_rows(d, "kernel_trace.csv"))
+    groups = {}
+    for s0, e0, n, g, w in rows:
+        groups.setdefault((n, g, w), []).append((e0 - s0) / 1e3)
+    out = [f"dispatches: {len(rows)}",
+           f"{'kernel':58s} {'wgs':>7s} {'wg':>5s} {'n':>6s} {'avg':>9s} {'med':>9s} "
+           f"{'min':>9s} {'max':>9s} | last{last}: avg med"]
+    for (n, g, w), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        tail = ds[-last:]
+        out.append(f"{n[:58]:58s} {g:7d} {w:5d} {len(ds):6d} {st.mean(ds):9.2f} "
+                   f"{st.median(ds):9.2f} {min(ds):9.2f} {max(ds):9.2f} | "
+                   f"{st.mean(tail):8.2f} {st.median(tail):8.2f}")
+    gaps = {}
+    tail = rows[-3 * last:]
+    for a, b in zip(tail, tail[1:]):
+        gaps.setdefault((a[2][:30], b[2][:30]), []).append((b[0] - a[1]) / 1e3)
+    out.append("gaps between consecutive dispatches (last ones), median us:")
+    out += [f"  {a} -> {b}: {st.median(v):.2f} (n={len(v)})" for (a, b), v in gaps.items()]
+    return out
+
+
+def summarize_counters(d):
+    """Per (kernel, workgroups, counter) of a rocprofv3 --pmc csv run: the dispatch count and
+    the mean, min and max of the counter summed over its instances (FETCH_SIZE and WRITE_SIZE
+    are in KiB). Written to DIR/counters.txt and printed."""
+    import statistics as st
+    vals = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        key = (_short_kernel_name(r["Kernel_Name"]), _grid(r)[0], r["Counter_Name"])
+        per = vals.setdefault(key, {})
+        per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    out = []
+    for (n, g, c), per in sorted(vals.items()):
+        v = list(per.values())
+        out.append(f"{n[:56]:56s} wgs={g:7d} {c:18s} n={len(v):4d} mean={st.mean(v):16.1f} "
+                   f"min={min(v):16.1f} max={max(v):16.1f}")
+    return out
+
+
+def _write_summary(d, name, lines, remove_csv):
+    import glob
+    open(os.path.join(d, name), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if remove_csv:  # the per-dispatch csv files, which can run to hundreds of MB
+        for f in glob.glob(os.path.join(d, "**", "*.csv"), recursive=True):
+            if f.endswith(("kernel_trace.csv", "counter_collection.csv")):
+                os.remove(f)
 
 
 def cpu_baseline(x, n_seq, min_seconds=10.0):
@@ -528,7 +606,18 @@ def main():
                     choices=["chain", "c2", "c3", "c5", "c3_no_top_p", "c3_greedy",
                              "c3_top_k_50", "markov", "tree", "tree_draft", "paged_kv",
                              "ngram"])
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--remove-csv", action="store_true")
     args = ap.parse_args()
+    if args.summarize_trace:
+        _write_summary(args.summarize_trace, "summary.txt",
+                       summarize_trace(args.summarize_trace, 100), args.remove_csv)
+        return
+    if args.summarize_counters:
+        _write_summary(args.summarize_counters, "counters.txt",
+                       summarize_counters(args.summarize_counters), args.remove_csv)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the verification step has no cross-GPU exchange in "
               "this build (batch sharding is independent per GPU); run it with --gpus 1.",
