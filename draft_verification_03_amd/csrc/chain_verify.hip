@@ -978,8 +978,9 @@ __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, 
 }
 
 // Phase 2 of a row draw, once tile_sum holds every tile's sum and each lane knows the last
-// positive-weight token it saw: wave 0 scans the tile sums, then re-reads the chosen tile
-// and scans it.
+// positive-weight vector it saw: wave 0 scans the tile sums, then re-reads the chosen tile
+// and scans it. When u * total lands at or past the end (rounding), the draw is the row's
+// last token with positive weight, found in the last such vector.
 template <int NT>
 __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool residual,
                                           int nvec, int V, float u, int last, float* tile_sum,
@@ -1030,7 +1031,7 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
       gstar = __shfl(gstar, src, kWave);
       base = __shfl(base, src, kWave);
     }
-    int token = lst < 0 ? 0 : lst;
+    int token = -1;
     float wtok = 0.0f;
     if (gstar >= 0) {
       const int v = gstar * kWave + lane;
@@ -1083,18 +1084,21 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
           wt = __shfl(lw, src, kWave);
         }
       }
-      if (tok >= 0) {
-        token = tok;
-        wtok = wt;
-      }
-    } else if (lst >= 0) {  // u*total at or past the end: the last token with weight
-      const int v = lst / 8;
+      token = tok;
+      wtok = wt;
+    }
+    if (token < 0 && lst >= 0) {  // u*total at or past the end: the last token with weight
       float w[8];
-      vec_weights(Lp, Lq, residual, v, nvec, V, w);
-      wtok = w[lst & 7];
+      vec_weights(Lp, Lq, residual, lst, nvec, V, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (w[e] > 0.0f) {
+          token = lst * 8 + e;
+          wtok = w[e];
+        }
     }
     if (lane == 0) {
-      sh_i[0] = token;
+      sh_i[0] = token < 0 ? 0 : token;
       sh_f[0] = total;
       sh_f[1] = wtok;
     }
@@ -1111,10 +1115,73 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
 // Pass 1 stores per-tile sums (a tile = 64 vectors = 512 logits, one coalesced wave load;
 // each wave keeps TI tiles of p and of q in flight); draw_scan finishes.
 // Per-tile sums of a row (pair): each wave takes TI tiles at a time (a tile = 64 vectors =
-// 512 logits, one coalesced wave load per row); tile g -> tile_sum[g]. Returns the last token
-// with positive weight this lane saw (-1: none). A vector past the row loads the row's last
+// 512 logits, one coalesced wave load per row); tile g -> tile_sum[g]. Returns the last
+// vector with positive weight this lane saw (-1: none). A vector past the row loads the row's last
 // vector instead (its weight is zero), so that every load is one unconditional 16-byte load:
 // a load under a per-lane condition compiles to four predicated 4-byte loads.
+// Vector v with its logits at or past V set to -inf (v >= nvec: all of them), whose weights
+// are then 0 under a law without a cut.
+__device__ __forceinline__ uint4 mask_past_v(uint4 d, int v, int V) {
+  uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (v * 8 + e >= V) {
+      if (e & 1) w[e >> 1] = (w[e >> 1] & 0x0000FFFFu) | 0xFF800000u;
+      else w[e >> 1] = (w[e >> 1] & 0xFFFF0000u) | 0x0000FF80u;
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// tile_sums for laws without a cut (t = -inf on p, and on q when RES): the weights are the
+// same expression as data_weights gives, bit for bit (every finite or -inf logit passes the
+// cut, and a -inf logit weighs exactly 0), with the row's end masked to -inf in the lanes
+// that hold it instead of per-logit bound checks. Returns the last vector with positive
+// weight this lane saw (-1: none). Contraction is off, as it is where data_weights computes
+// them (a select sits between the product and the difference there), so that the product
+// and the difference round separately in both.
+template <int NT, int TI, bool RES>
+__device__ __forceinline__ int tile_sums_nocut(const RowLaw& Lp, const RowLaw& Lq, int nvec,
+                                               int V, float* tile_sum) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nw = NT / kWave;
+  const int ntiles = (nvec + kWave - 1) / kWave;
+  int lastv = -1;
+  for (int g0 = wid * TI; g0 < ntiles; g0 += nw * TI) {
+    uint4 dp[TI], dq[TI];
+#pragma unroll
+    for (int t = 0; t < TI; ++t) dp[t] = Lp.row[min((g0 + t) * kWave + lane, nvec - 1)];
+    if (RES) {
+#pragma unroll
+      for (int t = 0; t < TI; ++t) dq[t] = Lq.row[min((g0 + t) * kWave + lane, nvec - 1)];
+    }
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      const int v = (g0 + t) * kWave + lane;
+      uint4 a = dp[t], b = RES ? dq[t] : dp[t];
+      if (v >= nvec - 1) {  // the row's last vector, or past the row
+        a = mask_past_v(a, v, V);
+        if (RES) b = mask_past_v(b, v, V);
+      }
+      float xp[8], xq[8];
+      unpack8(a, xp);
+      if (RES) unpack8(b, xq);
+      float ls = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float w = weight(xp[e], Lp.c, Lp.nref) * Lp.iz;
+        if (RES) w = fmaxf(0.0f, w - weight(xq[e], Lq.c, Lq.nref) * Lq.iz);
+        ls += w;
+      }
+      if (ls > 0.0f) lastv = v;
+      const float ts = wave_sum_dpp(ls);
+      if (lane == 0 && g0 + t < ntiles) tile_sum[g0 + t] = ts;
+    }
+  }
+  return lastv;
+}
+
 template <int NT, int TI>
 __device__ __forceinline__ int tile_sums(const RowLaw& Lp, const RowLaw& Lq, bool residual,
                                          int nvec, int V, float* tile_sum) {
@@ -1122,7 +1189,11 @@ __device__ __forceinline__ int tile_sums(const RowLaw& Lp, const RowLaw& Lq, boo
   const int nw = NT / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
   const bool with_q = residual && Lq.point < 0;
-  int last = -1;  // last token with positive weight seen by this lane
+  if (Lp.t == -INFINITY && (!residual || (with_q && Lq.t == -INFINITY))) {
+    if (residual) return tile_sums_nocut<NT, TI, true>(Lp, Lq, nvec, V, tile_sum);
+    return tile_sums_nocut<NT, TI, false>(Lp, Lq, nvec, V, tile_sum);
+  }
+  int lastv = -1;  // last vector with positive weight seen by this lane
   for (int g0 = wid * TI; g0 < ntiles; g0 += nw * TI) {
     uint4 dp[TI], dq[TI];
 #pragma unroll
@@ -1142,15 +1213,13 @@ __device__ __forceinline__ int tile_sums(const RowLaw& Lp, const RowLaw& Lq, boo
       data_weights(Lp, Lq, residual, v, nvec, V, dp[t], dq[t], w);
       float ls = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ls += w[e];
-        if (w[e] > 0.0f) last = v * 8 + e;
-      }
-      const float ts = wave_sum(ls);
+      for (int e = 0; e < 8; ++e) ls += w[e];
+      if (ls > 0.0f) lastv = v;  // the weights are >= 0: a positive sum has a positive weight
+      const float ts = wave_sum_dpp(ls);
       if (lane == 0 && g0 + t < ntiles) tile_sum[g0 + t] = ts;
     }
   }
-  return last;
+  return lastv;
 }
 
 template <int NT, int TI>
