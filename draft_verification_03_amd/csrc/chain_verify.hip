@@ -48,6 +48,10 @@ constexpr float kCaptureKTopK = 10.0f;
 constexpr int kCapN = 1024;        // captured vectors per row held in LDS
 constexpr int kCapG = 1024;        // further captured vector ids per row spilled to the workspace
 constexpr int kDepth = 2;          // trips of loads in flight per wave in the row pass
+// Rows of at least kLongRow logits without captures keep kDepthLong trips in flight: the
+// deeper ring costs the kernel its third workgroup per CU, which short rows need more.
+constexpr int kDepthLong = 3;
+constexpr int kLongRow = 1 << 16;
 constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per workgroup)
 constexpr int kRowThreads = kRowWgWaves * kWave;
 constexpr int kHist = 512;         // key offsets below the row max resolved by the window search
@@ -692,8 +696,9 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
 // p_{gamma_b+1} (needed only after a full accept, but read with the rest: one workgroup
 // cannot pull a row from HBM fast enough to do it later without stalling the resolve step).
 // TOPP: the batch carries a top-p or top-k array (the captures and the cut are compiled in).
+// PD: trips in flight per wave on rows without captures.
 // ----------------------------------------------------------------------------------------
-template <bool TOPP>
+template <bool TOPP, int PD>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void row_stats_kernel(ChainParams P) {
   __shared__ RowLds L;
@@ -782,7 +787,7 @@ void row_stats_kernel(ChainParams P) {
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
     });
   else
-    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<PD>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<false>(dd, v0, lane, c, capw, acc, &L, nullptr);
     });
@@ -1563,9 +1568,14 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st, void
   // bonus row
   const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
   if (a.top_p || a.top_k)
-    hipLaunchKernelGGL(row_stats_kernel<true>, dim3(nrows), dim3(kRowThreads), 0, st, P);
+    hipLaunchKernelGGL((row_stats_kernel<true, kDepth>), dim3(nrows), dim3(kRowThreads), 0, st,
+                       P);
+  else if (a.vocab >= kLongRow)
+    hipLaunchKernelGGL((row_stats_kernel<false, kDepthLong>), dim3(nrows), dim3(kRowThreads), 0,
+                       st, P);
   else
-    hipLaunchKernelGGL(row_stats_kernel<false>, dim3(nrows), dim3(kRowThreads), 0, st, P);
+    hipLaunchKernelGGL((row_stats_kernel<false, kDepth>), dim3(nrows), dim3(kRowThreads), 0, st,
+                       P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   if (a.batch > kNumCus)
