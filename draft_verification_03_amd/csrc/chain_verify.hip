@@ -381,20 +381,24 @@ __device__ Cut bins_cut(const uint64_t cnt[PER], const uint64_t ms[PER], bool us
   return r;
 }
 
-// The captured vectors: LDS slots, then spilled indexes (whose vectors are read again from
-// the row).
-struct CapSrc {
+// Sources of a row's vectors for the end phase, each read through one address space (a getter
+// that picked LDS or global memory per index would compile to generic flat loads, which wait
+// on the vector memory path even for LDS): the captured vectors held in LDS (slots below
+// kCapN), the spilled ones (indexes in the workspace, vectors read again from the row), and
+// the whole row.
+struct CapLds {
   const RowLds* L;
+  __device__ void operator()(int j, int& vi, uint4& dv) const {
+    vi = L->idx[j];
+    dv = L->data[j];
+  }
+};
+struct CapSpill {
   const uint16_t* spill;
   const uint4* row;
   __device__ void operator()(int j, int& vi, uint4& dv) const {
-    if (j < kCapN) {
-      vi = L->idx[j];
-      dv = L->data[j];
-    } else {
-      vi = spill[j - kCapN];
-      dv = row[vi];
-    }
+    vi = spill[j - kCapN];
+    dv = row[vi];
   }
 };
 struct RowSrc {
@@ -405,20 +409,21 @@ struct RowSrc {
   }
 };
 
-// Nucleus list of a row once t is known: every kept logit (>= t, token < V) of the n source
-// vectors, claimed into LDS by a wave-aggregated atomic, then written to the workspace in
-// token order (each entry's position is the number of kept tokens below it). Returns the
-// kept count; above kNucMax the list is not written.
+// Nucleus list of a row once t is known: every kept logit (>= t, token < V) of the source
+// vectors, claimed into LDS by a wave-aggregated atomic (collect_range, once per source
+// range), then written to the workspace in token order (collect_finish: each entry's position
+// is the number of kept tokens below it). Returns the kept count; above kNucMax the list is
+// not written.
 template <typename Src>
-__device__ int collect_wg(Src src, int n, int V, float t, float c, float nref, RowLds* L,
-                          NucEntry* list, int tid) {
+__device__ __forceinline__ void collect_range(Src src, int j_begin, int j_end, int V, float t,
+                                              float c, float nref, RowLds* L, int tid) {
   const int lane = tid % kWave;
-  for (int j0 = tid - lane; j0 < n; j0 += kRowThreads) {
+  for (int j0 = j_begin + tid - lane; j0 < j_end; j0 += kRowThreads) {
     const int j = j0 + lane;
     float x[8];
     int vi = 0;
     uint32_t keep = 0;
-    if (j < n) {
+    if (j < j_end) {
       uint4 dv;
       src(j, vi, dv);
       unpack8(dv, x);
@@ -441,6 +446,8 @@ __device__ int collect_wg(Src src, int n, int V, float t, float c, float nref, R
       }
     }
   }
+}
+__device__ int collect_finish(RowLds* L, NucEntry* list, int tid) {
   __syncthreads();
   const int K = L->nkept;
   if (K <= kNucMax) {
@@ -557,7 +564,8 @@ __device__ TopP topp_full_row(const uint4* __restrict__ row, int nvec, int V, fl
   }
   r.t = o < 0 ? -INFINITY : value_of_key(kM - (uint32_t)o);
   r.zs = (float)((double)zs / kFix);
-  const int n = collect_wg(RowSrc{row}, nvec, V, r.t, c, nref, L, list, tid);
+  collect_range(RowSrc{row}, 0, nvec, V, r.t, c, nref, L, tid);
+  const int n = collect_finish(L, list, tid);
   r.nuc = n <= kNucMax ? n : -1;
   return r;
 }
@@ -575,11 +583,7 @@ __device__ __forceinline__ Cut capture_cut(const uint4* __restrict__ row, int V,
   const float nref = -M * c;
   const uint32_t kM = key_of(M);
   const int ntot = L->ncap;
-  const CapSrc src{L, spill, row};
-  for (int j = tid; j < ntot; j += kRowThreads) {
-    int vi;
-    uint4 dv;
-    src(j, vi, dv);
+  auto hist_vec = [&](int vi, const uint4& dv) {
     float x[8];
     unpack8(dv, x);
 #pragma unroll
@@ -591,6 +595,11 @@ __device__ __forceinline__ Cut capture_cut(const uint4* __restrict__ row, int V,
         atomicAdd(&L->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
       }
     }
+  };
+  for (int j = tid; j < min(ntot, kCapN); j += kRowThreads) hist_vec(L->idx[j], L->data[j]);
+  for (int j = kCapN + tid; j < ntot; j += kRowThreads) {
+    const int vi = spill[j - kCapN];
+    hist_vec(vi, row[vi]);
   }
   __syncthreads();
   constexpr int PER = kHist / kWave;
@@ -677,7 +686,9 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
       r.slow = again;  // a second read of the row
       r.t = value_of_key(kM - (uint32_t)cut.o);
       r.zs = (float)((double)cut.zs / kFix);
-      const int n = collect_wg(CapSrc{L, spill, row}, L->ncap, V, r.t, c, nref, L, list, tid);
+      collect_range(CapLds{L}, 0, min(L->ncap, kCapN), V, r.t, c, nref, L, tid);
+      collect_range(CapSpill{spill, row}, kCapN, L->ncap, V, r.t, c, nref, L, tid);
+      const int n = collect_finish(L, list, tid);
       r.nuc = n <= kNucMax ? n : -1;
       return r;
     }

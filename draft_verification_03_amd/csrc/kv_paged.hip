@@ -238,9 +238,17 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
       bool ok = node >= 1;
       if (ok && src != dst) {
         const int64_t row = (int64_t)(b0 + i) * mb;
+        // the LDS tile and the global table in branches of their own: one load that picked
+        // either per thread would be a generic flat load
         int pbs = -1, pbd = -1;
-        if (src >= 0 && src < slots) pbs = in_lds ? s_bt[i * mb + src / P.bs] : P.bt[row + src / P.bs];
-        if (dst >= 0 && dst < slots) pbd = in_lds ? s_bt[i * mb + dst / P.bs] : P.bt[row + dst / P.bs];
+        const bool sv = src >= 0 && src < slots, dv = dst >= 0 && dst < slots;
+        if (in_lds) {
+          if (sv) pbs = s_bt[i * mb + src / P.bs];
+          if (dv) pbd = s_bt[i * mb + dst / P.bs];
+        } else {
+          if (sv) pbs = P.bt[row + src / P.bs];
+          if (dv) pbd = P.bt[row + dst / P.bs];
+        }
         ok = pbs >= 0 && pbs < P.num_blocks && pbd >= 0 && pbd < P.num_blocks;
       }
       if (!ok) atomicMin(&s_need[i], -1);
