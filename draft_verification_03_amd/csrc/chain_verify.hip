@@ -112,6 +112,14 @@ __device__ __forceinline__ uint64_t fixw(float w) {
   return sh >= 0 ? (m << sh) : (m >> -sh);
 }
 
+// Logit e (0..7) of a vector: one of its two 64-bit halves, shifted (a word picked by index
+// would be lowered to a scratch array).
+__device__ __forceinline__ float logit_at(const uint4& d, int e) {
+  const uint64_t lo = ((uint64_t)d.y << 32) | d.x, hi = ((uint64_t)d.w << 32) | d.z;
+  const uint64_t h = (e & 4) ? hi : lo;
+  return bf_lo((uint32_t)(h >> ((e & 3) * 16)));
+}
+
 __device__ __forceinline__ int wave_incl_scan_i(int v, int) { return wave_incl_scan_dpp(v); }
 
 // Parameters checked on their bit patterns (NaN fails every test). T: +0 or -0 (greedy), or
@@ -423,8 +431,8 @@ __device__ __forceinline__ void collect_range(Src src, int j_begin, int j_end, i
     float x[8];
     int vi = 0;
     uint32_t keep = 0;
+    uint4 dv{0u, 0u, 0u, 0u};
     if (j < j_end) {
-      uint4 dv;
       src(j, vi, dv);
       unpack8(dv, x);
 #pragma unroll
@@ -438,12 +446,12 @@ __device__ __forceinline__ void collect_range(Src src, int j_begin, int j_end, i
     int base = 0;
     if (lane == 0) base = atomicAdd(&L->nkept, tot);
     int pos = __builtin_amdgcn_readfirstlane(base) + incl - cnt;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if ((keep >> e) & 1u) {
-        if (pos < kNucMax) L->kept[pos] = NucEntry{vi * 8 + e, weight(x[e], c, nref)};
-        ++pos;
-      }
+    // the kept logits in increasing e, one round per kept logit of the busiest lane
+    while (keep) {
+      const int e = __builtin_ctz(keep);
+      keep &= keep - 1;
+      if (pos < kNucMax) L->kept[pos] = NucEntry{vi * 8 + e, weight(logit_at(dv, e), c, nref)};
+      ++pos;
     }
   }
 }
@@ -583,17 +591,21 @@ __device__ __forceinline__ Cut capture_cut(const uint4* __restrict__ row, int V,
   const float nref = -M * c;
   const uint32_t kM = key_of(M);
   const int ntot = L->ncap;
+  // The logits of the vector that fall in the bins first, as a mask; then only those: a wave
+  // takes as many rounds as its busiest lane has such logits (usually one or two of eight).
   auto hist_vec = [&](int vi, const uint4& dv) {
     float x[8];
     unpack8(dv, x);
+    uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (vi * 8 + e >= V || !(x[e] >= theta)) continue;
-      const uint32_t o = kM - key_of(x[e]);
-      if (o < (uint32_t)kHist) {
-        if (use_k) atomicAdd(&L->hcnt[o], 1u);
-        atomicAdd(&L->hist[o], (unsigned long long)fixw(weight(x[e], c, nref)));
-      }
+    for (int e = 0; e < 8; ++e)
+      if (vi * 8 + e < V && x[e] >= theta && kM - key_of(x[e]) < (uint32_t)kHist) m |= 1u << e;
+    while (m) {
+      const float xe = logit_at(dv, __builtin_ctz(m));
+      m &= m - 1;
+      const uint32_t o = kM - key_of(xe);
+      if (use_k) atomicAdd(&L->hcnt[o], 1u);
+      atomicAdd(&L->hist[o], (unsigned long long)fixw(weight(xe, c, nref)));
     }
   };
   for (int j = tid; j < min(ntot, kCapN); j += kRowThreads) hist_vec(L->idx[j], L->data[j]);
