@@ -54,6 +54,7 @@ constexpr int kDepthLong = 3;
 constexpr int kLongRow = 1 << 16;
 constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per workgroup)
 constexpr int kRowThreads = kRowWgWaves * kWave;
+constexpr int kCand = 1024;        // window logits kept as candidates for the nucleus list
 constexpr int kHist = 512;         // key offsets below the row max resolved by the window search
 // Resolve workgroup shapes (threads, row-pair tiles in flight per wave in the resolve pass):
 // one 1024-thread workgroup per CU while the batch fits the CUs, 256-thread workgroups
@@ -193,6 +194,8 @@ struct RowLds {
   unsigned long long hist[kHist];  // fixed-point masses by key offset below the row max
   uint32_t hcnt[kHist];            // logits by key offset below the row max (top-k)
   NucEntry kept[kNucMax];          // nucleus entries before they are put in token order
+  int32_t ctok[kCand];             // the window's logits as the bins take them: token ...
+  float cval[kCand];               // ... and logit (the nucleus list filters these)
   uint16_t idx[kCapN];             // vector index of each captured vector
   float wmax[kRowWgWaves];         // each wave's max so far, published for the others
   float lmax[kRowThreads];         // every lane's max at the end of the stream
@@ -201,6 +204,7 @@ struct RowLds {
   int trip;                        // trips of the row claimed by the waves
   int ncap;                        // capture slots claimed: LDS slots, then spill slots
   int nkept;                       // nucleus entries claimed
+  int ncand;                       // window logits claimed (past kCand: only counted)
 };
 
 // Claims slots for the trip's flagged vectors (one LDS atomic per wave) and writes them:
@@ -455,6 +459,27 @@ __device__ __forceinline__ void collect_range(Src src, int j_begin, int j_end, i
     }
   }
 }
+// The nucleus entries from the window's candidates: every logit >= t of the row lies in the
+// window and in the bins (t is the value of a non-empty bin), so filtering the candidates
+// gives the same kept set as a pass over the captured vectors.
+__device__ __forceinline__ void collect_cands(RowLds* L, int nc, float t, float c, float nref,
+                                              int tid) {
+  const int lane = tid % kWave;
+  for (int j0 = tid - lane; j0 < nc; j0 += kRowThreads) {
+    const int j = j0 + lane;
+    const bool keep = j < nc && L->cval[j] >= t;
+    const uint64_t bm = __ballot(keep);
+    if (!bm) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&L->nkept, __popcll(bm));
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (keep) {
+      const int pos = base + (int)lanes_below(bm);
+      if (pos < kNucMax) L->kept[pos] = NucEntry{L->ctok[j], weight(L->cval[j], c, nref)};
+    }
+  }
+}
+
 __device__ int collect_finish(RowLds* L, NucEntry* list, int tid) {
   __syncthreads();
   const int K = L->nkept;
@@ -601,11 +626,22 @@ __device__ __forceinline__ Cut capture_cut(const uint4* __restrict__ row, int V,
     for (int e = 0; e < 8; ++e)
       if (vi * 8 + e < V && x[e] >= theta && kM - key_of(x[e]) < (uint32_t)kHist) m |= 1u << e;
     while (m) {
-      const float xe = logit_at(dv, __builtin_ctz(m));
+      const int e = __builtin_ctz(m);
+      const float xe = logit_at(dv, e);
       m &= m - 1;
       const uint32_t o = kM - key_of(xe);
       if (use_k) atomicAdd(&L->hcnt[o], 1u);
       atomicAdd(&L->hist[o], (unsigned long long)fixw(weight(xe, c, nref)));
+      // the logit is also a candidate for the nucleus list: one claim per wave and round
+      const uint64_t act = __ballot(1);
+      const int r = (int)lanes_below(act);
+      int base = 0;
+      if (r == 0) base = atomicAdd(&L->ncand, __popcll(act));
+      const int pos = __builtin_amdgcn_readfirstlane(base) + r;
+      if (pos < kCand) {
+        L->ctok[pos] = vi * 8 + e;
+        L->cval[pos] = xe;
+      }
     }
   };
   for (int j = tid; j < min(ntot, kCapN); j += kRowThreads) hist_vec(L->idx[j], L->data[j]);
@@ -646,7 +682,10 @@ __device__ void recapture(const uint4* __restrict__ row, int nvec, int V, float 
                           uint16_t* spill, int tid) {
   const int lane = tid % kWave;
   __syncthreads();  // every thread is done with the first capture and its bins
-  if (tid == 0) L->ncap = 0;
+  if (tid == 0) {
+    L->ncap = 0;
+    L->ncand = 0;
+  }
   for (int i = tid; i < kHist; i += kRowThreads) {
     L->hist[i] = 0ull;
     L->hcnt[i] = 0u;
@@ -698,8 +737,13 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
       r.slow = again;  // a second read of the row
       r.t = value_of_key(kM - (uint32_t)cut.o);
       r.zs = (float)((double)cut.zs / kFix);
-      collect_range(CapLds{L}, 0, min(L->ncap, kCapN), V, r.t, c, nref, L, tid);
-      collect_range(CapSpill{spill, row}, kCapN, L->ncap, V, r.t, c, nref, L, tid);
+      const int nc = L->ncand;
+      if (nc <= kCand) {
+        collect_cands(L, nc, r.t, c, nref, tid);
+      } else {
+        collect_range(CapLds{L}, 0, min(L->ncap, kCapN), V, r.t, c, nref, L, tid);
+        collect_range(CapSpill{spill, row}, kCapN, L->ncap, V, r.t, c, nref, L, tid);
+      }
       const int n = collect_finish(L, list, tid);
       r.nuc = n <= kNucMax ? n : -1;
       return r;
@@ -765,6 +809,7 @@ void row_stats_kernel(ChainParams P) {
     L.trip = 0;
     L.ncap = 0;
     L.nkept = 0;
+    L.ncand = 0;
   }
   if (tid < kRowWgWaves) L.wmax[tid] = -INFINITY;
   if (filt)
