@@ -69,8 +69,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-# The row pass's sources: its kernel file and the library headers it includes.
+# Each workload's kernel sources: its kernel files and the library headers they include.
 CHAIN_SOURCES = ("chain_verify.hip", "row_ops.h", "spec_device.h", "specv_internal.h")
+TREE_SOURCES = ("tree_verify.hip", "kv_commit.hip", "row_ops.h", "spec_device.h",
+                "specv_internal.h")
+TREE_DRAFT_SOURCES = ("tree_draft.hip", "row_ops.h", "spec_device.h", "specv_internal.h")
+PAGED_SOURCES = ("kv_paged.hip", "spec_device.h", "specv_internal.h")
+NGRAM_SOURCES = ("ngram_draft.hip", "spec_device.h", "specv_internal.h")
 
 
 def kernel_source_hash(files=None) -> str:
@@ -313,7 +318,7 @@ def tree_draft_bench(args):
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
                      "bytes_per_launch": row_bytes, "avg_launch_us": ms * 1e3,
-                     "kernel_source_hash": kernel_source_hash()},
+                     "kernel_source_hash": kernel_source_hash(TREE_DRAFT_SOURCES)},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -414,7 +419,8 @@ def paged_kv_bench(args):
         "roofline": {"bound": "hbm", "kernel": "paged_copy_kernel + paged_release_kernel",
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": nbytes,
-                     "avg_launch_us": ms * 1e3, "kernel_source_hash": kernel_source_hash()},
+                     "avg_launch_us": ms * 1e3,
+                     "kernel_source_hash": kernel_source_hash(PAGED_SOURCES)},
     }
     print(json.dumps(res), flush=True)
     del caches
@@ -516,7 +522,7 @@ def tree_bench(args):
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
                      "bytes_per_launch": tree_bytes, "avg_launch_us": ms_tree * 1e3,
-                     "kernel_source_hash": kernel_source_hash()},
+                     "kernel_source_hash": kernel_source_hash(TREE_SOURCES)},
         "kv_commit": {"kernel": "kv_copy_kernel + kv_pointer_kernel", "us": ms_kv * 1e3,
                       "bytes": kv_bytes, "achieved": kv_gbs, "frac": kv_gbs / PEAK_HBM_GBS},
     }
@@ -575,7 +581,7 @@ def ngram_bench(args):
         "roofline": {"bound": "hbm", "kernel": "ngram_draft_kernel", "achieved": gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                      "traffic": None, "bytes_per_launch": nbytes, "avg_launch_us": ms * 1e3,
-                     "kernel_source_hash": kernel_source_hash()},
+                     "kernel_source_hash": kernel_source_hash(NGRAM_SOURCES)},
     }
     if not args.no_cpu_baseline:
         import oracle
