@@ -104,6 +104,37 @@ def test_top_p_nuclei_across_list_sizes():
         check_chain(x, seed=seed, label=f"top-p list sizes {sizes} seed {seed}")
 
 
+def _window_rows(rng, V, n_top, n_window):
+    """Rows with n_top tied logits at 12, n_window logits spread over [5.5, 7] (inside a 7*T
+    window at T = 1, but with little mass) and the rest near -6."""
+    row = rng.normal(-6.0, 1.0, V).astype(np.float32)
+    ids = rng.choice(V, size=n_top + n_window, replace=False)
+    row[ids[:n_top]] = 12.0
+    row[ids[n_top:]] = rng.uniform(5.5, 7.0, n_window).astype(np.float32)
+    return row
+
+
+def test_top_p_window_beyond_the_candidate_buffer():
+    """More than 1024 logits inside the capture window, a nucleus of ten: the list is built by
+    the pass over the captured vectors (some of them spilled), not from the bins' candidates,
+    and still matches the oracle."""
+    rng = np.random.default_rng(77)
+    V, gamma, Bn = 20000, 3, 8
+    tgt = np.stack([_window_rows(rng, V, 10, 1100) for _ in range(Bn * (gamma + 1))])
+    drf = np.stack([tgt[b * (gamma + 1) + k] + rng.normal(0.0, 0.3, V).astype(np.float32)
+                    for b in range(Bn) for k in range(gamma)])
+    x = dict(target=W.bf16_bits(tgt), draft=W.bf16_bits(drf),
+             cu_gamma=np.arange(Bn + 1, dtype=np.int32) * gamma,
+             temperature=np.ones(Bn, np.float32), top_p=np.full(Bn, 0.5, np.float32),
+             seq_id=np.arange(Bn, dtype=np.uint32),
+             committed_len=rng.integers(0, 4096, Bn).astype(np.int32), vocab=V, stride=V)
+    row0 = W.bf16_to_f32(x["target"][0])
+    assert int((row0 >= row0.max() - 7.0).sum()) > 1024
+    assert oracle.dist(x["target"][0], 1.0, 0.5)[1]["nucleus"] == 10
+    o, g, _ = check_chain(x, seed=29, label="window beyond the candidate buffer")
+    assert not np.any(g["seq_flags"] & B.FLAG_TOPP_SLOW)
+
+
 @pytest.mark.parametrize("V,topp", [(128256, 0.9), (128256, None), (200000, 0.9),
                                     (200000, None)])
 def test_every_draft_accepted_bonus_draw(V, topp):
