@@ -9,9 +9,10 @@
 // Structure
 //  1. row_stats_kernel -- one workgroup of kRowWgWaves waves per logits row: the target row
 //     p_k or the draft row q_k of draft position k = 1..gamma_b, and the bonus row
-//     p_{gamma_b+1}. The waves take the row's trips in turn (16-byte loads, two trips in
-//     flight per wave), so the row streams from HBM once as one wide sequential read, and
-//     the hardware hands rows to CUs as they free up:
+//     p_{gamma_b+1}. The waves claim the row's trips from an LDS counter (16-byte loads; two
+//     trips in flight per wave with captures, three on rows of 64K+ logits without), so the
+//     row streams from HBM once as one wide sequential read, and the hardware hands rows to
+//     CUs as they free up:
 //       - per trip (4 KB of the row): its max and its sum of exp2((l - max) * log2(e)/T),
 //         each reduced over the wave in a fixed order and kept by trip index, so that the
 //         row's (m, Z), combined in trip order, does not depend on which wave took a trip;
@@ -23,7 +24,8 @@
 //     After a workgroup barrier the end phase gives m, Z, the nucleus threshold t*
 //     (fixed-point mass histogram over bf16 keys of the captured logits; an exact multi-pass
 //     search over the whole row if the window did not hold the nucleus), the draft token's
-//     weight, and the nucleus list in token order (<= kNucMax tokens) for the residual draw.
+//     weight, and the nucleus list in token order (<= kNucMax tokens) for the residual draw,
+//     filtered from the window logits the histogram pass recorded.
 //  2. chain_resolve_kernel -- one workgroup per sequence: p_k(d_k), q_k(d_k) and the
 //     acceptance decisions from the row statistics, the first rejection (one ballot), then
 //     the residual or bonus draw -- from the nucleus lists when both are kept (their heads
@@ -58,7 +60,7 @@ constexpr int kCand = 1024;        // window logits kept as candidates for the n
 constexpr int kHist = 512;         // key offsets below the row max resolved by the window search
 // Resolve workgroup shapes (threads, row-pair tiles in flight per wave in the resolve pass):
 // one 1024-thread workgroup per CU while the batch fits the CUs, 256-thread workgroups
-// beyond (four per CU at 128 VGPRs), so that the latency-bound decisions and scans of some
+// beyond (four or more per CU), so that the latency-bound decisions and scans of some
 // sequences overlap the row traffic of others.
 constexpr int kResolveWide = 1024, kTilesWide = 4;
 constexpr int kResolveNarrow = 256, kTilesNarrow = 5;
