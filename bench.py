@@ -58,6 +58,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+# Copies of a workload's rows that the tree and tree-drafting legs take in turn: together
+# they exceed the 256 MB memory-side cache, so each call reads its rows from HBM.
+ROTATE = 3
 METRIC = "verify rows/sec at B=256 γ=8 V=128k; achieved HBM GB/s vs peak"
 SEED = 2024
 SEED_DRAFT = 9090
@@ -267,18 +270,22 @@ def tree_draft_bench(args):
              expand_nodes=torch.empty((Bn, max(th)), **i32))
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
         np.int16 if a.dtype == np.uint16 else a.dtype)).cuda()
-    rows = [dv(r) for r in x["rows"]]
+    # ROTATE copies of the draft rows (3 x 194 MB), one per round in turn, so that a round
+    # does not find its rows in the 256 MB memory-side cache from the round before
     root, pos = dv(x["root_token"]), dv(x["pos_base"])
-    steps = [B.tree_draft_args(top_head=th, top_k_spec=ks, step=s, draft_logits=rows[s],
-                               root_token=root, pos_base=pos, vocab=V, **t)
-             for s in range(len(th))]
+    rounds = []
+    for _ in range(ROTATE):
+        rows = [dv(r) for r in x["rows"]]
+        rounds.append([B.tree_draft_args(top_head=th, top_k_spec=ks, step=s,
+                                         draft_logits=rows[s], root_token=root, pos_base=pos,
+                                         vocab=V, **t) for s in range(len(th))])
     ws = torch.empty(B.spec_tree_draft_workspace_size(Bn, V, th, ks), dtype=torch.uint8,
                      device="cuda")
     L = B.lib()
     wsp, wsn = ws.data_ptr(), ws.numel()
 
-    def round_(stream):
-        for a in steps:
+    def round_(i, stream):
+        for a in rounds[i % ROTATE]:
             rc = L.spec_tree_draft_step(ctypes.byref(a), wsp, wsn, stream)
             if rc != 0:
                 raise B.SpecError(rc, B.spec_last_error())
@@ -288,15 +295,15 @@ def tree_draft_bench(args):
     done = 0
     while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
         for _ in range(10):
-            round_(st)
-        done += 10
+            round_(done, st)
+            done += 1
         torch.cuda.synchronize()
     log(f"timing {args.steps} rounds")
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
-        round_(st)
+    for i in range(args.steps):
+        round_(i, st)
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -444,16 +451,20 @@ def tree_bench(args):
     lg = x["logits"]
     dv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(  # noqa: E731
         {np.dtype(np.uint16): np.int16}.get(a.dtype, a.dtype))).cuda()
-    logits = dv(lg.reshape(-1, lg.shape[-1]))
+    # ROTATE copies of the target rows (3 x 194 MB), one per step in turn, so that a call
+    # does not find its rows in the 256 MB memory-side cache from the call before
+    logit_sets = [dv(lg.reshape(-1, lg.shape[-1])) for _ in range(ROTATE)]
     pn = torch.full((Bn, md), -1, dtype=torch.int32, device="cuda")
     pl = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     out = torch.full((Bn, md + 1), -1, dtype=torch.int32, device="cuda")
     ne = torch.zeros(Bn, dtype=torch.int32, device="cuda")
     tfl = torch.zeros(Bn, dtype=torch.int32, device="cuda")
-    ta = B.tree_args(target_logits=logits, parent=dv(x["parent"]), node_row=dv(x["node_row"]),
-                     node_token=dv(x["node_token"]), path_nodes=pn, path_len=pl,
-                     out_tokens=out, num_emitted=ne, seq_flags=tfl, vocab=V, rows_per_seq=R,
-                     max_depth=md, tree_stride=x["num_nodes"], row_stride=lg.shape[-1])
+    parent, node_row, node_token = dv(x["parent"]), dv(x["node_row"]), dv(x["node_token"])
+    tas = [B.tree_args(target_logits=lgs, parent=parent, node_row=node_row,
+                       node_token=node_token, path_nodes=pn, path_len=pl, out_tokens=out,
+                       num_emitted=ne, seq_flags=tfl, vocab=V, rows_per_seq=R, max_depth=md,
+                       tree_stride=x["num_nodes"], row_stride=lg.shape[-1])
+           for lgs in logit_sets]
     ws = torch.empty(max(B.spec_verify_tree_workspace_size(Bn, R), 1), dtype=torch.uint8,
                      device="cuda")
     NL, H, Dh, S = (W.KV_SHAPE[k] for k in ("num_layers", "num_kv_heads", "head_dim", "slots"))
@@ -468,15 +479,15 @@ def tree_bench(args):
                    num_kv_heads=H, head_dim=Dh, seq_stride=S * H * Dh, slot_stride=H * Dh,
                    head_stride=Dh, slot_capacity=S, lead_slots=1, max_depth=md)
 
-    def step():
-        B.spec_verify_tree(ta, workspace=ws)
+    def step(i):
+        B.spec_verify_tree(tas[i % ROTATE], workspace=ws)
         B.kv_commit_path(ka)
 
     t_warm = time.time()
     done = 0
     while done < args.warmup or time.time() - t_warm < args.warmup_seconds:
         Lt.copy_(L_init)
-        step()
+        step(done)
         done += 1
         if done % 10 == 0:
             torch.cuda.synchronize()
@@ -484,10 +495,10 @@ def tree_bench(args):
     log(f"timing {args.steps} steps")
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
            for _ in range(args.steps)]
-    for e0, e1, e2 in evs:
+    for i, (e0, e1, e2) in enumerate(evs):
         Lt.copy_(L_init)
         e0.record()
-        B.spec_verify_tree(ta, workspace=ws)
+        B.spec_verify_tree(tas[i % ROTATE], workspace=ws)
         e1.record()
         B.kv_commit_path(ka)
         e2.record()

@@ -9,10 +9,10 @@
 // Structure
 //  1. row_stats_kernel -- one workgroup of kRowWgWaves waves per logits row: the target row
 //     p_k or the draft row q_k of draft position k = 1..gamma_b, and the bonus row
-//     p_{gamma_b+1}. The waves claim the row's trips from an LDS counter (16-byte loads; two
-//     trips in flight per wave with captures, three on rows of 64K+ logits without), so the
-//     row streams from HBM once as one wide sequential read, and the hardware hands rows to
-//     CUs as they free up:
+//     p_{gamma_b+1}. The waves claim the row's trips from an LDS counter (16-byte loads,
+//     nontemporal unless the batch has a top-k array; two trips in flight per wave with
+//     captures, three on rows of 64K+ logits without), so the row streams from HBM once as
+//     one wide sequential read, and the hardware hands rows to CUs as they free up:
 //       - per trip (4 KB of the row): its max and its sum of exp2((l - max) * log2(e)/T),
 //         each reduced over the wave in a fixed order and kept by trip index, so that the
 //         row's (m, Z), combined in trip order, does not depend on which wave took a trip;
@@ -766,8 +766,10 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
 // cannot pull a row from HBM fast enough to do it later without stalling the resolve step).
 // TOPP: the batch carries a top-p or top-k array (the captures and the cut are compiled in).
 // PD: trips in flight per wave on rows without captures.
+// NT: the row streams use nontemporal loads; off for batches with a top-k array, whose rows
+// may be captured a second time.
 // ----------------------------------------------------------------------------------------
-template <bool TOPP, int PD>
+template <bool TOPP, int PD, bool NT>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void row_stats_kernel(ChainParams P) {
   __shared__ RowLds L;
@@ -824,7 +826,7 @@ void row_stats_kernel(ChainParams P) {
   if (s.T == 0.0f) {  // greedy: argmax of the target row, lowest index on ties
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
+    stream_row_claimed<kDepth, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
       argmax_trip(dd, v0, P.nvec, P.V, lane, bv, bi);
     });
     wave_argmax(bv, bi);
@@ -852,12 +854,12 @@ void row_stats_kernel(ChainParams P) {
   uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
   if (filt)
-    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepth, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
     });
   else
-    stream_row_claimed<PD>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<PD, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<false>(dd, v0, lane, c, capw, acc, &L, nullptr);
     });
@@ -1637,15 +1639,18 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st, void
   // per sequence: two rows (target, draft) per draft position slot k <= max_gamma, then the
   // bonus row
   const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
-  if (a.top_p || a.top_k)
-    hipLaunchKernelGGL((row_stats_kernel<true, kDepth>), dim3(nrows), dim3(kRowThreads), 0, st,
-                       P);
+  if (a.top_k)
+    hipLaunchKernelGGL((row_stats_kernel<true, kDepth, false>), dim3(nrows), dim3(kRowThreads),
+                       0, st, P);
+  else if (a.top_p)
+    hipLaunchKernelGGL((row_stats_kernel<true, kDepth, true>), dim3(nrows), dim3(kRowThreads),
+                       0, st, P);
   else if (a.vocab >= kLongRow)
-    hipLaunchKernelGGL((row_stats_kernel<false, kDepthLong>), dim3(nrows), dim3(kRowThreads), 0,
-                       st, P);
+    hipLaunchKernelGGL((row_stats_kernel<false, kDepthLong, true>), dim3(nrows),
+                       dim3(kRowThreads), 0, st, P);
   else
-    hipLaunchKernelGGL((row_stats_kernel<false, kDepth>), dim3(nrows), dim3(kRowThreads), 0, st,
-                       P);
+    hipLaunchKernelGGL((row_stats_kernel<false, kDepth, true>), dim3(nrows), dim3(kRowThreads),
+                       0, st, P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   if (a.batch > kNumCus)

@@ -3,7 +3,8 @@
 // come from one target forward with a tree attention mask, "10.6 投机解码" §10.6.3).
 //
 //  1. tree_argmax_kernel -- one 8-wave workgroup per provided target row: the waves claim the
-//     row's 4 KB trips from an LDS counter (two in flight per wave) and keep per-lane maxima
+//     row's 4 KB trips from an LDS counter (two in flight per wave, nontemporal 16-byte loads:
+//     every row is read once) and keep per-lane maxima
 //     with the earliest index; wave, then workgroup reductions give the argmax (lowest id on
 //     ties), written to the workspace.
 //  2. tree_walk_kernel   -- one wave per sequence: checks the topology, then walks from the
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kArgWaves * kWave) void tree_argmax_kernel(TreePara
   // earliest index of its maximum
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  stream_row_claimed<2>(rp, P.nvec, lane, &s_trip, [&](uint4* d, int v0, bool) {
+  stream_row_claimed<2, true>(rp, P.nvec, lane, &s_trip, [&](uint4* d, int v0, bool) {
     argmax_trip(d, v0, P.nvec, P.V, lane, bv, bi);
   });
   wave_argmax(bv, bi);
