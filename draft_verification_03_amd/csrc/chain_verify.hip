@@ -10,9 +10,9 @@
 //  1. row_stats_kernel -- one workgroup of kRowWgWaves waves per logits row: the target row
 //     p_k or the draft row q_k of draft position k = 1..gamma_b, and the bonus row
 //     p_{gamma_b+1}. The waves claim the row's trips from an LDS counter (16-byte loads,
-//     nontemporal unless the batch has a top-k array; two trips in flight per wave with
-//     captures, three on rows of 64K+ logits without), so the row streams from HBM once as
-//     one wide sequential read, and the hardware hands rows to CUs as they free up:
+//     nontemporal unless the batch has a top-k array; one trip in flight per wave while
+//     capturing, two otherwise), so the row streams from HBM once as one wide sequential
+//     read, and the hardware hands rows to CUs as they free up:
 //       - per trip (4 KB of the row): its max and its sum of exp2((l - max) * log2(e)/T),
 //         each reduced over the wave in a fixed order and kept by trip index, so that the
 //         row's (m, Z), combined in trip order, does not depend on which wave took a trip;
@@ -50,10 +50,10 @@ constexpr float kCaptureKTopK = 10.0f;
 constexpr int kCapN = 1024;        // captured vectors per row held in LDS
 constexpr int kCapG = 1024;        // further captured vector ids per row spilled to the workspace
 constexpr int kDepth = 2;          // trips of loads in flight per wave in the row pass
-// Rows of at least kLongRow logits without captures keep kDepthLong trips in flight: the
-// deeper ring costs the kernel its third workgroup per CU, which short rows need more.
-constexpr int kDepthLong = 3;
-constexpr int kLongRow = 1 << 16;
+// Rows with captures keep one trip in flight per wave: the capture registers then leave room
+// for three workgroups per CU (six waves per SIMD), and the third workgroup's stream covers
+// the end phases of the other two.
+constexpr int kDepthCap = 1;
 constexpr int kRowWgWaves = 8;     // waves of a row-pass workgroup (one row per workgroup)
 constexpr int kRowThreads = kRowWgWaves * kWave;
 constexpr int kCand = 1024;        // window logits kept as candidates for the nucleus list
@@ -765,12 +765,11 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
 // p_{gamma_b+1} (needed only after a full accept, but read with the rest: one workgroup
 // cannot pull a row from HBM fast enough to do it later without stalling the resolve step).
 // TOPP: the batch carries a top-p or top-k array (the captures and the cut are compiled in).
-// PD: trips in flight per wave on rows without captures.
 // NT: the row streams use nontemporal loads; off for batches with a top-k array, whose rows
 // may be captured a second time.
 // ----------------------------------------------------------------------------------------
-template <bool TOPP, int PD, bool NT>
-__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(4)))
+template <bool TOPP, bool NT>
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(6)))
 void row_stats_kernel(ChainParams P) {
   __shared__ RowLds L;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -854,12 +853,12 @@ void row_stats_kernel(ChainParams P) {
   uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
   if (filt)
-    stream_row_claimed<kDepth, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepthCap, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
     });
   else
-    stream_row_claimed<PD, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepth, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<false>(dd, v0, lane, c, capw, acc, &L, nullptr);
     });
@@ -1640,17 +1639,13 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st, void
   // bonus row
   const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
   if (a.top_k)
-    hipLaunchKernelGGL((row_stats_kernel<true, kDepth, false>), dim3(nrows), dim3(kRowThreads),
-                       0, st, P);
+    hipLaunchKernelGGL((row_stats_kernel<true, false>), dim3(nrows), dim3(kRowThreads), 0, st,
+                       P);
   else if (a.top_p)
-    hipLaunchKernelGGL((row_stats_kernel<true, kDepth, true>), dim3(nrows), dim3(kRowThreads),
-                       0, st, P);
-  else if (a.vocab >= kLongRow)
-    hipLaunchKernelGGL((row_stats_kernel<false, kDepthLong, true>), dim3(nrows),
-                       dim3(kRowThreads), 0, st, P);
+    hipLaunchKernelGGL((row_stats_kernel<true, true>), dim3(nrows), dim3(kRowThreads), 0, st, P);
   else
-    hipLaunchKernelGGL((row_stats_kernel<false, kDepth, true>), dim3(nrows), dim3(kRowThreads),
-                       0, st, P);
+    hipLaunchKernelGGL((row_stats_kernel<false, true>), dim3(nrows), dim3(kRowThreads), 0, st,
+                       P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   if (a.batch > kNumCus)
