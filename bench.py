@@ -24,7 +24,9 @@ bounded sample of the same workload as a reported baseline.
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
 大模型一次验证": top_head [1, 2, 2], top_k_spec [[6], [2, 2], [1, 1]]) over B=128 sequences
 with V=151936 draft rows: three spec_tree_draft_step calls reading 128, 256 and 256 draft
-rows. The line reports draft rows/s and the HBM bandwidth of the steps against 8 TB/s.
+rows. The rounds take three copies of the draft rows in turn (3 x 194 MB, more than the
+256 MB memory-side cache), so every round reads its rows from HBM. The line reports draft
+rows/s and the HBM bandwidth of the steps against 8 TB/s.
 
 With --workload paged_kv a step is one kv_commit_paged call committing the tree workload's
 accepted paths (B=128, depth <= 3) into a cache of 32 layers x K,V x 8 heads x 128 bf16 paged
@@ -35,8 +37,9 @@ that time it.
 With --workload tree a step is one spec_verify_tree call over the tree workload (B=128,
 V=151936, 5 target rows and 12 nodes per sequence, tree [6], [2, 2], [1, 1]) followed by one
 kv_commit_path of the accepted paths into a contiguous cache of 32 layers x K,V x 8 heads x
-128 bf16 (1024 slots per sequence, 17.2 GB). The committed lengths are restored before each
-step, outside the events. The line reports verify rows/s and the verify call's HBM bandwidth
+128 bf16 (1024 slots per sequence, 17.2 GB). The steps take three copies of the target rows
+in turn (3 x 194 MB, more than the 256 MB memory-side cache), so every call reads its rows
+from HBM. The committed lengths are restored before each step, outside the events. The line reports verify rows/s and the verify call's HBM bandwidth
 (the argmax kernel's rows, plus its small walk launch) against 8 TB/s; the commit's time and
 bytes ride along under "kv_commit".
 
@@ -320,7 +323,8 @@ def tree_draft_bench(args):
         "data": "synthetic",
         "config": {"workload": "tree drafting round, B=128, V=151936 bf16 draft rows "
                                "N(0,2^2), top_head [1,2,2], top_k_spec [[6],[2,2],[1,1]]",
-                   "draft_rows_per_round": nrows, "round_algorithmic_bytes": row_bytes},
+                   "draft_rows_per_round": nrows, "round_algorithmic_bytes": row_bytes,
+                   "input_sets": ROTATE},
         "roofline": {"bound": "hbm", "kernel": "draft_topk_kernel + tree_grow_kernel",
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
@@ -528,7 +532,7 @@ def tree_bench(args):
         "config": {"workload": "greedy tree verify, B=128, V=151936, tree [6], [2, 2], [1, 1] "
                                "(12 nodes, 5 rows), then KV commit of the accepted paths, 32 "
                                "layers x K,V x 8 heads x 128 bf16, 1024 slots",
-                   "rows": rows, "rows_moved": moved},
+                   "rows": rows, "rows_moved": moved, "input_sets": ROTATE},
         "roofline": {"bound": "hbm", "kernel": "tree_argmax_kernel + tree_walk_kernel",
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
