@@ -85,13 +85,16 @@ def test_tree_worked_example_on_gpu():
     assert g["num_emitted"][0] == 3 and g["seq_flags"][0] == B.FLAG_NO_ROW
 
 
+@pytest.mark.parametrize("Bn,V", [(64, 13), (160, 13), (64, 2309), (160, 2309)])
 @pytest.mark.parametrize("shared", [False, True])
-def test_tree_random_small(shared):
-    """Random topologies (duplicate sibling tokens, rows missing on some nodes), a small
-    vocabulary so that matches are frequent, ragged V, per-sequence or shared topology."""
+def test_tree_random_small(shared, Bn, V):
+    """Random topologies (duplicate sibling tokens, rows missing on some nodes), ragged V
+    (13: matches are frequent; 2309: nine trips of a row, the last partial), per-sequence or
+    shared topology; rounded normal logits, so ties (and -0 beside +0) are frequent; 64 and
+    160 sequences (1920 and 4800 row workgroups, more than the CUs hold at once)."""
     rng = np.random.default_rng(17 + shared)
-    Bn, N, R, V, depth = 64, 40, 30, 13, 6
-    stride = 16
+    N, R, depth = 40, 30, 6
+    stride = (V + 7) // 8 * 8 + 8 * (V > 100)
     par = np.zeros((1 if shared else Bn, N), np.int32)
     row = np.full((1 if shared else Bn, N), -1, np.int32)
     for s in range(par.shape[0]):
@@ -113,7 +116,7 @@ def test_tree_random_small(shared):
             if r >= 0 and rng.random() < 0.5:
                 tok[b, i] = am[b, r]
     ts = 0 if shared else N
-    say(f"[tree] random small shared={shared}")
+    say(f"[tree] random small shared={shared} B={Bn} V={V}")
     o = oracle.verify_tree(logits, np.broadcast_to(par, (Bn, N)).copy(),
                            np.broadcast_to(row, (Bn, N)).copy(), tok, R, depth, N, vocab=V)
     g = run_gpu_tree(logits, par, row, tok, R, depth, ts, V)
@@ -121,15 +124,24 @@ def test_tree_random_small(shared):
     assert (g["path_len"] >= 2).any()
 
 
-def test_tree_bad_topology_flagged():
-    par = np.array([[-1, 0, 2, 1], [-1, 0, 0, 1]], np.int32)  # seq 0: parent 2 of node 2
-    row = np.array([[0, -1, -1, -1], [0, 1, -1, -1]], np.int32)
-    tok = np.zeros((2, 4), np.int32)
-    logits = np.zeros((2, 2, 8), np.uint16)
-    say("[tree] bad topology")
+@pytest.mark.parametrize("Bn", [2, 130])
+def test_tree_bad_topology_flagged(Bn):
+    par = np.tile(np.array([[-1, 0, 0, 1]], np.int32), (Bn, 1))
+    par[0] = [-1, 0, 2, 1]  # seq 0: parent 2 of node 2
+    row = np.tile(np.array([[0, 1, -1, -1]], np.int32), (Bn, 1))
+    row[0] = [0, -1, -1, -1]
+    if Bn > 2:
+        row[2, 3] = 2  # a row index past rows_per_seq
+    tok = np.zeros((Bn, 4), np.int32)
+    logits = np.zeros((Bn, 2, 8), np.uint16)
+    say(f"[tree] bad topology B={Bn}")
     g = run_gpu_tree(logits, par, row, tok, 2, 3, 4, 8)
     assert g["seq_flags"][0] == B.FLAG_BAD_TREE and g["num_emitted"][0] == 0
     assert g["seq_flags"][1] != B.FLAG_BAD_TREE and g["num_emitted"][1] >= 1
+    if Bn > 2:
+        assert g["seq_flags"][2] == B.FLAG_BAD_TREE and g["num_emitted"][2] == 0
+        o = oracle.verify_tree(logits, par, row, tok, 2, 3, 4, vocab=8)
+        compare_tree(o, g)
 
 
 # ---- KV commit ---------------------------------------------------------------------------
