@@ -19,11 +19,13 @@
 //     rows and their table entries, kept in LDS -- and then decides from LDS alone: the
 //     commit predicate (one thread per path step, one per table entry for the ids of the
 //     blocks that would be freed), the new committed lengths, then the tile's entries taken
-//     in row-major order (8 consecutive per thread) are flagged and scanned, and a released
-//     entry's place in the free list is the number of released entries before it -- so the
-//     ids land in (sequence, logical block) order whatever the launch timing. An entry whose
-//     place falls at or past the free list's capacity stays in its table (FREE_FULL). It runs
-//     after every copy has read the tables.
+//     in row-major order (8 consecutive per thread, read and written back as two 16-byte
+//     vectors where aligned) are flagged and scanned, and a released entry's place in the
+//     free list is the number of released entries before it -- so the ids land in (sequence,
+//     logical block) order whatever the launch timing; they are gathered in LDS and written
+//     to the free list in one coalesced pass. An entry whose place falls at or past the free
+//     list's capacity stays in its table (FREE_FULL). It runs after every copy has read the
+//     tables.
 #include "spec_device.h"
 #include "specv_internal.h"
 
@@ -177,8 +179,44 @@ __global__ __launch_bounds__(kThreads) void paged_copy_kernel(PagedParams P) {
   }
 }
 
+// kRun consecutive table entries from entry g (entries at or past gend read as -1): two
+// 16-byte loads when the run lies before gend and starts 16-byte aligned (then a wave's loads
+// touch half the cache lines and issue a quarter of the instructions of 4-byte loads), else
+// kRun 4-byte loads.
+__device__ __forceinline__ void load_run(const int32_t* bt, int64_t g, int64_t gend,
+                                         int v[kRun]) {
+  static_assert(kRun == 8, "a run is two 16-byte vectors");
+  if (g + kRun <= gend && (reinterpret_cast<uintptr_t>(bt + g) & 15) == 0) {
+    const int4 a = *reinterpret_cast<const int4*>(bt + g);
+    const int4 c = *reinterpret_cast<const int4*>(bt + g + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
+    v[4] = c.x, v[5] = c.y, v[6] = c.z, v[7] = c.w;
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) v[r] = g + r < gend ? bt[g + r] : -1;
+  }
+}
+
+// Writes back a run whose entries rel[r] were released (set to -1 in v): as two 16-byte
+// stores when the run lies before gend and is 16-byte aligned (the other entries keep the
+// values just read: nothing else writes the table during the release), else the released
+// entries alone.
+__device__ __forceinline__ void store_run(int32_t* bt, int64_t g, int64_t gend,
+                                          const int v[kRun], const bool rel[kRun]) {
+  if (g + kRun <= gend && (reinterpret_cast<uintptr_t>(bt + g) & 15) == 0) {
+    *reinterpret_cast<int4*>(bt + g) = make_int4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<int4*>(bt + g + 4) = make_int4(v[4], v[5], v[6], v[7]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRun; ++r)
+      if (rel[r]) bt[g + r] = -1;
+  }
+}
+
 __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams P) {
-  __shared__ int32_t s_bt[kRelEntries];   // the tile's table entries, row-major
+  // the tile's table entries, row-major; in the release step, the chunk's released ids in
+  // free-list order
+  __shared__ __align__(16) int32_t s_bt[kRelEntries];
   __shared__ int32_t s_path[kRelPath];    // the tile's path rows
   __shared__ int s_need[kRelRows];        // first released logical block of a row (-1: invalid)
   __shared__ int s_L[kRelRows], s_D[kRelRows];
@@ -203,10 +241,8 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
 #pragma unroll
     for (int k = 0; k < kRelPath / kRelThreads; ++k)
       p_reg[k] = P.path[(size_t)b0 * md + min(tid + k * kRelThreads, nr * md - 1)];
-    int v_reg[kRun];
-#pragma unroll
-    for (int r = 0; r < kRun; ++r)
-      v_reg[r] = P.bt[e0 + min((int64_t)tid * kRun + r, ne - 1)];  // first chunk of the tile
+    int v_reg[kRun];  // the tile's first chunk, entries past the tile read as -1
+    load_run(P.bt, e0 + (int64_t)tid * kRun, e0 + ne, v_reg);
     if (tid < nr) {
       s_L[tid] = L0;
       s_D[tid] = D0;
@@ -218,11 +254,16 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
 #pragma unroll
     for (int k = 0; k < kRelPath / kRelThreads; ++k)
       if (tid + k * kRelThreads < nr * md) s_path[tid + k * kRelThreads] = p_reg[k];
+    if (in_lds) {
+      const int64_t e = (int64_t)tid * kRun;
+      if (e + kRun <= ne) {
+        *reinterpret_cast<int4*>(&s_bt[e]) = make_int4(v_reg[0], v_reg[1], v_reg[2], v_reg[3]);
+        *reinterpret_cast<int4*>(&s_bt[e + 4]) = make_int4(v_reg[4], v_reg[5], v_reg[6], v_reg[7]);
+      } else {
 #pragma unroll
-    for (int r = 0; r < kRun; ++r) {
-      const int64_t e = (int64_t)tid * kRun + r;
-      if (e >= ne) v_reg[r] = -1;
-      if (in_lds && e < ne) s_bt[e] = v_reg[r];
+        for (int r = 0; r < kRun; ++r)
+          if (e + r < ne) s_bt[e + r] = v_reg[r];
+      }
     }
     __syncthreads();
     // 2. the commit predicate from LDS: path steps (slots mapped to valid blocks), and the
@@ -259,13 +300,19 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
     for (int c0 = 0; c0 < ne32; c0 += kRelThreads * kRun) {
       const int ef = c0 + tid * kRun;
       int i = ef / mb, lb = ef - i * mb;
+      int vr[kRun];
+      if (c0 == 0) {
+#pragma unroll
+        for (int r = 0; r < kRun; ++r) vr[r] = v_reg[r];
+      } else {
+        load_run(P.bt, e0 + ef, e0 + ne, vr);
+      }
 #pragma unroll
       for (int r = 0; r < kRun; ++r) {
         const int e = ef + r;
         if (e < ne32) {
-          const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
           const int need = s_need[i];
-          if (need >= 0 && lb >= need && v >= P.num_blocks) atomicMin(&s_need[i], -1);
+          if (need >= 0 && lb >= need && vr[r] >= P.num_blocks) atomicMin(&s_need[i], -1);
         }
         if (++lb == mb) {
           lb = 0;
@@ -274,21 +321,21 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
       }
     }
     __syncthreads();
-    // 3. the new lengths and SLOT_OOB flags
-    for (int i = tid; i < nr; i += kRelThreads) {
-      if (s_need[i] >= 0) {
-        P.committed[b0 + i] = s_L[i] + P.lead + s_D[i];
-      } else if (P.flags) {
-        P.flags[b0 + i] |= SPEC_FLAG_SLOT_OOB;
-      }
-    }
-    // 4. the tile's entries in row-major order, kRun consecutive per thread: a released
+    // 3. the tile's entries in row-major order, kRun consecutive per thread: a released
     //    entry's free-list position is the count of released entries before it; one that
-    //    lands at or past the capacity stays in the table and flags its sequence FREE_FULL
+    //    lands at or past the capacity stays in the table and flags its sequence FREE_FULL.
+    //    The placed ids go to LDS at their positions, then to the free list in one coalesced
+    //    pass; a thread writes its run back with the placed entries set to -1.
     for (int c0 = 0; c0 < ne32; c0 += kRelThreads * kRun) {
       const int ef = c0 + tid * kRun;
       const int i0 = ef / mb;
-      int pb[kRun], pi[kRun];
+      int vr[kRun], pb[kRun], pi[kRun];
+      if (c0 == 0) {
+#pragma unroll
+        for (int r = 0; r < kRun; ++r) vr[r] = v_reg[r];
+      } else {
+        load_run(P.bt, e0 + ef, e0 + ne, vr);
+      }
       int cnt = 0;
       {
         int i = i0, lb = ef - i0 * mb;
@@ -299,8 +346,7 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
           pi[r] = i;
           if (e < ne32) {
             const int need = s_need[i];
-            const int v = c0 == 0 ? v_reg[r] : P.bt[e0 + e];
-            if (need >= 0 && lb >= need && v >= 0) pb[r] = v;
+            if (need >= 0 && lb >= need && vr[r] >= 0) pb[r] = vr[r];
           }
           cnt += pb[r] >= 0;
           if (++lb == mb) {
@@ -318,22 +364,42 @@ __global__ __launch_bounds__(kRelThreads) void paged_release_kernel(PagedParams 
         before += w < wave ? tw : 0;
         total += tw;
       }
-      int at = fc0 + carry + before + incl - cnt;
+      const int room = max(P.free_cap - (fc0 + carry), 0);  // free-list entries left
+      int k = before + incl - cnt;  // the chunk's count of released entries before this run
+      bool rel[kRun], any = false;
 #pragma unroll
       for (int r = 0; r < kRun; ++r) {
+        rel[r] = false;
         if (pb[r] >= 0) {
-          if (at < P.free_cap) {
-            P.free_list[at] = pb[r];
-            P.bt[e0 + ef + r] = -1;
+          if (k < room) {
+            s_bt[k] = pb[r];
+            vr[r] = -1;
+            rel[r] = any = true;
           } else if (P.flags) {
             atomicOr(&P.flags[b0 + pi[r]], SPEC_FLAG_FREE_FULL);
           }
-          ++at;
+          ++k;
         }
       }
+      __syncthreads();  // the chunk's placed ids are in LDS
+      // the global stores last: a register that a store reads is not reused before the
+      // store completes, so stores issued early would hold up the work after them
+      const int placed = min(total, room);
+      for (int j = tid; j < placed; j += kRelThreads) P.free_list[fc0 + carry + j] = s_bt[j];
+      if (any) store_run(P.bt, e0 + ef, e0 + ne, vr, rel);
       carry += total;
-      __syncthreads();  // s_wave is read by every thread before the next chunk writes it
+      if (c0 + kRelThreads * kRun < ne32)
+        __syncthreads();  // s_wave and the ids are read before the next chunk writes them
     }
+    // 4. the new lengths and SLOT_OOB flags
+    for (int i = tid; i < nr; i += kRelThreads) {
+      if (s_need[i] >= 0) {
+        P.committed[b0 + i] = s_L[i] + P.lead + s_D[i];
+      } else if (P.flags) {
+        P.flags[b0 + i] |= SPEC_FLAG_SLOT_OOB;
+      }
+    }
+    if (b0 + rows < P.B) __syncthreads();  // the tile's LDS is read before the next tile's
   }
   if (tid == 0) *P.free_count = min(fc0 + carry, P.free_cap);
 }
