@@ -18,7 +18,7 @@ bounded sample of the same workload as a reported baseline.
   python bench.py --workload c2|c5       # the other chain workloads (c3 is the default)
   python bench.py --workload c3_no_top_p|c3_greedy|c3_top_k_50   # c3 variants
   python bench.py --workload markov      # the vocab-4 Markov rounds (launch-bound)
-  python bench.py --summarize-trace DIR [--remove-csv]     # tables of a rocprofv3 trace
+  python bench.py --summarize-trace DIR [--cycle NAMES:K] [--remove-csv]  # rocprofv3 trace tables
   python bench.py --summarize-counters DIR [--remove-csv]  # tables of a rocprofv3 --pmc run
 
 With --workload tree_draft a step is one round of tree drafting ("投机推理：小模型搭树，
@@ -147,11 +147,15 @@ def _grid(r):
     return g // max(w, 1), w
 
 
-def summarize_trace(d, last=100):
+def summarize_trace(d, last=100, cycle=None):
     """Per (kernel, workgroups, workgroup size) of a rocprofv3 --kernel-trace csv run: the
     dispatch count and the mean, median, min and max duration in us, over every dispatch and
     over the last `last` ones, then the median gap between consecutive dispatches of the last
-    3 * `last`. Written to DIR/summary.txt and printed."""
+    3 * `last`. With cycle = (names, K): the dispatches of the kernels named (by prefix), in
+    launch order, are cut into runs of K (one call or round each; runs that do not hold the
+    same kernel sequence as the first are dropped), and each position of the run gets its
+    median duration and median gap after the dispatch before it. Written to DIR/summary.txt
+    and printed."""
     import statistics as st
     rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
                    _short_kernel_name(r["Kernel_Name"])) + _grid(r)
@@ -173,6 +177,19 @@ def summarize_trace(d, last=100):
         gaps.setdefault((a[2][:30], b[2][:30]), []).append((b[0] - a[1]) / 1e3)
     out.append("gaps between consecutive dispatches (last ones), median us:")
     out += [f"  {a} -> {b}: {st.median(v):.2f} (n={len(v)})" for (a, b), v in gaps.items()]
+    if cycle:
+        names, k = cycle
+        sel = [r for r in rows if any(r[2].startswith(n) for n in names)]
+        runs = [sel[i:i + k] for i in range(0, len(sel) - k + 1, k)]
+        runs = [r for r in runs if [x[2] for x in r] == [x[2] for x in runs[0]]][-last:]
+        out.append(f"runs of {k} dispatches of {', '.join(names)} (last {len(runs)}), median us:")
+        for j in range(k):
+            dur = st.median((r[j][1] - r[j][0]) / 1e3 for r in runs)
+            gap = st.median((r[j][0] - r[j - 1][1]) / 1e3 for r in runs) if j else float("nan")
+            out.append(f"  {j}: {runs[0][j][2][:40]:40s} wgs={runs[0][j][3]:6d} "
+                       f"duration {dur:7.2f}  gap before {gap:6.2f}")
+        out.append(f"  run (first start to last end): "
+                   f"{st.median((r[-1][1] - r[0][0]) / 1e3 for r in runs):.2f}")
     return out
 
 
@@ -628,12 +645,20 @@ def main():
                              "c3_top_k_50", "markov", "tree", "tree_draft", "paged_kv",
                              "ngram"])
     ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--cycle", metavar="NAMES:K",
+                    help="with --summarize-trace: per-position times of runs of K dispatches "
+                         "of the comma-separated kernels, e.g. "
+                         "draft_topk_kernel,tree_grow_kernel:6")
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--remove-csv", action="store_true")
     args = ap.parse_args()
     if args.summarize_trace:
+        cyc = None
+        if args.cycle:
+            names, k = args.cycle.rsplit(":", 1)
+            cyc = (names.split(","), int(k))
         _write_summary(args.summarize_trace, "summary.txt",
-                       summarize_trace(args.summarize_trace, 100), args.remove_csv)
+                       summarize_trace(args.summarize_trace, 100, cyc), args.remove_csv)
         return
     if args.summarize_counters:
         _write_summary(args.summarize_counters, "counters.txt",
