@@ -121,13 +121,15 @@ class Boundary:
     """Near-boundary sequences of one comparison, by the kind of their first such decision:
     ``acceptance`` (|u - a| < 1e-5 at a tested position), ``topp`` (the top-p cut of a tested
     position's p or q row), ``draw`` (the final residual/bonus draw's CDF step, or R < 1e-5),
-    ``draw_topp`` (the bonus row's top-p cut)."""
+    ``draw_topp`` (the bonus row's top-p cut). ``disagreed`` lists those whose GPU result
+    differs from the oracle's after that decision (accepted count, emitted count or tokens)."""
 
     KINDS = ("acceptance", "topp", "draw", "draw_topp")
 
     def __init__(self):
         for k in self.KINDS:
             setattr(self, k, [])
+        self.disagreed = []
 
     @property
     def before_draw(self):
@@ -177,6 +179,11 @@ def compare_chain(x, o, g, exact=False, probes=True):
             if probes and g["probe_rows"] is not None:
                 m = kb + 1 if law_ok else kb
                 assert _close(g["probe_rows"][d0:d0 + m], o["probe_rows"][d0:d0 + m], tol), ctx
+            ne = int(o["num_emitted"][b])
+            same = (int(g["num_accepted"][b]) == n and int(g["num_emitted"][b]) == ne and
+                    np.array_equal(g["out_tokens"][t0:t0 + ne], o["out_tokens"][t0:t0 + ne]))
+            if not same:
+                bnd.disagreed.append(b)
             continue
         full = m_all >= MARGIN
         if not full:
@@ -194,6 +201,10 @@ def compare_chain(x, o, g, exact=False, probes=True):
             assert g["num_emitted"][b] == ne, ctx
         m = ne if full else n
         assert np.array_equal(g["out_tokens"][t0:t0 + m], o["out_tokens"][t0:t0 + m]), ctx
+        if not full and (int(g["num_emitted"][b]) != ne or
+                         not np.array_equal(g["out_tokens"][t0:t0 + ne],
+                                            o["out_tokens"][t0:t0 + ne])):
+            bnd.disagreed.append(b)
         if probes and g["probe_rows"] is not None:
             tested = min(n + 1, gb) if drawn else n
             assert _close(g["probe_rows"][d0:d0 + tested], o["probe_rows"][d0:d0 + tested],
@@ -213,7 +224,8 @@ def record(label, sequences, kind, counts, **extra):
                  boundary={k: int(v) for k, v in counts.items()})
     entry.update(extra)
     REPORT.append(entry)
-    say(f"[parity] {label}: {sequences} sequences, near-boundary {entry['boundary']}")
+    say(f"[parity] {label}: {sequences} sequences, near-boundary {entry['boundary']}, "
+        f"disagreeing {entry.get('disagreed', '-')}")
 
 
 def expected_boundary(o, frac_slack=5.0):
@@ -238,7 +250,8 @@ def check_chain(x, seed=1234, override=None, lead=1, tokens=None, exact=False, l
     bnd = compare_chain(x, o, g, exact=exact)
     Bn = len(x["cu_gamma"]) - 1
     record(label, Bn, "chain greedy" if exact else "chain", bnd.counts(),
-           draft_rows=int(x["cu_gamma"][-1]), vocab=int(x["vocab"]))
+           disagreed=len(bnd.disagreed), draft_rows=int(x["cu_gamma"][-1]),
+           vocab=int(x["vocab"]))
     # acceptance tests sit within 1e-5 of their boundary with probability ~2e-5 per test
     assert len(bnd.before_draw) <= max(2, max_acc_boundary_frac * Bn)
     if override is None and not exact:

@@ -37,24 +37,30 @@ def main(path, command, build=""):
           "tokens carry less than 2e-5 of the mass, so a good share of whole-row draws are "
           "counted (C5); the tests bound the count by its expectation, the sum over draws of "
           "min(1, 2e-5 / w) for the drawn token's mass w, plus slack.\n")
+    print("\"Disagreeing\" counts the near-boundary cases whose GPU result after that decision "
+          "differs from the oracle's (accepted count, emitted count or tokens); blank where the "
+          "comparison does not count it.\n")
+    dis = lambda e: str(e["disagreed"]) if "disagreed" in e else ""  # noqa: E731
     print("## The five configurations\n")
-    print("| config | comparison | sequences / rounds | near-boundary cases |")
-    print("|---|---|---|---|")
+    print("| config | comparison | sequences / rounds | near-boundary cases | disagreeing |")
+    print("|---|---|---|---|---|")
     for prefix, name in CONFIGS:
         for e in ent:
             if e["label"].lower().startswith(prefix):
                 b = ", ".join(f"{k} {v}" for k, v in e["boundary"].items() if v) or "none"
-                print(f"| {name} | {e['label']} ({e['kind']}) | {e['sequences']} | {b} |")
+                print(f"| {name} | {e['label']} ({e['kind']}) | {e['sequences']} | {b} | "
+                      f"{dis(e)} |")
     print("\n## Every comparison\n")
-    print("| comparison | kind | sequences | " + " | ".join(kinds) + " |")
-    print("|---|---|---|" + "---|" * len(kinds))
+    print("| comparison | kind | sequences | " + " | ".join(kinds) + " | disagreeing |")
+    print("|---|---|---|" + "---|" * (len(kinds) + 1))
     for e in ent:
         cells = " | ".join(str(e["boundary"].get(k, "")) for k in kinds)
-        print(f"| {e['label']} | {e['kind']} | {e['sequences']} | {cells} |")
+        print(f"| {e['label']} | {e['kind']} | {e['sequences']} | {cells} | {dis(e)} |")
     tot = {k: sum(e["boundary"].get(k, 0) for e in ent) for k in kinds}
     seqs = sum(e["sequences"] for e in ent)
+    tdis = sum(e.get("disagreed", 0) for e in ent)
     print(f"| **total** ({len(ent)} comparisons) | | {seqs} | "
-          + " | ".join(str(tot[k]) for k in kinds) + " |")
+          + " | ".join(str(tot[k]) for k in kinds) + f" | {tdis} |")
 
 
 if __name__ == "__main__":

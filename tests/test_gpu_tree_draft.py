@@ -72,13 +72,14 @@ def run_oracle(x, tree_stride=None):
 
 
 def compare(x, o, g, label=""):
-    """Returns the number of sequences with a selection near its decision boundary."""
+    """Returns the number of sequences with a selection near its decision boundary, and how
+    many of those built a different tree (tokens or parents) than the oracle."""
     th = x["top_head"]
     depth = len(th)
     n = o["num_nodes"]
     ts = o["parent"].shape[1]
     layer = o["position_ids"] - x["pos_base"][:, None]  # depth of created nodes
-    boundary = 0
+    boundary = disagreed = 0
     for b in range(x["batch"]):
         sb = depth  # first step whose expansion is a near-boundary decision
         for s in range(1, depth):
@@ -86,6 +87,9 @@ def compare(x, o, g, label=""):
                 sb = s
                 break
         boundary += sb < depth
+        if sb < depth:
+            disagreed += not (np.array_equal(g["node_token"][b], o["node_token"][b]) and
+                              np.array_equal(g["parent"][b], o["parent"][b]))
         # nodes of layers 0..sb were made before the first uncertain expansion was used
         ok = np.zeros(ts, bool)
         ok[:n] = layer[b, :n] <= sb
@@ -115,7 +119,7 @@ def compare(x, o, g, label=""):
         assert (g["node_row"][b, n:] == -1).all() and (g["position_ids"][b, n:] == -1).all()
         assert np.isneginf(g["node_logp"][b, n:]).all() and (bits[n:] == 0).all()
     assert (g["seq_flags"] == 0).all()
-    return boundary
+    return boundary, disagreed
 
 
 def check(x, label, tree_stride=None, expand_stride=None):
@@ -123,9 +127,9 @@ def check(x, label, tree_stride=None, expand_stride=None):
         f"top_k_spec={x['top_k_spec']}")
     g = run_gpu(x, tree_stride, expand_stride)
     o = run_oracle(x, tree_stride)
-    nb = compare(x, o, g, label)
+    nb, nd = compare(x, o, g, label)
     record(f"tree drafting {label}", x["batch"], "tree drafting", {"expansion": nb},
-           vocab=int(x["vocab"]))
+           disagreed=nd, vocab=int(x["vocab"]))
     assert nb <= max(1, x["batch"] // 50)
     return o, g
 
@@ -215,7 +219,7 @@ def test_tree_round_draft_then_verify():
     x = W.tree_draft_inputs(seed=98, B=64, V=151936)
     g = run_gpu(x)
     o = run_oracle(x)
-    nb = compare(x, o, g, "round")
+    nb, _ = compare(x, o, g, "round")
     rng = np.random.default_rng(98)
     R = sum(x["top_head"])
     n = g["num_nodes"]
