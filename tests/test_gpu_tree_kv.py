@@ -124,6 +124,43 @@ def test_tree_random_small(shared, Bn, V):
     assert (g["path_len"] >= 2).any()
 
 
+@pytest.mark.parametrize("max_depth", [1, 64])
+def test_tree_largest_shape(max_depth):
+    """The largest tree the call takes: 256 nodes, each with its own row (256 rows per
+    sequence), and an 80-node spine whose tokens are the target argmax of their parent, so
+    the walk runs into the path capacity. Sequence 0 keeps the whole spine (a full path,
+    then the extra token at the last node), sequence 1 breaks it at depth 30, sequence 2
+    loses node 50's row (the walk stops there without an extra token), sequence 3 has
+    random tokens only."""
+    rng = np.random.default_rng(256)
+    Bn, N, R, V, spine = 4, 256, 256, 61, 80
+    stride = 64
+    par = np.zeros((Bn, N), np.int32)
+    par[:, 0] = -1
+    par[:, 1:spine + 1] = np.arange(spine)
+    for b in range(Bn):
+        par[b, spine + 1:] = [int(rng.integers(0, i)) for i in range(spine + 1, N)]
+    row = np.tile(np.arange(N, dtype=np.int32), (Bn, 1))
+    row[2, 50] = -1
+    logits = np.full((Bn, R, stride), 0xFF80, np.uint16)
+    logits[..., :V] = W.bf16_bits(np.round(rng.standard_normal((Bn, R, V)) * 2).astype(np.float32))
+    am = W.bf16_to_f32(logits[..., :V]).argmax(-1)
+    tok = rng.integers(0, V, size=(Bn, N)).astype(np.int32)
+    for b in range(3):
+        tok[b, 1:spine + 1] = am[b, np.arange(spine)]
+    tok[1, 30] = (am[1, 29] + 1) % V
+    say(f"[tree] largest shape N={N} R={R} max_depth={max_depth}")
+    o = oracle.verify_tree(logits, par, row, tok, R, max_depth, N, vocab=V)
+    g = run_gpu_tree(logits, par, row, tok, R, max_depth, N, V)
+    compare_tree(o, g)
+    assert g["path_len"][0] == max_depth and g["num_emitted"][0] == max_depth + 1
+    assert np.array_equal(g["path_nodes"][0], np.arange(1, max_depth + 1))
+    if max_depth == 64:
+        assert g["path_len"][1] >= 29
+        assert g["path_len"][2] == 50 and g["num_emitted"][2] == 50
+        assert g["seq_flags"][2] == B.FLAG_NO_ROW
+
+
 @pytest.mark.parametrize("Bn", [2, 130])
 def test_tree_bad_topology_flagged(Bn):
     par = np.tile(np.array([[-1, 0, 0, 1]], np.int32), (Bn, 1))
