@@ -1003,24 +1003,30 @@ __device__ __forceinline__ Draw draw_from_lists(const NucEntry* pl, int np, floa
   return d;
 }
 
-// A row's filtered law: weight(l) = exp2(l*c + nref) * iz for l >= t, else 0 (iz = 1/Z).
+// A row's filtered law: probability exp2(l*c + nref) / z for l >= t, else 0 (z = the law's
+// normaliser Z against the same reference).
 struct RowLaw {
   const uint4* row;
-  float c, nref, t, iz;
-  int point = -1;  // >= 0: the law is the point mass at this token (row is not read)
+  float c, nref, t, z;
+  int point = -1;  // >= 0: the law is the point mass at this token (row is not read; z = 1)
 };
 
+// Whole-row draws work on weights in units of p's normaliser: p's weight is exp2(l*c + nref)
+// (Z_p times its probability) and the residual's is max(0, p_w - rq * q_w) with
+// rq = Z_p / Z_q (Z_p times max(0, p - q)). An inverse-CDF draw is the same under a common
+// scale, so only the reported masses are multiplied by 1 / Z_p at the end; the residual
+// costs one fused multiply-add per logit instead of two products and a difference.
 __device__ __forceinline__ void law_weights(const RowLaw& L, const uint4& d, float w[8]) {
   float x[8];
   unpack8(d, x);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) w[e] = (x[e] >= L.t) ? weight(x[e], L.c, L.nref) * L.iz : 0.0f;
+  for (int e = 0; e < 8; ++e) w[e] = (x[e] >= L.t) ? weight(x[e], L.c, L.nref) : 0.0f;
 }
 
-// Weights of vector v from its loaded p (and q) data: p, or max(0, p - q). Vectors past the
-// row and logits past V weigh 0.
+// Weights of vector v from its loaded p (and q) data, in units of p's normaliser: p, or
+// max(0, p - q). Vectors past the row and logits past V weigh 0.
 __device__ __forceinline__ void data_weights(const RowLaw& Lp, const RowLaw& Lq, bool residual,
-                                             int v, int nvec, int V, const uint4& dp,
+                                             float rq, int v, int nvec, int V, const uint4& dp,
                                              const uint4& dq, float w[8]) {
   if (v >= nvec) {
 #pragma unroll
@@ -1037,20 +1043,20 @@ __device__ __forceinline__ void data_weights(const RowLaw& Lp, const RowLaw& Lq,
       law_weights(Lq, dq, wq);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = fmaxf(0.0f, w[e] - wq[e]);
+    for (int e = 0; e < 8; ++e) w[e] = fmaxf(0.0f, fmaf(-rq, wq[e], w[e]));
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     if (v * 8 + e >= V) w[e] = 0.0f;
 }
 __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, bool residual,
-                                            int v, int nvec, int V, float w[8]) {
+                                            float rq, int v, int nvec, int V, float w[8]) {
   // clamped, unconditional 16-byte loads; data_weights gives 0 past the row
   const int vc = min(v, nvec - 1);
   const uint4 dp = Lp.row[vc];
   uint4 dq{0u, 0u, 0u, 0u};
   if (residual && Lq.point < 0) dq = Lq.row[vc];
-  data_weights(Lp, Lq, residual, v, nvec, V, dp, dq, w);
+  data_weights(Lp, Lq, residual, rq, v, nvec, V, dp, dq, w);
 }
 
 // Phase 2 of a row draw, once tile_sum holds every tile's sum and each lane knows the last
@@ -1059,7 +1065,8 @@ __device__ __forceinline__ void vec_weights(const RowLaw& Lp, const RowLaw& Lq, 
 // last token with positive weight, found in the last such vector.
 template <int NT>
 __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool residual,
-                                          int nvec, int V, float u, int last, float* tile_sum,
+                                          float rq, int nvec, int V, float u, int last,
+                                          float* tile_sum,
                                           int* sh_i, float* sh_f) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int nw = NT / kWave;
@@ -1112,7 +1119,7 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
     if (gstar >= 0) {
       const int v = gstar * kWave + lane;
       float w[8];
-      vec_weights(Lp, Lq, residual, v, nvec, V, w);
+      vec_weights(Lp, Lq, residual, rq, v, nvec, V, w);
       float ls = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ls += w[e];
@@ -1165,7 +1172,7 @@ __device__ __forceinline__ Draw draw_scan(const RowLaw Lp, const RowLaw Lq, bool
     }
     if (token < 0 && lst >= 0) {  // u*total at or past the end: the last token with weight
       float w[8];
-      vec_weights(Lp, Lq, residual, lst, nvec, V, w);
+      vec_weights(Lp, Lq, residual, rq, lst, nvec, V, w);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (w[e] > 0.0f) {
@@ -1213,13 +1220,10 @@ __device__ __forceinline__ uint4 mask_past_v(uint4 d, int v, int V) {
 // same expression as data_weights gives, bit for bit (every finite or -inf logit passes the
 // cut, and a -inf logit weighs exactly 0), with the row's end masked to -inf in the lanes
 // that hold it instead of per-logit bound checks. Returns the last vector with positive
-// weight this lane saw (-1: none). Contraction is off, as it is where data_weights computes
-// them (a select sits between the product and the difference there), so that the product
-// and the difference round separately in both.
+// weight this lane saw (-1: none).
 template <int NT, int TI, bool RES>
-__device__ __forceinline__ int tile_sums_nocut(const RowLaw& Lp, const RowLaw& Lq, int nvec,
-                                               int V, float* tile_sum) {
-#pragma clang fp contract(off)
+__device__ __forceinline__ int tile_sums_nocut(const RowLaw& Lp, const RowLaw& Lq, float rq,
+                                               int nvec, int V, float* tile_sum) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int nw = NT / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
@@ -1246,8 +1250,8 @@ __device__ __forceinline__ int tile_sums_nocut(const RowLaw& Lp, const RowLaw& L
       float ls = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float w = weight(xp[e], Lp.c, Lp.nref) * Lp.iz;
-        if (RES) w = fmaxf(0.0f, w - weight(xq[e], Lq.c, Lq.nref) * Lq.iz);
+        float w = weight(xp[e], Lp.c, Lp.nref);
+        if (RES) w = fmaxf(0.0f, fmaf(-rq, weight(xq[e], Lq.c, Lq.nref), w));
         ls += w;
       }
       if (ls > 0.0f) lastv = v;
@@ -1260,14 +1264,14 @@ __device__ __forceinline__ int tile_sums_nocut(const RowLaw& Lp, const RowLaw& L
 
 template <int NT, int TI>
 __device__ __forceinline__ int tile_sums(const RowLaw& Lp, const RowLaw& Lq, bool residual,
-                                         int nvec, int V, float* tile_sum) {
+                                         float rq, int nvec, int V, float* tile_sum) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int nw = NT / kWave;
   const int ntiles = (nvec + kWave - 1) / kWave;
   const bool with_q = residual && Lq.point < 0;
   if (Lp.t == -INFINITY && (!residual || (with_q && Lq.t == -INFINITY))) {
-    if (residual) return tile_sums_nocut<NT, TI, true>(Lp, Lq, nvec, V, tile_sum);
-    return tile_sums_nocut<NT, TI, false>(Lp, Lq, nvec, V, tile_sum);
+    if (residual) return tile_sums_nocut<NT, TI, true>(Lp, Lq, rq, nvec, V, tile_sum);
+    return tile_sums_nocut<NT, TI, false>(Lp, Lq, rq, nvec, V, tile_sum);
   }
   int lastv = -1;  // last vector with positive weight seen by this lane
   for (int g0 = wid * TI; g0 < ntiles; g0 += nw * TI) {
@@ -1286,7 +1290,7 @@ __device__ __forceinline__ int tile_sums(const RowLaw& Lp, const RowLaw& Lq, boo
       const int v0 = (g0 + t) * kWave + lane;
       const int v = v0 < nvec ? v0 : nvec;  // data_weights gives 0 past the row
       float w[8];
-      data_weights(Lp, Lq, residual, v, nvec, V, dp[t], dq[t], w);
+      data_weights(Lp, Lq, residual, rq, v, nvec, V, dp[t], dq[t], w);
       float ls = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ls += w[e];
@@ -1302,8 +1306,13 @@ template <int NT, int TI>
 __device__ __forceinline__ Draw draw_from_rows(const RowLaw Lp, const RowLaw Lq, bool residual,
                                                int nvec, int V, float u, float* tile_sum,
                                                int* sh_i, float* sh_f) {
-  const int last = tile_sums<NT, TI>(Lp, Lq, residual, nvec, V, tile_sum);
-  return draw_scan<NT>(Lp, Lq, residual, nvec, V, u, last, tile_sum, sh_i, sh_f);
+  const float rq = residual ? Lp.z / Lq.z : 0.0f;
+  const int last = tile_sums<NT, TI>(Lp, Lq, residual, rq, nvec, V, tile_sum);
+  Draw d = draw_scan<NT>(Lp, Lq, residual, rq, nvec, V, u, last, tile_sum, sh_i, sh_f);
+  const float iz = 1.0f / Lp.z;  // back from units of Z_p to probabilities
+  d.total *= iz;
+  d.wtok *= iz;
+  return d;
 }
 
 // Per-sequence decision state the resolve step shares through LDS.
@@ -1518,7 +1527,7 @@ void chain_resolve_kernel(ChainParams P) {
         }
         d = wg_list_draw(lb, sbon.nuc, sbon.z, nullptr, 0, 1.0f, false, u, sh_i, sh_f);
       } else {
-        const RowLaw Lp{prow, c, -sbon.m * c, sbon.t, 1.0f / sbon.z};
+        const RowLaw Lp{prow, c, -sbon.m * c, sbon.t, sbon.z};
         d = draw_from_rows<NT, TI>(Lp, Lp, false, P.nvec, P.V, u, tile_sum, sh_i, sh_f);
       }
       y = d.token;
@@ -1532,11 +1541,11 @@ void chain_resolve_kernel(ChainParams P) {
     const float u = P.ovr ? P.ovr[(size_t)trow * 2 + 1]
                           : uniform24(P.seed_lo, P.seed_hi, s.id, (uint32_t)(s.L + kstar),
                                       SPEC_PURPOSE_RESIDUAL);
-    const RowLaw Lp{prow, c, -sp.m * c, sp.t, 1.0f / sp.z};
+    const RowLaw Lp{prow, c, -sp.m * c, sp.t, sp.z};
     // no draft rows: the draft law is the point mass at the draft token
     const RowLaw Lq = P.draft ? RowLaw{reinterpret_cast<const uint4*>(
                                            P.draft + (size_t)(s.d0 + kstar - 1) * P.stride),
-                                       c, -sq.m * c, sq.t, 1.0f / sq.z}
+                                       c, -sq.m * c, sq.t, sq.z}
                               : RowLaw{nullptr, c, 0.0f, -INFINITY, 1.0f,
                                        sd.tok[kstar - 1]};
     Draw d;
