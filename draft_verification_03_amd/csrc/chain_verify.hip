@@ -679,10 +679,13 @@ __device__ float lane_max_kth(RowLds* L, int K, int tid) {
 }
 
 // A second capture of the row: every vector whose max is >= vk, in the same LDS slots and
-// spill list (cleared first, as are the bins).
+// spill list (cleared first, as are the bins). The row is read in trips of the stream's
+// layout (vector v0 + u * kWave + lane in slot u), wave w taking trips w, w + 8, ...; a
+// trip's kU loads are issued together, from clamped indexes so that each stays one
+// unconditional 16-byte load, and the vectors past the row weigh as -inf.
 __device__ void recapture(const uint4* __restrict__ row, int nvec, int V, float vk, RowLds* L,
                           uint16_t* spill, int tid) {
-  const int lane = tid % kWave;
+  const int lane = tid % kWave, w = tid / kWave;
   __syncthreads();  // every thread is done with the first capture and its bins
   if (tid == 0) {
     L->ncap = 0;
@@ -693,23 +696,25 @@ __device__ void recapture(const uint4* __restrict__ row, int nvec, int V, float 
     L->hcnt[i] = 0u;
   }
   __syncthreads();
-  for (int v0 = tid - lane; v0 < nvec; v0 += kRowThreads) {
-    const int v = v0 + lane;
-    uint4 d[kU] = {};
+  constexpr int kTripVecs = kU * kWave;
+  // a finite threshold: vectors past the row (all -inf) are never captured, even if vk is -inf
+  const float thr = vmax3(vk, -3.4028235e38f, -3.4028235e38f);
+  for (int v0 = w * kTripVecs; v0 < nvec; v0 += kRowWgWaves * kTripVecs) {
+    uint4 d[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) d[u] = row[min(v0 + u * kWave + lane, nvec - 1)];
     float vm[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) vm[u] = -INFINITY;
-    if (v < nvec) {
-      d[0] = row[v];
+    for (int u = 0; u < kU; ++u) {
+      const int v = v0 + u * kWave + lane;
       float x[8];
-      unpack8(d[0], x);
+      unpack8(d[u], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (v * 8 + e >= V) x[e] = -INFINITY;
-      vm[0] = max8(x);
+        if (v * 8 + e >= V) x[e] = -INFINITY;  // v >= nvec: every logit, as v * 8 >= V
+      vm[u] = max8(x);
     }
-    // one vector per lane: the trip layout's first slot (vid = v0 + lane)
-    capture_trip(L, spill, d, vm, vmax3(vk, -3.4028235e38f, -3.4028235e38f), v0, lane);
+    capture_trip(L, spill, d, vm, thr, v0, lane);
   }
   __syncthreads();
 }
@@ -765,10 +770,10 @@ __device__ __forceinline__ TopP topp_select(const uint4* __restrict__ row, int n
 // p_{gamma_b+1} (needed only after a full accept, but read with the rest: one workgroup
 // cannot pull a row from HBM fast enough to do it later without stalling the resolve step).
 // TOPP: the batch carries a top-p or top-k array (the captures and the cut are compiled in).
-// NT: the row streams use nontemporal loads; off for batches with a top-k array, whose rows
-// may be captured a second time.
+// The row streams use nontemporal loads: the stream reads every row once (a top-k row
+// captured a second time reads it once more, in the end phase).
 // ----------------------------------------------------------------------------------------
-template <bool TOPP, bool NT>
+template <bool TOPP>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(6)))
 void row_stats_kernel(ChainParams P) {
   __shared__ RowLds L;
@@ -825,7 +830,7 @@ void row_stats_kernel(ChainParams P) {
   if (s.T == 0.0f) {  // greedy: argmax of the target row, lowest index on ties
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    stream_row_claimed<kDepth, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
+    stream_row_claimed<kDepth, true>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
       argmax_trip(dd, v0, P.nvec, P.V, lane, bv, bi);
     });
     wave_argmax(bv, bi);
@@ -853,12 +858,12 @@ void row_stats_kernel(ChainParams P) {
   uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
   if (filt)
-    stream_row_claimed<kDepthCap, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepthCap, true>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
     });
   else
-    stream_row_claimed<kDepth, NT>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepth, true>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<false>(dd, v0, lane, c, capw, acc, &L, nullptr);
     });
@@ -1647,14 +1652,10 @@ hipError_t launch_chain(const spec_chain_args& a, void* ws, hipStream_t st, void
   // per sequence: two rows (target, draft) per draft position slot k <= max_gamma, then the
   // bonus row
   const unsigned nrows = (unsigned)a.batch * (2u * (unsigned)a.max_gamma + 1u);
-  if (a.top_k)
-    hipLaunchKernelGGL((row_stats_kernel<true, false>), dim3(nrows), dim3(kRowThreads), 0, st,
-                       P);
-  else if (a.top_p)
-    hipLaunchKernelGGL((row_stats_kernel<true, true>), dim3(nrows), dim3(kRowThreads), 0, st, P);
+  if (a.top_k || a.top_p)
+    hipLaunchKernelGGL((row_stats_kernel<true>), dim3(nrows), dim3(kRowThreads), 0, st, P);
   else
-    hipLaunchKernelGGL((row_stats_kernel<false, true>), dim3(nrows), dim3(kRowThreads), 0, st,
-                       P);
+    hipLaunchKernelGGL((row_stats_kernel<false>), dim3(nrows), dim3(kRowThreads), 0, st, P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   if (a.batch > kNumCus)
