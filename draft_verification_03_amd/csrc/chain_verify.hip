@@ -9,10 +9,10 @@
 // Structure
 //  1. row_stats_kernel -- one workgroup of kRowWgWaves waves per logits row: the target row
 //     p_k or the draft row q_k of draft position k = 1..gamma_b, and the bonus row
-//     p_{gamma_b+1}. The waves claim the row's trips from an LDS counter (16-byte loads,
-//     nontemporal unless the batch has a top-k array; one trip in flight per wave while
-//     capturing, two otherwise), so the row streams from HBM once as one wide sequential
-//     read, and the hardware hands rows to CUs as they free up:
+//     p_{gamma_b+1}. The waves claim the row's trips from an LDS counter (nontemporal 16-byte
+//     loads; one trip in flight per wave while capturing, two otherwise), so the row
+//     streams from HBM once as one wide sequential read, and the hardware hands rows to CUs
+//     as they free up:
 //       - per trip (4 KB of the row): its max and its sum of exp2((l - max) * log2(e)/T),
 //         each reduced over the wave in a fixed order and kept by trip index, so that the
 //         row's (m, Z), combined in trip order, does not depend on which wave took a trip;
@@ -830,7 +830,7 @@ void row_stats_kernel(ChainParams P) {
   if (s.T == 0.0f) {  // greedy: argmax of the target row, lowest index on ties
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    stream_row_claimed<kDepth, true>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
+    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool) {
       argmax_trip(dd, v0, P.nvec, P.V, lane, bv, bi);
     });
     wave_argmax(bv, bi);
@@ -858,12 +858,12 @@ void row_stats_kernel(ChainParams P) {
   uint16_t* spill = P.spill + slot * kCapG;
   LaneAcc acc;
   if (filt)
-    stream_row_claimed<kDepthCap, true>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepthCap>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<true>(dd, v0, lane, c, capw, acc, &L, spill);
     });
   else
-    stream_row_claimed<kDepth, true>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
+    stream_row_claimed<kDepth>(rp, P.nvec, lane, &L.trip, [&](uint4* dd, int v0, bool ml) {
       if (ml) mask_tail(dd, v0, P.nvec, P.V, lane);
       consume_trip<false>(dd, v0, lane, c, capw, acc, &L, nullptr);
     });

@@ -8,48 +8,39 @@ namespace specv {
 
 constexpr int kU = 4;  // vectors per row per lane per trip
 
-// One 16-byte vector of a logits row. With NT the load carries the nontemporal hint: a row
-// that is read once streams faster with it, while a row that may be read again soon after
-// (a top-k row captured a second time) keeps plain loads, which leave it in the memory-side
-// cache for the second read.
-template <bool NT>
+// One 16-byte vector of a logits row, loaded with the nontemporal hint: the row streams
+// read each row once, and they run faster with it than with plain loads.
 __device__ __forceinline__ uint4 ld_row(const uint4* p) {
-  if constexpr (NT) {
-    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *p;
-  }
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Loads kU vectors of one row for this lane; vectors past the row read as -inf. A full trip
 // (every trip but possibly the last) loads from a uniform base with the lane's offset and an
 // immediate per vector: no predication and no per-load address arithmetic.
-template <bool NT>
 __device__ __forceinline__ void load_trip(const uint4* __restrict__ row, int v0, int nvec,
                                           int lane, uint4 d[kU]) {
   const uint4* base = row + v0;
   if (v0 + kU * kWave <= nvec) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) d[u] = ld_row<NT>(base + u * kWave + lane);
+    for (int u = 0; u < kU; ++u) d[u] = ld_row(base + u * kWave + lane);
   } else {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int v = v0 + u * kWave + lane;
-      d[u] = (v < nvec) ? ld_row<NT>(base + u * kWave + lane)
+      d[u] = (v < nvec) ? ld_row(base + u * kWave + lane)
                         : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
     }
   }
 }
 
 // Loads one full trip (every vector exists): no predication.
-template <bool NT>
 __device__ __forceinline__ void load_full(const uint4* __restrict__ row, int v0, int lane,
                                           uint4 d[kU]) {
   const uint4* base = row + v0;
 #pragma unroll
-  for (int u = 0; u < kU; ++u) d[u] = ld_row<NT>(base + u * kWave + lane);
+  for (int u = 0; u < kU; ++u) d[u] = ld_row(base + u * kWave + lane);
 }
 
 // Spare load target: a claim past a row's full trips loads these 4 KB instead (data never
@@ -62,8 +53,7 @@ static __device__ uint4 g_spare_trip[kU * kWave];
 // so the waves of a row finish together. The wave that claims index nfull also streams the
 // row's partial trip, if there is one. consume(d, v0, maybe_last) takes a trip of
 // kU vectors per lane starting at vector v0; maybe_last is true where it may hold vector nvec - 1.
-// NT: nontemporal loads (see ld_row).
-template <int DEPTH, bool NT, typename F>
+template <int DEPTH, typename F>
 __device__ __forceinline__ void stream_row_claimed(const uint4* __restrict__ row, int nvec,
                                                    int lane, int* ctr, F&& consume) {
   constexpr int kStep = kU * kWave;
@@ -84,7 +74,7 @@ __device__ __forceinline__ void stream_row_claimed(const uint4* __restrict__ row
   for (int s = 0; s < DEPTH; ++s) {
     tc[s] = claim();
     partial |= tc[s] == nfull;
-    load_full<NT>(src(tc[s]), 0, lane, buf[s]);
+    load_full(src(tc[s]), 0, lane, buf[s]);
   }
   // Each wave's claims grow and its buffers hold them in claim order (tc[0] < tc[1] < ...):
   // once tc[0] is past the full trips, so are the others.
@@ -95,14 +85,14 @@ __device__ __forceinline__ void stream_row_claimed(const uint4* __restrict__ row
       if (tc[s] < nfull) consume(buf[s], tc[s] * kStep, tc[s] == nfull - 1);
       const int tn = __builtin_amdgcn_readfirstlane(tq);
       partial |= tn == nfull;
-      load_full<NT>(src(tn), 0, lane, buf[s]);
+      load_full(src(tn), 0, lane, buf[s]);
       __builtin_amdgcn_sched_barrier(0);  // the reload issues before the next trip's waits
       tc[s] = tn;
     }
   }
   if (partial && nfull * kStep < nvec) {
     uint4 d[kU];
-    load_trip<NT>(row, nfull * kStep, nvec, lane, d);
+    load_trip(row, nfull * kStep, nvec, lane, d);
     consume(d, nfull * kStep, true);
   }
 }

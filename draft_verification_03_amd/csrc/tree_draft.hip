@@ -150,12 +150,12 @@ __device__ __forceinline__ void load_trip2(const uint4* __restrict__ base, int v
                                            int lane, uint4 (&d)[kTv]) {
   if (v0 + kTripVec <= nv) {
 #pragma unroll
-    for (int u = 0; u < kTv; ++u) d[u] = ld_row<true>(base + v0 + u * kWave + lane);
+    for (int u = 0; u < kTv; ++u) d[u] = ld_row(base + v0 + u * kWave + lane);
   } else {
 #pragma unroll
     for (int u = 0; u < kTv; ++u) {
       const int v = v0 + u * kWave + lane;
-      d[u] = v < nv ? ld_row<true>(base + v) : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+      d[u] = v < nv ? ld_row(base + v) : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
     }
   }
 }

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kArgWaves * kWave) void tree_argmax_kernel(TreePara
   // earliest index of its maximum
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  stream_row_claimed<2, true>(rp, P.nvec, lane, &s_trip, [&](uint4* d, int v0, bool) {
+  stream_row_claimed<2>(rp, P.nvec, lane, &s_trip, [&](uint4* d, int v0, bool) {
     argmax_trip(d, v0, P.nvec, P.V, lane, bv, bi);
   });
   wave_argmax(bv, bi);
