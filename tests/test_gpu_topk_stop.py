@@ -44,6 +44,25 @@ def test_top_k_per_sequence_mix():
     check_chain(x, seed=62, label="per-sequence top-k mix")
 
 
+def test_second_capture_on_a_ragged_vocabulary():
+    """Rows with one outlying maximum (20.5 above the next logits, T = 1): the 10·T top-k
+    window below it holds fewer than K = 50 logits, so every row is captured a second time
+    from a lower bound of its 50th largest logit (flag TOPP_SLOW). V = 20001 ends in a
+    partial vector and a partial trip, and the largest logits after the outlier sit in that
+    tail, so the second capture's clamped tail loads decide the result."""
+    Bn, V, stride = 8, 20001, 20008
+    x = W.chain_inputs("c2", B=Bn, V=V, stride=stride, top_p=None)
+    for key in ("target", "draft"):
+        a = W.bf16_to_f32(x[key][:, :V])
+        a[:, 1234] = 27.5
+        a[:, V - 3:] = np.array([6.0, 6.5, 7.0], np.float32)
+        x[key][:, :V] = W.bf16_bits(a)
+    x = _with(x, top_k=np.full(Bn, 50, np.int32))
+    x["temperature"] = np.full(Bn, 1.0, np.float32)
+    o, g, _ = check_chain(x, seed=64, label="second capture, ragged V")
+    assert ((g["seq_flags"] & B.FLAG_TOPP_SLOW) != 0).all()
+
+
 def test_top_k_outside_the_capture_window_takes_the_exact_search():
     """A large K on peaked rows puts the K-th largest logit far below the capture window, so
     the row kernel falls back to the whole-row radix search (flag TOPP_SLOW)."""
